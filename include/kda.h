@@ -1,0 +1,130 @@
+/*
+ * kda.h - C ABI of the KDA (Kimi Delta Attention) operator library for AMD
+ * Instinct MI355X (gfx950).  Plain pointers and sizes only.
+ *
+ * The operator.  KDA is a delta-rule linear-attention recurrence with a
+ * channel-wise forget gate ("Kimi K3 technical report summary", section 1,
+ * pre-training table, KDA row; "Kimi K3 NPU Training", section "confirmed
+ * skeleton": unlike the scalar gate per head of Gated DeltaNet, KDA gates every
+ * channel).  For each sequence n and head h it carries a dk x dv matrix state S
+ * (rows: key channels, columns: value channels) and, for each token t in order,
+ *
+ *     S <- (I - beta_t k_t k_t^T) Diag(alpha_t) S + beta_t k_t v_t^T,
+ *     o_t = S^T q_t,          alpha_t = exp(log_alpha_t) (one gate per key channel).
+ *
+ * q and k are expected L2-normalised per (token, head) by the caller (the layer
+ * normalises them before the recurrence, "Kimi K3 NPU Training", section
+ * "confirmed skeleton", list item 3); the kernels take them as stored.  There is
+ * no 1/sqrt(dk) scale: fold any scale into q.
+ *
+ * Memory layouts (all dense, row-major, element strides as listed):
+ *   q, k       [T_total, H, dk]   token-major, heads inner (a fixed-length
+ *                                  [B, T, H, d] tensor is the same memory)
+ *   v          [T_total, H, dv]
+ *   log_alpha  [T_total, H, dk]   fp32, finite, <= 0
+ *   beta       [T_total, H]       fp32, in [0, 1]
+ *   o          [T_total, H, dv]   fp32 output
+ *   h0, hT     [N, H, dk, dv]     fp32 states
+ *   cu_seqlens [N + 1]            int32 offsets of packed sequences
+ *
+ * Ownership and threading.  The caller allocates and frees every buffer.  The
+ * library allocates nothing, keeps no mutable global state and is safe to call
+ * from several host threads.  All pointers except cu_seqlens-for-fixed-length,
+ * h0 and hT are required.  Device pointers must be 16-byte aligned.
+ *
+ * Asynchrony and errors.  Calls enqueue kernels on `stream` (a hipStream_t;
+ * NULL is the default stream) and return at once; results are valid once the
+ * stream is synchronised.  Argument errors are detected on the host before any
+ * launch and return a status with no side effects.  A launch failure reported
+ * by the HIP runtime returns KDA_ERR_LAUNCH.  Nothing is printed and no C++
+ * exception crosses this interface.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, negative size, misalignment */
+  KDA_ERR_UNSUPPORTED = 2,      /* valid but outside the compiled shape / dtype set */
+  KDA_ERR_LAUNCH = 3            /* the HIP runtime rejected a kernel launch */
+} kda_status;
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
+
+/*
+ * kda_chunk_fwd - chunkwise-parallel forward (training / prefill).
+ *
+ * Computes the recurrence above over packed sequences, parallel inside each
+ * chunk of `chunk_size` tokens and recurrent across chunks ("Kimi K3 technical
+ * report summary", section 1, pre-training table, KDA row: chunk-wise parallel
+ * form).  The state is reset at every sequence boundary of cu_seqlens (state
+ * reset at packed boundaries: "Kimi K3 NPU Training", section "TND is not a
+ * layout switch", item 2); chunks never span two sequences and the last chunk
+ * of a sequence may be partial.
+ *
+ *   q, k, v      device, qkv_dtype (KDA_DTYPE_BF16: bfloat16; KDA_DTYPE_F32: float)
+ *   log_alpha    device fp32 [total_tokens, n_heads, dk]
+ *   beta         device fp32 [total_tokens, n_heads]
+ *   h0           device fp32 [n_seqs, n_heads, dk, dv], or NULL for zero states
+ *   cu_seqlens   device int32 [n_seqs + 1] with cu[0] = 0, non-decreasing,
+ *                cu[n_seqs] = total_tokens; or NULL for n_seqs equal sequences of
+ *                total_tokens / n_seqs tokens (total_tokens must divide evenly)
+ *   o            device fp32 [total_tokens, n_heads, dv], written for every token
+ *   hT           device fp32 [n_seqs, n_heads, dk, dv], the state after each
+ *                sequence's last token (h0 for an empty sequence), or NULL to skip.
+ *                hT may alias h0 (in-place advance); o must not alias any input.
+ *
+ * Supported: dk, dv in {64, 128}; chunk_size in {16, 32, 64}; qkv_dtype F32 or
+ * BF16 (F32 supports chunk_size <= 32 when dk = dv = 128).  Other shapes return
+ * KDA_ERR_UNSUPPORTED.  Preconditions not checked on the device: the decay over
+ * any 16 consecutive tokens of a chunk satisfies sum(log_alpha) > -170 per
+ * channel; with BF16 inputs the state, values and intermediate chunk results
+ * stay below 6e4 in magnitude (fp16 matrix-core operands).
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* h0, const int32_t* cu_seqlens,
+                         int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                         int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
+                         void* stream);
+
+/*
+ * kda_recurrent_step - decode / draft-replay state update.
+ *
+ * For each of n_seqs sequences, applies n_tokens consecutive tokens to the
+ * state S_inout in place and writes one output per token (decode updates each
+ * head's fixed matrix state per token: "Kimi K3 NPU Training", section
+ * "confirmed skeleton", list item 4; replay rebuilds the state from cached
+ * projected inputs of accepted draft tokens instead of restoring snapshots:
+ * "Kimi K3 model structure (7)", section "KDA state rollback").  The state is
+ * read once and written once per call for any n_tokens.
+ *
+ *   q, k, v      device, qkv_dtype, [n_seqs, n_tokens, n_heads, dk | dv]
+ *   log_alpha    device fp32 [n_seqs, n_tokens, n_heads, dk]
+ *   beta         device fp32 [n_seqs, n_tokens, n_heads]
+ *   S_inout      device fp32 [n_seqs, n_heads, dk, dv], updated in place
+ *   o            device fp32 [n_seqs, n_tokens, n_heads, dv]; must not alias inputs
+ *
+ * Supported: dk, dv in {64, 128}; n_tokens in [1, 8]; qkv_dtype F32 or BF16.
+ */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, float* S_inout, int32_t n_seqs, int32_t n_tokens,
+                              int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype, float* o,
+                              void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,153 @@
+"""KDA (Kimi Delta Attention) operator for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/kda.h (libkda.so).  This module
+only checks and marshals arguments; every step of the computation runs in the
+HIP kernels.  PyTorch provides device memory and the current stream.
+
+    o, hT = chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size=64)
+    o = recurrent_step(q, k, v, log_alpha, beta, S)      # updates S in place
+
+Shapes: q, k [T, H, dk]; v [T, H, dv]; log_alpha [T, H, dk] fp32; beta [T, H]
+fp32; h0/hT [N, H, dk, dv] fp32; cu_seqlens [N+1] int32.  A leading batch
+dimension [B, T, ...] is accepted for fixed-length input.  recurrent_step takes
+tokens as [N, n, H, d] and S as [N, H, dk, dv].
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+__all__ = ["chunk_fwd", "recurrent_step", "KDAError"]
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+def _check(code: int, what: str):
+    if code == _lib.KDA_OK:
+        return
+    msg = "%s failed: %s" % (what, _lib.status_string(code))
+    if code in (_lib.KDA_ERR_INVALID_ARGUMENT, _lib.KDA_ERR_UNSUPPORTED):
+        raise ValueError(msg)
+    raise KDAError(msg)
+
+
+def _dtype_code(*ts):
+    dt = ts[0].dtype
+    for t in ts:
+        if t.dtype != dt:
+            raise ValueError("q, k, v must share one dtype, got %s" % [x.dtype for x in ts])
+    if dt == torch.bfloat16:
+        return _lib.KDA_DTYPE_BF16
+    if dt == torch.float32:
+        return _lib.KDA_DTYPE_F32
+    raise ValueError("q, k, v must be bfloat16 or float32, got %s" % dt)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: int = 64,
+              output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+              hT: Optional[torch.Tensor] = None):
+    """Chunkwise KDA forward; returns (o fp32 [T, H, dv], hT fp32 [N, H, dk, dv] or None)."""
+    lib = _lib.load()
+    batched = q.dim() == 4
+    if batched:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens requires packed [T, H, d] inputs")
+        B, T = q.shape[0], q.shape[1]
+        q, k, v = q.reshape(B * T, *q.shape[2:]), k.reshape(B * T, *k.shape[2:]), v.reshape(B * T, *v.shape[2:])
+        log_alpha = log_alpha.reshape(B * T, *log_alpha.shape[2:])
+        beta = beta.reshape(B * T, *beta.shape[2:])
+        n_seqs = B
+    dev = q.device
+    q, k, v = _dev(q, "q", device=dev), _dev(k, "k", device=dev), _dev(v, "v", device=dev)
+    code = _dtype_code(q, k, v)
+    log_alpha = _dev(log_alpha, "log_alpha", torch.float32, dev)
+    beta = _dev(beta, "beta", torch.float32, dev)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [T, H, dk] and v [T, H, dv]")
+    T_total, H, dk = q.shape
+    dv = v.shape[2]
+    if log_alpha.shape != q.shape or beta.shape != (T_total, H):
+        raise ValueError("expected log_alpha [T, H, dk] and beta [T, H]")
+    if cu_seqlens is not None:
+        cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        n_seqs = cu_seqlens.numel() - 1
+    elif not batched:
+        n_seqs = 1 if T_total > 0 else 0
+    h0 = _dev(h0, "h0", torch.float32, dev)
+    if h0 is not None and tuple(h0.shape) != (n_seqs, H, dk, dv):
+        raise ValueError("h0 must be [N, H, dk, dv] = %s" % ((n_seqs, H, dk, dv),))
+    if o is None:
+        o = torch.empty(T_total, H, dv, dtype=torch.float32, device=dev)
+    else:
+        o = _dev(o, "o", torch.float32, dev)
+        if tuple(o.shape) != (T_total, H, dv):
+            raise ValueError("o must be [T, H, dv]")
+    if output_final_state:
+        if hT is None:
+            hT = torch.empty(n_seqs, H, dk, dv, dtype=torch.float32, device=dev)
+        else:
+            hT = _dev(hT, "hT", torch.float32, dev)
+            if tuple(hT.shape) != (n_seqs, H, dk, dv):
+                raise ValueError("hT must be [N, H, dk, dv]")
+    else:
+        hT = None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+                           n_seqs, T_total, H, dk, dv, int(chunk_size), code, _ptr(o), _ptr(hT), stream)
+    _check(rc, "kda_chunk_fwd")
+    if batched:
+        o = o.view(B, T, H, dv)
+    return o, hT
+
+
+def recurrent_step(q, k, v, log_alpha, beta, S, o: Optional[torch.Tensor] = None):
+    """Decode / replay of n tokens per sequence: updates S [N, H, dk, dv] in place, returns o [N, n, H, dv]."""
+    lib = _lib.load()
+    dev = S.device
+    q, k, v = _dev(q, "q", device=dev), _dev(k, "k", device=dev), _dev(v, "v", device=dev)
+    code = _dtype_code(q, k, v)
+    log_alpha = _dev(log_alpha, "log_alpha", torch.float32, dev)
+    beta = _dev(beta, "beta", torch.float32, dev)
+    S = _dev(S, "S", torch.float32, dev)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [N, n, H, dk] and v [N, n, H, dv]")
+    N, n, H, dk = q.shape
+    dv = v.shape[3]
+    if log_alpha.shape != q.shape or beta.shape != (N, n, H) or tuple(S.shape) != (N, H, dk, dv):
+        raise ValueError("expected log_alpha [N, n, H, dk], beta [N, n, H], S [N, H, dk, dv]")
+    if o is None:
+        o = torch.empty(N, n, H, dv, dtype=torch.float32, device=dev)
+    else:
+        o = _dev(o, "o", torch.float32, dev)
+        if tuple(o.shape) != (N, n, H, dv):
+            raise ValueError("o must be [N, n, H, dv]")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                N, n, H, dk, dv, code, _ptr(o), stream)
+    _check(rc, "kda_recurrent_step")
+    return o

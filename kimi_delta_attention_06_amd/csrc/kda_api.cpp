@@ -1,0 +1,113 @@
+// C ABI of the KDA library: argument validation on the host, then dispatch.
+// Every argument error is caught here, before any launch, and leaves no side
+// effects.  See include/kda.h for the contract of each entry point.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kda_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dims_ok(int32_t d) { return d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* h0, const int32_t* cu_seqlens,
+                         int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                         int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
+                         void* stream) {
+  if (n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0 || chunk_size <= 0)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (qkv_dtype != KDA_DTYPE_F32 && qkv_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  if (n_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, h0, cu_seqlens, o, hT};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_INVALID_ARGUMENT;
+  int64_t seq_len = 0;
+  if (!cu_seqlens && n_seqs > 0) {
+    if (total_tokens % n_seqs != 0) return KDA_ERR_INVALID_ARGUMENT;
+    seq_len = total_tokens / n_seqs;
+  }
+  // o must not overlap the inputs it is computed from (checked on the byte ranges)
+  if (o && total_tokens > 0) {
+    const char* ob = (const char*)o;
+    const char* oe = ob + (size_t)total_tokens * n_heads * dv * sizeof(float);
+    const size_t esz = qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    struct R { const void* p; size_t n; } ins[] = {
+        {q, (size_t)total_tokens * n_heads * dk * esz}, {k, (size_t)total_tokens * n_heads * dk * esz},
+        {v, (size_t)total_tokens * n_heads * dv * esz}, {log_alpha, (size_t)total_tokens * n_heads * dk * 4},
+        {beta, (size_t)total_tokens * n_heads * 4}};
+    for (const R& r : ins) {
+      const char* b = (const char*)r.p;
+      if (b < oe && ob < b + r.n) return KDA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // cu_seqlens is int32
+  if (!dims_ok(dk) || !dims_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  const bool bf16 = qkv_dtype == KDA_DTYPE_BF16;
+  if (!kda::chunk_fwd_supported(dk, dv, chunk_size, bf16)) return KDA_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return KDA_OK;
+
+  kda::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0;
+  a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT;
+  a.n_seqs = n_seqs; a.n_heads = n_heads; a.dk = dk; a.dv = dv; a.chunk_size = chunk_size;
+  a.total_tokens = total_tokens; a.seq_len = seq_len; a.bf16 = bf16; a.stream = stream;
+  return kda::launch_chunk_fwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, float* S_inout, int32_t n_seqs, int32_t n_tokens,
+                              int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype, float* o,
+                              void* stream) {
+  if (n_seqs < 0 || n_tokens <= 0 || n_heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (qkv_dtype != KDA_DTYPE_F32 && qkv_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (n_seqs > 0 && (!q || !k || !v || !log_alpha || !beta || !S_inout || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, S_inout, o};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!dims_ok(dk) || !dims_ok(dv) || n_tokens > 8) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)n_seqs * n_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return KDA_OK;
+  // o must not overlap the state or the token inputs
+  {
+    const bool bf16 = qkv_dtype == KDA_DTYPE_BF16;
+    const size_t ntok = (size_t)n_seqs * n_tokens * n_heads;
+    const char* ob = (const char*)o;
+    const char* oe = ob + ntok * dv * sizeof(float);
+    const size_t esz = bf16 ? 2 : 4;
+    struct R { const void* p; size_t n; } ins[] = {
+        {q, ntok * dk * esz}, {k, ntok * dk * esz}, {v, ntok * dv * esz},
+        {log_alpha, ntok * dk * 4}, {beta, ntok * 4}, {S_inout, (size_t)n_seqs * n_heads * dk * dv * 4}};
+    for (const R& r : ins) {
+      const char* b = (const char*)r.p;
+      if (b < oe && ob < b + r.n) return KDA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  kda::RecurrentArgs a;
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S = S_inout; a.o = o;
+  a.n_seqs = n_seqs; a.n_tokens = n_tokens; a.n_heads = n_heads; a.dk = dk; a.dv = dv;
+  a.bf16 = qkv_dtype == KDA_DTYPE_BF16; a.stream = stream;
+  return kda::launch_recurrent_step(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+int32_t kda_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal launch interface between the C ABI (kda_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct RecurrentArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const float* beta;
+  float* S;
+  float* o;
+  int n_seqs, n_tokens, n_heads, dk, dv;
+  bool bf16;
+  void* stream;
+};
+
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const float* beta;
+  const float* h0;          // may be null
+  const int32_t* cu_seqlens; // may be null (equal lengths)
+  float* o;
+  float* hT;                // may be null
+  int n_seqs, n_heads, dk, dv, chunk_size;
+  int64_t total_tokens;
+  int64_t seq_len;          // used when cu_seqlens is null
+  bool bf16;
+  void* stream;
+};
+
+hipError_t launch_recurrent_step(const RecurrentArgs& a);
+hipError_t launch_chunk_fwd(const ChunkArgs& a);
+// True if the chunk kernel has an instantiation for these parameters.
+bool chunk_fwd_supported(int dk, int dv, int chunk_size, bool bf16);
+
+}  // namespace kda

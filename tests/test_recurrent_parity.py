@@ -1,0 +1,83 @@
+"""kda_recurrent_step (HIP) against the fp64 oracle.
+
+Workload: 256 sequences x 32 heads, dk = dv = 128, fp32 state ~ N(0, 0.02^2),
+one decode token or a replay of 8 draft tokens, bf16 q/k/v (q, k unit-norm),
+per-channel log_alpha = -softplus(N(0,1)), beta = sigmoid(N(0,1)).
+Tolerance (bf16 inputs): max |err| <= 2e-2 * RMS(reference), for o and for the
+updated state separately; fp32 inputs: max |err| <= 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def errs(x, ref):
+    x = x.detach().cpu().double().numpy() if isinstance(x, torch.Tensor) else x
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float(np.abs(x - ref).max()), rms
+
+
+def run_case(n_tokens, n_seqs=None, dk=128, dv=128, dtype=torch.bfloat16, seed=None):
+    import kimi_delta_attention_06_amd as kda
+    w = kda_inputs.DecodeWorkload("t", kda_inputs.DECODE_256x32.n_seqs, 32, dk, dv, 0.02, dtype, 1005)
+    inp = kda_inputs.make_decode_inputs(w, n_tokens, device="cuda", n_seqs=n_seqs, seed=seed)
+    S_host = inp["S"].cpu()
+    o = kda.recurrent_step(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.kda_recurrent_step(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S_host)
+    return o, inp["S"], o_ref, S_ref
+
+
+@pytest.mark.parametrize("n_tokens", [1, 8])
+def test_decode_workload_matches_oracle(n_tokens):
+    print("decode 256x32 d128 n_tokens=%d" % n_tokens, flush=True)
+    o, S, o_ref, S_ref = run_case(n_tokens)
+    eo, ro = errs(o, o_ref)
+    es, rs = errs(S, S_ref)
+    print("o max err %.3e rms %.3e | S max err %.3e rms %.3e" % (eo, ro, es, rs))
+    assert eo <= 2e-2 * ro and es <= 2e-2 * rs
+    # the decode path is fp32 end to end: far inside the bound
+    assert eo <= 1e-5 and es <= 1e-5
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("n_tokens", [1, 3, 8])
+def test_decode_shapes_fp32_inputs(dk, dv, n_tokens):
+    o, S, o_ref, S_ref = run_case(n_tokens, n_seqs=5, dk=dk, dv=dv, dtype=torch.float32, seed=77 + n_tokens)
+    eo, _ = errs(o, o_ref)
+    es, _ = errs(S, S_ref)
+    assert eo <= 1e-4 and es <= 1e-4
+
+
+def test_decode_is_deterministic():
+    import kimi_delta_attention_06_amd as kda
+    inp = kda_inputs.make_decode_inputs(kda_inputs.DECODE_256x32, 8, device="cuda", n_seqs=16)
+    S1 = inp["S"].clone()
+    S2 = inp["S"].clone()
+    o1 = kda.recurrent_step(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S1)
+    o2 = kda.recurrent_step(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_successive_steps_equal_one_replay():
+    """Eight 1-token steps == one 8-token replay (same state, same outputs up to rounding)."""
+    import kimi_delta_attention_06_amd as kda
+    inp = kda_inputs.make_decode_inputs(kda_inputs.DECODE_256x32, 8, device="cuda", n_seqs=8)
+    S_a = inp["S"].clone()
+    o_a = kda.recurrent_step(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S_a)
+    S_b = inp["S"].clone()
+    outs = []
+    for t in range(8):
+        sl = lambda x: x[:, t:t + 1].contiguous()
+        outs.append(kda.recurrent_step(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["log_alpha"]),
+                                       sl(inp["beta"]), S_b))
+    torch.cuda.synchronize()
+    o_b = torch.cat(outs, dim=1)
+    assert (o_a - o_b).abs().max().item() <= 1e-5
+    assert (S_a - S_b).abs().max().item() <= 1e-5
