@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA operator on one MI355X.
+
+Timed step: one kda_chunk_fwd pass over the Kimi-Linear-shaped KDA layer
+(B=4, T=4096, H=32, dk=dv=128, chunk 64, bf16 q/k/v, fp32 gates and state;
+seeded synthetic inputs already resident in HBM).  `value` is tokens/s of that
+pass (B*T tokens, all 32 heads).  In the same run the decode/replay state update
+(256 sequences x 32 heads, fp32 state, 1 and 8 tokens) is timed and reported
+under "decode" (HBM GB/s against the 8 TB/s peak), and the fp64 CPU oracle is
+timed on a bounded sample of the chunk workload ("cpu_baseline").
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
+METRIC = "KDA chunked-fwd tokens/s (H=32,d=128) + MFMA util; decode state-update GB/s"
+
+# Algorithmic model of one chunked-forward token-head (dk = dv = d = 128, chunk C = 64):
+# bytes: q, k, v bf16 (3 x 256) + log_alpha fp32 (512) + beta fp32 (4) + o fp32 (512)
+BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 512
+# flops: 6 d^2 for the state products (W S, Qg S, Kd^T U) + C (3 dk + 2 dv) for the
+# lower-triangular intra-chunk products (A, M, W, Ut, M U); the UT inverse is not counted.
+FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_kimi_linear_layer_pmc.txt")
+CHUNK_SRC = os.path.join(ROOT, "kimi_delta_attention_06_amd", "csrc", "kda_chunk.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch measured by rocprofv3 counters for the current kernel source, else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != src_hash(CHUNK_SRC):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per launch
+
+
+def cpu_baseline(inp, n_seqs):
+    """fp64 oracle on the first `n_seqs` sequences of the workload, all heads (whole sequences)."""
+    import oracle
+    T = int(sum(inp["lens"][:n_seqs]))
+    sl = slice(0, T)
+    args = [inp[x][sl].cpu() for x in ("q", "k", "v", "log_alpha", "beta")]
+    cu = inp["cu_seqlens"][: n_seqs + 1].cpu()
+    nthreads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.kda_fwd(*args, None, cu, n_threads=nthreads)
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": "fp64 token-by-token oracle on %d of %d sequences (%d tokens x 32 heads), "
+                      "%.2f s wall on %d threads (%s); same token count convention as value"
+                      % (n_seqs, len(inp["lens"]), T, dt, nthreads, cpu)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kda_inputs
+    import kimi_delta_attention_06_amd as kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- chunked forward, Kimi-Linear-shaped layer ----------------
+    w = kda_inputs.KIMI_LINEAR_LAYER
+    log("generating %s inputs" % w.name)
+    inp = kda_inputs.make_chunk_inputs(w, device=dev)
+    o = torch.empty(w.total_tokens, w.n_heads, w.dv, dtype=torch.float32, device=dev)
+    hT = torch.empty(w.n_seqs, w.n_heads, w.dk, w.dv, dtype=torch.float32, device=dev)
+
+    # fixed-length batch: pass [B, T, H, d] views (no cu_seqlens)
+    qb = inp["q"].view(w.n_seqs, -1, w.n_heads, w.dk)
+    kb = inp["k"].view(w.n_seqs, -1, w.n_heads, w.dk)
+    vb = inp["v"].view(w.n_seqs, -1, w.n_heads, w.dv)
+    lab = inp["log_alpha"].view(w.n_seqs, -1, w.n_heads, w.dk)
+    beb = inp["beta"].view(w.n_seqs, -1, w.n_heads)
+
+    def step():
+        kda.chunk_fwd(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size, o=o, hT=hT)
+
+    log("timing chunk_fwd: %d warmup + %d steps" % (args.warmup, args.steps))
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    ms = time_launches(step, args.steps, args.warmup, stream)
+    t_wall = time.perf_counter() - t_wall0
+    tokens = w.total_tokens
+    tok_s = tokens / (ms * 1e-3)
+    alg_bytes = tokens * w.n_heads * BYTES_PER_TOKEN_HEAD + w.n_seqs * w.n_heads * w.dk * w.dv * 4
+    alg_flops = tokens * w.n_heads * FLOPS_PER_TOKEN_HEAD
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    tflops = alg_flops / (ms * 1e-3) / 1e12
+    log("chunk_fwd: %.4f ms/launch, %.1f M tokens/s, %.0f GB/s algorithmic, %.1f TFLOP/s algorithmic"
+        % (ms, tok_s / 1e6, gbs, tflops))
+
+    # ---------------- decode / replay ----------------
+    dw = kda_inputs.DECODE_256x32
+    decode = {}
+    for n_tok in (1, 8):
+        d_inp = kda_inputs.make_decode_inputs(dw, n_tok, device=dev)
+        d_o = torch.empty(dw.n_seqs, n_tok, dw.n_heads, dw.dv, dtype=torch.float32, device=dev)
+
+        def dstep(d_inp=d_inp, d_o=d_o):
+            kda.recurrent_step(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["log_alpha"], d_inp["beta"], d_inp["S"],
+                               o=d_o)
+
+        d_ms = time_launches(dstep, max(args.steps, 20), args.warmup, stream)
+        d_bytes = 2 * dw.n_seqs * dw.n_heads * dw.dk * dw.dv * 4 + dw.n_seqs * n_tok * dw.n_heads * BYTES_PER_TOKEN_HEAD
+        d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
+        decode["n%d" % n_tok] = {"ms_per_step": round(d_ms, 5), "GB/s": round(d_gbs, 1),
+                                 "frac_of_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4),
+                                 "tokens_per_s": round(dw.n_seqs * n_tok / (d_ms * 1e-3), 1),
+                                 "bytes_per_step": d_bytes}
+        log("recurrent_step n=%d: %.4f ms, %.0f GB/s (%.1f%% of peak)" % (n_tok, d_ms, d_gbs, 100 * d_gbs / HBM_PEAK_GBS))
+        del d_inp, d_o
+
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.n_seqs, "seq_len": w.seq_len, "heads": w.n_heads,
+                   "dk": w.dk, "dv": w.dv, "chunk": w.chunk_size, "tokens": tokens,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
+                     "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": alg_flops},
+        "decode": decode,
+        "wall_s_timed_region": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

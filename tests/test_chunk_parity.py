@@ -109,3 +109,21 @@ def test_varlen_packed_workload():
     o, hT = run(inp)
     o_ref, h_ref = ref(inp)
     check_bf16(o, hT, o_ref, h_ref)
+
+
+@pytest.mark.slow
+def test_long_context_workload_two_heads():
+    """B=1, T=1,048,576, H=32, d=128, chunk 64: o and hT checked on 2 seeded heads."""
+    heads = kda_inputs.long_context_oracle_heads()
+    print("long context: T=1048576 H=32 d=128 C=64, oracle heads %s" % list(heads), flush=True)
+    inp = kda_inputs.make_chunk_inputs(kda_inputs.LONG_CONTEXT, device="cuda")
+    o, hT = run(inp)
+    hs = torch.as_tensor(heads, device="cuda")
+    sub = {k: inp[k].index_select(1, hs).cpu() for k in ("q", "k", "v", "log_alpha", "beta")}
+    o_s = o.index_select(1, hs).cpu()
+    h_s = hT.index_select(1, hs).cpu()
+    del inp, o, hT
+    torch.cuda.empty_cache()
+    print("  running the oracle on 2 heads x 1M tokens", flush=True)
+    o_ref, h_ref = oracle.kda_fwd(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], None, None)
+    check_bf16(o_s, h_s, o_ref, h_ref)
