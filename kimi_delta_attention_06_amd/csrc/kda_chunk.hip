@@ -16,27 +16,36 @@
 //   O      = (Q * e^G) S + M U
 //   S     <- Diag(e^{g_last}) S + (K * e^{g_last - G})^T U
 //
-// One workgroup (256 threads, 4 waves) owns one (sequence, head, dv-tile of BV
-// value columns) and walks the sequence's chunks in order, resetting the state at
-// the sequence start (packed-sequence state reset, "Kimi K3 NPU Training",
-// section "TND is not a layout switch", item 2).  The fp32 master state lives in
-// MFMA accumulator registers; a 16-bit copy in LDS feeds the next chunk's MFMAs.
+// One workgroup (512 threads, 8 waves, one per CU) owns one (sequence, head,
+// tile of BV value columns) and walks that sequence's chunks in order, resetting
+// the state at the sequence start (packed-sequence state reset, "Kimi K3 NPU
+// Training", section "TND is not a layout switch", item 2).  The fp32 master
+// state lives in MFMA accumulator registers; a 16-bit copy in LDS feeds the
+// next chunk's matrix products.  The next chunk's inputs are loaded into
+// registers while the current chunk is computed.
 //
-// Overflow-safe decay.  Every MFMA operand is a product of a value and an
-// exponential <= 1, except inside the 16x16 diagonal sub-blocks of A and M:
-//   * sub-block pair (R > I): left = X_r e^{c_r}, right = k_i e^{s_I - c_i}
-//     scaled by e^{G_{R-1} - G_I} (all <= 1), where c is the in-block cumulative
-//     decay, s_I the block total and G_J the cumulative decay at the end of block J;
-//   * diagonal sub-block R: left = X_r e^{c_r - s_R/2}, right = k_i e^{s_R/2 - c_i},
-//     each bounded by e^{|s_R|/2}; finite when a 16-token block decays by less
-//     than ~170 nats per channel (the documented precondition).
+// Gate stage in matrix-core layout.  Waves (R, p) own 16-row sub-block R and
+// half p of the key channels; lane l holds token 16R + (l & 15) and DK/8
+// consecutive channels.  That is the MFMA operand layout of the Gram products
+// (the channel order inside a k-step is the same permutation for both
+// operands), so the 16x16 diagonal sub-blocks of A and M are formed from
+// registers; the in-block cumulative decay is a DPP scan across the 16 lanes
+// of a row.  Each channel half gives a partial Gram tile; the two are summed
+// through LDS.
+//
+// Overflow-safe decay.  With c the in-block cumulative decay and s the block
+// total (both <= 0) every operand is a value times an exponential:
+//   * diagonal sub-block R: left X_r e^{c_r - s/2}, right k_i e^{s/2 - c_i},
+//     each bounded by e^{|s|/2}: finite while a 16-token block decays by less
+//     than ~170 nats per channel (the documented precondition);
+//   * sub-block pair R > I: left X_r e^{c_r} e^{G_{R-1} - G_I}, right
+//     k_i e^{s_I - c_i}, all <= 1 (G_J: cumulative decay at the end of block J).
 // Entries above the diagonal are removed with a select, never a multiply.
 //
 // Precision policies:
-//   Mixed (bf16 inputs): fp16 MFMA operands for all products except the diagonal
-//     sub-blocks of the Gram matrices, which use bf16 (range) and, for M, a hi/lo
-//     bf16 split (three MFMAs).  The diagonal of M (q_r . k_r) is applied to U in
-//     fp32 outside the MFMA.  Accumulation is fp32 throughout.
+//   Mixed (bf16 inputs): fp16 MFMA operands except the diagonal Gram sub-blocks,
+//     which use bf16 for range and, for M, a hi/lo bf16 split (three MFMAs).
+//     The diagonal of M (q_r . k_r) multiplies U in fp32 outside the MFMA.
 //   F32 (fp32 inputs): every product on the fp32 MFMA (16x16x4).
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
@@ -45,18 +54,15 @@ namespace kda {
 namespace chunkk {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;
-constexpr int NW = NT / kWave;
+constexpr int NW = 8;
+constexpr int NT = NW * kWave;
 
 enum class Prec { Mixed, F32 };
 
-// ---------------------------------------------------------------------------
-// MFMA operand types.  T: element type of the LDS operand matrices.
-// KS: k-extent of one MMA step; each lane holds KS/4 consecutive k values.
-// ---------------------------------------------------------------------------
 template <Prec P> struct Op;
 template <> struct Op<Prec::Mixed> {
   using T = _Float16;
@@ -68,17 +74,26 @@ template <> struct Op<Prec::F32> {
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// acc += A(16 x KS) * B(16 x KS)^T for one MMA step.  `a` and `b` point at the
-// lane's first k element (row (lane & 15), k offset (lane >> 4) * KS/4).
+template <typename T> __device__ __forceinline__ T cvt(float x);
+template <> __device__ __forceinline__ _Float16 cvt<_Float16>(float x) { return (_Float16)x; }
+template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
+
+__device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<half4*>(p) = half4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+// One MMA step from LDS operands: `a`, `b` point at the lane's first k element.
 __device__ __forceinline__ void mma_step(f32x4& acc, const _Float16* a, const _Float16* b) {
-  const half8 av = *reinterpret_cast<const half8*>(a);
-  const half8 bv = *reinterpret_cast<const half8*>(b);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8*>(a),
+                                                *reinterpret_cast<const half8*>(b), acc, 0, 0, 0);
 }
 __device__ __forceinline__ void mma_step(f32x4& acc, const float* a, const float* b) {
-  // The four fp32 MFMAs take k = 4*(lane>>4) + j, j = 0..3: a permutation of the
-  // 16 k values that is the same for A and B, so the product is unchanged.
+  // four fp32 MFMAs on k = 4*(lane>>4) + j: the same k permutation for A and B
   const float4 av = *reinterpret_cast<const float4*>(a);
   const float4 bv = *reinterpret_cast<const float4*>(b);
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
@@ -87,91 +102,122 @@ __device__ __forceinline__ void mma_step(f32x4& acc, const float* a, const float
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
 }
 
-// C[16x16] (+)= A[m0.., k0..k0+K) * B[n0.., same k]^T with row-major operands.
-template <typename T, int KS>
-__device__ __forceinline__ void mma_tile(f32x4& acc, const T* A, int lda, const T* B, int ldb, int nsteps) {
+// acc (+)= A[16 rows, K] * B[16 rows, K]^T, both row-major with k contiguous, K = NST*KS.
+template <typename T, int KS, int NST>
+__device__ __forceinline__ void mma_lds(f32x4& acc, const T* A, int lda, const T* B, int ldb) {
   const int l = lane_id();
   const T* a = A + (l & 15) * lda + (l >> 4) * (KS / 4);
   const T* b = B + (l & 15) * ldb + (l >> 4) * (KS / 4);
-  for (int s = 0; s < nsteps; ++s) mma_step(acc, a + s * KS, b + s * KS);
+#pragma unroll
+  for (int s = 0; s < NST; ++s) mma_step(acc, a + s * KS, b + s * KS);
 }
 
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-template <typename T> __device__ __forceinline__ T cvt(float x);
-template <> __device__ __forceinline__ _Float16 cvt<_Float16>(float x) { return (_Float16)x; }
-template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
-
-// Four consecutive elements from fp32.
-__device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
-  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<half4*>(p) = half4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+// inclusive prefix sum across the 16 lanes of each DPP row
+template <int N>
+__device__ __forceinline__ float shr16(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xf, 0xf, false));
 }
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+__device__ __forceinline__ float scan16(float x) {
+  x += shr16<1>(x);
+  x += shr16<2>(x);
+  x += shr16<4>(x);
+  x += shr16<8>(x);
+  return x;
 }
 
 constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------------------
-// LDS layout (bytes).  Region 1 is time-shared: the fp32 decay-scaled q/k
-// operands of the Gram stage, then the 16-bit operands of the WY and state
-// stages.  The other regions persist.
+// LDS layout (bytes).  Regions with disjoint lifetimes share memory:
+//   RB (gate stage -> off-diagonal Gram) with WM (WY -> state stage 1),
+//   PT (partial Gram tiles) with TB (T stage -> WY) and UT (state 1 -> 2).
 // ---------------------------------------------------------------------------
 template <int C, int DK, int BV, Prec P>
 struct Lay {
   using T = typename Op<P>::T;
   static constexpr int KS = Op<P>::KS, PD = Op<P>::PAD;
-  static constexpr int NB = C / 16;                      // 16-row sub-blocks per chunk
-  static constexpr int CK = ((C + KS - 1) / KS) * KS;    // token k-extent rounded to the MMA step
-  static constexpr int LDF = DK + 4;                     // fp32 [C][DK] rows
-  static constexpr int LDD = DK + PD;                    // T [*][DK] rows (k = channel)
-  static constexpr int LDC = CK + PD;                    // T [*][CK] rows (k = token)
-  static constexpr int LDA = C + 4;                      // fp32 [C][C] rows
-  static constexpr int NPAIR = NB * (NB - 1) / 2;
-  // region 1, Gram view
-  static constexpr size_t LQ = 0;
-  static constexpr size_t LK = LQ + al16(size_t(C) * LDF * 4);
-  static constexpr size_t RK = LK + al16(size_t(C) * LDF * 4);
-  static constexpr size_t END_G = RK + al16(size_t(C) * LDF * 4);
-  // region 1, WY / state view
-  static constexpr size_t QG = 0;                                          // [C][LDD]
-  static constexpr size_t KGT = QG + al16(size_t(C) * LDD * sizeof(T));    // [DK][LDC]
-  static constexpr size_t KDT = KGT + al16(size_t(DK) * LDC * sizeof(T));  // [DK][LDC]
-  static constexpr size_t WM = KDT + al16(size_t(DK) * LDC * sizeof(T));   // [C][LDD]
-  static constexpr size_t TB = WM + al16(size_t(C) * LDD * sizeof(T));     // [C][LDC]
-  static constexpr size_t UT = TB + al16(size_t(C) * LDC * sizeof(T));     // [BV][LDC]
-  static constexpr size_t VT = UT + al16(size_t(BV) * LDC * sizeof(T));    // [BV][LDC]
-  static constexpr size_t END_W = VT + al16(size_t(BV) * LDC * sizeof(T));
-  static constexpr size_t R1 = al16(cmax(END_G, END_W));
+  static constexpr int NB = C / 16;
+  static constexpr int CK = ((C + KS - 1) / KS) * KS;   // token k-extent rounded to the MMA step
+  static constexpr int LDD = DK + PD;                   // [*][DK] rows (k = channel)
+  static constexpr int LDC = CK + PD;                   // [*][CK] rows (k = token)
+  static constexpr int LDA = C + 4;                     // fp32 [C][C] rows
+  static constexpr int NPAIR = NB * (NB - 1) / 2;       // off-diagonal sub-block pairs
+  static constexpr int NPALL = NB * (NB + 1) / 2;
   // persistent
-  static constexpr size_t ST = R1;                                          // S^T [BV][LDD] (T)
-  static constexpr size_t AK = ST + al16(size_t(BV) * LDD * sizeof(T));      // A then T, fp32 [C][LDA]
-  static constexpr size_t AQ = AK + al16(size_t(C) * LDA * 4);              // strict M, T [C][LDC]
-  static constexpr size_t AO = AQ + al16(size_t(C) * LDC * sizeof(T));      // off-diag A tiles, T [NPAIR][16][16]
-  static constexpr size_t SB = AO + al16(size_t(NPAIR) * 256 * sizeof(T));  // block totals s [NB][DK] f32
-  static constexpr size_t BB = SB + al16(size_t(NB) * DK * 4);              // e^{s_J} [NB][DK]
-  static constexpr size_t PS = BB + al16(size_t(NB) * DK * 4);              // e^{-s_J/2} [NB][DK]
-  static constexpr size_t GM = PS + al16(size_t(NB) * DK * 4);              // e^{g_last} [DK]
-  static constexpr size_t BE = GM + al16(size_t(DK) * 4);                   // beta [C]
-  static constexpr size_t DQ = BE + al16(size_t(C) * 4);                    // q_r . k_r [C]
-  static constexpr size_t TOTAL = DQ + al16(size_t(C) * 4);
+  static constexpr size_t BH = 0;                                         // e^{s_J/2} [NB][DK] f32
+  static constexpr size_t ST = BH + al16(size_t(NB) * DK * 4);            // S^T [BV][LDD]
+  static constexpr size_t AK = ST + al16(size_t(BV) * LDD * sizeof(T));   // A then T, f32 [C][LDA]
+  static constexpr size_t AQ = AK + al16(size_t(C) * LDA * 4);            // strict M [C][LDC]
+  static constexpr size_t AO = AQ + al16(size_t(C) * LDC * sizeof(T));    // off-diag A tiles f32 [NPAIR][16][16]
+  static constexpr size_t BE = AO + al16(size_t(NPAIR) * 256 * 4);        // beta [C]
+  static constexpr size_t DQ = BE + al16(size_t(C) * 4);                  // q_r . k_r [C]
+  static constexpr size_t GM = DQ + al16(size_t(C) * 4);                  // e^{g_last} [DK]
+  // per chunk
+  static constexpr size_t QG = GM + al16(size_t(DK) * 4);                 // Qg [C][LDD]
+  static constexpr size_t KGT = QG + al16(size_t(C) * LDD * sizeof(T));   // Kg^T [DK][LDC]
+  static constexpr size_t KDT = KGT + al16(size_t(DK) * LDC * sizeof(T)); // Kd^T [DK][LDC]
+  static constexpr size_t VT = KDT + al16(size_t(DK) * LDC * sizeof(T));  // V^T [BV][LDC]
+  static constexpr size_t X1 = VT + al16(size_t(BV) * LDC * sizeof(T));   // RB | WM
+  static constexpr size_t RB = X1;                                        // right base [C][LDD]
+  static constexpr size_t WM = X1;                                        // W [C][LDD]
+  static constexpr size_t X2 = X1 + al16(size_t(C) * LDD * sizeof(T));    // PT | (TB, UT)
+  static constexpr size_t PT = X2;                                        // partial tiles f32 [2*NPALL][64][4]
+  static constexpr size_t TB = X2;                                        // T Diag(b) [C][LDC]
+  static constexpr size_t UT = TB + al16(size_t(C) * LDC * sizeof(T));    // U^T [BV][LDC]
+  static constexpr size_t X2END = cmax(PT + al16(size_t(2 * NPALL) * 1024),
+                                       UT + al16(size_t(BV) * LDC * sizeof(T)));
+  static constexpr size_t TOTAL = X2END;
 };
 
 template <int C, int DK, int BV, Prec P>
 constexpr size_t lds_bytes() { return Lay<C, DK, BV, P>::TOTAL; }
 
-// index of the off-diagonal block pair (R, I), R > I, in row-major lower order
+// index of the off-diagonal block pair (R, I), R > I
 __host__ __device__ constexpr int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }
 
-// bf16 hi/lo split of eight fp32 values (hi = RNE(x), lo = RNE(x - hi)).
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const __bf16 h = (__bf16)x[j];
     hi[j] = h;
     lo[j] = (__bf16)(x[j] - (float)h);
+  }
+}
+
+// Raw global loads of one lane's inputs, held in registers one chunk ahead.
+template <typename InT, int CPL>
+struct GateRegs {
+  static constexpr int QW = CPL * (int)sizeof(InT) / 16;  // 16-byte words for q or k
+  uint4 q[QW], k[QW];
+  float4 la[CPL / 4];
+  float b;
+};
+template <typename InT>
+struct VRegs {
+  static constexpr int VW = 8 * (int)sizeof(InT) / 16;
+  uint4 v[VW];
+};
+
+template <typename InT>
+__device__ __forceinline__ void unpack(const uint4* w, float* out, int n) {
+  if constexpr (sizeof(InT) == 2) {
+    for (int i = 0; i < n / 8; ++i) {
+      const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float2 f = bf16x2_to_f32x2(ww[j]);
+        out[8 * i + 2 * j] = f.x;
+        out[8 * i + 2 * j + 1] = f.y;
+      }
+    }
+  } else {
+    for (int i = 0; i < n / 4; ++i) {
+      out[4 * i] = __uint_as_float(w[i].x);
+      out[4 * i + 1] = __uint_as_float(w[i].y);
+      out[4 * i + 2] = __uint_as_float(w[i].z);
+      out[4 * i + 3] = __uint_as_float(w[i].w);
+    }
   }
 }
 
@@ -187,41 +233,39 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   using L = Lay<C, DK, BV, P>;
   using T = typename L::T;
   constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
-  constexpr int LDF = L::LDF, LDD = L::LDD, LDC = L::LDC, LDA = L::LDA;
+  constexpr int LDD = L::LDD, LDC = L::LDC, LDA = L::LDA;
   constexpr int NA = DK / 16;   // channel tiles
   constexpr int NJ = BV / 16;   // value-column tiles
-  constexpr int LPR = DK / 4;   // elementwise lanes per row (4 channels each)
-  constexpr int HB = C / 8;     // half-blocks of 8 rows
-  static_assert(C % 16 == 0 && C <= 64 && DK % 64 == 0 && BV % 16 == 0, "shape");
-  static_assert(NB <= NW, "one wave per diagonal sub-block");
-  static_assert(HB * LPR <= NT, "elementwise map");
+  constexpr int CPL = DK / 8;   // gate-stage channels per lane
+  constexpr int VPR = BV / 8;   // value loads: lanes per row (8 columns each)
+  static_assert(C % 16 == 0 && C <= 64 && (DK == 64 || DK == 128) && BV % 16 == 0 && BV <= 64, "shape");
+  static_assert(2 * NB <= NW, "two waves per 16-row sub-block");
+  static_assert(C * VPR <= NT, "value load map");
+  static_assert(P == Prec::F32 || CPL % 8 == 0, "k-step");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* sLQ = reinterpret_cast<float*>(smem + L::LQ);
-  float* sLK = reinterpret_cast<float*>(smem + L::LK);
-  float* sRK = reinterpret_cast<float*>(smem + L::RK);
-  T* sQG = reinterpret_cast<T*>(smem + L::QG);
-  T* sKGT = reinterpret_cast<T*>(smem + L::KGT);
-  T* sKDT = reinterpret_cast<T*>(smem + L::KDT);
-  T* sW = reinterpret_cast<T*>(smem + L::WM);
-  T* sTB = reinterpret_cast<T*>(smem + L::TB);
-  T* sUT = reinterpret_cast<T*>(smem + L::UT);
-  T* sVT = reinterpret_cast<T*>(smem + L::VT);
+  float* sBH = reinterpret_cast<float*>(smem + L::BH);
   T* sST = reinterpret_cast<T*>(smem + L::ST);
   float* sAK = reinterpret_cast<float*>(smem + L::AK);
   T* sAQ = reinterpret_cast<T*>(smem + L::AQ);
-  T* sAO = reinterpret_cast<T*>(smem + L::AO);
-  float* sSB = reinterpret_cast<float*>(smem + L::SB);
-  float* sBB = reinterpret_cast<float*>(smem + L::BB);
-  float* sPS = reinterpret_cast<float*>(smem + L::PS);
-  float* sGM = reinterpret_cast<float*>(smem + L::GM);
+  float* sAO = reinterpret_cast<float*>(smem + L::AO);
   float* sBE = reinterpret_cast<float*>(smem + L::BE);
   float* sDQ = reinterpret_cast<float*>(smem + L::DQ);
+  float* sGM = reinterpret_cast<float*>(smem + L::GM);
+  T* sQG = reinterpret_cast<T*>(smem + L::QG);
+  T* sKGT = reinterpret_cast<T*>(smem + L::KGT);
+  T* sKDT = reinterpret_cast<T*>(smem + L::KDT);
+  T* sVT = reinterpret_cast<T*>(smem + L::VT);
+  T* sRB = reinterpret_cast<T*>(smem + L::RB);
+  T* sW = reinterpret_cast<T*>(smem + L::WM);
+  float4* sPT = reinterpret_cast<float4*>(smem + L::PT);
+  T* sTB = reinterpret_cast<T*>(smem + L::TB);
+  T* sUT = reinterpret_cast<T*>(smem + L::UT);
 
-  // ---- which (sequence, head, value tile): dv tiles of one chain share an XCD
+  // ---- (sequence, head, value tile); the value tiles of one chain share an XCD
   const int ntile = DV / BV;
-  const int b = blockIdx.x;
-  const int xcd = b & 7, qd = b >> 3;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, qd = bid >> 3;
   const int tile = qd % ntile;
   const int chain = (qd / ntile) * 8 + xcd;
   if (chain >= n_chains) return;
@@ -237,15 +281,16 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   }
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave0 = __builtin_amdgcn_readfirstlane(tid / kWave);
+  int wave = wave0;
   const int l = lane_id();
+  const int lr = l & 15, lg = l >> 4;
 
-  // ---- one-time zero fill of the persistent triangular operands
+  // one-time zero fill of the persistent strictly-lower operands' upper parts
   for (int i = tid; i < C * LDA; i += NT) sAK[i] = 0.f;
   for (int i = tid; i < C * LDC; i += NT) sAQ[i] = cvt<T>(0.f);
 
-  // ---- state: fp32 master tiles (a, j) in MFMA accumulator layout.
-  // Tile id = a + NA*j, owned by wave id % NW, slot id / NW.
+  // ---- fp32 master state: tiles (a, j), id = a + NA*j owned by wave id % NW
   constexpr int S_SLOTS = (NA * NJ + NW - 1) / NW;
   f32x4 Sacc[S_SLOTS];
   const float* h0p = h0 ? h0 + (size_t)chain * DK * DV : nullptr;
@@ -256,434 +301,381 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     if (id < NA * NJ && h0p) {
       const int a = id % NA, j = id / NA;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Sacc[s][i] = h0p[(size_t)(16 * a + 4 * (l >> 4) + i) * DV + j0 + 16 * j + (l & 15)];
+      for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr];
     }
   }
-  // 16-bit copy S^T [BV][DK] for the MFMAs
   auto write_ST = [&]() {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
       if (id < NA * NJ) {
         const int a = id % NA, j = id / NA;
-        store4(sST + (16 * j + (l & 15)) * LDD + 16 * a + 4 * (l >> 4), Sacc[s][0], Sacc[s][1], Sacc[s][2],
-               Sacc[s][3]);
+        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
       }
     }
   };
   write_ST();
 
-  // ---- elementwise thread map: 8 rows x 4 channels per thread
-  const int e_hb = tid / LPR, e_cg = tid % LPR;
-  const bool e_act = e_hb < HB;
-  const int e_r0 = 8 * e_hb, e_c0 = 4 * e_cg;
-  const int e_R = e_hb >> 1;
-  const bool e_second = (e_hb & 1) != 0;
-  // value-tile map: 2 rows x 8 columns per thread
-  constexpr int VLPR = BV / 8;
-  const int v_p = tid / VLPR, v_c0 = 8 * (tid % VLPR);
-  const bool v_act = v_p < C / 2;
+  // ---- gate-stage map: waves (R = wave/2, p = wave%2) for 2*NB waves
+  const bool e_act = wave0 < 2 * NB;
+  const int ld_row = 16 * (e_act ? (wave0 >> 1) : 0) + lr;          // gate-stage load map
+  const int ld_cb = (wave0 & 1) * (DK / 2) + CPL * lg;
+  // value-load map: thread t < C*VPR loads 8 columns of one row
+  const bool v_act = tid < C * VPR;
+  const int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
 
-  // U / O tiles (R, j): id = R + NB*j, owned by wave id % NW
+  // U / O tiles (R, j): id = R + NB*j owned by wave id % NW
   constexpr int U_SLOTS = (NB * NJ + NW - 1) / NW;
 
   const int64_t nchunks = (t_end - t_begin + C - 1) / C;
+
+  using GR = GateRegs<InT, CPL>;
+  using VR = VRegs<InT>;
+  GR gnext;
+  VR vnext;
+  auto load_chunk = [&](int64_t cb, int Lc) {
+    if (e_act && ld_row < Lc) {
+      const size_t off = ((size_t)(cb + ld_row) * H + h) * DK + ld_cb;
+      const uint4* qp = reinterpret_cast<const uint4*>(q + off);
+      const uint4* kp = reinterpret_cast<const uint4*>(k + off);
+#pragma unroll
+      for (int i = 0; i < GR::QW; ++i) {
+        gnext.q[i] = qp[i];
+        gnext.k[i] = kp[i];
+      }
+      const float4* lp = reinterpret_cast<const float4*>(log_alpha + off);
+#pragma unroll
+      for (int i = 0; i < CPL / 4; ++i) gnext.la[i] = lp[i];
+      gnext.b = beta[(size_t)(cb + ld_row) * H + h];
+    } else {
+#pragma unroll
+      for (int i = 0; i < GR::QW; ++i) gnext.q[i] = gnext.k[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < CPL / 4; ++i) gnext.la[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      gnext.b = 0.f;
+    }
+    if (v_act && v_row < Lc) {
+      const uint4* vp = reinterpret_cast<const uint4*>(v + ((size_t)(cb + v_row) * H + h) * DV + j0 + v_c0);
+#pragma unroll
+      for (int i = 0; i < VR::VW; ++i) vnext.v[i] = vp[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < VR::VW; ++i) vnext.v[i] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto chunk_len = [&](int64_t ch) -> int {
+    const int64_t rem = t_end - (t_begin + ch * C);
+    return (int)(rem < C ? rem : C);
+  };
+  if (nchunks > 0) load_chunk(t_begin, chunk_len(0));
   __syncthreads();
 
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
-    const int Lc = (int)((t_end - c_begin) < C ? (t_end - c_begin) : C);
+    const int Lc = chunk_len(ch);
+    // Wave-dependent LDS offsets are cheap scalar arithmetic; an opaque copy of the
+    // wave index keeps the compiler from hoisting (and spilling) them out of the loop.
+    wave = wave0;
+    asm volatile("" : "+s"(wave));
+    const int eR = e_act ? (wave >> 1) : 0, ep = wave & 1;
+    const int e_row = 16 * eR + lr;
+    const int e_cb = ep * (DK / 2) + CPL * lg;
 
-    // ================= E1: load the chunk, in-block cumulative decay =================
-    float eq[8][4], ek[8][4], ec[8][4];
-    float vv[2][8];
+    // ================= gate stage, part a: decay, diagonal Gram sub-blocks =================
+    // qL = q e^{c - s/2}, kL = k e^{c - s/2}, kR = k e^{s/2 - c}; c: in-block cumulative
+    // decay, s: block total.  The next chunk's loads are issued once these registers
+    // have been consumed, so they are in flight for the rest of this chunk.
+    float qL[CPL], kL[CPL], kR[CPL];
+    f32x4 accQd = zero4(), accKd = zero4();
     {
+      float la[CPL];
+      unpack<InT>(gnext.q, qL, CPL);
+      unpack<InT>(gnext.k, kL, CPL);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = e_r0 + i;
-        const bool ok = e_act && r < Lc;
-        const size_t off = ((size_t)(c_begin + r) * H + h) * DK + e_c0;
-        if (ok) {
-          const float4 la = *reinterpret_cast<const float4*>(log_alpha + off);
-          ec[i][0] = la.x; ec[i][1] = la.y; ec[i][2] = la.z; ec[i][3] = la.w;
-          if constexpr (sizeof(InT) == 2) {
-            const uint2 qw = *reinterpret_cast<const uint2*>(q + off);
-            const uint2 kw = *reinterpret_cast<const uint2*>(k + off);
-            float2 a0 = bf16x2_to_f32x2(qw.x), a1 = bf16x2_to_f32x2(qw.y);
-            float2 b0 = bf16x2_to_f32x2(kw.x), b1 = bf16x2_to_f32x2(kw.y);
-            eq[i][0] = a0.x; eq[i][1] = a0.y; eq[i][2] = a1.x; eq[i][3] = a1.y;
-            ek[i][0] = b0.x; ek[i][1] = b0.y; ek[i][2] = b1.x; ek[i][3] = b1.y;
-          } else {
-            const float4 qa = *reinterpret_cast<const float4*>(q + off);
-            const float4 ka = *reinterpret_cast<const float4*>(k + off);
-            eq[i][0] = qa.x; eq[i][1] = qa.y; eq[i][2] = qa.z; eq[i][3] = qa.w;
-            ek[i][0] = ka.x; ek[i][1] = ka.y; ek[i][2] = ka.z; ek[i][3] = ka.w;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) ec[i][c] = eq[i][c] = ek[i][c] = 0.f;
-        }
+      for (int i = 0; i < CPL / 4; ++i) {
+        la[4 * i] = gnext.la[i].x; la[4 * i + 1] = gnext.la[i].y;
+        la[4 * i + 2] = gnext.la[i].z; la[4 * i + 3] = gnext.la[i].w;
       }
+      const float bcur = gnext.b;
+      if (v_act) {
+        float vv[8];
+        unpack<InT>(vnext.v, vv, 8);
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int r = 2 * v_p + rr;
-        const bool ok = v_act && r < Lc;
-        const size_t off = ((size_t)(c_begin + r) * H + h) * DV + j0 + v_c0;
-        if (ok) {
-          if constexpr (sizeof(InT) == 2) {
-            const uint4 w = *reinterpret_cast<const uint4*>(v + off);
-            float2 x0 = bf16x2_to_f32x2(w.x), x1 = bf16x2_to_f32x2(w.y), x2 = bf16x2_to_f32x2(w.z),
-                   x3 = bf16x2_to_f32x2(w.w);
-            vv[rr][0] = x0.x; vv[rr][1] = x0.y; vv[rr][2] = x1.x; vv[rr][3] = x1.y;
-            vv[rr][4] = x2.x; vv[rr][5] = x2.y; vv[rr][6] = x3.x; vv[rr][7] = x3.y;
-          } else {
-            const float4 w0 = *reinterpret_cast<const float4*>(v + off);
-            const float4 w1 = *reinterpret_cast<const float4*>(v + off + 4);
-            vv[rr][0] = w0.x; vv[rr][1] = w0.y; vv[rr][2] = w0.z; vv[rr][3] = w0.w;
-            vv[rr][4] = w1.x; vv[rr][5] = w1.y; vv[rr][6] = w1.z; vv[rr][7] = w1.w;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) vv[rr][c] = 0.f;
-        }
+        for (int c = 0; c < 8; ++c) sVT[(v_c0 + c) * LDC + v_row] = cvt<T>(vv[c]);
       }
-      // in-half cumulative sum, then combine the two halves of the 16-row block
-      float tot[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          acc += ec[i][c];
-          ec[i][c] = acc;
-        }
-        tot[c] = acc;
-      }
-      float s_blk[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float other = wave_xor(tot[c], LPR);
-        s_blk[c] = tot[c] + other;
-        if (e_second) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) ec[i][c] += other;
-        }
-      }
-      if (e_act && e_second)
-        *reinterpret_cast<float4*>(sSB + e_R * DK + e_c0) = make_float4(s_blk[0], s_blk[1], s_blk[2], s_blk[3]);
-      if (tid < C) sBE[tid] = tid < Lc ? beta[(size_t)(c_begin + tid) * H + h] : 0.f;
-
-      __syncthreads();  // ---------------------------------------------------------- B1
-
-      // ================= E2: decay-scaled operands (fp32) =================
+      if (ch + 1 < nchunks) load_chunk(c_begin + C, chunk_len(ch + 1));
       if (e_act) {
+        float rb[CPL];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float sR = sSB[e_R * DK + e_c0 + c];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float e = __expf(ec[i][c]);           // e^{c_r} <= 1
-            const float rgt = __expf(sR - ec[i][c]);    // e^{s_R - c_r} <= 1
-            ec[i][c] = rgt;
-            eq[i][c] *= e;
-            const float kk = ek[i][c];
-            ek[i][c] = kk * e;
-            // reuse: eq = q e^{c}, ek = k e^{c}, ec = e^{s-c} (k applied at the store)
-            ec[i][c] = kk * rgt;
-          }
+        for (int j = 0; j < CPL; ++j) {
+          const float c = scan16(la[j]);                     // in-block cumulative decay
+          const float s = __shfl(c, (l & ~15) | 15, kWave);  // block total
+          const float eL = __expf(c - 0.5f * s);             // <= e^{|s|/2}
+          const float eRt = __expf(0.5f * s - c);
+          const float bh = __expf(0.5f * s);                 // e^{s/2} <= 1
+          const float kk = kL[j];
+          qL[j] *= eL;
+          kL[j] = kk * eL;
+          kR[j] = kk * eRt;
+          rb[j] = kR[j] * bh;                                // right base k e^{s - c} <= |k|
+          if (lr == 15) sBH[eR * DK + e_cb + j] = bh;
         }
+        if (eR < NB - 1) {
+          T* dst = sRB + e_row * LDD + e_cb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = e_r0 + i;
-          *reinterpret_cast<float4*>(sLQ + r * LDF + e_c0) = make_float4(eq[i][0], eq[i][1], eq[i][2], eq[i][3]);
-          *reinterpret_cast<float4*>(sLK + r * LDF + e_c0) = make_float4(ek[i][0], ek[i][1], ek[i][2], ek[i][3]);
-          *reinterpret_cast<float4*>(sRK + r * LDF + e_c0) = make_float4(ec[i][0], ec[i][1], ec[i][2], ec[i][3]);
+          for (int j = 0; j < CPL; j += 4) store4(dst + j, rb[j], rb[j + 1], rb[j + 2], rb[j + 3]);
         }
-        // per-channel block vectors, written once (by the first half-block's threads)
-        if (e_hb == 0) {
-          float gl[4] = {1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-          for (int J = 0; J < NB; ++J) {
-            float bj[4], pj[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float sJ = sSB[J * DK + e_c0 + c];
-              bj[c] = __expf(sJ);
-              pj[c] = __expf(-0.5f * sJ);
-              gl[c] *= bj[c];
-            }
-            *reinterpret_cast<float4*>(sBB + J * DK + e_c0) = make_float4(bj[0], bj[1], bj[2], bj[3]);
-            *reinterpret_cast<float4*>(sPS + J * DK + e_c0) = make_float4(pj[0], pj[1], pj[2], pj[3]);
-          }
-          *reinterpret_cast<float4*>(sGM + e_c0) = make_float4(gl[0], gl[1], gl[2], gl[3]);
-        }
-      }
-    }
-    __syncthreads();  // ---------------------------------------------------------------- B2
-
-    // ================= Gram stage: A (key-key) and M (query-key) =================
-    {
-      const int row = l & 15;
-      const int kof = (l >> 4) * 8;  // Mixed: 8 k values per lane per 32-wide step
-      constexpr int NPAIRS_ALL = NB * (NB + 1) / 2;
-      // pairs enumerated as: diagonal R = 0..NB-1 first (one per wave), then off-diagonal
-      for (int pidx = wave; pidx < NPAIRS_ALL; pidx += NW) {
-        int R, I;
-        if (pidx < NB) {
-          R = I = pidx;
-        } else {
-          int o2 = pidx - NB;
-          R = 1;
-          while (o2 >= R) { o2 -= R; ++R; }
-          I = o2;
-        }
-        const bool diag = R == I;
-        f32x4 accQ = zero4(), accK = zero4();
-        const float* lq = sLQ + (16 * R + row) * LDF;
-        const float* lk = sLK + (16 * R + row) * LDF;
-        const float* rk = sRK + (16 * I + row) * LDF;
+        // diagonal Gram sub-block partials over this wave's channels
         if constexpr (P == Prec::Mixed) {
-          for (int ks = 0; ks < DK / 32; ++ks) {
-            const int c0 = ks * 32 + kof;
-            float a[8], ak[8], bq[8], f[8];
-            *reinterpret_cast<float4*>(&a[0]) = *reinterpret_cast<const float4*>(lq + c0);
-            *reinterpret_cast<float4*>(&a[4]) = *reinterpret_cast<const float4*>(lq + c0 + 4);
-            *reinterpret_cast<float4*>(&ak[0]) = *reinterpret_cast<const float4*>(lk + c0);
-            *reinterpret_cast<float4*>(&ak[4]) = *reinterpret_cast<const float4*>(lk + c0 + 4);
-            *reinterpret_cast<float4*>(&bq[0]) = *reinterpret_cast<const float4*>(rk + c0);
-            *reinterpret_cast<float4*>(&bq[4]) = *reinterpret_cast<const float4*>(rk + c0 + 4);
-            if (diag) {
-              *reinterpret_cast<float4*>(&f[0]) = *reinterpret_cast<const float4*>(sPS + R * DK + c0);
-              *reinterpret_cast<float4*>(&f[4]) = *reinterpret_cast<const float4*>(sPS + R * DK + c0 + 4);
 #pragma unroll
-              for (int j = 0; j < 8; ++j) { a[j] *= f[j]; ak[j] *= f[j]; bq[j] *= f[j]; }
-              bf16x8 ah, al, bh, bl, kh;
-              split8(a, ah, al);
-              split8(bq, bh, bl);
+          for (int t = 0; t < CPL / 8; ++t) {
+            bf16x8 ah, al, bh8, bl, kh;
+            split8(&qL[8 * t], ah, al);
+            split8(&kR[8 * t], bh8, bl);
 #pragma unroll
-              for (int j = 0; j < 8; ++j) kh[j] = (__bf16)ak[j];
-              accQ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, accQ, 0, 0, 0);
-              accQ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, accQ, 0, 0, 0);
-              accQ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, accQ, 0, 0, 0);
-              accK = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh, accK, 0, 0, 0);
-            } else {
+            for (int j = 0; j < 8; ++j) kh[j] = (__bf16)kL[8 * t + j];
+            accQd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh8, accQd, 0, 0, 0);
+            accQd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, accQd, 0, 0, 0);
+            accQd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh8, accQd, 0, 0, 0);
+            accKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh8, accKd, 0, 0, 0);
+          }
+        } else {
 #pragma unroll
-              for (int j = 0; j < 8; ++j) f[j] = 1.f;
-              for (int J = I + 1; J < R; ++J) {
-                float g[8];
-                *reinterpret_cast<float4*>(&g[0]) = *reinterpret_cast<const float4*>(sBB + J * DK + c0);
-                *reinterpret_cast<float4*>(&g[4]) = *reinterpret_cast<const float4*>(sBB + J * DK + c0 + 4);
+          for (int j = 0; j < CPL; ++j) {
+            accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j], kR[j], accQd, 0, 0, 0);
+            accKd = __builtin_amdgcn_mfma_f32_16x16x4f32(kL[j], kR[j], accKd, 0, 0, 0);
+          }
+        }
+        if (ep == 0 && lg == 0) sBE[e_row] = bcur;
+      }
+    }
+    __syncthreads();  // ------------------------------------------------------------- B_a
+
+    // ================= gate stage, part b: off-diagonal Gram, state operands =================
+    f32x4 accQo[NB > 1 ? NB - 1 : 1], accKo[NB > 1 ? NB - 1 : 1];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) f[j] *= g[j];
+    for (int I = 0; I < NB - 1; ++I) accQo[I] = accKo[I] = zero4();
+    if (e_act) {
+      // per channel: Qg = q e^{g} = qL bh_R prod_{J<R} bh_J^2 ; Kg likewise from kL ;
+      // Kd = k e^{g_last - g} = kR bh_R prod_{J>R} bh_J^2 (bh_J = e^{s_J/2} <= 1)
+#pragma unroll
+      for (int j4 = 0; j4 < CPL; j4 += 4) {
+        float pre[4], post[4];
+        const float4 own = *reinterpret_cast<const float4*>(sBH + eR * DK + e_cb + j4);
+        pre[0] = post[0] = own.x; pre[1] = post[1] = own.y; pre[2] = post[2] = own.z; pre[3] = post[3] = own.w;
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+          if (J == eR) continue;
+          const float4 b = *reinterpret_cast<const float4*>(sBH + J * DK + e_cb + j4);
+          const float b2[4] = {b.x * b.x, b.y * b.y, b.z * b.z, b.w * b.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (J < eR) pre[u] *= b2[u];
+            else post[u] *= b2[u];
+          }
+        }
+        store4(sQG + e_row * LDD + e_cb + j4, qL[j4] * pre[0], qL[j4 + 1] * pre[1], qL[j4 + 2] * pre[2],
+               qL[j4 + 3] * pre[3]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sKGT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kL[j4 + u] * pre[u]);
+          sKDT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kR[j4 + u] * post[u]);
+        }
+        if (eR == 0 && lr == 0) {
+          // e^{g_last} = prod_J bh_J^2: for block 0, post * bh_0 = prod_J bh_J^2
+          store4(sGM + e_cb + j4, post[0] * own.x, post[1] * own.y, post[2] * own.z, post[3] * own.w);
+        }
+      }
+      // off-diagonal pairs (eR, I), I < eR: left X e^{c} e^{G_{R-1} - G_I} = X{L} bh_R prod_{J=I+1}^{R-1} bh_J^2,
+      // right = the stored right base of block I
+      if (eR > 0) {
+        if constexpr (P == Prec::Mixed) {
+#pragma unroll
+          for (int t = 0; t < CPL / 8; ++t) {
+            float f[8];
+            {
+              const float4 b0 = *reinterpret_cast<const float4*>(sBH + eR * DK + e_cb + 8 * t);
+              const float4 b1 = *reinterpret_cast<const float4*>(sBH + eR * DK + e_cb + 8 * t + 4);
+              f[0] = b0.x; f[1] = b0.y; f[2] = b0.z; f[3] = b0.w; f[4] = b1.x; f[5] = b1.y; f[6] = b1.z; f[7] = b1.w;
+            }
+#pragma unroll
+            for (int I = NB - 2; I >= 0; --I) {
+              if (I < eR) {
+                if (I < eR - 1) {
+                  const float4 b0 = *reinterpret_cast<const float4*>(sBH + (I + 1) * DK + e_cb + 8 * t);
+                  const float4 b1 = *reinterpret_cast<const float4*>(sBH + (I + 1) * DK + e_cb + 8 * t + 4);
+                  f[0] *= b0.x * b0.x; f[1] *= b0.y * b0.y; f[2] *= b0.z * b0.z; f[3] *= b0.w * b0.w;
+                  f[4] *= b1.x * b1.x; f[5] *= b1.y * b1.y; f[6] *= b1.z * b1.z; f[7] *= b1.w * b1.w;
+                }
+                half8 aq, ak;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                  aq[j] = (_Float16)(qL[8 * t + j] * f[j]);
+                  ak[j] = (_Float16)(kL[8 * t + j] * f[j]);
+                }
+                const half8 b = *reinterpret_cast<const half8*>(sRB + (16 * I + lr) * LDD + e_cb + 8 * t);
+                accQo[I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, b, accQo[I], 0, 0, 0);
+                accKo[I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, b, accKo[I], 0, 0, 0);
               }
-              half8 ah, kh, bh;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                ah[j] = (_Float16)a[j];
-                kh[j] = (_Float16)ak[j];
-                bh[j] = (_Float16)(bq[j] * f[j]);
-              }
-              accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, accQ, 0, 0, 0);
-              accK = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, bh, accK, 0, 0, 0);
             }
           }
         } else {
-          const int kf = (l >> 4) * 4;
-          for (int ks = 0; ks < DK / 16; ++ks) {
-            const int c0 = ks * 16 + kf;
-            float4 a = *reinterpret_cast<const float4*>(lq + c0);
-            float4 ak = *reinterpret_cast<const float4*>(lk + c0);
-            float4 bq = *reinterpret_cast<const float4*>(rk + c0);
-            float4 f;
-            if (diag) {
-              f = *reinterpret_cast<const float4*>(sPS + R * DK + c0);
-              a.x *= f.x; a.y *= f.y; a.z *= f.z; a.w *= f.w;
-              ak.x *= f.x; ak.y *= f.y; ak.z *= f.z; ak.w *= f.w;
-            } else {
-              f = make_float4(1.f, 1.f, 1.f, 1.f);
-              for (int J = I + 1; J < R; ++J) {
-                const float4 g = *reinterpret_cast<const float4*>(sBB + J * DK + c0);
-                f.x *= g.x; f.y *= g.y; f.z *= g.z; f.w *= g.w;
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            float f = sBH[eR * DK + e_cb + j];
+#pragma unroll
+            for (int I = NB - 2; I >= 0; --I) {
+              if (I < eR) {
+                if (I < eR - 1) {
+                  const float b = sBH[(I + 1) * DK + e_cb + j];
+                  f *= b * b;
+                }
+                const float b = (float)sRB[(16 * I + lr) * LDD + e_cb + j];
+                accQo[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j] * f, b, accQo[I], 0, 0, 0);
+                accKo[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(kL[j] * f, b, accKo[I], 0, 0, 0);
               }
             }
-            bq.x *= f.x; bq.y *= f.y; bq.z *= f.z; bq.w *= f.w;
-            accQ = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, bq.x, accQ, 0, 0, 0);
-            accQ = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, bq.y, accQ, 0, 0, 0);
-            accQ = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, bq.z, accQ, 0, 0, 0);
-            accQ = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, bq.w, accQ, 0, 0, 0);
-            accK = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.x, bq.x, accK, 0, 0, 0);
-            accK = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.y, bq.y, accK, 0, 0, 0);
-            accK = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.z, bq.z, accK, 0, 0, 0);
-            accK = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.w, bq.w, accK, 0, 0, 0);
           }
         }
-        // write out: lane holds rows 4*(l>>4)+i, column l&15 of the 16x16 tile
-        const int ci = l & 15;
+      }
+      // channel half 1 hands its partial tiles to half 0
+      if (ep == 1) {
+        const int base = eR * (eR + 1);  // tiles of row block eR: diag Q, diag K, then (Q, K) per I < eR
+        sPT[(base + 0) * 64 + l] = make_float4(accQd[0], accQd[1], accQd[2], accQd[3]);
+        sPT[(base + 1) * 64 + l] = make_float4(accKd[0], accKd[1], accKd[2], accKd[3]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ri = 4 * (l >> 4) + i;
-          const int r = 16 * R + ri, cc = 16 * I + ci;
-          const bool strict = !diag || ri > ci;
-          const float akv = strict ? sBE[r] * accK[i] : 0.f;
-          sAK[r * LDA + cc] = akv;
-          sAQ[r * LDC + cc] = cvt<T>(strict ? accQ[i] : 0.f);
-          if (diag && ri == ci) sDQ[r] = accQ[i];
-          if (!diag) sAO[pair_index(R, I) * 256 + ri * 16 + ci] = cvt<T>(akv);
+        for (int I = 0; I < NB - 1; ++I) {
+          if (I < eR) {
+            sPT[(base + 2 + 2 * I) * 64 + l] = make_float4(accQo[I][0], accQo[I][1], accQo[I][2], accQo[I][3]);
+            sPT[(base + 3 + 2 * I) * 64 + l] = make_float4(accKo[I][0], accKo[I][1], accKo[I][2], accKo[I][3]);
+          }
         }
       }
     }
-    __syncthreads();  // ---------------------------------------------------------------- B3
+    __syncthreads();  // ------------------------------------------------------------- B_b
 
-    // ================= E3 (read) + UT inverse of the diagonal sub-blocks =================
-    float qg[8][4], kg[8][4], kd[8][4];
-    if (e_act) {
-      float es[4], ee[4];
+    // ================= Gram reduction and finalisation (waves (R, 0)) =================
+    if (e_act && ep == 0) {
+      const int base = eR * (eR + 1);
+      const float4 pq = sPT[(base + 0) * 64 + l], pk = sPT[(base + 1) * 64 + l];
+      accQd[0] += pq.x; accQd[1] += pq.y; accQd[2] += pq.z; accQd[3] += pq.w;
+      accKd[0] += pk.x; accKd[1] += pk.y; accKd[2] += pk.z; accKd[3] += pk.w;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float pre = 1.f, post = 1.f;
-        for (int J = 0; J < NB; ++J) {
-          const float bj = sBB[J * DK + e_c0 + c];
-          if (J < e_R) pre *= bj;
-          if (J > e_R) post *= bj;
-        }
-        es[c] = pre;   // e^{G_{R-1}}
-        ee[c] = post;  // e^{g_last - G_R}
+      for (int i = 0; i < 4; ++i) {
+        const int ri = 4 * lg + i;
+        const int r = 16 * eR + ri, cc = 16 * eR + lr;
+        const bool strict = ri > lr;
+        sAK[r * LDA + cc] = strict ? sBE[r] * accKd[i] : 0.f;
+        sAQ[r * LDC + cc] = cvt<T>(strict ? accQd[i] : 0.f);
+        if (ri == lr) sDQ[r] = accQd[i];
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = e_r0 + i;
-        const float4 a = *reinterpret_cast<const float4*>(sLQ + r * LDF + e_c0);
-        const float4 b2 = *reinterpret_cast<const float4*>(sLK + r * LDF + e_c0);
-        const float4 c2 = *reinterpret_cast<const float4*>(sRK + r * LDF + e_c0);
-        qg[i][0] = a.x * es[0]; qg[i][1] = a.y * es[1]; qg[i][2] = a.z * es[2]; qg[i][3] = a.w * es[3];
-        kg[i][0] = b2.x * es[0]; kg[i][1] = b2.y * es[1]; kg[i][2] = b2.z * es[2]; kg[i][3] = b2.w * es[3];
-        kd[i][0] = c2.x * ee[0]; kd[i][1] = c2.y * ee[1]; kd[i][2] = c2.z * ee[2]; kd[i][3] = c2.w * ee[3];
+      for (int I = 0; I < NB - 1; ++I) {
+        if (I < eR) {
+          const float4 xq = sPT[(base + 2 + 2 * I) * 64 + l], xk = sPT[(base + 3 + 2 * I) * 64 + l];
+          accQo[I][0] += xq.x; accQo[I][1] += xq.y; accQo[I][2] += xq.z; accQo[I][3] += xq.w;
+          accKo[I][0] += xk.x; accKo[I][1] += xk.y; accKo[I][2] += xk.z; accKo[I][3] += xk.w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ri = 4 * lg + i;
+            const int r = 16 * eR + ri, cc = 16 * I + lr;
+            const float akv = sBE[r] * accKo[I][i];
+            sAK[r * LDA + cc] = akv;
+            sAQ[r * LDC + cc] = cvt<T>(accQo[I][i]);
+            sAO[pair_index(eR, I) * 256 + ri * 16 + lr] = akv;
+          }
+        }
       }
     }
-    // diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution: wave R,
-    // lane (column j = l & 15, part p = l >> 4) keeps T[p + 4m][j], m = 0..3.
-    if (wave < NB) {
-      const int R = wave, j = l & 15, p = l >> 4;
-      const float* Ab = sAK + (16 * R) * LDA + 16 * R;
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // ------------------------------------------------------------- B_c
+
+    // ================= T = (I + A)^-1: diagonal sub-blocks =================
+    // wave 0: DPP row R = lane >> 4 inverts block R; lane column j = lane & 15 keeps T[.][j].
+    if (wave == 0) {
+      const int R = lg < NB ? lg : 0, j = lr;
+      float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float sum = 0.f;
+        const float* row = sAK + (16 * R + r) * LDA + 16 * R;
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int i = p + 4 * m;
-          if (i < r) sum += Ab[r * LDA + i] * x[m];
+        for (int i = 0; i < r; ++i) {
+          if (i & 1) s1 += row[i] * x[i];
+          else s0 += row[i] * x[i];
         }
-        sum += wave_xor(sum, 16);
-        sum += wave_xor(sum, 32);
-        const float t = (r == j ? 1.f : 0.f) - sum;
-        if ((r & 3) == p) x[r >> 2] = t;
+        x[r] = (r == j ? 1.f : 0.f) - (s0 + s1);
       }
-      // in place: every lane has read all of its block's A rows above
+      if (lg < NB) {
+        const float bj = sBE[16 * R + j];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int i = p + 4 * m;
-        sAK[(16 * R + i) * LDA + 16 * R + j] = x[m];
-        sTB[(16 * R + i) * LDC + 16 * R + j] = cvt<T>(x[m] * sBE[16 * R + j]);
+        for (int i = 0; i < 16; ++i) {
+          sAK[(16 * R + i) * LDA + 16 * R + j] = x[i];
+          sTB[(16 * R + i) * LDC + 16 * R + j] = cvt<T>(x[i] * bj);
+        }
+      }
+    } else {
+      // zero the strictly-upper tiles and the padded token columns of Tb (it shares memory)
+      for (int idx = tid - kWave; idx < C * CK; idx += NT - kWave) {
+        const int r = idx / CK, c = idx % CK;
+        if (c >= C || (c >> 4) > (r >> 4)) sTB[r * LDC + c] = cvt<T>(0.f);
+      }
+      if constexpr (CK > C) {
+        // padded token columns of Kg^T, Kd^T, V^T and U^T (U^T shares memory with the partials)
+        for (int idx = tid - kWave; idx < (2 * DK + 2 * BV) * (CK - C); idx += NT - kWave) {
+          const int rowi = idx / (CK - C), col = C + idx % (CK - C);
+          T* base = rowi < DK            ? sKGT + rowi * LDC
+                    : rowi < 2 * DK      ? sKDT + (rowi - DK) * LDC
+                    : rowi < 2 * DK + BV ? sVT + (rowi - 2 * DK) * LDC
+                                         : sUT + (rowi - 2 * DK - BV) * LDC;
+          base[col] = cvt<T>(0.f);
+        }
       }
     }
-    __syncthreads();  // ---------------------------------------------------------------- B4
+    __syncthreads();  // ------------------------------------------------------------- B_d
 
-    // ================= E3 (write) + off-diagonal blocks of T, level 1 =================
-    if (e_act) {
+    // ================= T: off-diagonal levels T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI =================
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        store4(sQG + (e_r0 + i) * LDD + e_c0, qg[i][0], qg[i][1], qg[i][2], qg[i][3]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        T* pg = sKGT + (e_c0 + c) * LDC + e_r0;
-        T* pd = sKDT + (e_c0 + c) * LDC + e_r0;
-        store4(pg, kg[0][c], kg[1][c], kg[2][c], kg[3][c]);
-        store4(pg + 4, kg[4][c], kg[5][c], kg[6][c], kg[7][c]);
-        store4(pd, kd[0][c], kd[1][c], kd[2][c], kd[3][c]);
-        store4(pd + 4, kd[4][c], kd[5][c], kd[6][c], kd[7][c]);
-      }
-    }
-    if (v_act) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        T* p = sVT + (v_c0 + c) * LDC + 2 * v_p;
-        p[0] = cvt<T>(vv[0][c]);
-        p[1] = cvt<T>(vv[1][c]);
-      }
-    }
-    if constexpr (NB > 1) {
-      // Tb lives in region 1: its strictly-upper 16x16 tiles hold stale bytes and
-      // are read by the MMA steps that round the token range up to KS.
-      for (int idx = tid; idx < C * C; idx += NT) {
-        const int r = idx / C, c = idx % C;
-        if ((c >> 4) > (r >> 4)) sTB[r * LDC + c] = cvt<T>(0.f);
-      }
-    }
-    if constexpr (CK > C) {
-      // zero the padded token columns [C, CK) of the token-k operands in region 1
-      for (int idx = tid; idx < (2 * DK + C + 2 * BV) * (CK - C); idx += NT) {
-        const int rowi = idx / (CK - C), col = C + idx % (CK - C);
-        T* base;
-        int rr;
-        if (rowi < DK) { base = sKGT; rr = rowi; }
-        else if (rowi < 2 * DK) { base = sKDT; rr = rowi - DK; }
-        else if (rowi < 2 * DK + C) { base = sTB; rr = rowi - 2 * DK; }
-        else if (rowi < 2 * DK + C + BV) { base = sUT; rr = rowi - 2 * DK - C; }
-        else { base = sVT; rr = rowi - 2 * DK - C - BV; }
-        base[rr * LDC + col] = cvt<T>(0.f);
-      }
-    }
-    // off-diagonal blocks: T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI, level d = R - I
     for (int d = 1; d < NB; ++d) {
       const int R = d + wave, I = wave;
       if (R < NB) {
         f32x4 X = zero4();
-        const int kq = 4 * (l >> 4), nn = l & 15, mm = l & 15;
+        const int kq = 4 * lg;
         for (int J = I; J < R; ++J) {
-          const T* Aj = sAO + pair_index(R, J) * 256;
-          float a4[4], b4[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            a4[jj] = (float)Aj[mm * 16 + kq + jj];
-            b4[jj] = sAK[(16 * J + kq + jj) * LDA + 16 * I + nn];
-          }
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) X = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[jj], b4[jj], X, 0, 0, 0);
+          const float4 a = *reinterpret_cast<const float4*>(sAO + pair_index(R, J) * 256 + lr * 16 + kq);
+          const float* tj = sAK + (16 * J + kq) * LDA + 16 * I + lr;
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, tj[0], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, tj[LDA], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, tj[2 * LDA], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, tj[3 * LDA], X, 0, 0, 0);
         }
-        // Y = T_RR X ; the accumulator layout of X is the B operand layout (k = 4(l>>4)+i)
+        // the accumulator layout of X is the B-operand layout (k = 4*(lane>>4) + i)
         f32x4 Y = zero4();
-        const float4 tr = *reinterpret_cast<const float4*>(sAK + (16 * R + mm) * LDA + 16 * R + kq);
+        const float4 tr = *reinterpret_cast<const float4*>(sAK + (16 * R + lr) * LDA + 16 * R + kq);
         Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.x, X[0], Y, 0, 0, 0);
         Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.y, X[1], Y, 0, 0, 0);
         Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.z, X[2], Y, 0, 0, 0);
         Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.w, X[3], Y, 0, 0, 0);
-        const float bcol = sBE[16 * I + nn];
+        const float bcol = sBE[16 * I + lr];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * R + kq + i;
-          sAK[r * LDA + 16 * I + nn] = -Y[i];
-          sTB[r * LDC + 16 * I + nn] = cvt<T>(-Y[i] * bcol);
+          sAK[r * LDA + 16 * I + lr] = -Y[i];
+          sTB[r * LDC + 16 * I + lr] = cvt<T>(-Y[i] * bcol);
         }
       }
-      __syncthreads();  // ------------------------------------------------------ B5 (per level)
+      __syncthreads();  // --------------------------------------------------- B_e (per level)
     }
-    if (NB == 1) __syncthreads();
 
-    // ================= WY stage: W^T = Kg^T Tb^T ; Ut = Tb V =================
-    {
+    // ================= WY: W^T = Kg^T Tb^T ; Ut = Tb V =================
 #pragma unroll
-      for (int s = 0; s < (NA * NB + NW - 1) / NW; ++s) {
-        const int id = wave + NW * s;
-        if (id < NA * NB) {
-          const int a = id % NA, R = id / NA;
-          f32x4 acc = zero4();
-          const int nst = (16 * R + 16 + KS - 1) / KS;
-          mma_tile<T, KS>(acc, sKGT + 16 * a * LDC, LDC, sTB + 16 * R * LDC, LDC, nst);
-          // acc rows = channels 16a + 4(l>>4) + i, column = token 16R + (l&15)
-          store4(sW + (16 * R + (l & 15)) * LDD + 16 * a + 4 * (l >> 4), acc[0], acc[1], acc[2], acc[3]);
-        }
+    for (int s = 0; s < (NA * NB + NW - 1) / NW; ++s) {
+      const int id = wave + NW * s;
+      if (id < NA * NB) {
+        const int a = id % NA, R = id / NA;
+        f32x4 acc = zero4();
+        mma_lds<T, KS, CK / KS>(acc, sKGT + 16 * a * LDC, LDC, sTB + 16 * R * LDC, LDC);
+        // rows = channels 16a + 4*lg + i, column = token 16R + lr
+        store4(sW + (16 * R + lr) * LDD + 16 * a + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
       }
     }
     f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
@@ -694,11 +686,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       Oacc[s] = zero4();
       if (id < NB * NJ) {
         const int R = id % NB, j = id / NB;
-        const int nst = (16 * R + 16 + KS - 1) / KS;
-        mma_tile<T, KS>(Uacc[s], sTB + 16 * R * LDC, LDC, sVT + 16 * j * LDC, LDC, nst);
+        mma_lds<T, KS, CK / KS>(Uacc[s], sTB + 16 * R * LDC, LDC, sVT + 16 * j * LDC, LDC);
       }
     }
-    __syncthreads();  // ---------------------------------------------------------------- B6
+    __syncthreads();  // ------------------------------------------------------------- B_f
 
     // ================= state stage 1: U = Ut - W S ; O = Qg S =================
 #pragma unroll
@@ -707,16 +698,14 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if (id < NB * NJ) {
         const int R = id % NB, j = id / NB;
         f32x4 ws = zero4();
-        mma_tile<T, KS>(ws, sW + 16 * R * LDD, LDD, sST + 16 * j * LDD, LDD, DK / KS);
-        mma_tile<T, KS>(Oacc[s], sQG + 16 * R * LDD, LDD, sST + 16 * j * LDD, LDD, DK / KS);
+        mma_lds<T, KS, DK / KS>(ws, sW + 16 * R * LDD, LDD, sST + 16 * j * LDD, LDD);
+        mma_lds<T, KS, DK / KS>(Oacc[s], sQG + 16 * R * LDD, LDD, sST + 16 * j * LDD, LDD);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Uacc[s][i] -= ws[i];
-        // U^T [BV][CK]: lane holds U[token 16R + 4(l>>4) + i][column 16j + (l&15)]
-        store4(sUT + (16 * j + (l & 15)) * LDC + 16 * R + 4 * (l >> 4), Uacc[s][0], Uacc[s][1], Uacc[s][2],
-               Uacc[s][3]);
+        store4(sUT + (16 * j + lr) * LDC + 16 * R + 4 * lg, Uacc[s][0], Uacc[s][1], Uacc[s][2], Uacc[s][3]);
       }
     }
-    __syncthreads();  // ---------------------------------------------------------------- B7
+    __syncthreads();  // ------------------------------------------------------------- B_g
 
     // ================= state stage 2: O += M U ; S <- e^{g} S + Kd^T U =================
 #pragma unroll
@@ -724,13 +713,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       const int id = wave + NW * s;
       if (id < NB * NJ) {
         const int R = id % NB, j = id / NB;
-        const int nst = (16 * R + 16 + KS - 1) / KS;
-        mma_tile<T, KS>(Oacc[s], sAQ + 16 * R * LDC, LDC, sUT + 16 * j * LDC, LDC, nst);
+        mma_lds<T, KS, CK / KS>(Oacc[s], sAQ + 16 * R * LDC, LDC, sUT + 16 * j * LDC, LDC);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * R + 4 * (l >> 4) + i;
+          const int r = 16 * R + 4 * lg + i;
           const float ov = Oacc[s][i] + sDQ[r] * Uacc[s][i];
-          if (r < Lc) o[((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + (l & 15)] = ov;
+          if (r < Lc) o[((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + lr] = ov;
         }
       }
     }
@@ -740,12 +728,13 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if (id < NA * NJ) {
         const int a = id % NA, j = id / NA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * (l >> 4) + i];
-        mma_tile<T, KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC, CK / KS);
+        for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
+        mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
       }
     }
     write_ST();
-    // the next chunk's first barrier (B1) orders these reads/writes against region 1 reuse
+    // The next chunk's gate stage writes only RB (shared with W, dead after B_g) and BH
+    // before its first barrier; everything read above is untouched until then.
   }
 
   if (hT) {
@@ -756,7 +745,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if (id < NA * NJ) {
         const int a = id % NA, j = id / NA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hp[(size_t)(16 * a + 4 * (l >> 4) + i) * DV + j0 + 16 * j + (l & 15)] = Sacc[s][i];
+        for (int i = 0; i < 4; ++i) hp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
       }
     }
   }
@@ -814,7 +803,7 @@ static hipError_t dispatch_c(const ChunkArgs& a) {
     if (a.chunk_size == 16) return dispatch_bv<16, DK, 64, P, InT>(a);
     if (a.chunk_size == 32) return dispatch_bv<32, DK, (DK == 128 ? 32 : 64), P, InT>(a);
     if constexpr (DK == 64) {
-      if (a.chunk_size == 64) return dispatch_bv<64, DK, 16, P, InT>(a);
+      if (a.chunk_size == 64) return dispatch_bv<64, DK, 32, P, InT>(a);
     }
   }
   return hipErrorInvalidValue;
