@@ -242,6 +242,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   static_assert(2 * NB <= NW, "two waves per 16-row sub-block");
   static_assert(C * VPR <= NT, "value load map");
   static_assert(P == Prec::F32 || CPL % 8 == 0, "k-step");
+  static_assert((2 * NB + L::NPAIR) * DK <= C * LDA, "factor table fits the A/T region");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* sBH = reinterpret_cast<float*>(smem + L::BH);
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
-      if (id < NA * NJ) {
+      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
         store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
       }
@@ -333,20 +334,28 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   using VR = VRegs<InT>;
   GR gnext;
   VR vnext;
+  // Global addressing: a chunk-uniform 64-bit base plus a 32-bit per-lane byte offset
+  // (the scalar-base form of the global loads and stores; no 64-bit lane arithmetic).
+  const uint32_t ld_off = (uint32_t)(ld_row * H * DK + ld_cb) * (uint32_t)sizeof(InT);
+  const uint32_t ld_off_f = (uint32_t)(ld_row * H * DK + ld_cb) * 4u;
+  const uint32_t ld_off_b = (uint32_t)(ld_row * H) * 4u;
+  const uint32_t v_off = (uint32_t)(v_row * H * DV + v_c0) * (uint32_t)sizeof(InT);
   auto load_chunk = [&](int64_t cb, int Lc) {
+    const size_t tok = (size_t)cb * H + h;
+    const char* qb = reinterpret_cast<const char*>(q + tok * DK);
+    const char* kb = reinterpret_cast<const char*>(k + tok * DK);
+    const char* lb = reinterpret_cast<const char*>(log_alpha + tok * DK);
+    const char* bb = reinterpret_cast<const char*>(beta + tok);
+    const char* vb = reinterpret_cast<const char*>(v + tok * DV + j0);
     if (e_act && ld_row < Lc) {
-      const size_t off = ((size_t)(cb + ld_row) * H + h) * DK + ld_cb;
-      const uint4* qp = reinterpret_cast<const uint4*>(q + off);
-      const uint4* kp = reinterpret_cast<const uint4*>(k + off);
 #pragma unroll
       for (int i = 0; i < GR::QW; ++i) {
-        gnext.q[i] = qp[i];
-        gnext.k[i] = kp[i];
+        gnext.q[i] = *reinterpret_cast<const uint4*>(qb + ld_off + 16 * i);
+        gnext.k[i] = *reinterpret_cast<const uint4*>(kb + ld_off + 16 * i);
       }
-      const float4* lp = reinterpret_cast<const float4*>(log_alpha + off);
 #pragma unroll
-      for (int i = 0; i < CPL / 4; ++i) gnext.la[i] = lp[i];
-      gnext.b = beta[(size_t)(cb + ld_row) * H + h];
+      for (int i = 0; i < CPL / 4; ++i) gnext.la[i] = *reinterpret_cast<const float4*>(lb + ld_off_f + 16 * i);
+      gnext.b = *reinterpret_cast<const float*>(bb + ld_off_b);
     } else {
 #pragma unroll
       for (int i = 0; i < GR::QW; ++i) gnext.q[i] = gnext.k[i] = make_uint4(0, 0, 0, 0);
@@ -355,9 +364,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       gnext.b = 0.f;
     }
     if (v_act && v_row < Lc) {
-      const uint4* vp = reinterpret_cast<const uint4*>(v + ((size_t)(cb + v_row) * H + h) * DV + j0 + v_c0);
 #pragma unroll
-      for (int i = 0; i < VR::VW; ++i) vnext.v[i] = vp[i];
+      for (int i = 0; i < VR::VW; ++i) vnext.v[i] = *reinterpret_cast<const uint4*>(vb + v_off + 16 * i);
     } else {
 #pragma unroll
       for (int i = 0; i < VR::VW; ++i) vnext.v[i] = make_uint4(0, 0, 0, 0);
@@ -368,6 +376,28 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     return (int)(rem < C ? rem : C);
   };
   if (nchunks > 0) load_chunk(t_begin, chunk_len(0));
+  // The outputs of chunk c are stored during chunk c+1, after its prefetch is
+  // issued: the loop-carried input registers force a wait on the memory counter
+  // (which also counts stores) once per chunk, and deferred stores are long done.
+  f32x4 Opend[U_SLOTS];
+  int64_t o_begin = 0;
+  int o_len = 0;
+  auto store_pending = [&]() {
+    char* ob = reinterpret_cast<char*>(o + ((size_t)o_begin * H + h) * DV + j0);
+#pragma unroll
+    for (int s = 0; s < U_SLOTS; ++s) {
+      const int id = wave + NW * s;
+      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
+        const int R = id % NB, j = id / NB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * R + 4 * lg + i;
+          const uint32_t off = (uint32_t)(r * H * DV + 16 * j + lr) * 4u;
+          if (r < o_len) *reinterpret_cast<float*>(ob + off) = Opend[s][i];
+        }
+      }
+    }
+  };
   __syncthreads();
 
   for (int64_t ch = 0; ch < nchunks; ++ch) {
@@ -404,21 +434,38 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         for (int c = 0; c < 8; ++c) sVT[(v_c0 + c) * LDC + v_row] = cvt<T>(vv[c]);
       }
       if (ch + 1 < nchunks) load_chunk(c_begin + C, chunk_len(ch + 1));
+      if (ch > 0) store_pending();
       if (e_act) {
-        float rb[CPL];
+        // in-block cumulative decay c and block total s, in log2 units; every phase
+        // runs across all channels so the DPP and permute latencies overlap
+        float cc[CPL], ss[CPL], rb[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) cc[j] = la[j] * 1.4426950408889634f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) cc[j] += shr16<1>(cc[j]);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) cc[j] += shr16<2>(cc[j]);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) cc[j] += shr16<4>(cc[j]);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) cc[j] += shr16<8>(cc[j]);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) ss[j] = __shfl(cc[j], (l & ~15) | 15, kWave);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-          const float c = scan16(la[j]);                     // in-block cumulative decay
-          const float s = __shfl(c, (l & ~15) | 15, kWave);  // block total
-          const float eL = __expf(c - 0.5f * s);             // <= e^{|s|/2}
-          const float eRt = __expf(0.5f * s - c);
-          const float bh = __expf(0.5f * s);                 // e^{s/2} <= 1
+          const float eL = __builtin_amdgcn_exp2f(cc[j] - 0.5f * ss[j]);  // e^{c - s/2} <= e^{|s|/2}
+          const float eRt = __builtin_amdgcn_exp2f(0.5f * ss[j] - cc[j]);
+          const float bh = __builtin_amdgcn_exp2f(0.5f * ss[j]);  // e^{s/2} <= 1 (below 2^-126 flushes to 0)
           const float kk = kL[j];
           qL[j] *= eL;
           kL[j] = kk * eL;
           kR[j] = kk * eRt;
-          rb[j] = kR[j] * bh;                                // right base k e^{s - c} <= |k|
-          if (lr == 15) sBH[eR * DK + e_cb + j] = bh;
+          rb[j] = kR[j] * bh;                                      // right base k e^{s - c} <= |k|
+          ss[j] = bh;
+        }
+        if (lr == 15) {
+#pragma unroll
+          for (int j = 0; j < CPL; j += 4) store4(sBH + eR * DK + e_cb + j, ss[j], ss[j + 1], ss[j + 2], ss[j + 3]);
         }
         if (eR < NB - 1) {
           T* dst = sRB + e_row * LDD + e_cb;
@@ -451,89 +498,96 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     }
     __syncthreads();  // ------------------------------------------------------------- B_a
 
+    // ================= per-channel block factors (once per chunk) =================
+    // With bh_J = e^{s_J/2} (<= 1), for row block R and channel c:
+    //   pre_R  = bh_R prod_{J<R} bh_J^2 = e^{G_{R-1} + s_R/2}      Qg = qL pre, Kg = kL pre
+    //   post_R = bh_R prod_{J>R} bh_J^2 = e^{g_last - G_R + s_R/2} Kd = kR post
+    //   f_RI   = bh_R prod_{I<J<R} bh_J^2                          off-diagonal left factor (I < R)
+    //   gamma  = prod_J bh_J^2 = e^{g_last}
+    // Stored in the A/T region, which is free from the previous chunk's WY stage until
+    // this chunk's Gram reduction.
+    float* sFT = sAK;
+    if (tid < DK) {
+      float bh[NB], b2[NB];
+#pragma unroll
+      for (int J = 0; J < NB; ++J) {
+        bh[J] = sBH[J * DK + tid];
+        b2[J] = bh[J] * bh[J];
+      }
+      float g = 1.f;
+#pragma unroll
+      for (int R = 0; R < NB; ++R) {
+        float pre = bh[R], post = bh[R];
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+          if (J < R) pre *= b2[J];
+          if (J > R) post *= b2[J];
+        }
+        sFT[R * DK + tid] = pre;
+        sFT[(NB + R) * DK + tid] = post;
+        float f = bh[R];
+#pragma unroll
+        for (int I = R - 1; I >= 0; --I) {
+          sFT[(2 * NB + pair_index(R, I)) * DK + tid] = f;
+          f *= b2[I];
+        }
+        g *= b2[R];
+      }
+      sGM[tid] = g;
+    }
+    __syncthreads();  // ------------------------------------------------------------- B_f1
+
     // ================= gate stage, part b: off-diagonal Gram, state operands =================
     f32x4 accQo[NB > 1 ? NB - 1 : 1], accKo[NB > 1 ? NB - 1 : 1];
 #pragma unroll
     for (int I = 0; I < NB - 1; ++I) accQo[I] = accKo[I] = zero4();
     if (e_act) {
-      // per channel: Qg = q e^{g} = qL bh_R prod_{J<R} bh_J^2 ; Kg likewise from kL ;
-      // Kd = k e^{g_last - g} = kR bh_R prod_{J>R} bh_J^2 (bh_J = e^{s_J/2} <= 1)
+      {
+        const float* fpre = sFT + eR * DK + e_cb;
+        const float* fpost = sFT + (NB + eR) * DK + e_cb;
 #pragma unroll
-      for (int j4 = 0; j4 < CPL; j4 += 4) {
-        float pre[4], post[4];
-        const float4 own = *reinterpret_cast<const float4*>(sBH + eR * DK + e_cb + j4);
-        pre[0] = post[0] = own.x; pre[1] = post[1] = own.y; pre[2] = post[2] = own.z; pre[3] = post[3] = own.w;
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-          if (J == eR) continue;
-          const float4 b = *reinterpret_cast<const float4*>(sBH + J * DK + e_cb + j4);
-          const float b2[4] = {b.x * b.x, b.y * b.y, b.z * b.z, b.w * b.w};
+        for (int j4 = 0; j4 < CPL; j4 += 4) {
+          const float4 pr = *reinterpret_cast<const float4*>(fpre + j4);
+          const float4 po = *reinterpret_cast<const float4*>(fpost + j4);
+          const float pre[4] = {pr.x, pr.y, pr.z, pr.w}, post[4] = {po.x, po.y, po.z, po.w};
+          store4(sQG + e_row * LDD + e_cb + j4, qL[j4] * pre[0], qL[j4 + 1] * pre[1], qL[j4 + 2] * pre[2],
+                 qL[j4 + 3] * pre[3]);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            if (J < eR) pre[u] *= b2[u];
-            else post[u] *= b2[u];
+            sKGT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kL[j4 + u] * pre[u]);
+            sKDT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kR[j4 + u] * post[u]);
           }
-        }
-        store4(sQG + e_row * LDD + e_cb + j4, qL[j4] * pre[0], qL[j4 + 1] * pre[1], qL[j4 + 2] * pre[2],
-               qL[j4 + 3] * pre[3]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          sKGT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kL[j4 + u] * pre[u]);
-          sKDT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kR[j4 + u] * post[u]);
-        }
-        if (eR == 0 && lr == 0) {
-          // e^{g_last} = prod_J bh_J^2: for block 0, post * bh_0 = prod_J bh_J^2
-          store4(sGM + e_cb + j4, post[0] * own.x, post[1] * own.y, post[2] * own.z, post[3] * own.w);
         }
       }
-      // off-diagonal pairs (eR, I), I < eR: left X e^{c} e^{G_{R-1} - G_I} = X{L} bh_R prod_{J=I+1}^{R-1} bh_J^2,
+      // off-diagonal pairs (eR, I), I < eR: left X e^{c} e^{G_{R-1} - G_I} = X{L} f_RI,
       // right = the stored right base of block I
-      if (eR > 0) {
-        if constexpr (P == Prec::Mixed) {
 #pragma unroll
-          for (int t = 0; t < CPL / 8; ++t) {
-            float f[8];
-            {
-              const float4 b0 = *reinterpret_cast<const float4*>(sBH + eR * DK + e_cb + 8 * t);
-              const float4 b1 = *reinterpret_cast<const float4*>(sBH + eR * DK + e_cb + 8 * t + 4);
-              f[0] = b0.x; f[1] = b0.y; f[2] = b0.z; f[3] = b0.w; f[4] = b1.x; f[5] = b1.y; f[6] = b1.z; f[7] = b1.w;
-            }
+      for (int I = 0; I < NB - 1; ++I) {
+        if (I < eR) {
+          const float* ff = sFT + (2 * NB + pair_index(eR, I)) * DK + e_cb;
+          if constexpr (P == Prec::Mixed) {
 #pragma unroll
-            for (int I = NB - 2; I >= 0; --I) {
-              if (I < eR) {
-                if (I < eR - 1) {
-                  const float4 b0 = *reinterpret_cast<const float4*>(sBH + (I + 1) * DK + e_cb + 8 * t);
-                  const float4 b1 = *reinterpret_cast<const float4*>(sBH + (I + 1) * DK + e_cb + 8 * t + 4);
-                  f[0] *= b0.x * b0.x; f[1] *= b0.y * b0.y; f[2] *= b0.z * b0.z; f[3] *= b0.w * b0.w;
-                  f[4] *= b1.x * b1.x; f[5] *= b1.y * b1.y; f[6] *= b1.z * b1.z; f[7] *= b1.w * b1.w;
-                }
-                half8 aq, ak;
+            for (int t = 0; t < CPL / 8; ++t) {
+              const float4 f0 = *reinterpret_cast<const float4*>(ff + 8 * t);
+              const float4 f1 = *reinterpret_cast<const float4*>(ff + 8 * t + 4);
+              const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+              half8 aq, ak;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                  aq[j] = (_Float16)(qL[8 * t + j] * f[j]);
-                  ak[j] = (_Float16)(kL[8 * t + j] * f[j]);
-                }
-                const half8 b = *reinterpret_cast<const half8*>(sRB + (16 * I + lr) * LDD + e_cb + 8 * t);
-                accQo[I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, b, accQo[I], 0, 0, 0);
-                accKo[I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, b, accKo[I], 0, 0, 0);
+              for (int j = 0; j < 8; ++j) {
+                aq[j] = (_Float16)(qL[8 * t + j] * f[j]);
+                ak[j] = (_Float16)(kL[8 * t + j] * f[j]);
               }
+              const half8 b = *reinterpret_cast<const half8*>(sRB + (16 * I + lr) * LDD + e_cb + 8 * t);
+              accQo[I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, b, accQo[I], 0, 0, 0);
+              accKo[I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, b, accKo[I], 0, 0, 0);
             }
-          }
-        } else {
+          } else {
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) {
-            float f = sBH[eR * DK + e_cb + j];
-#pragma unroll
-            for (int I = NB - 2; I >= 0; --I) {
-              if (I < eR) {
-                if (I < eR - 1) {
-                  const float b = sBH[(I + 1) * DK + e_cb + j];
-                  f *= b * b;
-                }
-                const float b = (float)sRB[(16 * I + lr) * LDD + e_cb + j];
-                accQo[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j] * f, b, accQo[I], 0, 0, 0);
-                accKo[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(kL[j] * f, b, accKo[I], 0, 0, 0);
-              }
+            for (int j = 0; j < CPL; ++j) {
+              const float f = ff[j];
+              const float b = (float)sRB[(16 * I + lr) * LDD + e_cb + j];
+              accQo[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j] * f, b, accQo[I], 0, 0, 0);
+              accKo[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(kL[j] * f, b, accKo[I], 0, 0, 0);
             }
           }
         }
@@ -557,6 +611,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     // ================= Gram reduction and finalisation (waves (R, 0)) =================
     if (e_act && ep == 0) {
       const int base = eR * (eR + 1);
+      const float4 bet4 = *reinterpret_cast<const float4*>(sBE + 16 * eR + 4 * lg);
+      const float bet[4] = {bet4.x, bet4.y, bet4.z, bet4.w};
       const float4 pq = sPT[(base + 0) * 64 + l], pk = sPT[(base + 1) * 64 + l];
       accQd[0] += pq.x; accQd[1] += pq.y; accQd[2] += pq.z; accQd[3] += pq.w;
       accKd[0] += pk.x; accKd[1] += pk.y; accKd[2] += pk.z; accKd[3] += pk.w;
@@ -565,7 +621,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         const int ri = 4 * lg + i;
         const int r = 16 * eR + ri, cc = 16 * eR + lr;
         const bool strict = ri > lr;
-        sAK[r * LDA + cc] = strict ? sBE[r] * accKd[i] : 0.f;
+        sAK[r * LDA + cc] = strict ? bet[i] * accKd[i] : 0.f;
         sAQ[r * LDC + cc] = cvt<T>(strict ? accQd[i] : 0.f);
         if (ri == lr) sDQ[r] = accQd[i];
       }
@@ -579,7 +635,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
           for (int i = 0; i < 4; ++i) {
             const int ri = 4 * lg + i;
             const int r = 16 * eR + ri, cc = 16 * I + lr;
-            const float akv = sBE[r] * accKo[I][i];
+            const float akv = bet[i] * accKo[I][i];
             sAK[r * LDA + cc] = akv;
             sAQ[r * LDC + cc] = cvt<T>(accQo[I][i]);
             sAO[pair_index(eR, I) * 256 + ri * 16 + lr] = akv;
@@ -596,14 +652,18 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        // T[r][j] = [r == j] - sum_{i<r} A[r][i] T[i][j]; four partial sums keep the chain short
         const float* row = sAK + (16 * R + r) * LDA + 16 * R;
-        float s0 = 0.f, s1 = 0.f;
+        float a[16];
 #pragma unroll
-        for (int i = 0; i < r; ++i) {
-          if (i & 1) s1 += row[i] * x[i];
-          else s0 += row[i] * x[i];
+        for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(row + 4 * i4);
+          a[4 * i4] = v4.x; a[4 * i4 + 1] = v4.y; a[4 * i4 + 2] = v4.z; a[4 * i4 + 3] = v4.w;
         }
-        x[r] = (r == j ? 1.f : 0.f) - (s0 + s1);
+        float sp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < r; ++i) sp[i & 3] += a[i] * x[i];
+        x[r] = (r == j ? 1.f : 0.f) - ((sp[0] + sp[1]) + (sp[2] + sp[3]));
       }
       if (lg < NB) {
         const float bj = sBE[16 * R + j];
@@ -670,7 +730,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
     for (int s = 0; s < (NA * NB + NW - 1) / NW; ++s) {
       const int id = wave + NW * s;
-      if (id < NA * NB) {
+      if ((NA * NB) % NW == 0 || id < NA * NB) {
         const int a = id % NA, R = id / NA;
         f32x4 acc = zero4();
         mma_lds<T, KS, CK / KS>(acc, sKGT + 16 * a * LDC, LDC, sTB + 16 * R * LDC, LDC);
@@ -684,7 +744,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       const int id = wave + NW * s;
       Uacc[s] = zero4();
       Oacc[s] = zero4();
-      if (id < NB * NJ) {
+      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         const int R = id % NB, j = id / NB;
         mma_lds<T, KS, CK / KS>(Uacc[s], sTB + 16 * R * LDC, LDC, sVT + 16 * j * LDC, LDC);
       }
@@ -695,7 +755,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
     for (int s = 0; s < U_SLOTS; ++s) {
       const int id = wave + NW * s;
-      if (id < NB * NJ) {
+      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         const int R = id % NB, j = id / NB;
         f32x4 ws = zero4();
         mma_lds<T, KS, DK / KS>(ws, sW + 16 * R * LDD, LDD, sST + 16 * j * LDD, LDD);
@@ -711,21 +771,17 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
     for (int s = 0; s < U_SLOTS; ++s) {
       const int id = wave + NW * s;
-      if (id < NB * NJ) {
+      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         const int R = id % NB, j = id / NB;
         mma_lds<T, KS, CK / KS>(Oacc[s], sAQ + 16 * R * LDC, LDC, sUT + 16 * j * LDC, LDC);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * R + 4 * lg + i;
-          const float ov = Oacc[s][i] + sDQ[r] * Uacc[s][i];
-          if (r < Lc) o[((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + lr] = ov;
-        }
+        for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + sDQ[16 * R + 4 * lg + i] * Uacc[s][i];
       }
     }
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
-      if (id < NA * NJ) {
+      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
 #pragma unroll
         for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
@@ -733,16 +789,19 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
     write_ST();
+    o_begin = c_begin;
+    o_len = Lc;
     // The next chunk's gate stage writes only RB (shared with W, dead after B_g) and BH
     // before its first barrier; everything read above is untouched until then.
   }
 
+  if (nchunks > 0) store_pending();
   if (hT) {
     float* hp = hT + (size_t)chain * DK * DV;
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
-      if (id < NA * NJ) {
+      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
 #pragma unroll
         for (int i = 0; i < 4; ++i) hp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
