@@ -332,50 +332,64 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 
   using GR = GateRegs<InT, CPL>;
   using VR = VRegs<InT>;
-  GR gnext;
-  VR vnext;
   // Global addressing: a chunk-uniform 64-bit base plus a 32-bit per-lane byte offset
   // (the scalar-base form of the global loads and stores; no 64-bit lane arithmetic).
   const uint32_t ld_off = (uint32_t)(ld_row * H * DK + ld_cb) * (uint32_t)sizeof(InT);
   const uint32_t ld_off_f = (uint32_t)(ld_row * H * DK + ld_cb) * 4u;
   const uint32_t ld_off_b = (uint32_t)(ld_row * H) * 4u;
   const uint32_t v_off = (uint32_t)(v_row * H * DV + v_c0) * (uint32_t)sizeof(InT);
-  auto load_chunk = [&](int64_t cb, int Lc) {
+  GR gbuf;
+  VR vbuf;
+  // The next chunk's inputs are loaded in three groups (q and k; the log-decay; v and
+  // beta) so that each group can be issued at a different point of the chunk.
+  auto load_qk = [&](int64_t cb, int Lc) {
     const size_t tok = (size_t)cb * H + h;
     const char* qb = reinterpret_cast<const char*>(q + tok * DK);
     const char* kb = reinterpret_cast<const char*>(k + tok * DK);
-    const char* lb = reinterpret_cast<const char*>(log_alpha + tok * DK);
-    const char* bb = reinterpret_cast<const char*>(beta + tok);
-    const char* vb = reinterpret_cast<const char*>(v + tok * DV + j0);
     if (e_act && ld_row < Lc) {
 #pragma unroll
       for (int i = 0; i < GR::QW; ++i) {
-        gnext.q[i] = *reinterpret_cast<const uint4*>(qb + ld_off + 16 * i);
-        gnext.k[i] = *reinterpret_cast<const uint4*>(kb + ld_off + 16 * i);
+        gbuf.q[i] = *reinterpret_cast<const uint4*>(qb + ld_off + 16 * i);
+        gbuf.k[i] = *reinterpret_cast<const uint4*>(kb + ld_off + 16 * i);
       }
-#pragma unroll
-      for (int i = 0; i < CPL / 4; ++i) gnext.la[i] = *reinterpret_cast<const float4*>(lb + ld_off_f + 16 * i);
-      gnext.b = *reinterpret_cast<const float*>(bb + ld_off_b);
     } else {
 #pragma unroll
-      for (int i = 0; i < GR::QW; ++i) gnext.q[i] = gnext.k[i] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < CPL / 4; ++i) gnext.la[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      gnext.b = 0.f;
+      for (int i = 0; i < GR::QW; ++i) gbuf.q[i] = gbuf.k[i] = make_uint4(0, 0, 0, 0);
     }
+  };
+  auto load_la = [&](int64_t cb, int Lc) {
+    const size_t tok = (size_t)cb * H + h;
+    const char* lb = reinterpret_cast<const char*>(log_alpha + tok * DK);
+    if (e_act && ld_row < Lc) {
+#pragma unroll
+      for (int i = 0; i < CPL / 4; ++i) gbuf.la[i] = *reinterpret_cast<const float4*>(lb + ld_off_f + 16 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPL / 4; ++i) gbuf.la[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto load_vb = [&](int64_t cb, int Lc) {
+    const size_t tok = (size_t)cb * H + h;
+    const char* bb = reinterpret_cast<const char*>(beta + tok);
+    const char* vb = reinterpret_cast<const char*>(v + tok * DV + j0);
+    gbuf.b = (e_act && ld_row < Lc) ? *reinterpret_cast<const float*>(bb + ld_off_b) : 0.f;
     if (v_act && v_row < Lc) {
 #pragma unroll
-      for (int i = 0; i < VR::VW; ++i) vnext.v[i] = *reinterpret_cast<const uint4*>(vb + v_off + 16 * i);
+      for (int i = 0; i < VR::VW; ++i) vbuf.v[i] = *reinterpret_cast<const uint4*>(vb + v_off + 16 * i);
     } else {
 #pragma unroll
-      for (int i = 0; i < VR::VW; ++i) vnext.v[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < VR::VW; ++i) vbuf.v[i] = make_uint4(0, 0, 0, 0);
     }
+  };
+  auto load_chunk = [&](int64_t cb, int Lc) {
+    load_qk(cb, Lc);
+    load_la(cb, Lc);
+    load_vb(cb, Lc);
   };
   auto chunk_len = [&](int64_t ch) -> int {
     const int64_t rem = t_end - (t_begin + ch * C);
     return (int)(rem < C ? rem : C);
   };
-  if (nchunks > 0) load_chunk(t_begin, chunk_len(0));
   // The outputs of chunk c are stored during chunk c+1, after its prefetch is
   // issued: the loop-carried input registers force a wait on the memory counter
   // (which also counts stores) once per chunk, and deferred stores are long done.
@@ -400,9 +414,14 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   };
   __syncthreads();
 
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
-    const int64_t c_begin = t_begin + ch * C;
-    const int Lc = chunk_len(ch);
+  // Software pipeline: the inputs of chunk c+1 are loaded at the start of iteration c
+  // and its gate stage (part a) runs at the end of iteration c, so loaded registers
+  // never cross the loop back-edge (only computed gate values do).
+  float qL[CPL], kL[CPL], kR[CPL];
+  f32x4 accQd, accKd;
+  auto gate_a = [&](int64_t ch) {
+    [[maybe_unused]] const int64_t c_begin = t_begin + ch * C;
+    [[maybe_unused]] const int Lc = chunk_len(ch);
     // Wave-dependent LDS offsets are cheap scalar arithmetic; an opaque copy of the
     // wave index keeps the compiler from hoisting (and spilling) them out of the loop.
     wave = wave0;
@@ -415,26 +434,24 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     // qL = q e^{c - s/2}, kL = k e^{c - s/2}, kR = k e^{s/2 - c}; c: in-block cumulative
     // decay, s: block total.  The next chunk's loads are issued once these registers
     // have been consumed, so they are in flight for the rest of this chunk.
-    float qL[CPL], kL[CPL], kR[CPL];
-    f32x4 accQd = zero4(), accKd = zero4();
+    accQd = zero4();
+    accKd = zero4();
     {
       float la[CPL];
-      unpack<InT>(gnext.q, qL, CPL);
-      unpack<InT>(gnext.k, kL, CPL);
+      unpack<InT>(gbuf.q, qL, CPL);
+      unpack<InT>(gbuf.k, kL, CPL);
 #pragma unroll
       for (int i = 0; i < CPL / 4; ++i) {
-        la[4 * i] = gnext.la[i].x; la[4 * i + 1] = gnext.la[i].y;
-        la[4 * i + 2] = gnext.la[i].z; la[4 * i + 3] = gnext.la[i].w;
+        la[4 * i] = gbuf.la[i].x; la[4 * i + 1] = gbuf.la[i].y;
+        la[4 * i + 2] = gbuf.la[i].z; la[4 * i + 3] = gbuf.la[i].w;
       }
-      const float bcur = gnext.b;
+      const float bcur = gbuf.b;
       if (v_act) {
         float vv[8];
-        unpack<InT>(vnext.v, vv, 8);
+        unpack<InT>(vbuf.v, vv, 8);
 #pragma unroll
         for (int c = 0; c < 8; ++c) sVT[(v_c0 + c) * LDC + v_row] = cvt<T>(vv[c]);
       }
-      if (ch + 1 < nchunks) load_chunk(c_begin + C, chunk_len(ch + 1));
-      if (ch > 0) store_pending();
       if (e_act) {
         // in-block cumulative decay c and block total s, in log2 units; every phase
         // runs across all channels so the DPP and permute latencies overlap
@@ -474,16 +491,17 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         }
         // diagonal Gram sub-block partials over this wave's channels
         if constexpr (P == Prec::Mixed) {
+          // M: fp32 matrix core (its diagonal carries q_r . k_r); A: bf16 (range), one MFMA per step
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j], kR[j], accQd, 0, 0, 0);
 #pragma unroll
           for (int t = 0; t < CPL / 8; ++t) {
-            bf16x8 ah, al, bh8, bl, kh;
-            split8(&qL[8 * t], ah, al);
-            split8(&kR[8 * t], bh8, bl);
+            bf16x8 kh, bh8;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) kh[j] = (__bf16)kL[8 * t + j];
-            accQd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh8, accQd, 0, 0, 0);
-            accQd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, accQd, 0, 0, 0);
-            accQd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh8, accQd, 0, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+              kh[j] = (__bf16)kL[8 * t + j];
+              bh8[j] = (__bf16)kR[8 * t + j];
+            }
             accKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh8, accKd, 0, 0, 0);
           }
         } else {
@@ -496,7 +514,25 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         if (ep == 0 && lg == 0) sBE[e_row] = bcur;
       }
     }
+  };
+  if (nchunks > 0) {
+    load_chunk(t_begin, chunk_len(0));
+    gate_a(0);
+  }
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    const int64_t c_begin = t_begin + ch * C;
+    const int Lc = chunk_len(ch);
+    // Wave-dependent LDS offsets are cheap scalar arithmetic; an opaque copy of the
+    // wave index keeps the compiler from hoisting (and spilling) them out of the loop.
+    wave = wave0;
+    asm volatile("" : "+s"(wave));
+    const int eR = e_act ? (wave >> 1) : 0, ep = wave & 1;
+    const int e_row = 16 * eR + lr;
+    const int e_cb = ep * (DK / 2) + CPL * lg;
+
     __syncthreads();  // ------------------------------------------------------------- B_a
+    if (ch + 1 < nchunks) load_qk(c_begin + C, chunk_len(ch + 1));
+    if (ch > 0) store_pending();
 
     // ================= per-channel block factors (once per chunk) =================
     // With bh_J = e^{s_J/2} (<= 1), for row block R and channel c:
@@ -607,6 +643,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_b
+    if (ch + 1 < nchunks) load_la(c_begin + C, chunk_len(ch + 1));
 
     // ================= Gram reduction and finalisation (waves (R, 0)) =================
     if (e_act && ep == 0) {
@@ -649,21 +686,25 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     // wave 0: DPP row R = lane >> 4 inverts block R; lane column j = lane & 15 keeps T[.][j].
     if (wave == 0) {
       const int R = lg < NB ? lg : 0, j = lr;
+      // right-looking forward substitution: once T[i][j] is final, fold it into every
+      // later row (15 - i independent updates), so the dependency chain is 16 steps
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // T[r][j] = [r == j] - sum_{i<r} A[r][i] T[i][j]; four partial sums keep the chain short
-        const float* row = sAK + (16 * R + r) * LDA + 16 * R;
-        float a[16];
+      for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+      // four column quarters keep at most ~60 matrix entries in registers
 #pragma unroll
-        for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(row + 4 * i4);
-          a[4 * i4] = v4.x; a[4 * i4 + 1] = v4.y; a[4 * i4 + 2] = v4.z; a[4 * i4 + 3] = v4.w;
+      for (int h4 = 0; h4 < 4; ++h4) {
+        float a[16][4];
+#pragma unroll
+        for (int r = 4 * h4 + 1; r < 16; ++r) {
+          const float4 v4 = *reinterpret_cast<const float4*>(sAK + (16 * R + r) * LDA + 16 * R + 4 * h4);
+          a[r][0] = v4.x; a[r][1] = v4.y; a[r][2] = v4.z; a[r][3] = v4.w;
         }
-        float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < r; ++i) sp[i & 3] += a[i] * x[i];
-        x[r] = (r == j ? 1.f : 0.f) - ((sp[0] + sp[1]) + (sp[2] + sp[3]));
+        for (int i = 4 * h4; i < 4 * h4 + 4 && i < 15; ++i) {
+#pragma unroll
+          for (int r = i + 1; r < 16; ++r) x[r] -= a[r][i - 4 * h4] * x[i];
+        }
       }
       if (lg < NB) {
         const float bj = sBE[16 * R + j];
@@ -692,25 +733,36 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_d
+    if (ch + 1 < nchunks) load_vb(c_begin + C, chunk_len(ch + 1));
 
     // ================= T: off-diagonal levels T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI =================
 #pragma unroll
     for (int d = 1; d < NB; ++d) {
       const int R = d + wave, I = wave;
       if (R < NB) {
-        f32x4 X = zero4();
         const int kq = 4 * lg;
-        for (int J = I; J < R; ++J) {
-          const float4 a = *reinterpret_cast<const float4*>(sAO + pair_index(R, J) * 256 + lr * 16 + kq);
+        // all operands of this level first (d terms), then the MFMA chain
+        float4 a[NB > 1 ? NB - 1 : 1];
+        float b[NB > 1 ? NB - 1 : 1][4];
+#pragma unroll
+        for (int t = 0; t < d; ++t) {
+          const int J = I + t;
+          a[t] = *reinterpret_cast<const float4*>(sAO + pair_index(R, J) * 256 + lr * 16 + kq);
           const float* tj = sAK + (16 * J + kq) * LDA + 16 * I + lr;
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, tj[0], X, 0, 0, 0);
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, tj[LDA], X, 0, 0, 0);
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, tj[2 * LDA], X, 0, 0, 0);
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, tj[3 * LDA], X, 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) b[t][u] = tj[u * LDA];
+        }
+        const float4 tr = *reinterpret_cast<const float4*>(sAK + (16 * R + lr) * LDA + 16 * R + kq);
+        f32x4 X = zero4();
+#pragma unroll
+        for (int t = 0; t < d; ++t) {
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].x, b[t][0], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].y, b[t][1], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].z, b[t][2], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].w, b[t][3], X, 0, 0, 0);
         }
         // the accumulator layout of X is the B-operand layout (k = 4*(lane>>4) + i)
         f32x4 Y = zero4();
-        const float4 tr = *reinterpret_cast<const float4*>(sAK + (16 * R + lr) * LDA + 16 * R + kq);
         Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.x, X[0], Y, 0, 0, 0);
         Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.y, X[1], Y, 0, 0, 0);
         Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.z, X[2], Y, 0, 0, 0);
@@ -793,6 +845,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     o_len = Lc;
     // The next chunk's gate stage writes only RB (shared with W, dead after B_g) and BH
     // before its first barrier; everything read above is untouched until then.
+      if (ch + 1 < nchunks) gate_a(ch + 1);
   }
 
   if (nchunks > 0) store_pending();
