@@ -9,8 +9,11 @@ pass (B*T tokens, all 32 heads).  In the same run the decode/replay state update
 under "decode" (HBM GB/s against the 8 TB/s peak), and the fp64 CPU oracle is
 timed on a bounded sample of the chunk workload ("cpu_baseline").
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-Prints exactly one JSON line on stdout.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
+Prints exactly one JSON line on stdout.  --copy-calibration adds three launches of a
+plain elementwise copy of known size (1 GiB read, 1 GiB written) after the timed
+region, so that hardware byte counters (FETCH_SIZE / WRITE_SIZE) taken over the
+same run can be scaled to bytes.
 """
 from __future__ import annotations
 
@@ -106,6 +109,20 @@ def cpu_baseline(inp, n_seqs):
                       % (n_seqs, len(inp["lens"]), T, dt, nthreads, cpu)}
 
 
+def copy_calibration(dev, nbytes=1 << 30):
+    """Three launches of a plain elementwise copy (y = -x, fp32) of `nbytes` each way."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 launches of neg over %d bytes (reads %d B, writes %d B each)" % (nbytes, nbytes, nbytes))
+    del src, dst
+    return {"kernel": "elementwise neg (fp32)", "read_bytes_per_launch": nbytes, "write_bytes_per_launch": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +130,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -203,6 +221,8 @@ def main():
         "decode": decode,
         "wall_s_timed_region": round(t_wall, 3),
     }
+    if args.copy_calibration:
+        result["copy_calibration"] = copy_calibration(dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)

@@ -22,7 +22,10 @@
 // Training", section "TND is not a layout switch", item 2).  The fp32 master
 // state lives in MFMA accumulator registers; a 16-bit copy in LDS feeds the
 // next chunk's matrix products.  The next chunk's inputs are loaded into
-// registers while the current chunk is computed.
+// registers while the current chunk is computed, in three groups issued after
+// different barriers (a single burst stalls instruction issue on the CU's memory
+// pipeline), and the next chunk's gate stage (part a) runs at the end of the
+// current iteration, so no loaded register is live across the loop back-edge.
 //
 // Gate stage in matrix-core layout.  Waves (R, p) own 16-row sub-block R and
 // half p of the key channels; lane l holds token 16R + (l & 15) and DK/8
@@ -43,8 +46,8 @@
 // Entries above the diagonal are removed with a select, never a multiply.
 //
 // Precision policies:
-//   Mixed (bf16 inputs): fp16 MFMA operands except the diagonal Gram sub-blocks,
-//     which use bf16 for range and, for M, a hi/lo bf16 split (three MFMAs).
+//   Mixed (bf16 inputs): fp16 MFMA operands except the diagonal Gram sub-blocks:
+//     A's in bf16 (range), M's on the fp32 matrix core (range and precision).
 //     The diagonal of M (q_r . k_r) multiplies U in fp32 outside the MFMA.
 //   F32 (fp32 inputs): every product on the fp32 MFMA (16x16x4).
 #include "kda_common.hpp"
@@ -175,15 +178,6 @@ constexpr size_t lds_bytes() { return Lay<C, DK, BV, P>::TOTAL; }
 
 // index of the off-diagonal block pair (R, I), R > I
 __host__ __device__ constexpr int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }
-
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)x[j];
-    hi[j] = h;
-    lo[j] = (__bf16)(x[j] - (float)h);
-  }
-}
 
 // Raw global loads of one lane's inputs, held in registers one chunk ahead.
 template <typename InT, int CPL>
