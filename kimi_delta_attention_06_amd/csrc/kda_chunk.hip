@@ -50,6 +50,8 @@
 //     A's in bf16 (range), M's on the fp32 matrix core (range and precision).
 //     The diagonal of M (q_r . k_r) multiplies U in fp32 outside the MFMA.
 //   F32 (fp32 inputs): every product on the fp32 MFMA (16x16x4).
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -116,6 +118,21 @@ __device__ __forceinline__ void mma_lds(f32x4& acc, const T* A, int lda, const T
 }
 
 // inclusive prefix sum across the 16 lanes of each DPP row
+// f(std::integral_constant<int, I>{}) for I = B .. E-1, each I a compile-time constant
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// every lane of a 16-lane row receives lane N of that row (DPP row_newbcast)
+template <int N>
+__device__ __forceinline__ float row_bcast16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+}
+
 template <int N>
 __device__ __forceinline__ float shr16(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xf, 0xf, false));
@@ -179,6 +196,17 @@ constexpr size_t lds_bytes() { return Lay<C, DK, BV, P>::TOTAL; }
 // index of the off-diagonal block pair (R, I), R > I
 __host__ __device__ constexpr int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }
 
+// Gate-stage row block of wave w (two waves per block, channel half = w & 1).  Waves w and
+// w + 4 share a SIMD; with four blocks they take blocks R and 3 - R, so each SIMD carries
+// the same number of off-diagonal sub-block pairs (block R has R of them).
+template <int NB>
+__device__ __forceinline__ int row_block_of(int w) {
+  return (NB == 4 && w >= 4) ? 5 - (w >> 1) : (w >> 1);
+}
+// The channel half whose wave inverts the diagonal block R of A (the other half finishes the
+// rest of the Gram reduction); chosen so the four inverting waves sit on four SIMDs.
+__device__ __forceinline__ int inv_half(int R) { return ((R >> 1) & 1) ^ 1; }
+
 // Raw global loads of one lane's inputs, held in registers one chunk ahead.
 template <typename InT, int CPL>
 struct GateRegs {
@@ -228,6 +256,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   using T = typename L::T;
   constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
   constexpr int LDD = L::LDD, LDC = L::LDC, LDA = L::LDA;
+  constexpr int NPAIR = L::NPAIR;
   constexpr int NA = DK / 16;   // channel tiles
   constexpr int NJ = BV / 16;   // value-column tiles
   constexpr int CPL = DK / 8;   // gate-stage channels per lane
@@ -236,7 +265,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   static_assert(2 * NB <= NW, "two waves per 16-row sub-block");
   static_assert(C * VPR <= NT, "value load map");
   static_assert(P == Prec::F32 || CPL % 8 == 0, "k-step");
-  static_assert((2 * NB + L::NPAIR) * DK <= C * LDA, "factor table fits the A/T region");
+  static_assert((2 * NB + NPAIR) * DK <= C * LDA, "factor table fits the A/T region");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* sBH = reinterpret_cast<float*>(smem + L::BH);
@@ -275,11 +304,24 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     t_end = t_begin + seq_len;
   }
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
   const int wave0 = __builtin_amdgcn_readfirstlane(tid / kWave);
   int wave = wave0;
-  const int l = lane_id();
-  const int lr = l & 15, lg = l >> 4;
+  int l = lane_id();
+  int lr = l & 15, lg = l >> 4;
+  // A lane index the compiler cannot see through: lane-derived addresses are recomputed
+  // where they are used instead of being held (or spilled) across the chunk loop.
+  auto fresh_lane = [&]() {
+    int x = lane_id();
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  auto refresh_lane = [&]() {
+    l = fresh_lane();
+    lr = l & 15;
+    lg = l >> 4;
+    tid = wave0 * kWave + l;
+  };
 
   // one-time zero fill of the persistent strictly-lower operands' upper parts
   for (int i = tid; i < C * LDA; i += NT) sAK[i] = 0.f;
@@ -313,11 +355,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 
   // ---- gate-stage map: waves (R = wave/2, p = wave%2) for 2*NB waves
   const bool e_act = wave0 < 2 * NB;
-  const int ld_row = 16 * (e_act ? (wave0 >> 1) : 0) + lr;          // gate-stage load map
-  const int ld_cb = (wave0 & 1) * (DK / 2) + CPL * lg;
+  // gate-stage load map: lane (r, g) of wave (R, p) loads row 16R + r, channels p*DK/2 + CPL*g ..
   // value-load map: thread t < C*VPR loads 8 columns of one row
   const bool v_act = tid < C * VPR;
-  const int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
+  int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
 
   // U / O tiles (R, j): id = R + NB*j owned by wave id % NW
   constexpr int U_SLOTS = (NB * NJ + NW - 1) / NW;
@@ -326,17 +367,21 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 
   using GR = GateRegs<InT, CPL>;
   using VR = VRegs<InT>;
-  // Global addressing: a chunk-uniform 64-bit base plus a 32-bit per-lane byte offset
+  // Global addressing: a chunk-uniform 64-bit base plus a 32-bit per-lane element offset
   // (the scalar-base form of the global loads and stores; no 64-bit lane arithmetic).
-  const uint32_t ld_off = (uint32_t)(ld_row * H * DK + ld_cb) * (uint32_t)sizeof(InT);
-  const uint32_t ld_off_f = (uint32_t)(ld_row * H * DK + ld_cb) * 4u;
-  const uint32_t ld_off_b = (uint32_t)(ld_row * H) * 4u;
-  const uint32_t v_off = (uint32_t)(v_row * H * DV + v_c0) * (uint32_t)sizeof(InT);
+  auto gate_map = [&](int& row, int& elem) {
+    const int x = fresh_lane();
+    row = 16 * (e_act ? row_block_of<NB>(wave0) : 0) + (x & 15);
+    elem = row * H * DK + (wave0 & 1) * (DK / 2) + CPL * (x >> 4);
+  };
   GR gbuf;
   VR vbuf;
   // The next chunk's inputs are loaded in three groups (q and k; the log-decay; v and
   // beta) so that each group can be issued at a different point of the chunk.
   auto load_qk = [&](int64_t cb, int Lc) {
+    int ld_row, el;
+    gate_map(ld_row, el);
+    const uint32_t ld_off = (uint32_t)el * (uint32_t)sizeof(InT);
     const size_t tok = (size_t)cb * H + h;
     const char* qb = reinterpret_cast<const char*>(q + tok * DK);
     const char* kb = reinterpret_cast<const char*>(k + tok * DK);
@@ -352,6 +397,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     }
   };
   auto load_la = [&](int64_t cb, int Lc) {
+    int ld_row, el;
+    gate_map(ld_row, el);
+    const uint32_t ld_off_f = (uint32_t)el * 4u;
     const size_t tok = (size_t)cb * H + h;
     const char* lb = reinterpret_cast<const char*>(log_alpha + tok * DK);
     if (e_act && ld_row < Lc) {
@@ -363,6 +411,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     }
   };
   auto load_vb = [&](int64_t cb, int Lc) {
+    int ld_row, el;
+    gate_map(ld_row, el);
+    const uint32_t ld_off_b = (uint32_t)(ld_row * H) * 4u;
+    const int t = wave0 * kWave + fresh_lane();
+    const int v_row = t / VPR, v_c0 = 8 * (t % VPR);
+    const uint32_t v_off = (uint32_t)(v_row * H * DV + v_c0) * (uint32_t)sizeof(InT);
     const size_t tok = (size_t)cb * H + h;
     const char* bb = reinterpret_cast<const char*>(beta + tok);
     const char* vb = reinterpret_cast<const char*>(v + tok * DV + j0);
@@ -420,7 +474,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     // wave index keeps the compiler from hoisting (and spilling) them out of the loop.
     wave = wave0;
     asm volatile("" : "+s"(wave));
-    const int eR = e_act ? (wave >> 1) : 0, ep = wave & 1;
+    refresh_lane();
+    v_row = tid / VPR;
+    v_c0 = 8 * (tid % VPR);
+    const int eR = e_act ? row_block_of<NB>(wave) : 0, ep = wave & 1;
     const int e_row = 16 * eR + lr;
     const int e_cb = ep * (DK / 2) + CPL * lg;
 
@@ -520,7 +577,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     // wave index keeps the compiler from hoisting (and spilling) them out of the loop.
     wave = wave0;
     asm volatile("" : "+s"(wave));
-    const int eR = e_act ? (wave >> 1) : 0, ep = wave & 1;
+    refresh_lane();
+    v_row = tid / VPR;
+    v_c0 = 8 * (tid % VPR);
+    const int eR = e_act ? row_block_of<NB>(wave) : 0, ep = wave & 1;
     const int e_row = 16 * eR + lr;
     const int e_cb = ep * (DK / 2) + CPL * lg;
 
@@ -622,11 +682,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
           }
         }
       }
-      // channel half 1 hands its partial tiles to half 0
-      if (ep == 1) {
-        const int base = eR * (eR + 1);  // tiles of row block eR: diag Q, diag K, then (Q, K) per I < eR
+      // Partial tiles change hands: the inverting half gives its M tiles and off-diagonal A
+      // tiles to the other half, which gives back its diagonal A tile.
+      const int base = eR * (eR + 1);  // tiles of row block eR: diag Q, diag K, then (Q, K) per I < eR
+      if (ep == inv_half(eR)) {
         sPT[(base + 0) * 64 + l] = make_float4(accQd[0], accQd[1], accQd[2], accQd[3]);
-        sPT[(base + 1) * 64 + l] = make_float4(accKd[0], accKd[1], accKd[2], accKd[3]);
 #pragma unroll
         for (int I = 0; I < NB - 1; ++I) {
           if (I < eR) {
@@ -634,143 +694,143 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
             sPT[(base + 3 + 2 * I) * 64 + l] = make_float4(accKo[I][0], accKo[I][1], accKo[I][2], accKo[I][3]);
           }
         }
+      } else {
+        sPT[(base + 1) * 64 + l] = make_float4(accKd[0], accKd[1], accKd[2], accKd[3]);
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_b
     if (ch + 1 < nchunks) load_la(c_begin + C, chunk_len(ch + 1));
 
-    // ================= Gram reduction and finalisation (waves (R, 0)) =================
-    if (e_act && ep == 0) {
+    // ===== Gram reduction by one wave of each row block, in parallel with the inverse of
+    //       that block's diagonal sub-block of A by the other =====
+    if (e_act) {
       const int base = eR * (eR + 1);
       const float4 bet4 = *reinterpret_cast<const float4*>(sBE + 16 * eR + 4 * lg);
       const float bet[4] = {bet4.x, bet4.y, bet4.z, bet4.w};
-      const float4 pq = sPT[(base + 0) * 64 + l], pk = sPT[(base + 1) * 64 + l];
-      accQd[0] += pq.x; accQd[1] += pq.y; accQd[2] += pq.z; accQd[3] += pq.w;
-      accKd[0] += pk.x; accKd[1] += pk.y; accKd[2] += pk.z; accKd[3] += pk.w;
+      if (ep != inv_half(eR)) {
+        const float4 pq = sPT[(base + 0) * 64 + l];
+        accQd[0] += pq.x; accQd[1] += pq.y; accQd[2] += pq.z; accQd[3] += pq.w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ri = 4 * lg + i;
-        const int r = 16 * eR + ri, cc = 16 * eR + lr;
-        const bool strict = ri > lr;
-        sAK[r * LDA + cc] = strict ? bet[i] * accKd[i] : 0.f;
-        sAQ[r * LDC + cc] = cvt<T>(strict ? accQd[i] : 0.f);
-        if (ri == lr) sDQ[r] = accQd[i];
+        for (int i = 0; i < 4; ++i) {
+          const int ri = 4 * lg + i;
+          const int r = 16 * eR + ri, cc = 16 * eR + lr;
+          sAQ[r * LDC + cc] = cvt<T>(ri > lr ? accQd[i] : 0.f);
+          if (ri == lr) sDQ[r] = accQd[i];
+        }
+#pragma unroll
+        for (int I = 0; I < NB - 1; ++I) {
+          if (I < eR) {
+            const float4 xq = sPT[(base + 2 + 2 * I) * 64 + l], xk = sPT[(base + 3 + 2 * I) * 64 + l];
+            accQo[I][0] += xq.x; accQo[I][1] += xq.y; accQo[I][2] += xq.z; accQo[I][3] += xq.w;
+            accKo[I][0] += xk.x; accKo[I][1] += xk.y; accKo[I][2] += xk.z; accKo[I][3] += xk.w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ri = 4 * lg + i;
+              sAQ[(16 * eR + ri) * LDC + 16 * I + lr] = cvt<T>(accQo[I][i]);
+              sAO[pair_index(eR, I) * 256 + ri * 16 + lr] = bet[i] * accKo[I][i];
+            }
+          }
+        }
+      } else {
+        const float4 pk = sPT[(base + 1) * 64 + l];
+        accKd[0] += pk.x; accKd[1] += pk.y; accKd[2] += pk.z; accKd[3] += pk.w;
+        // A_RR (strict lower, rows scaled by beta) stays in the accumulator layout: lane
+        // (column lr, group lg) holds A[4lg + u][lr].  Lane (lg, j) computes rows 4lg..4lg+3
+        // of column j of T_RR = (I + A_RR)^-1 by right-looking forward substitution: at
+        // pivot i, A[4lg + u][i] comes from lane i of the same 16-lane row (a DPP row
+        // broadcast, independent of x) and the final x[i] from lane group i/4 (one lane
+        // permute).  A is zero on and above the diagonal, so the update needs no mask.
+        float av[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) av[u] = (4 * lg + u > lr) ? bet[u] * accKd[u] : 0.f;
+        float xr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xr[u] = (4 * lg + u == lr) ? 1.f : 0.f;
+        static_for<0, 15>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const float xi = __shfl(xr[i & 3], 16 * (i >> 2) + lr, kWave);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xr[u] -= row_bcast16<i>(av[u]) * xi;
+        });
+        float* blk = sAK + 16 * eR * LDA + 16 * eR;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) blk[(4 * lg + u) * LDA + lr] = xr[u];
       }
+    }
+    __syncthreads();  // ------------------------------------------------------------- B_c
+    if (ch + 1 < nchunks) load_vb(c_begin + C, chunk_len(ch + 1));
+
+    // ===== T off-diagonal blocks, one block column per wave (wave I): for R = I+1 .. NB-1,
+    //       T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI, with T_JI (J > I) kept in registers.
+    //       The accumulator layout of a 16x16 fp32 MFMA tile is the B-operand layout
+    //       (k = 4*(lane>>4) + i), so results feed the next block without LDS. =====
+    if (wave < NB - 1) {
+      const int kq = 4 * lg;
+      const float bcol = sBE[16 * wave + lr];
 #pragma unroll
-      for (int I = 0; I < NB - 1; ++I) {
-        if (I < eR) {
-          const float4 xq = sPT[(base + 2 + 2 * I) * 64 + l], xk = sPT[(base + 3 + 2 * I) * 64 + l];
-          accQo[I][0] += xq.x; accQo[I][1] += xq.y; accQo[I][2] += xq.z; accQo[I][3] += xq.w;
-          accKo[I][0] += xk.x; accKo[I][1] += xk.y; accKo[I][2] += xk.z; accKo[I][3] += xk.w;
+      for (int I0 = 0; I0 < NB - 1; ++I0) {
+        if (I0 == wave) {
+          float tb[NB][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ri = 4 * lg + i;
-            const int r = 16 * eR + ri, cc = 16 * I + lr;
-            const float akv = bet[i] * accKo[I][i];
-            sAK[r * LDA + cc] = akv;
-            sAQ[r * LDC + cc] = cvt<T>(accQo[I][i]);
-            sAO[pair_index(eR, I) * 256 + ri * 16 + lr] = akv;
+          for (int u = 0; u < 4; ++u) tb[I0][u] = sAK[(16 * I0 + kq + u) * LDA + 16 * I0 + lr];
+#pragma unroll
+          for (int R = I0 + 1; R < NB; ++R) {
+            float4 a[NB];
+#pragma unroll
+            for (int J = I0; J < R; ++J)
+              a[J] = *reinterpret_cast<const float4*>(sAO + pair_index(R, J) * 256 + lr * 16 + kq);
+            const float4 tr = *reinterpret_cast<const float4*>(sAK + (16 * R + lr) * LDA + 16 * R + kq);
+            f32x4 X = zero4();
+#pragma unroll
+            for (int J = I0; J < R; ++J) {
+              X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J].x, tb[J][0], X, 0, 0, 0);
+              X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J].y, tb[J][1], X, 0, 0, 0);
+              X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J].z, tb[J][2], X, 0, 0, 0);
+              X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J].w, tb[J][3], X, 0, 0, 0);
+            }
+            f32x4 Y = zero4();
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.x, X[0], Y, 0, 0, 0);
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.y, X[1], Y, 0, 0, 0);
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.z, X[2], Y, 0, 0, 0);
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.w, X[3], Y, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              tb[R][i] = -Y[i];
+              sTB[(16 * R + kq + i) * LDC + 16 * I0 + lr] = cvt<T>(-Y[i] * bcol);
+            }
           }
         }
       }
     }
-    __syncthreads();  // ------------------------------------------------------------- B_c
-
-    // ================= T = (I + A)^-1: diagonal sub-blocks =================
-    // wave 0: DPP row R = lane >> 4 inverts block R; lane column j = lane & 15 keeps T[.][j].
-    if (wave == 0) {
-      const int R = lg < NB ? lg : 0, j = lr;
-      // right-looking forward substitution: once T[i][j] is final, fold it into every
-      // later row (15 - i independent updates), so the dependency chain is 16 steps
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
-      // four column quarters keep at most ~60 matrix entries in registers
-#pragma unroll
-      for (int h4 = 0; h4 < 4; ++h4) {
-        float a[16][4];
-#pragma unroll
-        for (int r = 4 * h4 + 1; r < 16; ++r) {
-          const float4 v4 = *reinterpret_cast<const float4*>(sAK + (16 * R + r) * LDA + 16 * R + 4 * h4);
-          a[r][0] = v4.x; a[r][1] = v4.y; a[r][2] = v4.z; a[r][3] = v4.w;
-        }
-#pragma unroll
-        for (int i = 4 * h4; i < 4 * h4 + 4 && i < 15; ++i) {
-#pragma unroll
-          for (int r = i + 1; r < 16; ++r) x[r] -= a[r][i - 4 * h4] * x[i];
-        }
+    if (wave >= NB - 1) {
+      // the other waves: T Diag(beta) on the diagonal blocks, zero upper tiles and padding
+      constexpr int NH = NW - (NB - 1);
+      const int hw = wave - (NB - 1);
+      for (int idx = hw * kWave + l; idx < C * 16; idx += NH * kWave) {
+        const int r = idx >> 4, c = 16 * (r >> 4) + (idx & 15);
+        sTB[r * LDC + c] = cvt<T>(sAK[r * LDA + c] * sBE[c]);
       }
-      if (lg < NB) {
-        const float bj = sBE[16 * R + j];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sAK[(16 * R + i) * LDA + 16 * R + j] = x[i];
-          sTB[(16 * R + i) * LDC + 16 * R + j] = cvt<T>(x[i] * bj);
-        }
-      }
-    } else {
-      // zero the strictly-upper tiles and the padded token columns of Tb (it shares memory)
-      for (int idx = tid - kWave; idx < C * CK; idx += NT - kWave) {
-        const int r = idx / CK, c = idx % CK;
-        if (c >= C || (c >> 4) > (r >> 4)) sTB[r * LDC + c] = cvt<T>(0.f);
+      // strictly-upper tiles (Tb shares memory with the partial tiles)
+      for (int t = hw; t < NPAIR; t += NH) {
+        int I = 1;
+        while (I * (I + 1) / 2 <= t) ++I;
+        const int R = t - I * (I - 1) / 2;  // upper tile (row block R, column block I > R)
+        store4(sTB + (16 * R + (l >> 2)) * LDC + 16 * I + 4 * (l & 3), 0.f, 0.f, 0.f, 0.f);
       }
       if constexpr (CK > C) {
-        // padded token columns of Kg^T, Kd^T, V^T and U^T (U^T shares memory with the partials)
-        for (int idx = tid - kWave; idx < (2 * DK + 2 * BV) * (CK - C); idx += NT - kWave) {
+        // padded token columns of Kg^T, Kd^T, V^T, U^T and Tb (U^T and Tb share memory with the partials)
+        for (int idx = hw * kWave + l; idx < (2 * DK + 2 * BV + C) * (CK - C); idx += NH * kWave) {
           const int rowi = idx / (CK - C), col = C + idx % (CK - C);
           T* base = rowi < DK            ? sKGT + rowi * LDC
                     : rowi < 2 * DK      ? sKDT + (rowi - DK) * LDC
                     : rowi < 2 * DK + BV ? sVT + (rowi - 2 * DK) * LDC
-                                         : sUT + (rowi - 2 * DK - BV) * LDC;
+                    : rowi < 2 * DK + 2 * BV ? sUT + (rowi - 2 * DK - BV) * LDC
+                                             : sTB + (rowi - 2 * DK - 2 * BV) * LDC;
           base[col] = cvt<T>(0.f);
         }
       }
     }
-    __syncthreads();  // ------------------------------------------------------------- B_d
-    if (ch + 1 < nchunks) load_vb(c_begin + C, chunk_len(ch + 1));
-
-    // ================= T: off-diagonal levels T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI =================
-#pragma unroll
-    for (int d = 1; d < NB; ++d) {
-      const int R = d + wave, I = wave;
-      if (R < NB) {
-        const int kq = 4 * lg;
-        // all operands of this level first (d terms), then the MFMA chain
-        float4 a[NB > 1 ? NB - 1 : 1];
-        float b[NB > 1 ? NB - 1 : 1][4];
-#pragma unroll
-        for (int t = 0; t < d; ++t) {
-          const int J = I + t;
-          a[t] = *reinterpret_cast<const float4*>(sAO + pair_index(R, J) * 256 + lr * 16 + kq);
-          const float* tj = sAK + (16 * J + kq) * LDA + 16 * I + lr;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) b[t][u] = tj[u * LDA];
-        }
-        const float4 tr = *reinterpret_cast<const float4*>(sAK + (16 * R + lr) * LDA + 16 * R + kq);
-        f32x4 X = zero4();
-#pragma unroll
-        for (int t = 0; t < d; ++t) {
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].x, b[t][0], X, 0, 0, 0);
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].y, b[t][1], X, 0, 0, 0);
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].z, b[t][2], X, 0, 0, 0);
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].w, b[t][3], X, 0, 0, 0);
-        }
-        // the accumulator layout of X is the B-operand layout (k = 4*(lane>>4) + i)
-        f32x4 Y = zero4();
-        Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.x, X[0], Y, 0, 0, 0);
-        Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.y, X[1], Y, 0, 0, 0);
-        Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.z, X[2], Y, 0, 0, 0);
-        Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.w, X[3], Y, 0, 0, 0);
-        const float bcol = sBE[16 * I + lr];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * R + kq + i;
-          sAK[r * LDA + 16 * I + lr] = -Y[i];
-          sTB[r * LDC + 16 * I + lr] = cvt<T>(-Y[i] * bcol);
-        }
-      }
-      __syncthreads();  // --------------------------------------------------- B_e (per level)
-    }
+    __syncthreads();  // ------------------------------------------------------------- B_e
 
     // ================= WY: W^T = Kg^T Tb^T ; Ut = Tb V =================
 #pragma unroll
