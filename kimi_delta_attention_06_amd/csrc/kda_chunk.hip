@@ -46,8 +46,10 @@
 // Entries above the diagonal are removed with a select, never a multiply.
 //
 // Precision policies:
-//   Mixed (bf16 inputs): fp16 MFMA operands except the diagonal Gram sub-blocks:
-//     A's in bf16 (range), M's on the fp32 matrix core (range and precision).
+//   Mixed (bf16 inputs): fp16 MFMA operands.  The diagonal Gram sub-blocks use fp16
+//     too when every channel of the wave decays by less than 8 nats over the 16-token
+//     block (the balanced operands then stay within e^{+-4} of the inputs); otherwise
+//     A's are bf16 (range) and M's go on the fp32 matrix core (range and precision).
 //     The diagonal of M (q_r . k_r) multiplies U in fp32 outside the MFMA.
 //   F32 (fp32 inputs): every product on the fp32 MFMA (16x16x4).
 #include <type_traits>
@@ -519,6 +521,14 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         for (int j = 0; j < CPL; ++j) cc[j] += shr16<8>(cc[j]);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) ss[j] = __shfl(cc[j], (l & ~15) | 15, kWave);
+        // When every channel of this wave decays by less than 8 nats over the block, the
+        // balanced operands stay within e^{+-4} of the inputs and fp16 represents them as
+        // well as the off-diagonal operands; otherwise the diagonal sub-blocks take the
+        // wide path.  The vote is wave-uniform (NaN votes for the wide path).
+        bool narrow = true;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) narrow = narrow && (ss[j] > -11.5415603f);  // 8 nats in log2 units
+        const bool fast16 = __builtin_amdgcn_ballot_w64(!narrow) == 0;
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
           const float eL = __builtin_amdgcn_exp2f(cc[j] - 0.5f * ss[j]);  // e^{c - s/2} <= e^{|s|/2}
@@ -542,18 +552,34 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         }
         // diagonal Gram sub-block partials over this wave's channels
         if constexpr (P == Prec::Mixed) {
-          // M: fp32 matrix core (its diagonal carries q_r . k_r); A: bf16 (range), one MFMA per step
+          if (fast16) {
+            // narrow decay: fp16 operands, one MFMA per 8 channels for each of M and A
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j], kR[j], accQd, 0, 0, 0);
+            for (int t = 0; t < CPL / 8; ++t) {
+              half8 qh, kh, rh;
 #pragma unroll
-          for (int t = 0; t < CPL / 8; ++t) {
-            bf16x8 kh, bh8;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              kh[j] = (__bf16)kL[8 * t + j];
-              bh8[j] = (__bf16)kR[8 * t + j];
+              for (int j = 0; j < 8; ++j) {
+                qh[j] = (_Float16)qL[8 * t + j];
+                kh[j] = (_Float16)kL[8 * t + j];
+                rh[j] = (_Float16)kR[8 * t + j];
+              }
+              accQd = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, rh, accQd, 0, 0, 0);
+              accKd = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, rh, accKd, 0, 0, 0);
             }
-            accKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh8, accKd, 0, 0, 0);
+          } else {
+            // wide decay: M on the fp32 matrix core; A in bf16 (range), one MFMA per 8 channels
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j], kR[j], accQd, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < CPL / 8; ++t) {
+              bf16x8 kh, bh8;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                kh[j] = (__bf16)kL[8 * t + j];
+                bh8[j] = (__bf16)kR[8 * t + j];
+              }
+              accKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh8, accKd, 0, 0, 0);
+            }
           }
         } else {
 #pragma unroll

@@ -79,6 +79,30 @@ def test_small_varlen_bf16(C, dk, dv):
     check_bf16(o, hT, o_ref, h_ref)
 
 
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_small_varlen_bf16_narrow_decay(C, dk, dv):
+    """Gate law x0.1 (blocks decay by < 8 nats: the fp16 path for the diagonal sub-blocks)."""
+    lens = [150, 0, 1, 64, 97, 33]
+    print("small varlen bf16, narrow decay, C=%d dk=%d dv=%d" % (C, dk, dv), flush=True)
+    inp = kda_inputs.make_custom_chunk_inputs(lens, 3, dk, dv, torch.bfloat16, gate_scale=0.1, h0_std=0.02,
+                                              seed=31 + C + dk, device="cuda")
+    o, hT = run(inp, chunk_size=C)
+    o_ref, h_ref = ref(inp)
+    check_bf16(o, hT, o_ref, h_ref)
+
+
+def test_mixed_narrow_and_wide_decay_channels():
+    """One channel half decays by < 8 nats per block and the other by more, so the two waves
+    of a row block take different paths for the diagonal sub-blocks."""
+    inp = kda_inputs.make_custom_chunk_inputs([200, 77], 4, 128, 128, torch.bfloat16, gate_scale=0.1,
+                                              h0_std=0.02, seed=41, device="cuda")
+    inp["log_alpha"][:, :, 64:96] = -0.6  # 9.6 nats per 16-token block on these channels
+    o, hT = run(inp, chunk_size=64)
+    o_ref, h_ref = ref(inp)
+    check_bf16(o, hT, o_ref, h_ref)
+
+
 @pytest.mark.parametrize("C", [16, 32])
 @pytest.mark.parametrize("dk", [64, 128])
 def test_small_varlen_fp32(C, dk):
