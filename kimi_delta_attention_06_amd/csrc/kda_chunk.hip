@@ -316,7 +316,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   auto fresh_lane = [&]() {
     int x = lane_id();
     asm volatile("" : "+v"(x));
-    return x;
+    return x & (kWave - 1);  // keeps the known range (24-bit multiplies, shifts)
   };
   auto refresh_lane = [&]() {
     l = fresh_lane();
@@ -453,11 +453,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       const int id = wave + NW * s;
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         const int R = id % NB, j = id / NB;
+        const uint32_t hdv = (uint32_t)(H * DV);
+        const uint32_t off0 = ((uint32_t)(16 * R + 4 * lg) * hdv + (uint32_t)(16 * j + lr)) * 4u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * R + 4 * lg + i;
-          const uint32_t off = (uint32_t)(r * H * DV + 16 * j + lr) * 4u;
-          if (r < o_len) *reinterpret_cast<float*>(ob + off) = Opend[s][i];
+          if (r < o_len) *reinterpret_cast<float*>(ob + off0 + (uint32_t)i * hdv * 4u) = Opend[s][i];
         }
       }
     }
@@ -520,15 +521,15 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
         for (int j = 0; j < CPL; ++j) cc[j] += shr16<8>(cc[j]);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) ss[j] = __shfl(cc[j], (l & ~15) | 15, kWave);
+        for (int j = 0; j < CPL; ++j) ss[j] = row_bcast16<15>(cc[j]);
         // When every channel of this wave decays by less than 8 nats over the block, the
         // balanced operands stay within e^{+-4} of the inputs and fp16 represents them as
         // well as the off-diagonal operands; otherwise the diagonal sub-blocks take the
-        // wide path.  The vote is wave-uniform (NaN votes for the wide path).
-        bool narrow = true;
+        // wide path.  The vote is wave-uniform.
+        float smin = ss[0];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) narrow = narrow && (ss[j] > -11.5415603f);  // 8 nats in log2 units
-        const bool fast16 = __builtin_amdgcn_ballot_w64(!narrow) == 0;
+        for (int j = 1; j < CPL; ++j) smin = fminf(smin, ss[j]);
+        const bool fast16 = __builtin_amdgcn_ballot_w64(!(smin > -11.5415603f)) == 0;  // 8 nats in log2 units
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
           const float eL = __builtin_amdgcn_exp2f(cc[j] - 0.5f * ss[j]);  // e^{c - s/2} <= e^{|s|/2}
@@ -796,29 +797,43 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
       for (int I0 = 0; I0 < NB - 1; ++I0) {
         if (I0 == wave) {
+          // operands first: T_II, T_RR and A_RJ for I0 <= J < R
           float tb[NB][4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) tb[I0][u] = sAK[(16 * I0 + kq + u) * LDA + 16 * I0 + lr];
+          float4 a[NB][NB], tr[NB];
 #pragma unroll
           for (int R = I0 + 1; R < NB; ++R) {
-            float4 a[NB];
+            tr[R] = *reinterpret_cast<const float4*>(sAK + (16 * R + lr) * LDA + 16 * R + kq);
 #pragma unroll
             for (int J = I0; J < R; ++J)
-              a[J] = *reinterpret_cast<const float4*>(sAO + pair_index(R, J) * 256 + lr * 16 + kq);
-            const float4 tr = *reinterpret_cast<const float4*>(sAK + (16 * R + lr) * LDA + 16 * R + kq);
-            f32x4 X = zero4();
+              a[R][J] = *reinterpret_cast<const float4*>(sAO + pair_index(R, J) * 256 + lr * 16 + kq);
+          }
+          // one accumulator per term A_RJ T_JI: the J = I0 terms of every R start at once,
+          // and each later term waits only for its own T_JI
+          f32x4 Xp[NB][NB];
+          auto term = [&](int R, int J) {
+            f32x4 acc = zero4();
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[R][J].x, tb[J][0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[R][J].y, tb[J][1], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[R][J].z, tb[J][2], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[R][J].w, tb[J][3], acc, 0, 0, 0);
+            return acc;
+          };
 #pragma unroll
-            for (int J = I0; J < R; ++J) {
-              X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J].x, tb[J][0], X, 0, 0, 0);
-              X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J].y, tb[J][1], X, 0, 0, 0);
-              X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J].z, tb[J][2], X, 0, 0, 0);
-              X = __builtin_amdgcn_mfma_f32_16x16x4f32(a[J].w, tb[J][3], X, 0, 0, 0);
-            }
+          for (int R = I0 + 1; R < NB; ++R) Xp[R][I0] = term(R, I0);
+#pragma unroll
+          for (int R = I0 + 1; R < NB; ++R) {
+#pragma unroll
+            for (int J = I0 + 1; J < R; ++J) Xp[R][J] = term(R, J);
+            f32x4 X = Xp[R][I0];
+#pragma unroll
+            for (int J = I0 + 1; J < R; ++J) X += Xp[R][J];
             f32x4 Y = zero4();
-            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.x, X[0], Y, 0, 0, 0);
-            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.y, X[1], Y, 0, 0, 0);
-            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.z, X[2], Y, 0, 0, 0);
-            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr.w, X[3], Y, 0, 0, 0);
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr[R].x, X[0], Y, 0, 0, 0);
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr[R].y, X[1], Y, 0, 0, 0);
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr[R].z, X[2], Y, 0, 0, 0);
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr[R].w, X[3], Y, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               tb[R][i] = -Y[i];
