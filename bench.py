@@ -5,8 +5,9 @@ Timed step: one kda_chunk_fwd pass over the Kimi-Linear-shaped KDA layer
 (B=4, T=4096, H=32, dk=dv=128, chunk 64, bf16 q/k/v, fp32 gates and state;
 seeded synthetic inputs already resident in HBM).  `value` is tokens/s of that
 pass (B*T tokens, all 32 heads).  In the same run the decode/replay state update
-(256 sequences x 32 heads, fp32 state, 1 and 8 tokens) is timed and reported
-under "decode" (HBM GB/s against the 8 TB/s peak), and the fp64 CPU oracle is
+(256 sequences x 32 heads, fp32 state, 1 and 8 tokens) and the replay + verify
+variant (8 tokens, per-sequence commit counts) are timed and reported under
+"decode" (HBM GB/s against the 8 TB/s peak), and the fp64 CPU oracle is
 timed on a bounded sample of the chunk workload ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
@@ -196,6 +197,28 @@ def main():
                                  "bytes_per_step": d_bytes}
         log("recurrent_step n=%d: %.4f ms, %.0f GB/s (%.1f%% of peak)" % (n_tok, d_ms, d_gbs, 100 * d_gbs / HBM_PEAK_GBS))
         del d_inp, d_o
+
+    # replay + verify: 8 tokens, per-sequence commit counts drawn uniformly from 0..8 (seeded)
+    v_inp = kda_inputs.make_decode_inputs(dw, 8, device=dev)
+    gen = torch.Generator().manual_seed(1005 + 7)
+    n_commit = torch.randint(0, 9, (dw.n_seqs,), generator=gen, dtype=torch.int32).to(dev)
+    v_o = torch.empty(dw.n_seqs, 8, dw.n_heads, dw.dv, dtype=torch.float32, device=dev)
+
+    def vstep():
+        kda.recurrent_verify(v_inp["q"], v_inp["k"], v_inp["v"], v_inp["log_alpha"], v_inp["beta"], v_inp["S"],
+                             n_commit, o=v_o)
+
+    v_ms = time_launches(vstep, max(args.steps, 20), args.warmup, stream)
+    n_writing = int((n_commit > 0).sum().item())
+    state_bytes = dw.n_heads * dw.dk * dw.dv * 4
+    v_bytes = (dw.n_seqs + n_writing) * state_bytes + dw.n_seqs * 8 * dw.n_heads * BYTES_PER_TOKEN_HEAD
+    v_gbs = v_bytes / (v_ms * 1e-3) / 1e9
+    decode["verify_n8"] = {"ms_per_step": round(v_ms, 5), "GB/s": round(v_gbs, 1),
+                           "frac_of_hbm_peak": round(v_gbs / HBM_PEAK_GBS, 4),
+                           "sequences_committing": n_writing, "bytes_per_step": v_bytes}
+    log("recurrent_verify n=8 (%d of %d sequences commit): %.4f ms, %.0f GB/s (%.1f%% of peak)"
+        % (n_writing, dw.n_seqs, v_ms, v_gbs, 100 * v_gbs / HBM_PEAK_GBS))
+    del v_inp, v_o
 
     result = {
         "metric": METRIC,

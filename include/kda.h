@@ -117,6 +117,31 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype, float* o,
                               void* stream);
 
+/*
+ * kda_recurrent_verify - replay accepted drafts and verify new ones in one pass.
+ *
+ * Speculative decoding keeps only the projected inputs of accepted draft tokens
+ * and replays them onto the committed state on-chip, fused with the verification
+ * of the next drafts ("Kimi K3 model structure (7)", section "KDA state
+ * rollback").  For sequence n the n_tokens tokens are applied in order to the
+ * state read from S_inout[n] and every token writes its output, exactly as
+ * kda_recurrent_step; but S_inout[n] is overwritten with the state as it stands
+ * after the first n_commit[n] tokens (left untouched when n_commit[n] == 0).
+ * The later tokens are drafts: their outputs see the continued state, their
+ * updates are dropped.  State traffic is one read and at most one write.
+ *
+ *   q, k, v, log_alpha, beta, S_inout, o   as for kda_recurrent_step
+ *   n_commit     device int32 [n_seqs], caller-owned; values are clamped to
+ *                [0, n_tokens] on the device (the host cannot read them)
+ *
+ * Errors: as kda_recurrent_step, plus KDA_ERR_INVALID_ARGUMENT for a NULL or
+ * misaligned n_commit when n_seqs > 0, or for o overlapping n_commit.
+ */
+kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const float* log_alpha,
+                                const float* beta, float* S_inout, const int32_t* n_commit, int32_t n_seqs,
+                                int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype,
+                                float* o, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 

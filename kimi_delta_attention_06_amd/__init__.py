@@ -6,11 +6,13 @@ HIP kernels.  PyTorch provides device memory and the current stream.
 
     o, hT = chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size=64)
     o = recurrent_step(q, k, v, log_alpha, beta, S)      # updates S in place
+    o = recurrent_verify(q, k, v, log_alpha, beta, S, n_commit)  # commits a prefix per sequence
 
 Shapes: q, k [T, H, dk]; v [T, H, dv]; log_alpha [T, H, dk] fp32; beta [T, H]
 fp32; h0/hT [N, H, dk, dv] fp32; cu_seqlens [N+1] int32.  A leading batch
-dimension [B, T, ...] is accepted for fixed-length input.  recurrent_step takes
-tokens as [N, n, H, d] and S as [N, H, dk, dv].
+dimension [B, T, ...] is accepted for fixed-length input.  recurrent_step and
+recurrent_verify take tokens as [N, n, H, d] and S as [N, H, dk, dv];
+recurrent_verify also takes n_commit [N] int32 (tokens whose updates are kept).
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "recurrent_step", "KDAError"]
+__all__ = ["chunk_fwd", "recurrent_step", "recurrent_verify", "KDAError"]
 
 
 class KDAError(RuntimeError):
@@ -125,8 +127,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: in
     return o, hT
 
 
-def recurrent_step(q, k, v, log_alpha, beta, S, o: Optional[torch.Tensor] = None):
-    """Decode / replay of n tokens per sequence: updates S [N, H, dk, dv] in place, returns o [N, n, H, dv]."""
+def _recurrent(fn_name, q, k, v, log_alpha, beta, S, n_commit, o):
     lib = _lib.load()
     dev = S.device
     q, k, v = _dev(q, "q", device=dev), _dev(k, "k", device=dev), _dev(v, "v", device=dev)
@@ -147,7 +148,25 @@ def recurrent_step(q, k, v, log_alpha, beta, S, o: Optional[torch.Tensor] = None
         if tuple(o.shape) != (N, n, H, dv):
             raise ValueError("o must be [N, n, H, dv]")
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
-                                N, n, H, dk, dv, code, _ptr(o), stream)
-    _check(rc, "kda_recurrent_step")
+    if fn_name == "kda_recurrent_step":
+        rc = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                    N, n, H, dk, dv, code, _ptr(o), stream)
+    else:
+        n_commit = _dev(n_commit, "n_commit", torch.int32, dev)
+        if tuple(n_commit.shape) != (N,):
+            raise ValueError("n_commit must be [N] int32")
+        rc = lib.kda_recurrent_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                      _ptr(n_commit), N, n, H, dk, dv, code, _ptr(o), stream)
+    _check(rc, fn_name)
     return o
+
+
+def recurrent_step(q, k, v, log_alpha, beta, S, o: Optional[torch.Tensor] = None):
+    """Decode / replay of n tokens per sequence: updates S [N, H, dk, dv] in place, returns o [N, n, H, dv]."""
+    return _recurrent("kda_recurrent_step", q, k, v, log_alpha, beta, S, None, o)
+
+
+def recurrent_verify(q, k, v, log_alpha, beta, S, n_commit, o: Optional[torch.Tensor] = None):
+    """Replay + verify: every token writes o [N, n, H, dv]; S [N, H, dk, dv] keeps the state after the
+    first n_commit[i] tokens of sequence i (unchanged for 0); the later (draft) updates are dropped."""
+    return _recurrent("kda_recurrent_verify", q, k, v, log_alpha, beta, S, n_commit, o)

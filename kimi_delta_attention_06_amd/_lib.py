@@ -23,6 +23,8 @@ SIGNATURES = {
                                      ctypes.c_int, _P, _P, _P]),
     "kda_recurrent_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                           ctypes.c_int, _P, _P]),
+    "kda_recurrent_verify": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                            ctypes.c_int, _P, _P]),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_version": (ctypes.c_int32, []),
 }

@@ -63,20 +63,22 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   return kda::launch_chunk_fwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* log_alpha,
-                              const float* beta, float* S_inout, int32_t n_seqs, int32_t n_tokens,
-                              int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype, float* o,
-                              void* stream) {
+static kda_status recurrent_common(const void* q, const void* k, const void* v, const float* log_alpha,
+                                   const float* beta, float* S_inout, const int32_t* n_commit, bool need_commit,
+                                   int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv,
+                                   kda_dtype qkv_dtype, float* o, void* stream) {
   if (n_seqs < 0 || n_tokens <= 0 || n_heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
   if (qkv_dtype != KDA_DTYPE_F32 && qkv_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
   if (n_seqs > 0 && (!q || !k || !v || !log_alpha || !beta || !S_inout || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  if (n_seqs > 0 && need_commit && !n_commit) return KDA_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {q, k, v, log_alpha, beta, S_inout, o};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_INVALID_ARGUMENT;
+  if (n_commit && ((uintptr_t)n_commit & 3)) return KDA_ERR_INVALID_ARGUMENT;
   if (!dims_ok(dk) || !dims_ok(dv) || n_tokens > 8) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)n_seqs * n_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   if (n_seqs == 0) return KDA_OK;
-  // o must not overlap the state or the token inputs
+  // o must not overlap the state, the token inputs or the commit counts
   {
     const bool bf16 = qkv_dtype == KDA_DTYPE_BF16;
     const size_t ntok = (size_t)n_seqs * n_tokens * n_heads;
@@ -85,17 +87,35 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     const size_t esz = bf16 ? 2 : 4;
     struct R { const void* p; size_t n; } ins[] = {
         {q, ntok * dk * esz}, {k, ntok * dk * esz}, {v, ntok * dv * esz},
-        {log_alpha, ntok * dk * 4}, {beta, ntok * 4}, {S_inout, (size_t)n_seqs * n_heads * dk * dv * 4}};
+        {log_alpha, ntok * dk * 4}, {beta, ntok * 4}, {S_inout, (size_t)n_seqs * n_heads * dk * dv * 4},
+        {n_commit, n_commit ? (size_t)n_seqs * 4 : 0}};
     for (const R& r : ins) {
       const char* b = (const char*)r.p;
-      if (b < oe && ob < b + r.n) return KDA_ERR_INVALID_ARGUMENT;
+      if (r.n && b < oe && ob < b + r.n) return KDA_ERR_INVALID_ARGUMENT;
     }
   }
   kda::RecurrentArgs a;
   a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S = S_inout; a.o = o;
+  a.n_commit = n_commit;
   a.n_seqs = n_seqs; a.n_tokens = n_tokens; a.n_heads = n_heads; a.dk = dk; a.dv = dv;
   a.bf16 = qkv_dtype == KDA_DTYPE_BF16; a.stream = stream;
   return kda::launch_recurrent_step(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, float* S_inout, int32_t n_seqs, int32_t n_tokens,
+                              int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype, float* o,
+                              void* stream) {
+  return recurrent_common(q, k, v, log_alpha, beta, S_inout, nullptr, false, n_seqs, n_tokens, n_heads, dk, dv,
+                          qkv_dtype, o, stream);
+}
+
+kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const float* log_alpha,
+                                const float* beta, float* S_inout, const int32_t* n_commit, int32_t n_seqs,
+                                int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype,
+                                float* o, void* stream) {
+  return recurrent_common(q, k, v, log_alpha, beta, S_inout, n_commit, true, n_seqs, n_tokens, n_heads, dk, dv,
+                          qkv_dtype, o, stream);
 }
 
 const char* kda_status_string(kda_status s) {

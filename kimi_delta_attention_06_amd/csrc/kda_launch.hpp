@@ -14,6 +14,7 @@ struct RecurrentArgs {
   const float* beta;
   float* S;
   float* o;
+  const int32_t* n_commit;  // may be null: every token is committed
   int n_seqs, n_tokens, n_heads, dk, dv;
   bool bf16;
   void* stream;

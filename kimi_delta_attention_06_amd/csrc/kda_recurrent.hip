@@ -12,6 +12,12 @@
 // which is the recurrence S_new = (I - beta k k^T) S' + beta k v^T, o = S_new^T q
 // regrouped so the state is traversed once per token.
 //
+// Replay + verify (same section: the cached inputs of accepted drafts are replayed
+// onto the committed state, fused with verifying the new drafts): with a per-sequence
+// commit count c, every token produces o, but the state is written back as it stands
+// after token c - 1 (not at all for c = 0); later tokens are drafts whose updates are
+// dropped.  Without counts, every token is committed.
+//
 // Thread map (256 threads): thread t owns value columns [4 cg, 4 cg + 4) and
 // RPT consecutive key rows of row group rg, cg = t % (DV/4), rg = t / (DV/4).
 // Every HBM access of S is a float4 per lane; lanes 0..DV/4-1 of a row cover
@@ -35,7 +41,7 @@ template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(kRecThreads) void recurrent_step_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, float* __restrict__ S,
-    float* __restrict__ o, int n_tokens, int H) {
+    float* __restrict__ o, const int32_t* __restrict__ n_commit, int n_tokens, int H) {
   constexpr int CG = DV / 4;           // column groups (float4 each)
   constexpr int RG = kRecThreads / CG; // row groups
   constexpr int RPT = DK / RG;         // rows per thread
@@ -56,6 +62,10 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_step_kernel(
   const int t = threadIdx.x;
   const int cg = t % CG, rg = t / CG;
   const int lane = t % kWave, wave = t / kWave;
+
+  // tokens whose updates reach the stored state (clamped to [0, n_tokens])
+  int commit = n_tokens;
+  if (n_commit) commit = min(max(n_commit[n], 0), n_tokens);
 
   float* Sp = S + (size_t)nh * DK * DV;
   float4 st[RPT];
@@ -132,11 +142,12 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_step_kernel(
       const float kr = s_k[tok][rg * RPT + i];
       st[i].x += kr * d.x; st[i].y += kr * d.y; st[i].z += kr * d.z; st[i].w += kr * d.w;
     }
-  }
-
+    if (tok + 1 == commit) {
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    *reinterpret_cast<float4*>(Sp + (size_t)(rg * RPT + i) * DV + cg * 4) = st[i];
+      for (int i = 0; i < RPT; ++i)
+        *reinterpret_cast<float4*>(Sp + (size_t)(rg * RPT + i) * DV + cg * 4) = st[i];
+    }
+  }
 }
 
 template <int DK, int DV, typename InT>
@@ -144,7 +155,7 @@ static hipError_t launch_rec(const RecurrentArgs& a) {
   dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_heads)), block(kRecThreads);
   hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, InT>), grid, block, 0, (hipStream_t)a.stream,
                      (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, a.S, a.o,
-                     a.n_tokens, a.n_heads);
+                     a.n_commit, a.n_tokens, a.n_heads);
   return hipGetLastError();
 }
 

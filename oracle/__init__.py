@@ -112,3 +112,26 @@ def kda_recurrent_step(q, k, v, log_alpha, beta, S, n_threads: int = 0):
     o, hT = kda_fwd(q.reshape(N * n, H, dk), k.reshape(N * n, H, dk), v.reshape(N * n, H, dv),
                     la.reshape(N * n, H, dk), be.reshape(N * n, H), S, cu, n_threads)
     return o.reshape(N, n, H, dv), hT
+
+
+def kda_recurrent_verify(q, k, v, log_alpha, beta, S, n_commit, n_threads: int = 0):
+    """Oracle replay + verify ("Kimi K3 model structure (7)", section "KDA state rollback").
+
+    Every token of a sequence is applied in order and writes its output (the later,
+    uncommitted draft tokens see the continued state); the returned state of sequence i
+    is the state after its first n_commit[i] tokens (S itself for 0).  Both parts are the
+    recurrence of `kda_fwd`: the outputs on all n tokens, the state on the committed
+    prefix packed as its own sequences.  Returns (o [N, n, H, dv], S_new [N, H, dk, dv]).
+    """
+    q, k, v, la, be, S = (_f32(x) for x in (q, k, v, log_alpha, beta, S))
+    n_commit = np.asarray(n_commit.cpu() if hasattr(n_commit, "cpu") else n_commit, dtype=np.int64)
+    N, n, H, dk = q.shape
+    dv = v.shape[3]
+    o, _ = kda_recurrent_step(q, k, v, la, be, S, n_threads)
+    c = np.clip(n_commit, 0, n)
+    if c.sum() == 0:
+        return o, S.astype(np.float64)
+    cu = np.concatenate([[0], np.cumsum(c)]).astype(np.int64)
+    take = lambda x: np.concatenate([x[i, :c[i]] for i in range(N)], axis=0)
+    _, S_new = kda_fwd(take(q), take(k), take(v), take(la), take(be), S, cu, n_threads)
+    return o, S_new

@@ -19,7 +19,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_recurrent_step", "kda_status_string", "kda_version"}
+    assert set(names) == {"kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_verify", "kda_status_string",
+                          "kda_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -72,3 +73,23 @@ def test_recurrent_step_rejects(kw, code):
 
 def test_recurrent_step_zero_sequences_is_a_no_op():
     assert step(N=0) == 0
+
+
+def verify(**kw):
+    a = dict(q=P, k=P, v=P, la=P, b=P, S=P * 4, nc=P * 16, N=2, n=4, H=2, dk=128, dv=128, dt=_lib.KDA_DTYPE_BF16,
+             o=P * 8)
+    a.update(kw)
+    return lib.kda_recurrent_verify(a["q"], a["k"], a["v"], a["la"], a["b"], a["S"], a["nc"], a["N"], a["n"],
+                                    a["H"], a["dk"], a["dv"], a["dt"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nc=None), 1), (dict(nc=P * 16 + 2), 1), (dict(q=None), 1), (dict(n=0), 1), (dict(n=9), 2),
+    (dict(dk=96), 2), (dict(nc=P * 8), 1),  # o overlaps the commit counts
+])
+def test_recurrent_verify_rejects(kw, code):
+    assert verify(**kw) == code
+
+
+def test_recurrent_verify_zero_sequences_is_a_no_op():
+    assert verify(N=0, nc=None) == 0

@@ -322,6 +322,30 @@ def test_recurrent_step_wrapper_is_packed_forward():
         assert np.array_equal(o[i], o1) and np.array_equal(S1[i], h1[0])
 
 
+def test_replay_verify_commits_a_prefix_and_outputs_continue_from_it():
+    """Replay + verify ("Kimi K3 model structure (7)", section "KDA state rollback"): the kept
+    state is the one after the committed prefix, and the draft outputs are what stepping the
+    drafts from that kept state gives (so o and the kept state agree at the commit point)."""
+    rng = np.random.default_rng(21)
+    N, n, H, dk, dv = 4, 6, 2, 8, 8
+    q, k, v, la, be = (x.reshape(N, n, *x.shape[1:]) for x in rand_inputs(rng, N * n, H, dk, dv))
+    S = f32(rng.standard_normal((N, H, dk, dv)))
+    commit = np.array([0, 2, 6, 9])  # 9 is clamped to n
+    o, Sk = oracle.kda_recurrent_verify(q, k, v, la, be, S, commit)
+    o_all, S_all = oracle.kda_recurrent_step(q, k, v, la, be, S)
+    assert np.array_equal(o, o_all)
+    assert np.array_equal(Sk[0], S[0])                      # nothing committed: state untouched
+    assert np.array_equal(Sk[2], S_all[2]) and np.array_equal(Sk[3], S_all[3])  # everything committed
+    c = 2
+    o_pre, S_pre = oracle.kda_recurrent_step(q[1:2, :c], k[1:2, :c], v[1:2, :c], la[1:2, :c], be[1:2, :c], S[1:2])
+    assert np.array_equal(Sk[1], S_pre[0])
+    o_draft, _ = oracle.kda_recurrent_step(q[1:2, c:], k[1:2, c:], v[1:2, c:], la[1:2, c:], be[1:2, c:],
+                                           f32(Sk[1:2]))
+    # the draft outputs continue from the kept state (to fp32 rounding of that state)
+    assert rel(o[1, c:], o_draft[0]) < 1e-6
+    assert np.array_equal(o[1, :c], o_pre[0])
+
+
 def test_rejects_bad_cu_seqlens():
     rng = np.random.default_rng(13)
     q, k, v, la, be = rand_inputs(rng, 10, 1, 4, 4)

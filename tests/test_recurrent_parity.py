@@ -81,3 +81,54 @@ def test_successive_steps_equal_one_replay():
     o_b = torch.cat(outs, dim=1)
     assert (o_a - o_b).abs().max().item() <= 1e-5
     assert (S_a - S_b).abs().max().item() <= 1e-5
+
+
+def run_verify(n_tokens, commit, dk=128, dv=128, dtype=torch.bfloat16, seed=None):
+    import kimi_delta_attention_06_amd as kda
+    w = kda_inputs.DecodeWorkload("t", kda_inputs.DECODE_256x32.n_seqs, 32, dk, dv, 0.02, dtype, 1005)
+    inp = kda_inputs.make_decode_inputs(w, n_tokens, device="cuda", n_seqs=len(commit), seed=seed)
+    S_host = inp["S"].cpu()
+    nc = torch.tensor(commit, dtype=torch.int32, device="cuda")
+    o = kda.recurrent_verify(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S"], nc)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.kda_recurrent_verify(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S_host,
+                                               np.asarray(commit))
+    return o, inp["S"], o_ref, S_ref, S_host
+
+
+def test_verify_commits_per_sequence_prefix():
+    """Replay + verify, 8 tokens: per-sequence commit counts 0..8 (and out-of-range values, clamped)."""
+    commit = [0, 1, 2, 3, 4, 5, 6, 7, 8, -3, 11, 8, 0, 5, 2, 7]
+    print("verify n_tokens=8 commit=%s" % commit, flush=True)
+    o, S, o_ref, S_ref, S0 = run_verify(8, commit, seed=91)
+    eo, ro = errs(o, o_ref)
+    es, rs = errs(S, S_ref)
+    print("o max err %.3e rms %.3e | S max err %.3e rms %.3e" % (eo, ro, es, rs))
+    assert eo <= 1e-5 and es <= 1e-5
+    # nothing committed: the state is not written at all (bit-identical)
+    for i, c in enumerate(commit):
+        if c <= 0:
+            assert torch.equal(S[i].cpu(), S0[i])
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("n_tokens", [1, 5])
+def test_verify_shapes_fp32_inputs(dk, dv, n_tokens):
+    commit = [n_tokens, 0, 1, n_tokens - 1, 3]
+    o, S, o_ref, S_ref, _ = run_verify(n_tokens, commit, dk=dk, dv=dv, dtype=torch.float32, seed=5 + n_tokens)
+    eo, _ = errs(o, o_ref)
+    es, _ = errs(S, S_ref)
+    assert eo <= 1e-4 and es <= 1e-4
+
+
+def test_verify_with_full_commit_equals_step():
+    """n_commit = n_tokens everywhere is kda_recurrent_step, bit for bit."""
+    import kimi_delta_attention_06_amd as kda
+    inp = kda_inputs.make_decode_inputs(kda_inputs.DECODE_256x32, 8, device="cuda", n_seqs=12, seed=93)
+    S1 = inp["S"].clone()
+    o1 = kda.recurrent_step(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S1)
+    S2 = inp["S"].clone()
+    o2 = kda.recurrent_verify(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S2,
+                              torch.full((12,), 8, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
