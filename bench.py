@@ -4,7 +4,8 @@
 Timed step: one kda_chunk_fwd pass over the Kimi-Linear-shaped KDA layer
 (B=4, T=4096, H=32, dk=dv=128, chunk 64, bf16 q/k/v, fp32 gates and state;
 seeded synthetic inputs already resident in HBM).  `value` is tokens/s of that
-pass (B*T tokens, all 32 heads).  In the same run the decode/replay state update
+pass (B*T tokens, all 32 heads).  The same pass with state checkpoints every 512
+tokens is timed and reported under "checkpointed".  In the same run the decode/replay state update
 (256 sequences x 32 heads, fp32 state, 1 and 8 tokens) and the replay + verify
 variant (8 tokens, per-sequence commit counts) are timed and reported under
 "decode" (HBM GB/s against the 8 TB/s peak), and the fp64 CPU oracle is
@@ -177,6 +178,22 @@ def main():
     log("chunk_fwd: %.4f ms/launch, %.1f M tokens/s, %.0f GB/s algorithmic, %.1f TFLOP/s algorithmic"
         % (ms, tok_s / 1e6, gbs, tflops))
 
+    # ---------------- the same pass with 512-token state checkpoints ----------------
+    ck_every = 512
+    ck = torch.empty(tokens // ck_every, w.n_heads, w.dk, w.dv, dtype=torch.float32, device=dev)
+
+    def cstep():
+        kda.chunk_fwd_checkpointed(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size, ckpt_every=ck_every,
+                                   o=o, hT=hT, ckpt=ck)
+
+    c_ms = time_launches(cstep, args.steps, args.warmup, stream)
+    ck_bytes = ck.numel() * 4
+    checkpointed = {"ckpt_every": ck_every, "ms_per_step": round(c_ms, 5),
+                    "overhead_vs_plain": round(c_ms / ms - 1.0, 4), "checkpoint_bytes_per_step": ck_bytes,
+                    "algorithmic_GB/s": round((alg_bytes + ck_bytes) / (c_ms * 1e-3) / 1e9, 1)}
+    log("chunk_fwd_checkpointed (every %d tokens): %.4f ms/launch (%+.1f%%)" % (ck_every, c_ms, 100 * (c_ms / ms - 1)))
+    del ck
+
     # ---------------- decode / replay ----------------
     dw = kda_inputs.DECODE_256x32
     decode = {}
@@ -241,6 +258,7 @@ def main():
                      "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": alg_flops},
+        "checkpointed": checkpointed,
         "decode": decode,
         "wall_s_timed_region": round(t_wall, 3),
     }

@@ -94,6 +94,35 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* stream);
 
 /*
+ * kda_chunk_fwd_checkpointed - kda_chunk_fwd that also stores periodic states.
+ *
+ * For prefix-cache reuse the state is kept only at the ends of fixed-size hash
+ * blocks of 512 tokens ("Kimi K3 model structure (7)", section "Prefix cache:
+ * decoupled granularity, 512-token reuse").  Same arguments and results as
+ * kda_chunk_fwd, plus:
+ *
+ *   ckpt_every   checkpoint spacing in tokens, > 0 and a multiple of chunk_size
+ *                (512 for 512-token hash blocks)
+ *   ckpt         device fp32 [total_tokens / ckpt_every, n_heads, dk, dv]; the
+ *                state of sequence n after its first p tokens, for every positive
+ *                multiple p of ckpt_every up to the sequence length, is written to
+ *                slot (cu_seqlens[n] + p) / ckpt_every - 1 (n * seq_len in place
+ *                of cu_seqlens[n] for equal lengths).  These slots are distinct;
+ *                slots that no checkpoint maps to are left untouched.  May be NULL
+ *                only when total_tokens < ckpt_every.  Must not overlap any other
+ *                buffer.
+ *
+ * Errors: as kda_chunk_fwd, plus KDA_ERR_INVALID_ARGUMENT for ckpt_every <= 0,
+ * ckpt_every not a multiple of chunk_size, a NULL or misaligned ckpt when slots
+ * exist, or ckpt overlapping another buffer.
+ */
+kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* v, const float* log_alpha,
+                                      const float* beta, const float* h0, const int32_t* cu_seqlens,
+                                      int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                      int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
+                                      int32_t ckpt_every, float* ckpt, void* stream);
+
+/*
  * kda_recurrent_step - decode / draft-replay state update.
  *
  * For each of n_seqs sequences, applies n_tokens consecutive tokens to the

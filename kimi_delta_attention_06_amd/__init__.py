@@ -5,6 +5,7 @@ only checks and marshals arguments; every step of the computation runs in the
 HIP kernels.  PyTorch provides device memory and the current stream.
 
     o, hT = chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size=64)
+    o, hT, ckpt = chunk_fwd_checkpointed(..., ckpt_every=512)  # + states every 512 tokens
     o = recurrent_step(q, k, v, log_alpha, beta, S)      # updates S in place
     o = recurrent_verify(q, k, v, log_alpha, beta, S, n_commit)  # commits a prefix per sequence
 
@@ -22,7 +23,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "recurrent_step", "recurrent_verify", "KDAError"]
+__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "recurrent_step", "recurrent_verify", "KDAError"]
 
 
 class KDAError(RuntimeError):
@@ -74,6 +75,21 @@ def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: in
               output_final_state: bool = True, o: Optional[torch.Tensor] = None,
               hT: Optional[torch.Tensor] = None):
     """Chunkwise KDA forward; returns (o fp32 [T, H, dv], hT fp32 [N, H, dk, dv] or None)."""
+    o, hT, _ = _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, 0, None)
+    return o, hT
+
+
+def chunk_fwd_checkpointed(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: int = 64,
+                           ckpt_every: int = 512, output_final_state: bool = True,
+                           o: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None,
+                           ckpt: Optional[torch.Tensor] = None):
+    """chunk_fwd that also returns ckpt fp32 [T // ckpt_every, H, dk, dv]: the state of sequence n after
+    p tokens (p a positive multiple of ckpt_every) is in slot (start_n + p) // ckpt_every - 1."""
+    return _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT,
+                  int(ckpt_every), ckpt)
+
+
+def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, ckpt_every, ckpt):
     lib = _lib.load()
     batched = q.dim() == 4
     if batched:
@@ -119,12 +135,28 @@ def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: in
     else:
         hT = None
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
-                           n_seqs, T_total, H, dk, dv, int(chunk_size), code, _ptr(o), _ptr(hT), stream)
-    _check(rc, "kda_chunk_fwd")
+    if ckpt_every == 0:
+        rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                               _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code, _ptr(o),
+                               _ptr(hT), stream)
+        _check(rc, "kda_chunk_fwd")
+    else:
+        if ckpt_every < 0:
+            raise ValueError("ckpt_every must be positive")
+        n_slots = T_total // ckpt_every
+        if ckpt is None:
+            ckpt = torch.empty(n_slots, H, dk, dv, dtype=torch.float32, device=dev)
+        else:
+            ckpt = _dev(ckpt, "ckpt", torch.float32, dev)
+            if tuple(ckpt.shape) != (n_slots, H, dk, dv):
+                raise ValueError("ckpt must be [T // ckpt_every, H, dk, dv] = %s" % ((n_slots, H, dk, dv),))
+        rc = lib.kda_chunk_fwd_checkpointed(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                                            _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code,
+                                            _ptr(o), _ptr(hT), int(ckpt_every), _ptr(ckpt), stream)
+        _check(rc, "kda_chunk_fwd_checkpointed")
     if batched:
         o = o.view(B, T, H, dv)
-    return o, hT
+    return o, hT, ckpt
 
 
 def _recurrent(fn_name, q, k, v, log_alpha, beta, S, n_commit, o):

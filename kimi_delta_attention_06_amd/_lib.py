@@ -21,6 +21,8 @@ _P, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 SIGNATURES = {
     "kda_chunk_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
                                      ctypes.c_int, _P, _P, _P]),
+    "kda_chunk_fwd_checkpointed": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
+                                                  _I32, ctypes.c_int, _P, _P, _I32, _P, _P]),
     "kda_recurrent_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                           ctypes.c_int, _P, _P]),
     "kda_recurrent_verify": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,

@@ -17,13 +17,38 @@ bool dims_ok(int32_t d) { return d == 64 || d == 128; }
 
 extern "C" {
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
-                         const float* beta, const float* h0, const int32_t* cu_seqlens,
-                         int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
-                         int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
-                         void* stream) {
+static kda_status chunk_common(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta, const float* h0, const int32_t* cu_seqlens, int32_t n_seqs,
+                               int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk_size,
+                               kda_dtype qkv_dtype, float* o, float* hT, int32_t ckpt_every, float* ckpt,
+                               void* stream) {
   if (n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0 || chunk_size <= 0)
     return KDA_ERR_INVALID_ARGUMENT;
+  // checkpoints: ckpt_every > 0 and a multiple of the chunk size; ckpt holds
+  // total_tokens / ckpt_every slots and may be NULL only when that is zero
+  int64_t n_slots = 0;
+  if (ckpt_every != 0 || ckpt) {
+    if (ckpt_every <= 0 || ckpt_every % chunk_size != 0) return KDA_ERR_INVALID_ARGUMENT;
+    n_slots = total_tokens / ckpt_every;
+    if (n_slots > 0 && (!ckpt || !aligned16(ckpt))) return KDA_ERR_INVALID_ARGUMENT;
+    if (n_slots == 0) ckpt = nullptr;
+  }
+  if (ckpt) {
+    // the checkpoints are outputs: they must not overlap any input or other output
+    const char* cb = (const char*)ckpt;
+    const char* ce = cb + (size_t)n_slots * n_heads * dk * dv * sizeof(float);
+    const size_t esz = qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    struct R { const void* p; size_t n; } bufs[] = {
+        {q, (size_t)total_tokens * n_heads * dk * esz}, {k, (size_t)total_tokens * n_heads * dk * esz},
+        {v, (size_t)total_tokens * n_heads * dv * esz}, {log_alpha, (size_t)total_tokens * n_heads * dk * 4},
+        {beta, (size_t)total_tokens * n_heads * 4}, {o, (size_t)total_tokens * n_heads * dv * 4},
+        {h0, h0 ? (size_t)n_seqs * n_heads * dk * dv * 4 : 0}, {hT, hT ? (size_t)n_seqs * n_heads * dk * dv * 4 : 0},
+        {cu_seqlens, cu_seqlens ? (size_t)(n_seqs + 1) * 4 : 0}};
+    for (const R& r : bufs) {
+      const char* b = (const char*)r.p;
+      if (r.n && b < ce && cb < b + r.n) return KDA_ERR_INVALID_ARGUMENT;
+    }
+  }
   if (qkv_dtype != KDA_DTYPE_F32 && qkv_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
   if (n_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -57,10 +82,29 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
 
   kda::ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0;
-  a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT;
+  a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT; a.ckpt = ckpt; a.ckpt_every = ckpt ? ckpt_every : 1;
   a.n_seqs = n_seqs; a.n_heads = n_heads; a.dk = dk; a.dv = dv; a.chunk_size = chunk_size;
   a.total_tokens = total_tokens; a.seq_len = seq_len; a.bf16 = bf16; a.stream = stream;
   return kda::launch_chunk_fwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* h0, const int32_t* cu_seqlens,
+                         int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                         int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
+                         void* stream) {
+  return chunk_common(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, chunk_size,
+                      qkv_dtype, o, hT, 0, nullptr, stream);
+}
+
+kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* v, const float* log_alpha,
+                                      const float* beta, const float* h0, const int32_t* cu_seqlens,
+                                      int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                      int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
+                                      int32_t ckpt_every, float* ckpt, void* stream) {
+  if (ckpt_every <= 0) return KDA_ERR_INVALID_ARGUMENT;
+  return chunk_common(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, chunk_size,
+                      qkv_dtype, o, hT, ckpt_every, ckpt, stream);
 }
 
 static kda_status recurrent_common(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -252,8 +252,8 @@ template <int C, int DK, int BV, Prec P, typename InT>
 __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* h0,
-    const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT, int n_chains, int H, int DV,
-    int64_t seq_len) {
+    const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT, float* __restrict__ ckpt,
+    int ckpt_every, int n_chains, int H, int DV, int64_t seq_len) {
   using L = Lay<C, DK, BV, P>;
   using T = typename L::T;
   constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
@@ -446,6 +446,18 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   f32x4 Opend[U_SLOTS];
   int64_t o_begin = 0;
   int o_len = 0;
+  // the fp32 master state of this value tile into a [DK][DV] row-major state
+  auto store_state = [&](float* sp) {
+#pragma unroll
+    for (int s = 0; s < S_SLOTS; ++s) {
+      const int id = wave + NW * s;
+      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
+        const int a = id % NA, j = id / NA;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
+      }
+    }
+  };
   auto store_pending = [&]() {
     char* ob = reinterpret_cast<char*>(o + ((size_t)o_begin * H + h) * DV + j0);
 #pragma unroll
@@ -936,6 +948,13 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
     write_ST();
+    // prefix-cache checkpoint: the state after p tokens of this sequence, p a multiple of
+    // ckpt_every, goes to slot (sequence start + p) / ckpt_every - 1 (distinct for every
+    // checkpoint of every packed sequence)
+    if (ckpt && (c_begin + Lc - t_begin) % ckpt_every == 0) {
+      const int64_t slot = (c_begin + Lc) / ckpt_every - 1;
+      store_state(ckpt + ((size_t)slot * H + h) * DK * DV);
+    }
     o_begin = c_begin;
     o_len = Lc;
     // The next chunk's gate stage writes only RB (shared with W, dead after B_g) and BH
@@ -944,18 +963,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   }
 
   if (nchunks > 0) store_pending();
-  if (hT) {
-    float* hp = hT + (size_t)chain * DK * DV;
-#pragma unroll
-    for (int s = 0; s < S_SLOTS; ++s) {
-      const int id = wave + NW * s;
-      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
-        const int a = id % NA, j = id / NA;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
-      }
-    }
-  }
+  if (hT) store_state(hT + (size_t)chain * DK * DV);
 }
 
 // ---------------------------------------------------------------------------
@@ -976,8 +984,8 @@ static hipError_t launch_one(const ChunkArgs& a) {
   const int ntile = a.dv / BV;
   const int grid = ((n_chains + 7) / 8) * 8 * ntile;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q, (const InT*)a.k,
-                     (const InT*)a.v, a.log_alpha, a.beta, a.h0, a.cu_seqlens, a.o, a.hT, n_chains, a.n_heads, a.dv,
-                     a.seq_len);
+                     (const InT*)a.v, a.log_alpha, a.beta, a.h0, a.cu_seqlens, a.o, a.hT, a.ckpt, a.ckpt_every,
+                     n_chains, a.n_heads, a.dv, a.seq_len);
   return hipGetLastError();
 }
 

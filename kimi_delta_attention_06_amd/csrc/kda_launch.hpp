@@ -30,6 +30,8 @@ struct ChunkArgs {
   const int32_t* cu_seqlens; // may be null (equal lengths)
   float* o;
   float* hT;                // may be null
+  float* ckpt;              // may be null: no checkpoints
+  int ckpt_every;           // checkpoint spacing in tokens (a multiple of chunk_size)
   int n_seqs, n_heads, dk, dv, chunk_size;
   int64_t total_tokens;
   int64_t seq_len;          // used when cu_seqlens is null

@@ -19,8 +19,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_recurrent_step", "kda_recurrent_verify", "kda_status_string",
-                          "kda_version"}
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_checkpointed", "kda_recurrent_step",
+                          "kda_recurrent_verify", "kda_status_string", "kda_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -93,3 +93,27 @@ def test_recurrent_verify_rejects(kw, code):
 
 def test_recurrent_verify_zero_sequences_is_a_no_op():
     assert verify(N=0, nc=None) == 0
+
+
+def ckpt_call(**kw):
+    a = dict(q=P, k=P, v=P, la=P, b=P, h0=None, cu=None, N=1, T=1024, H=2, dk=128, dv=128, C=64,
+             dt=_lib.KDA_DTYPE_BF16, o=P * 8, hT=None, every=512, ck=P * 32)
+    a.update(kw)
+    return lib.kda_chunk_fwd_checkpointed(a["q"], a["k"], a["v"], a["la"], a["b"], a["h0"], a["cu"], a["N"],
+                                          a["T"], a["H"], a["dk"], a["dv"], a["C"], a["dt"], a["o"], a["hT"],
+                                          a["every"], a["ck"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(every=0), 1), (dict(every=-512), 1), (dict(every=96), 1), (dict(ck=None), 1), (dict(ck=P * 32 + 4), 1),
+    (dict(ck=P * 8), 1),  # checkpoints overlap o
+    (dict(ck=P), 1),      # checkpoints overlap q
+    (dict(dk=96), 2),
+])
+def test_chunk_fwd_checkpointed_rejects(kw, code):
+    assert ckpt_call(**kw) == code
+
+
+def test_chunk_fwd_checkpointed_without_slots_accepts_null():
+    # no tokens: no checkpoint slot exists, so ckpt may be NULL
+    assert ckpt_call(N=0, T=0, q=None, k=None, v=None, la=None, b=None, o=None, ck=None) == 0
