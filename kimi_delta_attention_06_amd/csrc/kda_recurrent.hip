@@ -18,18 +18,18 @@
 // after token c - 1 (not at all for c = 0); later tokens are drafts whose updates are
 // dropped.  Without counts, every token is committed.
 //
-// Thread map (256 threads): thread t owns value columns [4 cg, 4 cg + 4) and
-// RPT consecutive key rows of row group rg, cg = t % (DV/4), rg = t / (DV/4).
+// Thread map (NTH threads: 512 for a 128x128 state, else 256): thread t owns value
+// columns [4 cg, 4 cg + 4) and RPT consecutive key rows of row group rg,
+// cg = t % (DV/4), rg = t / (DV/4).
 // Every HBM access of S is a float4 per lane; lanes 0..DV/4-1 of a row cover
 // the row's DV*4 contiguous bytes.  The dk reduction is in-lane over RPT rows,
-// then across the row groups of a wave by xor-shuffles, then across the four
-// waves through LDS (one barrier per token, double-buffered partials).
+// then across the row groups of a wave by xor-shuffles, then across the waves
+// through LDS (one barrier per token, double-buffered partials).
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
-constexpr int kRecThreads = 256;
 constexpr int kMaxReplay = 8;
 
 template <typename InT>
@@ -37,17 +37,17 @@ __device__ __forceinline__ float ld_in(const InT* p, size_t i) {
   return to_f32(p[i]);
 }
 
-template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(kRecThreads) void recurrent_step_kernel(
+template <int DK, int DV, int NTH, typename InT>
+__global__ __launch_bounds__(NTH) void recurrent_step_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, float* __restrict__ S,
     float* __restrict__ o, const int32_t* __restrict__ n_commit, int n_tokens, int H) {
-  constexpr int CG = DV / 4;           // column groups (float4 each)
-  constexpr int RG = kRecThreads / CG; // row groups
-  constexpr int RPT = DK / RG;         // rows per thread
-  constexpr int NW = kRecThreads / kWave;
+  constexpr int CG = DV / 4;    // column groups (float4 each)
+  constexpr int RG = NTH / CG;  // row groups
+  constexpr int RPT = DK / RG;  // rows per thread
+  constexpr int NW = NTH / kWave;
   constexpr int RG_PER_WAVE = kWave / CG;
-  static_assert(RPT * RG == DK && CG * RG == kRecThreads, "thread map");
+  static_assert(RPT * RG == DK && CG * RG == NTH, "thread map");
 
   __shared__ float s_q[kMaxReplay][DK];
   __shared__ float s_k[kMaxReplay][DK];
@@ -74,14 +74,14 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_step_kernel(
     st[i] = *reinterpret_cast<const float4*>(Sp + (size_t)(rg * RPT + i) * DV + cg * 4);
 
   // Stage the token inputs (the state loads above are still in flight).
-  for (int idx = t; idx < n_tokens * DK; idx += kRecThreads) {
+  for (int idx = t; idx < n_tokens * DK; idx += NTH) {
     const int tok = idx / DK, c = idx - tok * DK;
     const size_t off = ((size_t)(n * n_tokens + tok) * H + h) * DK + c;
     s_q[tok][c] = ld_in(q, off);
     s_k[tok][c] = ld_in(k, off);
     s_a[tok][c] = expf(log_alpha[off]);
   }
-  for (int idx = t; idx < n_tokens * DV; idx += kRecThreads) {
+  for (int idx = t; idx < n_tokens * DV; idx += NTH) {
     const int tok = idx / DV, j = idx - tok * DV;
     s_v[tok][j] = ld_in(v, ((size_t)(n * n_tokens + tok) * H + h) * DV + j);
   }
@@ -152,8 +152,9 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_step_kernel(
 
 template <int DK, int DV, typename InT>
 static hipError_t launch_rec(const RecurrentArgs& a) {
-  dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_heads)), block(kRecThreads);
-  hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, InT>), grid, block, 0, (hipStream_t)a.stream,
+  constexpr int NTH = (DK == 128 && DV == 128) ? 512 : 256;
+  dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_heads)), block(NTH);
+  hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, NTH, InT>), grid, block, 0, (hipStream_t)a.stream,
                      (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, a.S, a.o,
                      a.n_commit, a.n_tokens, a.n_heads);
   return hipGetLastError();

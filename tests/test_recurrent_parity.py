@@ -132,3 +132,19 @@ def test_verify_with_full_commit_equals_step():
                               torch.full((12,), 8, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_steep_decay_rows():
+    """Rows decaying by 60-80 nats over the call (state rows driven to ~0) beside ordinary ones."""
+    import kimi_delta_attention_06_amd as kda
+    inp = kda_inputs.make_decode_inputs(kda_inputs.DECODE_256x32, 8, device="cuda", n_seqs=6, seed=95)
+    inp["log_alpha"][1, :, 3, :16] = -10.0   # sequence 1, head 3: 80 nats over 8 tokens
+    inp["log_alpha"][4, :, :, 100:] = -7.6   # sequence 4, all heads: 60.8 nats
+    S0 = inp["S"].cpu()
+    o = kda.recurrent_step(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.kda_recurrent_step(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S0)
+    eo, _ = errs(o, o_ref)
+    es, _ = errs(inp["S"], S_ref)
+    print("steep decay: o max err %.3e | S max err %.3e" % (eo, es))
+    assert eo <= 1e-5 and es <= 1e-5
