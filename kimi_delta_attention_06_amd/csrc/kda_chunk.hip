@@ -824,14 +824,23 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
           // one accumulator per term A_RJ T_JI: the J = I0 terms of every R start at once,
           // and each later term waits only for its own T_JI
           f32x4 Xp[NB][NB];
-          auto term = [&](int R, int J) {
+          // one 16x16x16 product: fp16 operands for bf16 inputs (rounding at the level of the
+          // fp16 T Diag(beta) the WY products use anyway), four fp32 steps for fp32 inputs
+          auto prod = [&](const float4& x, const float (&y)[4]) {
             f32x4 acc = zero4();
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[R][J].x, tb[J][0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[R][J].y, tb[J][1], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[R][J].z, tb[J][2], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[R][J].w, tb[J][3], acc, 0, 0, 0);
+            if constexpr (P == Prec::Mixed) {
+              const half4 xh = {(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w};
+              const half4 yh = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+              acc = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, yh, acc, 0, 0, 0);
+            } else {
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, y[0], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, y[1], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, y[2], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, y[3], acc, 0, 0, 0);
+            }
             return acc;
           };
+          auto term = [&](int R, int J) { return prod(a[R][J], tb[J]); };
 #pragma unroll
           for (int R = I0 + 1; R < NB; ++R) Xp[R][I0] = term(R, I0);
 #pragma unroll
@@ -841,11 +850,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
             f32x4 X = Xp[R][I0];
 #pragma unroll
             for (int J = I0 + 1; J < R; ++J) X += Xp[R][J];
-            f32x4 Y = zero4();
-            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr[R].x, X[0], Y, 0, 0, 0);
-            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr[R].y, X[1], Y, 0, 0, 0);
-            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr[R].z, X[2], Y, 0, 0, 0);
-            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tr[R].w, X[3], Y, 0, 0, 0);
+            const float xv[4] = {X[0], X[1], X[2], X[3]};
+            const f32x4 Y = prod(tr[R], xv);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               tb[R][i] = -Y[i];
