@@ -773,27 +773,36 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       } else {
         const float4 pk = sPT[(base + 1) * 64 + l];
         accKd[0] += pk.x; accKd[1] += pk.y; accKd[2] += pk.z; accKd[3] += pk.w;
-        // A_RR (strict lower, rows scaled by beta) stays in the accumulator layout: lane
-        // (column lr, group lg) holds A[4lg + u][lr].  Lane (lg, j) computes rows 4lg..4lg+3
-        // of column j of T_RR = (I + A_RR)^-1 by right-looking forward substitution: at
-        // pivot i, A[4lg + u][i] comes from lane i of the same 16-lane row (a DPP row
-        // broadcast, independent of x) and the final x[i] from lane group i/4 (one lane
-        // permute).  A is zero on and above the diagonal, so the update needs no mask.
-        float av[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) av[u] = (4 * lg + u > lr) ? bet[u] * accKd[u] : 0.f;
-        float xr[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xr[u] = (4 * lg + u == lr) ? 1.f : 0.f;
-        static_for<0, 15>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          const float xi = __shfl(xr[i & 3], 16 * (i >> 2) + lr, kWave);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) xr[u] -= row_bcast16<i>(av[u]) * xi;
-        });
+        // A_RR (strict lower, rows scaled by beta), row-major into the diagonal tile of the
+        // A/T region; each lane then reads back one row (one wave's LDS operations complete
+        // in order, so no barrier is needed).
         float* blk = sAK + 16 * eR * LDA + 16 * eR;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) blk[(4 * lg + u) * LDA + lr] = xr[u];
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * lg + u;
+          blk[r * LDA + lr] = r > lr ? bet[u] * accKd[u] : 0.f;
+        }
+        __builtin_amdgcn_wave_barrier();  // the rows read below were written by other lanes
+        float ar[16];  // A[lr][0..15]
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(blk + lr * LDA + 4 * q4);
+          ar[4 * q4] = v4.x; ar[4 * q4 + 1] = v4.y; ar[4 * q4 + 2] = v4.z; ar[4 * q4 + 3] = v4.w;
+        }
+        // T_RR = (I + A_RR)^-1 by right-looking forward substitution over its rows: lane
+        // (row r = lane & 15, group g) holds T[r][4g .. 4g+3].  Row i is final once pivots
+        // < i are folded in; it reaches every lane of the 16-lane row through a DPP row
+        // broadcast from lane i, and A[r][i] = 0 for r <= i, so the update needs no mask.
+        float xr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xr[u] = (lr == 4 * lg + u) ? 1.f : 0.f;
+        static_for<0, 15>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xr[u] -= ar[i] * row_bcast16<i>(xr[u]);
+        });
+        // T_RR row-major over A (all reads of A precede these writes)
+        store4(blk + lr * LDA + 4 * lg, xr[0], xr[1], xr[2], xr[3]);
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_c
