@@ -546,7 +546,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         for (int j = 0; j < CPL; ++j) {
           const float eL = __builtin_amdgcn_exp2f(cc[j] - 0.5f * ss[j]);  // e^{c - s/2} <= e^{|s|/2}
           const float eRt = __builtin_amdgcn_exp2f(0.5f * ss[j] - cc[j]);
-          const float bh = __builtin_amdgcn_exp2f(0.5f * ss[j]);  // e^{s/2} <= 1 (below 2^-126 flushes to 0)
+          // e^{s/2} <= 1 is e^{c - s/2} at the block's last row (c = s there, and s - s/2
+          // is exact), so lane 15 of the row supplies it (below 2^-126 it flushes to 0)
+          const float bh = row_bcast16<15>(eL);
           const float kk = kL[j];
           qL[j] *= eL;
           kL[j] = kk * eL;
