@@ -18,13 +18,12 @@
 // after token c - 1 (not at all for c = 0); later tokens are drafts whose updates are
 // dropped.  Without counts, every token is committed.
 //
-// Thread map (NTH threads: 512 for a 128x128 state, else 256): thread t owns value
-// columns [4 cg, 4 cg + 4) and RPT consecutive key rows of row group rg,
-// cg = t % (DV/4), rg = t / (DV/4).
-// Every HBM access of S is a float4 per lane; lanes 0..DV/4-1 of a row cover
-// the row's DV*4 contiguous bytes.  The dk reduction is in-lane over RPT rows,
-// then across the row groups of a wave by xor-shuffles, then across the waves
-// through LDS (one barrier per token, double-buffered partials).
+// Thread map: each wave owns 16 value columns and all DK rows, so the dk reductions
+// never leave the wave and the token loop has no barrier.  Lane l of wave w holds
+// row group rg = l & 15 (RPT = DK/16 rows: rg, rg + 16, ...) and columns
+// [4 cg, 4 cg + 4) with cg = 4 w + (l >> 4); DV/16 waves per workgroup.  A
+// reduction is in-lane over RPT rows, then a DPP scan across the 16 lanes of a row
+// and a DPP broadcast of lane 15.  Every HBM access of S is a float4 per lane.
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -37,17 +36,30 @@ __device__ __forceinline__ float ld_in(const InT* p, size_t i) {
   return to_f32(p[i]);
 }
 
-template <int DK, int DV, int NTH, typename InT>
-__global__ __launch_bounds__(NTH) void recurrent_step_kernel(
+// sum over the 16 lanes of each DPP row, returned to every lane of the row
+template <int N>
+__device__ __forceinline__ float row_shr_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 | N, 0xf,
+                                                                       0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x = row_shr_add<1>(x);
+  x = row_shr_add<2>(x);
+  x = row_shr_add<4>(x);
+  x = row_shr_add<8>(x);
+  // lane 15 of the row now holds the total: DPP row_newbcast:15
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x15f, 0xf, 0xf,
+                                                                false));
+}
+
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(DV * 4) void recurrent_step_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, float* __restrict__ S,
     float* __restrict__ o, const int32_t* __restrict__ n_commit, int n_tokens, int H) {
-  constexpr int CG = DV / 4;    // column groups (float4 each)
-  constexpr int RG = NTH / CG;  // row groups
-  constexpr int RPT = DK / RG;  // rows per thread
-  constexpr int NW = NTH / kWave;
-  constexpr int RG_PER_WAVE = kWave / CG;
-  static_assert(RPT * RG == DK && CG * RG == NTH, "thread map");
+  constexpr int NTH = DV * 4;  // DV/16 waves
+  constexpr int RPT = DK / 16;
+  static_assert(DV % 16 == 0 && DK % 16 == 0, "thread map");
 
   __shared__ float s_q[kMaxReplay][DK];
   __shared__ float s_k[kMaxReplay][DK];
@@ -55,13 +67,12 @@ __global__ __launch_bounds__(NTH) void recurrent_step_kernel(
   __shared__ float s_v[kMaxReplay][DV];
   __shared__ float s_b[kMaxReplay];
   __shared__ float s_qk[kMaxReplay];
-  __shared__ float4 s_part[2][NW][CG][2];
 
   const int nh = blockIdx.x;  // sequence * H + head
   const int n = nh / H, h = nh - n * H;
   const int t = threadIdx.x;
-  const int cg = t % CG, rg = t / CG;
   const int lane = t % kWave, wave = t / kWave;
+  const int rg = lane & 15, cg = 4 * wave + (lane >> 4);
 
   // tokens whose updates reach the stored state (clamped to [0, n_tokens])
   int commit = n_tokens;
@@ -71,7 +82,7 @@ __global__ __launch_bounds__(NTH) void recurrent_step_kernel(
   float4 st[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    st[i] = *reinterpret_cast<const float4*>(Sp + (size_t)(rg * RPT + i) * DV + cg * 4);
+    st[i] = *reinterpret_cast<const float4*>(Sp + (size_t)(rg + 16 * i) * DV + cg * 4);
 
   // Stage the token inputs (the state loads above are still in flight).
   for (int idx = t; idx < n_tokens * DK; idx += NTH) {
@@ -87,9 +98,8 @@ __global__ __launch_bounds__(NTH) void recurrent_step_kernel(
   }
   if (t < n_tokens) s_b[t] = beta[(size_t)(n * n_tokens + t) * H + h];
   __syncthreads();
-
-  // q . k per token: wave w reduces tokens w, w + NW, ...
-  for (int tok = wave; tok < n_tokens; tok += NW) {
+  // q . k per token: wave w reduces tokens w, w + waves, ...
+  for (int tok = wave; tok < n_tokens; tok += NTH / kWave) {
     float p = 0.f;
     for (int c = lane; c < DK; c += kWave) p += s_q[tok][c] * s_k[tok][c];
 #pragma unroll
@@ -102,32 +112,14 @@ __global__ __launch_bounds__(NTH) void recurrent_step_kernel(
     float4 u = make_float4(0.f, 0.f, 0.f, 0.f), w = u;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = rg * RPT + i;
+      const int r = rg + 16 * i;
       const float a = s_a[tok][r], kr = s_k[tok][r], qr = s_q[tok][r];
       st[i].x *= a; st[i].y *= a; st[i].z *= a; st[i].w *= a;
       u.x += st[i].x * kr; u.y += st[i].y * kr; u.z += st[i].z * kr; u.w += st[i].w * kr;
       w.x += st[i].x * qr; w.y += st[i].y * qr; w.z += st[i].z * qr; w.w += st[i].w * qr;
     }
-#pragma unroll
-    for (int m = CG; m < kWave; m <<= 1) {
-      u.x += wave_xor(u.x, m); u.y += wave_xor(u.y, m); u.z += wave_xor(u.z, m); u.w += wave_xor(u.w, m);
-      w.x += wave_xor(w.x, m); w.y += wave_xor(w.y, m); w.z += wave_xor(w.z, m); w.w += wave_xor(w.w, m);
-    }
-    const int buf = tok & 1;
-    if (lane < CG) {
-      s_part[buf][wave][cg][0] = u;
-      s_part[buf][wave][cg][1] = w;
-    }
-    (void)RG_PER_WAVE;
-    __syncthreads();
-    u = s_part[buf][0][cg][0];
-    w = s_part[buf][0][cg][1];
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) {
-      const float4 pu = s_part[buf][ww][cg][0], pw = s_part[buf][ww][cg][1];
-      u.x += pu.x; u.y += pu.y; u.z += pu.z; u.w += pu.w;
-      w.x += pw.x; w.y += pw.y; w.z += pw.z; w.w += pw.w;
-    }
+    u.x = row_sum16(u.x); u.y = row_sum16(u.y); u.z = row_sum16(u.z); u.w = row_sum16(u.w);
+    w.x = row_sum16(w.x); w.y = row_sum16(w.y); w.z = row_sum16(w.z); w.w = row_sum16(w.w);
     const float b = s_b[tok], qk = s_qk[tok];
     const float4 vv = *reinterpret_cast<const float4*>(&s_v[tok][cg * 4]);
     float4 d;
@@ -139,22 +131,21 @@ __global__ __launch_bounds__(NTH) void recurrent_step_kernel(
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const float kr = s_k[tok][rg * RPT + i];
+      const float kr = s_k[tok][rg + 16 * i];
       st[i].x += kr * d.x; st[i].y += kr * d.y; st[i].z += kr * d.z; st[i].w += kr * d.w;
     }
     if (tok + 1 == commit) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i)
-        *reinterpret_cast<float4*>(Sp + (size_t)(rg * RPT + i) * DV + cg * 4) = st[i];
+        *reinterpret_cast<float4*>(Sp + (size_t)(rg + 16 * i) * DV + cg * 4) = st[i];
     }
   }
 }
 
 template <int DK, int DV, typename InT>
 static hipError_t launch_rec(const RecurrentArgs& a) {
-  constexpr int NTH = (DK == 128 && DV == 128) ? 512 : 256;
-  dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_heads)), block(NTH);
-  hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, NTH, InT>), grid, block, 0, (hipStream_t)a.stream,
+  dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_heads)), block(DV * 4);
+  hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, InT>), grid, block, 0, (hipStream_t)a.stream,
                      (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, a.S, a.o,
                      a.n_commit, a.n_tokens, a.n_heads);
   return hipGetLastError();
