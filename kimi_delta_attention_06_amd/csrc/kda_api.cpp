@@ -75,6 +75,7 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
     }
   }
   if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // cu_seqlens is int32
+  if ((int64_t)n_seqs * n_heads * 8 > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // grid: chains x value tiles
   if (!dims_ok(dk) || !dims_ok(dv)) return KDA_ERR_UNSUPPORTED;
   const bool bf16 = qkv_dtype == KDA_DTYPE_BF16;
   if (!kda::chunk_fwd_supported(dk, dv, chunk_size, bf16)) return KDA_ERR_UNSUPPORTED;

@@ -52,6 +52,7 @@
 //     A's are bf16 (range) and M's go on the fp32 matrix core (range and precision).
 //     The diagonal of M (q_r . k_r) multiplies U in fp32 outside the MFMA.
 //   F32 (fp32 inputs): every product on the fp32 MFMA (16x16x4).
+#include <atomic>
 #include <type_traits>
 
 #include "kda_common.hpp"
@@ -991,11 +992,17 @@ static hipError_t launch_one(const ChunkArgs& a) {
   constexpr size_t lds = lds_bytes<C, DK, BV, P>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = chunk_fwd_kernel<C, DK, BV, P, InT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // the dynamic-LDS limit is a per-device attribute: set it once per device (one bit
+  // each, thread-safe); devices past the 64th set it on every launch
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (bit) attr_done.fetch_or(bit, std::memory_order_release);
   }
   const int n_chains = a.n_seqs * a.n_heads;
   const int ntile = a.dv / BV;

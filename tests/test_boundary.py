@@ -54,6 +54,7 @@ def step(**kw):
     (dict(dt=7), 1), (dict(q=P + 4), 1), (dict(T=63, N=2), 1), (dict(N=0, T=5), 1),
     (dict(dk=96), 2), (dict(dv=32), 2), (dict(C=48), 2), (dict(C=128), 2),
     (dict(o=P), 1),  # o overlaps q
+    (dict(N=1 << 20, H=1024, T=1 << 20, o=1 << 50), 2),  # chains x value tiles exceed the grid
 ])
 def test_chunk_fwd_rejects(kw, code):
     assert chunk(**kw) == code
