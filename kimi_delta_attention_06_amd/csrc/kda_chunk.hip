@@ -363,7 +363,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   const bool v_act = tid < C * VPR;
   int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
 
-  // U / O tiles (R, j): id = R + NB*j owned by wave id % NW
+  // U / O tiles (R, j): id = R + NB*j owned by wave id % NW, held transposed: lane
+  // (token 16R + (l & 15), columns 16j + 4 (l >> 4) .. +3)
   constexpr int U_SLOTS = (NB * NJ + NW - 1) / NW;
 
   const int64_t nchunks = (t_end - t_begin + C - 1) / C;
@@ -467,12 +468,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         const int R = id % NB, j = id / NB;
         const uint32_t hdv = (uint32_t)(H * DV);
-        const uint32_t off0 = ((uint32_t)(16 * R + 4 * lg) * hdv + (uint32_t)(16 * j + lr)) * 4u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * R + 4 * lg + i;
-          if (r < o_len) *reinterpret_cast<float*>(ob + off0 + (uint32_t)i * hdv * 4u) = Opend[s][i];
-        }
+        // lane (token lr, column group lg) holds o[16R + lr][16j + 4lg .. +3]
+        const int r = 16 * R + lr;
+        const uint32_t off = ((uint32_t)r * hdv + (uint32_t)(16 * j + 4 * lg)) * 4u;
+        if (r < o_len)
+          *reinterpret_cast<float4*>(ob + off) = make_float4(Opend[s][0], Opend[s][1], Opend[s][2], Opend[s][3]);
       }
     }
   };
@@ -923,7 +923,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       Oacc[s] = zero4();
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         const int R = id % NB, j = id / NB;
-        mma_lds<T, KS, CK / KS>(Uacc[s], sTB + 16 * R * LDC, LDC, sVT + 16 * j * LDC, LDC);
+        mma_lds<T, KS, CK / KS>(Uacc[s], sVT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_f
@@ -935,11 +935,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         const int R = id % NB, j = id / NB;
         f32x4 ws = zero4();
-        mma_lds<T, KS, DK / KS>(ws, sW + 16 * R * LDD, LDD, sST + 16 * j * LDD, LDD);
-        mma_lds<T, KS, DK / KS>(Oacc[s], sQG + 16 * R * LDD, LDD, sST + 16 * j * LDD, LDD);
+        mma_lds<T, KS, DK / KS>(ws, sST + 16 * j * LDD, LDD, sW + 16 * R * LDD, LDD);
+        mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Uacc[s][i] -= ws[i];
-        store4(sUT + (16 * j + lr) * LDC + 16 * R + 4 * lg, Uacc[s][0], Uacc[s][1], Uacc[s][2], Uacc[s][3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(Uacc[s][i]);
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_g
@@ -950,9 +951,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       const int id = wave + NW * s;
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         const int R = id % NB, j = id / NB;
-        mma_lds<T, KS, CK / KS>(Oacc[s], sAQ + 16 * R * LDC, LDC, sUT + 16 * j * LDC, LDC);
+        mma_lds<T, KS, CK / KS>(Oacc[s], sUT + 16 * j * LDC, LDC, sAQ + 16 * R * LDC, LDC);
+        {
+          const float dq = sDQ[16 * R + lr];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + sDQ[16 * R + 4 * lg + i] * Uacc[s][i];
+          for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
+        }
       }
     }
 #pragma unroll
