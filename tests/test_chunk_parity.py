@@ -103,6 +103,20 @@ def test_mixed_narrow_and_wide_decay_channels():
     check_bf16(o, hT, o_ref, h_ref)
 
 
+@pytest.mark.parametrize("C,dk,dv", [(64, 64, 64), (64, 64, 128), (32, 128, 64), (16, 64, 128)])
+def test_small_varlen_fp32_more_shapes(C, dk, dv):
+    """fp32 inputs at the remaining supported (chunk, dk, dv) combinations (C = 64 needs dk = 64)."""
+    lens = [140, 0, 1, 64, 29]
+    print("small varlen fp32 C=%d dk=%d dv=%d" % (C, dk, dv), flush=True)
+    inp = kda_inputs.make_custom_chunk_inputs(lens, 2, dk, dv, torch.float32, h0_std=0.02, seed=17 + C + dv,
+                                              device="cuda")
+    o, hT = run(inp, chunk_size=C)
+    o_ref, h_ref = ref(inp)
+    eo, _ = report("o", o, o_ref)
+    eh, _ = report("hT", hT, h_ref)
+    assert eo <= F32_TOL and eh <= F32_TOL
+
+
 @pytest.mark.parametrize("C", [16, 32])
 @pytest.mark.parametrize("dk", [64, 128])
 def test_small_varlen_fp32(C, dk):
