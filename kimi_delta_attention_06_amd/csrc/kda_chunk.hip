@@ -120,7 +120,6 @@ __device__ __forceinline__ void mma_lds(f32x4& acc, const T* A, int lda, const T
   for (int s = 0; s < NST; ++s) mma_step(acc, a + s * KS, b + s * KS);
 }
 
-// inclusive prefix sum across the 16 lanes of each DPP row
 // f(std::integral_constant<int, I>{}) for I = B .. E-1, each I a compile-time constant
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -136,6 +135,8 @@ __device__ __forceinline__ float row_bcast16(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
 }
 
+
+// lane i of each 16-lane row receives lane i - N (0 for i < N): a step of the row scan
 template <int N>
 __device__ __forceinline__ float shr16(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xf, 0xf, false));
@@ -363,9 +364,24 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   const bool v_act = tid < C * VPR;
   int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
 
-  // U / O tiles (R, j): id = R + NB*j owned by wave id % NW, held transposed: lane
-  // (token 16R + (l & 15), columns 16j + 4 (l >> 4) .. +3)
+  // U / O tiles (R, j), held transposed: lane (token 16R + (l & 15), columns
+  // 16j + 4 (l >> 4) .. +3)
   constexpr int U_SLOTS = (NB * NJ + NW - 1) / NW;
+  // With 4 row blocks, 4 value tiles and 8 waves, slot s of wave w holds row block
+  // 2s + w/4: slot 0 only ever sees tokens below 32 and slot 1 below 64, so products
+  // over tokens whose token operand is block-lower-triangular (T Diag(beta), M) stop
+  // at a compile-time k-step.
+  constexpr bool UO_SPLIT = NB == 4 && NJ == 4 && NW == 8;
+  auto uo_tile = [&](int s, int& R, int& j) {
+    if constexpr (UO_SPLIT) {
+      R = 2 * s + (wave >> 2);
+      j = wave & 3;
+    } else {
+      const int id = wave + NW * s;
+      R = id % NB;
+      j = id / NB;
+    }
+  };
 
   const int64_t nchunks = (t_end - t_begin + C - 1) / C;
 
@@ -466,7 +482,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     for (int s = 0; s < U_SLOTS; ++s) {
       const int id = wave + NW * s;
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        const int R = id % NB, j = id / NB;
+        int R, j;
+        uo_tile(s, R, j);
         const uint32_t hdv = (uint32_t)(H * DV);
         // lane (token lr, column group lg) holds o[16R + lr][16j + 4lg .. +3]
         const int r = 16 * R + lr;
@@ -904,28 +921,37 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     __syncthreads();  // ------------------------------------------------------------- B_e
 
     // ================= WY: W^T = Kg^T Tb^T ; Ut = Tb V =================
-#pragma unroll
-    for (int s = 0; s < (NA * NB + NW - 1) / NW; ++s) {
+    static_for<0, (NA * NB + NW - 1) / NW>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
       const int id = wave + NW * s;
       if ((NA * NB) % NW == 0 || id < NA * NB) {
         const int a = id % NA, R = id / NA;
         f32x4 acc = zero4();
-        mma_lds<T, KS, CK / KS>(acc, sKGT + 16 * a * LDC, LDC, sTB + 16 * R * LDC, LDC);
+        if constexpr (NA == NW) {
+          // slot s holds row block s: only tokens below 16 (s + 1) contribute (T is lower triangular)
+          constexpr int steps = (16 * (s + 1) + KS - 1) / KS < CK / KS ? (16 * (s + 1) + KS - 1) / KS : CK / KS;
+          mma_lds<T, KS, steps>(acc, sKGT + 16 * a * LDC, LDC, sTB + 16 * R * LDC, LDC);
+        } else {
+          mma_lds<T, KS, CK / KS>(acc, sKGT + 16 * a * LDC, LDC, sTB + 16 * R * LDC, LDC);
+        }
         // rows = channels 16a + 4*lg + i, column = token 16R + lr
         store4(sW + (16 * R + lr) * LDD + 16 * a + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
       }
-    }
+    });
     f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
-#pragma unroll
-    for (int s = 0; s < U_SLOTS; ++s) {
+    static_for<0, U_SLOTS>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
+                                     : CK / KS;
       const int id = wave + NW * s;
       Uacc[s] = zero4();
       Oacc[s] = zero4();
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        const int R = id % NB, j = id / NB;
-        mma_lds<T, KS, CK / KS>(Uacc[s], sVT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
+        int R, j;
+        uo_tile(s, R, j);
+        mma_lds<T, KS, steps>(Uacc[s], sVT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
       }
-    }
+    });
     __syncthreads();  // ------------------------------------------------------------- B_f
 
     // ================= state stage 1: U = Ut - W S ; O = Qg S =================
@@ -933,7 +959,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     for (int s = 0; s < U_SLOTS; ++s) {
       const int id = wave + NW * s;
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        const int R = id % NB, j = id / NB;
+        int R, j;
+        uo_tile(s, R, j);
         f32x4 ws = zero4();
         mma_lds<T, KS, DK / KS>(ws, sST + 16 * j * LDD, LDD, sW + 16 * R * LDD, LDD);
         mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
@@ -946,19 +973,20 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     __syncthreads();  // ------------------------------------------------------------- B_g
 
     // ================= state stage 2: O += M U ; S <- e^{g} S + Kd^T U =================
-#pragma unroll
-    for (int s = 0; s < U_SLOTS; ++s) {
+    static_for<0, U_SLOTS>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
+                                     : CK / KS;
       const int id = wave + NW * s;
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        const int R = id % NB, j = id / NB;
-        mma_lds<T, KS, CK / KS>(Oacc[s], sUT + 16 * j * LDC, LDC, sAQ + 16 * R * LDC, LDC);
-        {
-          const float dq = sDQ[16 * R + lr];
+        int R, j;
+        uo_tile(s, R, j);
+        mma_lds<T, KS, steps>(Oacc[s], sUT + 16 * j * LDC, LDC, sAQ + 16 * R * LDC, LDC);
+        const float dq = sDQ[16 * R + lr];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
-        }
+        for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
       }
-    }
+    });
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
