@@ -173,8 +173,11 @@ struct Lay {
   static constexpr size_t ST = BH + al16(size_t(NB) * DK * 4);            // S^T [BV][LDD]
   static constexpr size_t AK = ST + al16(size_t(BV) * LDD * sizeof(T));   // A then T, f32 [C][LDA]
   static constexpr size_t AQ = AK + al16(size_t(C) * LDA * 4);            // strict M [C][LDC]
-  static constexpr size_t AO = AQ + al16(size_t(C) * LDC * sizeof(T));    // off-diag A tiles f32 [NPAIR][16][16]
-  static constexpr size_t BE = AO + al16(size_t(NPAIR) * 256 * 4);        // beta [C]
+  // off-diagonal A tiles, f32 [NPAIR][16][AOR]: rows padded to 20 floats so the float4 row
+  // reads of eight consecutive rows fall on distinct LDS bank groups
+  static constexpr int AOR = 20;
+  static constexpr size_t AO = AQ + al16(size_t(C) * LDC * sizeof(T));
+  static constexpr size_t BE = AO + al16(size_t(NPAIR) * 16 * AOR * 4);   // beta [C]
   static constexpr size_t DQ = BE + al16(size_t(C) * 4);                  // q_r . k_r [C]
   static constexpr size_t GM = DQ + al16(size_t(C) * 4);                  // e^{g_last} [DK]
   // per chunk
@@ -786,7 +789,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
             for (int i = 0; i < 4; ++i) {
               const int ri = 4 * lg + i;
               sAQ[(16 * eR + ri) * LDC + 16 * I + lr] = cvt<T>(accQo[I][i]);
-              sAO[pair_index(eR, I) * 256 + ri * 16 + lr] = bet[i] * accKo[I][i];
+              sAO[(pair_index(eR, I) * 16 + ri) * L::AOR + lr] = bet[i] * accKo[I][i];
             }
           }
         }
@@ -848,7 +851,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
             tr[R] = *reinterpret_cast<const float4*>(sAK + (16 * R + lr) * LDA + 16 * R + kq);
 #pragma unroll
             for (int J = I0; J < R; ++J)
-              a[R][J] = *reinterpret_cast<const float4*>(sAO + pair_index(R, J) * 256 + lr * 16 + kq);
+              a[R][J] = *reinterpret_cast<const float4*>(sAO + (pair_index(R, J) * 16 + lr) * L::AOR + kq);
           }
           // one accumulator per term A_RJ T_JI: the J = I0 terms of every R start at once,
           // and each later term waits only for its own T_JI
@@ -894,9 +897,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       // the other waves: T Diag(beta) on the diagonal blocks, zero upper tiles and padding
       constexpr int NH = NW - (NB - 1);
       const int hw = wave - (NB - 1);
-      for (int idx = hw * kWave + l; idx < C * 16; idx += NH * kWave) {
-        const int r = idx >> 4, c = 16 * (r >> 4) + (idx & 15);
-        sTB[r * LDC + c] = cvt<T>(sAK[r * LDA + c] * sBE[c]);
+      for (int idx = hw * kWave + l; idx < C * 4; idx += NH * kWave) {
+        const int r = idx >> 2, c = 16 * (r >> 4) + 4 * (idx & 3);  // 4 columns of row r's diagonal block
+        const float4 tv = *reinterpret_cast<const float4*>(sAK + r * LDA + c);
+        const float4 bv = *reinterpret_cast<const float4*>(sBE + c);
+        store4(sTB + r * LDC + c, tv.x * bv.x, tv.y * bv.y, tv.z * bv.z, tv.w * bv.w);
       }
       // strictly-upper tiles (Tb shares memory with the partial tiles)
       for (int t = hw; t < NPAIR; t += NH) {
