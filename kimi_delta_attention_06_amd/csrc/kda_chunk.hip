@@ -11,10 +11,13 @@
 //   A[r,i] = b_r sum_c k_rc k_ic e^{g_rc - g_ic}   (i < r)      key Gram, decay-scaled
 //   M[r,i] =     sum_c q_rc k_ic e^{g_rc - g_ic}   (i <= r)     query-key Gram
 //   T      = (I + A)^-1                                         UT lower-triangular inverse
-//   W      = T Diag(b) (K * e^G),  Ut = T Diag(b) V             WY pseudo-keys / values
-//   U      = Ut - W S                                           (serial part starts here)
+//   U      = T Diag(b) (V - (K * e^G) S)                        pseudo-values
 //   O      = (Q * e^G) S + M U
 //   S     <- Diag(e^{g_last}) S + (K * e^{g_last - G})^T U
+//
+// U equals the WY form T Diag(b) V - (T Diag(b) (K * e^G)) S; with the entering state at
+// hand the pseudo-key product T Diag(b) (K * e^G) is never formed, and (K * e^G) S does
+// not wait for T, so it runs beside the inverse.
 //
 // One workgroup (512 threads, 8 waves, one per CU) owns one (sequence, head,
 // tile of BV value columns) and walks that sequence's chunks in order, resetting
@@ -94,20 +97,29 @@ __device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, f
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
-
-// One MMA step from LDS operands: `a`, `b` point at the lane's first k element.
-__device__ __forceinline__ void mma_step(f32x4& acc, const _Float16* a, const _Float16* b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8*>(a),
-                                                *reinterpret_cast<const half8*>(b), acc, 0, 0, 0);
+__device__ __forceinline__ float4 load4(const _Float16* p) {
+  const half4 h = *reinterpret_cast<const half4*>(p);
+  return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
 }
-__device__ __forceinline__ void mma_step(f32x4& acc, const float* a, const float* b) {
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// One lane's operand fragment of one MMA k-step, loaded from LDS.
+__device__ __forceinline__ half8 ld_frag(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
+__device__ __forceinline__ float4 ld_frag(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void mma_frag(f32x4& acc, const half8& a, const half8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_frag(f32x4& acc, const float4& a, const float4& b) {
   // four fp32 MFMAs on k = 4*(lane>>4) + j: the same k permutation for A and B
-  const float4 av = *reinterpret_cast<const float4*>(a);
-  const float4 bv = *reinterpret_cast<const float4*>(b);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+}
+// One MMA step from LDS operands: `a`, `b` point at the lane's first k element.
+template <typename T>
+__device__ __forceinline__ void mma_step(f32x4& acc, const T* a, const T* b) {
+  mma_frag(acc, ld_frag(a), ld_frag(b));
 }
 
 // acc (+)= A[16 rows, K] * B[16 rows, K]^T, both row-major with k contiguous, K = NST*KS.
@@ -154,8 +166,8 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------------------
 // LDS layout (bytes).  Regions with disjoint lifetimes share memory:
-//   RB (gate stage -> off-diagonal Gram) with WM (WY -> state stage 1),
-//   PT (partial Gram tiles) with TB (T stage -> WY) and UT (state 1 -> 2).
+//   RB (gate stage -> off-diagonal Gram) with YT (T stage -> U),
+//   PT (partial Gram tiles) with TB (T stage -> U) and UT (U -> state update).
 // ---------------------------------------------------------------------------
 template <int C, int DK, int BV, Prec P>
 struct Lay {
@@ -181,14 +193,15 @@ struct Lay {
   static constexpr size_t DQ = BE + al16(size_t(C) * 4);                  // q_r . k_r [C]
   static constexpr size_t GM = DQ + al16(size_t(C) * 4);                  // e^{g_last} [DK]
   // per chunk
+  static constexpr int LDV = BV + PD;                   // [C][BV] rows (value columns)
   static constexpr size_t QG = GM + al16(size_t(DK) * 4);                 // Qg [C][LDD]
-  static constexpr size_t KGT = QG + al16(size_t(C) * LDD * sizeof(T));   // Kg^T [DK][LDC]
-  static constexpr size_t KDT = KGT + al16(size_t(DK) * LDC * sizeof(T)); // Kd^T [DK][LDC]
-  static constexpr size_t VT = KDT + al16(size_t(DK) * LDC * sizeof(T));  // V^T [BV][LDC]
-  static constexpr size_t X1 = VT + al16(size_t(BV) * LDC * sizeof(T));   // RB | WM
+  static constexpr size_t KG = QG + al16(size_t(C) * LDD * sizeof(T));    // Kg [C][LDD]
+  static constexpr size_t KDT = KG + al16(size_t(C) * LDD * sizeof(T));   // Kd^T [DK][LDC]
+  static constexpr size_t VR = KDT + al16(size_t(DK) * LDC * sizeof(T));  // V [C][LDV]
+  static constexpr size_t X1 = VR + al16(size_t(C) * LDV * sizeof(T));    // RB | YT
   static constexpr size_t RB = X1;                                        // right base [C][LDD]
-  static constexpr size_t WM = X1;                                        // W [C][LDD]
-  static constexpr size_t X2 = X1 + al16(size_t(C) * LDD * sizeof(T));    // PT | (TB, UT)
+  static constexpr size_t YT = X1;                                        // (V - Kg S)^T [BV][LDC]
+  static constexpr size_t X2 = X1 + cmax(al16(size_t(C) * LDD * sizeof(T)), al16(size_t(BV) * LDC * sizeof(T)));
   static constexpr size_t PT = X2;                                        // partial tiles f32 [2*NPALL][64][4]
   static constexpr size_t TB = X2;                                        // T Diag(b) [C][LDC]
   static constexpr size_t UT = TB + al16(size_t(C) * LDC * sizeof(T));    // U^T [BV][LDC]
@@ -228,6 +241,18 @@ struct VRegs {
   uint4 v[VW];
 };
 
+// An empty use of every loaded register on every path: the memory counter is waited on
+// here, where the data has long arrived, instead of before the next loads into the same
+// registers (a wave that skipped a conditional use would otherwise carry the pending load
+// into the next chunk and wait for every load in flight when it reloads the register).
+__device__ __forceinline__ void retire(const uint4& x) {
+  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+}
+__device__ __forceinline__ void retire(const float4& x) {
+  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+}
+__device__ __forceinline__ void retire(float x) { asm volatile("" ::"v"(x)); }
+
 template <typename InT>
 __device__ __forceinline__ void unpack(const uint4* w, float* out, int n) {
   if constexpr (sizeof(InT) == 2) {
@@ -262,7 +287,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   using L = Lay<C, DK, BV, P>;
   using T = typename L::T;
   constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
-  constexpr int LDD = L::LDD, LDC = L::LDC, LDA = L::LDA;
+  constexpr int LDD = L::LDD, LDC = L::LDC, LDA = L::LDA, LDV = L::LDV;
   constexpr int NPAIR = L::NPAIR;
   constexpr int NA = DK / 16;   // channel tiles
   constexpr int NJ = BV / 16;   // value-column tiles
@@ -284,11 +309,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   float* sDQ = reinterpret_cast<float*>(smem + L::DQ);
   float* sGM = reinterpret_cast<float*>(smem + L::GM);
   T* sQG = reinterpret_cast<T*>(smem + L::QG);
-  T* sKGT = reinterpret_cast<T*>(smem + L::KGT);
+  T* sKG = reinterpret_cast<T*>(smem + L::KG);
   T* sKDT = reinterpret_cast<T*>(smem + L::KDT);
-  T* sVT = reinterpret_cast<T*>(smem + L::VT);
+  T* sV = reinterpret_cast<T*>(smem + L::VR);
   T* sRB = reinterpret_cast<T*>(smem + L::RB);
-  T* sW = reinterpret_cast<T*>(smem + L::WM);
+  T* sYT = reinterpret_cast<T*>(smem + L::YT);
   float4* sPT = reinterpret_cast<float4*>(smem + L::PT);
   T* sTB = reinterpret_cast<T*>(smem + L::TB);
   T* sUT = reinterpret_cast<T*>(smem + L::UT);
@@ -361,10 +386,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   write_ST();
 
   // ---- gate-stage map: waves (R = wave/2, p = wave%2) for 2*NB waves
-  const bool e_act = wave0 < 2 * NB;
+  const bool e_act = 2 * NB >= NW || wave0 < 2 * NB;
   // gate-stage load map: lane (r, g) of wave (R, p) loads row 16R + r, channels p*DK/2 + CPL*g ..
   // value-load map: thread t < C*VPR loads 8 columns of one row
-  const bool v_act = tid < C * VPR;
+  const bool v_act = C * VPR >= NT || tid < C * VPR;
   int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
 
   // U / O tiles (R, j), held transposed: lane (token 16R + (l & 15), columns
@@ -536,8 +561,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if (v_act) {
         float vv[8];
         unpack<InT>(vbuf.v, vv, 8);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) sVT[(v_c0 + c) * LDC + v_row] = cvt<T>(vv[c]);
+        store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
+        store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
       }
       if (e_act) {
         // in-block cumulative decay c and block total s, in log2 units; every phase
@@ -626,6 +651,16 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         }
         if (ep == 0 && lg == 0) sBE[e_row] = bcur;
       }
+#pragma unroll
+      for (int i = 0; i < GR::QW; ++i) {
+        retire(gbuf.q[i]);
+        retire(gbuf.k[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < CPL / 4; ++i) retire(gbuf.la[i]);
+      retire(gbuf.b);
+#pragma unroll
+      for (int i = 0; i < VR::VW; ++i) retire(vbuf.v[i]);
     }
   };
   if (nchunks > 0) {
@@ -647,7 +682,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     const int e_cb = ep * (DK / 2) + CPL * lg;
 
     __syncthreads();  // ------------------------------------------------------------- B_a
-    if (ch + 1 < nchunks) load_qk(c_begin + C, chunk_len(ch + 1));
+    // Next-chunk loads and gate stage run unconditionally: past the last chunk the length is
+    // <= 0, every lane's load is masked off and the gate stage writes only dead LDS.  With no
+    // path that skips them, no load is still pending where its registers are reloaded.
+    load_qk(c_begin + C, chunk_len(ch + 1));
     if (ch > 0) store_pending();
 
     // ================= per-channel block factors (once per chunk) =================
@@ -704,11 +742,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
           const float pre[4] = {pr.x, pr.y, pr.z, pr.w}, post[4] = {po.x, po.y, po.z, po.w};
           store4(sQG + e_row * LDD + e_cb + j4, qL[j4] * pre[0], qL[j4 + 1] * pre[1], qL[j4 + 2] * pre[2],
                  qL[j4 + 3] * pre[3]);
+          store4(sKG + e_row * LDD + e_cb + j4, kL[j4] * pre[0], kL[j4 + 1] * pre[1], kL[j4 + 2] * pre[2],
+                 kL[j4 + 3] * pre[3]);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            sKGT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kL[j4 + u] * pre[u]);
-            sKDT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kR[j4 + u] * post[u]);
-          }
+          for (int u = 0; u < 4; ++u) sKDT[(e_cb + j4 + u) * LDC + e_row] = cvt<T>(kR[j4 + u] * post[u]);
         }
       }
       // off-diagonal pairs (eR, I), I < eR: left X e^{c} e^{G_{R-1} - G_I} = X{L} f_RI,
@@ -761,7 +798,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_b
-    if (ch + 1 < nchunks) load_la(c_begin + C, chunk_len(ch + 1));
+    load_la(c_begin + C, chunk_len(ch + 1));
 
     // ===== Gram reduction by one wave of each row block, in parallel with the inverse of
     //       that block's diagonal sub-block of A by the other =====
@@ -829,7 +866,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_c
-    if (ch + 1 < nchunks) load_vb(c_begin + C, chunk_len(ch + 1));
+    load_vb(c_begin + C, chunk_len(ch + 1));
 
     // ===== T off-diagonal blocks, one block column per wave (wave I): for R = I+1 .. NB-1,
     //       T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI, with T_JI (J > I) kept in registers.
@@ -894,9 +931,60 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
     if (wave >= NB - 1) {
-      // the other waves: T Diag(beta) on the diagonal blocks, zero upper tiles and padding
+      // the other waves: Y = V - Kg S (does not need T), T Diag(beta) on the diagonal
+      // blocks, zero upper tiles and padding
       constexpr int NH = NW - (NB - 1);
       const int hw = wave - (NB - 1);
+      // Y tile (R, j): lane (token 16R + (l & 15), columns 16j + 4 (l >> 4) .. +3), stored
+      // transposed (token contiguous) as the operand of U = T Diag(beta) Y.  With even tile
+      // counts a wave takes a 2x2 block of tiles, so each operand fragment feeds two products.
+      auto y_store = [&](int R, int j, const f32x4& ks) {
+        const float4 v4 = load4(sV + (16 * R + lr) * LDV + 16 * j + 4 * lg);
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(vv[i] - ks[i]);
+      };
+      if constexpr (NB % 2 == 0 && NJ % 2 == 0) {
+        constexpr int NYB = (NB / 2) * (NJ / 2);
+        static_for<0, (NYB + NH - 1) / NH>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          const int id = hw + NH * s;
+          if (NYB % NH == 0 || id < NYB) {
+            const int R0 = 2 * (id % (NB / 2)), j0 = 2 * (id / (NB / 2));
+            f32x4 ks[2][2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+              for (int b = 0; b < 2; ++b) ks[a][b] = zero4();
+            const T* pa = sST + (16 * j0 + lr) * LDD + lg * (KS / 4);
+            const T* pb = sKG + (16 * R0 + lr) * LDD + lg * (KS / 4);
+#pragma unroll
+            for (int st = 0; st < DK / KS; ++st) {
+              const auto a0 = ld_frag(pa + st * KS), a1 = ld_frag(pa + 16 * LDD + st * KS);
+              const auto b0 = ld_frag(pb + st * KS), b1 = ld_frag(pb + 16 * LDD + st * KS);
+              mma_frag(ks[0][0], a0, b0);
+              mma_frag(ks[0][1], a0, b1);
+              mma_frag(ks[1][0], a1, b0);
+              mma_frag(ks[1][1], a1, b1);
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+              for (int b = 0; b < 2; ++b) y_store(R0 + b, j0 + a, ks[a][b]);
+          }
+        });
+      } else {
+        static_for<0, (NB * NJ + NH - 1) / NH>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          const int id = hw + NH * s;
+          if ((NB * NJ) % NH == 0 || id < NB * NJ) {
+            const int R = id % NB, j = id / NB;
+            f32x4 ks = zero4();
+            mma_lds<T, KS, DK / KS>(ks, sST + 16 * j * LDD, LDD, sKG + 16 * R * LDD, LDD);
+            y_store(R, j, ks);
+          }
+        });
+      }
       for (int idx = hw * kWave + l; idx < C * 4; idx += NH * kWave) {
         const int r = idx >> 2, c = 16 * (r >> 4) + 4 * (idx & 3);  // 4 columns of row r's diagonal block
         const float4 tv = *reinterpret_cast<const float4*>(sAK + r * LDA + c);
@@ -911,38 +999,21 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         store4(sTB + (16 * R + (l >> 2)) * LDC + 16 * I + 4 * (l & 3), 0.f, 0.f, 0.f, 0.f);
       }
       if constexpr (CK > C) {
-        // padded token columns of Kg^T, Kd^T, V^T, U^T and Tb (U^T and Tb share memory with the partials)
-        for (int idx = hw * kWave + l; idx < (2 * DK + 2 * BV + C) * (CK - C); idx += NH * kWave) {
+        // padded token columns of Kd^T, Y^T, U^T and Tb (Y^T shares memory with the right
+        // base, U^T and Tb with the partials)
+        for (int idx = hw * kWave + l; idx < (DK + 2 * BV + C) * (CK - C); idx += NH * kWave) {
           const int rowi = idx / (CK - C), col = C + idx % (CK - C);
-          T* base = rowi < DK            ? sKGT + rowi * LDC
-                    : rowi < 2 * DK      ? sKDT + (rowi - DK) * LDC
-                    : rowi < 2 * DK + BV ? sVT + (rowi - 2 * DK) * LDC
-                    : rowi < 2 * DK + 2 * BV ? sUT + (rowi - 2 * DK - BV) * LDC
-                                             : sTB + (rowi - 2 * DK - 2 * BV) * LDC;
+          T* base = rowi < DK            ? sKDT + rowi * LDC
+                    : rowi < DK + BV     ? sYT + (rowi - DK) * LDC
+                    : rowi < DK + 2 * BV ? sUT + (rowi - DK - BV) * LDC
+                                         : sTB + (rowi - DK - 2 * BV) * LDC;
           base[col] = cvt<T>(0.f);
         }
       }
     }
     __syncthreads();  // ------------------------------------------------------------- B_e
 
-    // ================= WY: W^T = Kg^T Tb^T ; Ut = Tb V =================
-    static_for<0, (NA * NB + NW - 1) / NW>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      const int id = wave + NW * s;
-      if ((NA * NB) % NW == 0 || id < NA * NB) {
-        const int a = id % NA, R = id / NA;
-        f32x4 acc = zero4();
-        if constexpr (NA == NW) {
-          // slot s holds row block s: only tokens below 16 (s + 1) contribute (T is lower triangular)
-          constexpr int steps = (16 * (s + 1) + KS - 1) / KS < CK / KS ? (16 * (s + 1) + KS - 1) / KS : CK / KS;
-          mma_lds<T, KS, steps>(acc, sKGT + 16 * a * LDC, LDC, sTB + 16 * R * LDC, LDC);
-        } else {
-          mma_lds<T, KS, CK / KS>(acc, sKGT + 16 * a * LDC, LDC, sTB + 16 * R * LDC, LDC);
-        }
-        // rows = channels 16a + 4*lg + i, column = token 16R + lr
-        store4(sW + (16 * R + lr) * LDD + 16 * a + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
-      }
-    });
+    // ================= U = Tb Y ; O = Qg S =================
     f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
     static_for<0, U_SLOTS>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
@@ -954,30 +1025,15 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         int R, j;
         uo_tile(s, R, j);
-        mma_lds<T, KS, steps>(Uacc[s], sVT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
+        mma_lds<T, KS, steps>(Uacc[s], sYT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
+        mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(Uacc[s][i]);
       }
     });
     __syncthreads();  // ------------------------------------------------------------- B_f
 
-    // ================= state stage 1: U = Ut - W S ; O = Qg S =================
-#pragma unroll
-    for (int s = 0; s < U_SLOTS; ++s) {
-      const int id = wave + NW * s;
-      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        int R, j;
-        uo_tile(s, R, j);
-        f32x4 ws = zero4();
-        mma_lds<T, KS, DK / KS>(ws, sST + 16 * j * LDD, LDD, sW + 16 * R * LDD, LDD);
-        mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Uacc[s][i] -= ws[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(Uacc[s][i]);
-      }
-    }
-    __syncthreads();  // ------------------------------------------------------------- B_g
-
-    // ================= state stage 2: O += M U ; S <- e^{g} S + Kd^T U =================
+    // ================= O += M U ; S <- e^{g} S + Kd^T U =================
     static_for<0, U_SLOTS>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
       constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
@@ -1012,9 +1068,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     }
     o_begin = c_begin;
     o_len = Lc;
-    // The next chunk's gate stage writes only RB (shared with W, dead after B_g) and BH
-    // before its first barrier; everything read above is untouched until then.
-      if (ch + 1 < nchunks) gate_a(ch + 1);
+    // The next chunk's gate stage writes V, RB (shared with Y^T, dead after B_f), BH and
+    // beta before its first barrier; everything read above is untouched until then.
+    gate_a(ch + 1);
   }
 
   if (nchunks > 0) store_pending();
