@@ -523,10 +523,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   };
   __syncthreads();
 
-  // Software pipeline: the inputs of chunk c+1 are loaded at the start of iteration c
-  // and its gate stage (part a) runs at the end of iteration c, so loaded registers
-  // never cross the loop back-edge (only computed gate values do).
-  float qL[CPL], kL[CPL], kR[CPL];
+  // Software pipeline: the inputs of chunk c+1 are loaded during iteration c and its gate
+  // stage (part a) runs beside iteration c's state products, so loaded registers never
+  // cross the loop back-edge (only computed gate values do).  The right base it computes
+  // shares LDS with Y^T and is stored only after Y^T's last use.
+  float qL[CPL], kL[CPL], kR[CPL], rbv[CPL];
   f32x4 accQd, accKd;
   auto gate_a = [&](int64_t ch) {
     [[maybe_unused]] const int64_t c_begin = t_begin + ch * C;
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if (e_act) {
         // in-block cumulative decay c and block total s, in log2 units; every phase
         // runs across all channels so the DPP and permute latencies overlap
-        float cc[CPL], ss[CPL], rb[CPL];
+        float cc[CPL], ss[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) cc[j] = la[j] * 1.4426950408889634f;
 #pragma unroll
@@ -590,8 +591,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         const bool fast16 = __builtin_amdgcn_ballot_w64(!(smin > -11.5415603f)) == 0;  // 8 nats in log2 units
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-          const float eL = __builtin_amdgcn_exp2f(cc[j] - 0.5f * ss[j]);  // e^{c - s/2} <= e^{|s|/2}
-          const float eRt = __builtin_amdgcn_exp2f(0.5f * ss[j] - cc[j]);
+          const float x = cc[j] - 0.5f * ss[j];
+          const float eL = __builtin_amdgcn_exp2f(x);  // e^{c - s/2} <= e^{|s|/2}
+          const float eRt = __builtin_amdgcn_exp2f(-x);
           // e^{s/2} <= 1 is e^{c - s/2} at the block's last row (c = s there, and s - s/2
           // is exact), so lane 15 of the row supplies it (below 2^-126 it flushes to 0)
           const float bh = row_bcast16<15>(eL);
@@ -599,17 +601,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
           qL[j] *= eL;
           kL[j] = kk * eL;
           kR[j] = kk * eRt;
-          rb[j] = kR[j] * bh;                                      // right base k e^{s - c} <= |k|
+          rbv[j] = kR[j] * bh;                                     // right base k e^{s - c} <= |k|
           ss[j] = bh;
         }
         if (lr == 15) {
 #pragma unroll
           for (int j = 0; j < CPL; j += 4) store4(sBH + eR * DK + e_cb + j, ss[j], ss[j + 1], ss[j + 2], ss[j + 3]);
-        }
-        if (eR < NB - 1) {
-          T* dst = sRB + e_row * LDD + e_cb;
-#pragma unroll
-          for (int j = 0; j < CPL; j += 4) store4(dst + j, rb[j], rb[j + 1], rb[j + 2], rb[j + 3]);
         }
         // diagonal Gram sub-block partials over this wave's channels
         if constexpr (P == Prec::Mixed) {
@@ -663,9 +660,19 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       for (int i = 0; i < VR::VW; ++i) retire(vbuf.v[i]);
     }
   };
+  auto store_rb = [&]() {
+    const int x = fresh_lane();
+    const int eR = e_act ? row_block_of<NB>(wave0) : 0;
+    if (e_act && eR < NB - 1) {
+      T* dst = sRB + (16 * eR + (x & 15)) * LDD + (wave0 & 1) * (DK / 2) + CPL * (x >> 4);
+#pragma unroll
+      for (int j = 0; j < CPL; j += 4) store4(dst + j, rbv[j], rbv[j + 1], rbv[j + 2], rbv[j + 3]);
+    }
+  };
   if (nchunks > 0) {
     load_chunk(t_begin, chunk_len(0));
     gate_a(0);
+    store_rb();
   }
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
@@ -1013,7 +1020,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     }
     __syncthreads();  // ------------------------------------------------------------- B_e
 
-    // ================= U = Tb Y ; O = Qg S =================
+    // ================= U = Tb Y ; O = Qg S ; next chunk's gate stage =================
+    // The products are issued first; the next chunk's gate stage (vector ALU) runs while
+    // they complete.  It writes V, BH and beta, none of which is read after the barrier
+    // above; the loads it consumes were issued two stages ago.
     f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
     static_for<0, U_SLOTS>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
@@ -1027,11 +1037,21 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         uo_tile(s, R, j);
         mma_lds<T, KS, steps>(Uacc[s], sYT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
         mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
+      }
+    });
+    gate_a(ch + 1);
+#pragma unroll
+    for (int s = 0; s < U_SLOTS; ++s) {
+      const int id = wave + NW * s;
+      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
+        int R, j;
+        uo_tile(s, R, j);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(Uacc[s][i]);
       }
-    });
+    }
     __syncthreads();  // ------------------------------------------------------------- B_f
+    store_rb();
 
     // ================= O += M U ; S <- e^{g} S + Kd^T U =================
     static_for<0, U_SLOTS>([&](auto sc) {
@@ -1068,9 +1088,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     }
     o_begin = c_begin;
     o_len = Lc;
-    // The next chunk's gate stage writes V, RB (shared with Y^T, dead after B_f), BH and
-    // beta before its first barrier; everything read above is untouched until then.
-    gate_a(ch + 1);
   }
 
   if (nchunks > 0) store_pending();
