@@ -424,24 +424,21 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   };
   GR gbuf;
   VR vbuf;
-  // The next chunk's inputs are loaded in three groups (q and k; the log-decay; v and
-  // beta) so that each group can be issued at a different point of the chunk.
-  auto load_qk = [&](int64_t cb, int Lc) {
+  // The next chunk's inputs are loaded in four groups (q; k; the log-decay; v and beta),
+  // each issued after a different barrier: every CU reaches a barrier at about the same
+  // time, and one large group per chunk would be a device-wide burst that saturates HBM
+  // and stalls instruction issue while the rest of the chunk leaves it idle.
+  auto load_qk1 = [&](const InT* src, uint4 (&dst)[GR::QW], int64_t cb, int Lc) {
     int ld_row, el;
     gate_map(ld_row, el);
     const uint32_t ld_off = (uint32_t)el * (uint32_t)sizeof(InT);
-    const size_t tok = (size_t)cb * H + h;
-    const char* qb = reinterpret_cast<const char*>(q + tok * DK);
-    const char* kb = reinterpret_cast<const char*>(k + tok * DK);
+    const char* base = reinterpret_cast<const char*>(src + ((size_t)cb * H + h) * DK);
     if (e_act && ld_row < Lc) {
 #pragma unroll
-      for (int i = 0; i < GR::QW; ++i) {
-        gbuf.q[i] = *reinterpret_cast<const uint4*>(qb + ld_off + 16 * i);
-        gbuf.k[i] = *reinterpret_cast<const uint4*>(kb + ld_off + 16 * i);
-      }
+      for (int i = 0; i < GR::QW; ++i) dst[i] = *reinterpret_cast<const uint4*>(base + ld_off + 16 * i);
     } else {
 #pragma unroll
-      for (int i = 0; i < GR::QW; ++i) gbuf.q[i] = gbuf.k[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < GR::QW; ++i) dst[i] = make_uint4(0, 0, 0, 0);
     }
   };
   auto load_la = [&](int64_t cb, int Lc) {
@@ -478,7 +475,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     }
   };
   auto load_chunk = [&](int64_t cb, int Lc) {
-    load_qk(cb, Lc);
+    load_qk1(q, gbuf.q, cb, Lc);
+    load_qk1(k, gbuf.k, cb, Lc);
     load_la(cb, Lc);
     load_vb(cb, Lc);
   };
@@ -486,9 +484,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     const int64_t rem = t_end - (t_begin + ch * C);
     return (int)(rem < C ? rem : C);
   };
-  // The outputs of chunk c are stored during chunk c+1, after its prefetch is
-  // issued: the loop-carried input registers force a wait on the memory counter
-  // (which also counts stores) once per chunk, and deferred stores are long done.
   f32x4 Opend[U_SLOTS];
   int64_t o_begin = 0;
   int o_len = 0;
@@ -692,8 +687,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     // Next-chunk loads and gate stage run unconditionally: past the last chunk the length is
     // <= 0, every lane's load is masked off and the gate stage writes only dead LDS.  With no
     // path that skips them, no load is still pending where its registers are reloaded.
-    load_qk(c_begin + C, chunk_len(ch + 1));
-    if (ch > 0) store_pending();
+    load_qk1(q, gbuf.q, c_begin + C, chunk_len(ch + 1));
 
     // ================= per-channel block factors (once per chunk) =================
     // With bh_J = e^{s_J/2} (<= 1), for row block R and channel c:
@@ -733,6 +727,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       sGM[tid] = g;
     }
     __syncthreads();  // ------------------------------------------------------------- B_f1
+    load_qk1(k, gbuf.k, c_begin + C, chunk_len(ch + 1));
 
     // ================= gate stage, part b: off-diagonal Gram, state operands =================
     f32x4 accQo[NB > 1 ? NB - 1 : 1], accKo[NB > 1 ? NB - 1 : 1];
@@ -1068,6 +1063,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
       }
     });
+    o_begin = c_begin;
+    o_len = Lc;
+    store_pending();
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
@@ -1086,11 +1084,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       const int64_t slot = (c_begin + Lc) / ckpt_every - 1;
       store_state(ckpt + ((size_t)slot * H + h) * DK * DV);
     }
-    o_begin = c_begin;
-    o_len = Lc;
   }
 
-  if (nchunks > 0) store_pending();
   if (hT) store_state(hT + (size_t)chain * DK * DV);
 }
 
