@@ -241,6 +241,20 @@ struct VRegs {
   uint4 v[VW];
 };
 
+// Raw buffer loads (gfx9 descriptor: stride 0, 32-bit data format); an access at or past
+// `nbytes` from `base` returns zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // An empty use of every loaded register on every path: the memory counter is waited on
 // here, where the data has long arrived, instead of before the next loads into the same
 // registers (a wave that skipped a conditional use would otherwise carry the pending load
@@ -428,51 +442,42 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   // each issued after a different barrier: every CU reaches a barrier at about the same
   // time, and one large group per chunk would be a device-wide burst that saturates HBM
   // and stalls instruction issue while the rest of the chunk leaves it idle.
+  // Each group is a raw buffer load whose descriptor covers the chunk's valid rows of this
+  // head: rows past the chunk's length (and every row past the last chunk) read as zero
+  // in hardware, so the loads need no branch and no zero fill.
+  auto row_bytes = [&](int Lc, uint32_t bytes_per_row) -> uint32_t {
+    return (e_act && Lc > 0) ? (uint32_t)Lc * bytes_per_row : 0u;
+  };
   auto load_qk1 = [&](const InT* src, uint4 (&dst)[GR::QW], int64_t cb, int Lc) {
     int ld_row, el;
     gate_map(ld_row, el);
     const uint32_t ld_off = (uint32_t)el * (uint32_t)sizeof(InT);
-    const char* base = reinterpret_cast<const char*>(src + ((size_t)cb * H + h) * DK);
-    if (e_act && ld_row < Lc) {
+    const auto rs = make_rsrc(src + ((size_t)cb * H + h) * DK, row_bytes(Lc, (uint32_t)(H * DK * sizeof(InT))));
 #pragma unroll
-      for (int i = 0; i < GR::QW; ++i) dst[i] = *reinterpret_cast<const uint4*>(base + ld_off + 16 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < GR::QW; ++i) dst[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < GR::QW; ++i) dst[i] = buf_load16(rs, ld_off + 16 * i);
   };
   auto load_la = [&](int64_t cb, int Lc) {
     int ld_row, el;
     gate_map(ld_row, el);
     const uint32_t ld_off_f = (uint32_t)el * 4u;
-    const size_t tok = (size_t)cb * H + h;
-    const char* lb = reinterpret_cast<const char*>(log_alpha + tok * DK);
-    if (e_act && ld_row < Lc) {
+    const auto rs = make_rsrc(log_alpha + ((size_t)cb * H + h) * DK, row_bytes(Lc, (uint32_t)(H * DK * 4)));
 #pragma unroll
-      for (int i = 0; i < CPL / 4; ++i) gbuf.la[i] = *reinterpret_cast<const float4*>(lb + ld_off_f + 16 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < CPL / 4; ++i) gbuf.la[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int i = 0; i < CPL / 4; ++i) gbuf.la[i] = __builtin_bit_cast(float4, buf_load16(rs, ld_off_f + 16 * i));
   };
   auto load_vb = [&](int64_t cb, int Lc) {
     int ld_row, el;
     gate_map(ld_row, el);
     const uint32_t ld_off_b = (uint32_t)(ld_row * H) * 4u;
     const int t = wave0 * kWave + fresh_lane();
+    // lanes past the C * VPR value loads have v_row >= C, past every chunk's valid rows
     const int v_row = t / VPR, v_c0 = 8 * (t % VPR);
     const uint32_t v_off = (uint32_t)(v_row * H * DV + v_c0) * (uint32_t)sizeof(InT);
-    const size_t tok = (size_t)cb * H + h;
-    const char* bb = reinterpret_cast<const char*>(beta + tok);
-    const char* vb = reinterpret_cast<const char*>(v + tok * DV + j0);
-    gbuf.b = (e_act && ld_row < Lc) ? *reinterpret_cast<const float*>(bb + ld_off_b) : 0.f;
-    if (v_act && v_row < Lc) {
+    const auto rb_ = make_rsrc(beta + (size_t)cb * H + h, row_bytes(Lc, (uint32_t)(H * 4)));
+    const auto rv = make_rsrc(v + ((size_t)cb * H + h) * DV + j0,
+                              Lc > 0 ? (uint32_t)Lc * (uint32_t)(H * DV * sizeof(InT)) : 0u);
+    gbuf.b = buf_load4(rb_, ld_off_b);
 #pragma unroll
-      for (int i = 0; i < VR::VW; ++i) vbuf.v[i] = *reinterpret_cast<const uint4*>(vb + v_off + 16 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < VR::VW; ++i) vbuf.v[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < VR::VW; ++i) vbuf.v[i] = buf_load16(rv, v_off + 16 * i);
   };
   auto load_chunk = [&](int64_t cb, int Lc) {
     load_qk1(q, gbuf.q, cb, Lc);
@@ -524,136 +529,149 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   // shares LDS with Y^T and is stored only after Y^T's last use.
   float qL[CPL], kL[CPL], kR[CPL], rbv[CPL];
   f32x4 accQd, accKd;
-  auto gate_a = [&](int64_t ch) {
-    [[maybe_unused]] const int64_t c_begin = t_begin + ch * C;
-    [[maybe_unused]] const int Lc = chunk_len(ch);
+  // Gate stage, part a, in GH channel parts of GC channels (each a whole number of the
+  // diagonal Gram's MMA k-steps), then the value / beta part.  The parts of chunk c+1 run
+  // beside chunk c's latency-bound MMA stages: part 0 with the inverse levels, the rest
+  // with the U / O products.
+  constexpr int GH = (P == Prec::Mixed ? CPL >= 16 : CPL >= 8) ? 2 : 1;
+  constexpr int GC = CPL / GH;
+  auto gate_part = [&](auto hc) {
+    constexpr int hh = decltype(hc)::value;
     // Wave-dependent LDS offsets are cheap scalar arithmetic; an opaque copy of the
     // wave index keeps the compiler from hoisting (and spilling) them out of the loop.
     wave = wave0;
     asm volatile("" : "+s"(wave));
     refresh_lane();
-    v_row = tid / VPR;
-    v_c0 = 8 * (tid % VPR);
-    const int eR = e_act ? row_block_of<NB>(wave) : 0, ep = wave & 1;
-    const int e_row = 16 * eR + lr;
-    const int e_cb = ep * (DK / 2) + CPL * lg;
-
-    // ================= gate stage, part a: decay, diagonal Gram sub-blocks =================
-    // qL = q e^{c - s/2}, kL = k e^{c - s/2}, kR = k e^{s/2 - c}; c: in-block cumulative
-    // decay, s: block total.  The next chunk's loads are issued once these registers
-    // have been consumed, so they are in flight for the rest of this chunk.
-    accQd = zero4();
-    accKd = zero4();
-    {
-      float la[CPL];
-      unpack<InT>(gbuf.q, qL, CPL);
-      unpack<InT>(gbuf.k, kL, CPL);
+    const int eR = e_act ? row_block_of<NB>(wave) : 0;
+    const int e_cb = (wave & 1) * (DK / 2) + CPL * lg + hh * GC;
+    if constexpr (hh == 0) {
+      accQd = zero4();
+      accKd = zero4();
+    }
+    float* const qh_ = qL + hh * GC;
+    float* const kh_ = kL + hh * GC;
+    float* const rh_ = kR + hh * GC;
+    float* const bh_ = rbv + hh * GC;
+    unpack<InT>(gbuf.q + hh * (GR::QW / GH), qh_, GC);
+    unpack<InT>(gbuf.k + hh * (GR::QW / GH), kh_, GC);
+    float la[GC];
 #pragma unroll
-      for (int i = 0; i < CPL / 4; ++i) {
-        la[4 * i] = gbuf.la[i].x; la[4 * i + 1] = gbuf.la[i].y;
-        la[4 * i + 2] = gbuf.la[i].z; la[4 * i + 3] = gbuf.la[i].w;
+    for (int i = 0; i < GC / 4; ++i) {
+      const float4 x = gbuf.la[hh * (GC / 4) + i];
+      la[4 * i] = x.x; la[4 * i + 1] = x.y; la[4 * i + 2] = x.z; la[4 * i + 3] = x.w;
+    }
+    if (e_act) {
+      // in-block cumulative decay c and block total s, in log2 units; every phase
+      // runs across all channels so the DPP and permute latencies overlap
+      float cc[GC], ss[GC];
+#pragma unroll
+      for (int j = 0; j < GC; ++j) cc[j] = la[j] * 1.4426950408889634f;
+#pragma unroll
+      for (int j = 0; j < GC; ++j) cc[j] += shr16<1>(cc[j]);
+#pragma unroll
+      for (int j = 0; j < GC; ++j) cc[j] += shr16<2>(cc[j]);
+#pragma unroll
+      for (int j = 0; j < GC; ++j) cc[j] += shr16<4>(cc[j]);
+#pragma unroll
+      for (int j = 0; j < GC; ++j) cc[j] += shr16<8>(cc[j]);
+#pragma unroll
+      for (int j = 0; j < GC; ++j) ss[j] = row_bcast16<15>(cc[j]);
+      // When every channel of this part decays by less than 8 nats over the block, the
+      // balanced operands stay within e^{+-4} of the inputs and fp16 represents them as
+      // well as the off-diagonal operands; otherwise the part's diagonal products take
+      // the wide path.  The vote is wave-uniform.
+      float smin = ss[0];
+#pragma unroll
+      for (int j = 1; j < GC; ++j) smin = fminf(smin, ss[j]);
+      [[maybe_unused]] const bool fast16 = __builtin_amdgcn_ballot_w64(!(smin > -11.5415603f)) == 0;  // 8 nats in log2 units
+#pragma unroll
+      for (int j = 0; j < GC; ++j) {
+        const float x = cc[j] - 0.5f * ss[j];
+        const float eL = __builtin_amdgcn_exp2f(x);  // e^{c - s/2} <= e^{|s|/2}
+        const float eRt = __builtin_amdgcn_exp2f(-x);
+        // e^{s/2} <= 1 is e^{c - s/2} at the block's last row (c = s there, and s - s/2
+        // is exact), so lane 15 of the row supplies it (below 2^-126 it flushes to 0)
+        const float bh = row_bcast16<15>(eL);
+        const float kk = kh_[j];
+        qh_[j] *= eL;
+        kh_[j] = kk * eL;
+        rh_[j] = kk * eRt;
+        bh_[j] = rh_[j] * bh;                                    // right base k e^{s - c} <= |k|
+        ss[j] = bh;
       }
-      const float bcur = gbuf.b;
-      if (v_act) {
-        float vv[8];
-        unpack<InT>(vbuf.v, vv, 8);
-        store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
-        store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
+      if (lr == 15) {
+#pragma unroll
+        for (int j = 0; j < GC; j += 4) store4(sBH + eR * DK + e_cb + j, ss[j], ss[j + 1], ss[j + 2], ss[j + 3]);
       }
-      if (e_act) {
-        // in-block cumulative decay c and block total s, in log2 units; every phase
-        // runs across all channels so the DPP and permute latencies overlap
-        float cc[CPL], ss[CPL];
+      // diagonal Gram sub-block partials over this part's channels
+      if constexpr (P == Prec::Mixed) {
+        if (fast16) {
+          // narrow decay: fp16 operands, one MFMA per 8 channels for each of M and A
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) cc[j] = la[j] * 1.4426950408889634f;
+          for (int t = 0; t < GC / 8; ++t) {
+            half8 qh, kh, rh;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) cc[j] += shr16<1>(cc[j]);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) cc[j] += shr16<2>(cc[j]);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) cc[j] += shr16<4>(cc[j]);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) cc[j] += shr16<8>(cc[j]);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) ss[j] = row_bcast16<15>(cc[j]);
-        // When every channel of this wave decays by less than 8 nats over the block, the
-        // balanced operands stay within e^{+-4} of the inputs and fp16 represents them as
-        // well as the off-diagonal operands; otherwise the diagonal sub-blocks take the
-        // wide path.  The vote is wave-uniform.
-        float smin = ss[0];
-#pragma unroll
-        for (int j = 1; j < CPL; ++j) smin = fminf(smin, ss[j]);
-        const bool fast16 = __builtin_amdgcn_ballot_w64(!(smin > -11.5415603f)) == 0;  // 8 nats in log2 units
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const float x = cc[j] - 0.5f * ss[j];
-          const float eL = __builtin_amdgcn_exp2f(x);  // e^{c - s/2} <= e^{|s|/2}
-          const float eRt = __builtin_amdgcn_exp2f(-x);
-          // e^{s/2} <= 1 is e^{c - s/2} at the block's last row (c = s there, and s - s/2
-          // is exact), so lane 15 of the row supplies it (below 2^-126 it flushes to 0)
-          const float bh = row_bcast16<15>(eL);
-          const float kk = kL[j];
-          qL[j] *= eL;
-          kL[j] = kk * eL;
-          kR[j] = kk * eRt;
-          rbv[j] = kR[j] * bh;                                     // right base k e^{s - c} <= |k|
-          ss[j] = bh;
-        }
-        if (lr == 15) {
-#pragma unroll
-          for (int j = 0; j < CPL; j += 4) store4(sBH + eR * DK + e_cb + j, ss[j], ss[j + 1], ss[j + 2], ss[j + 3]);
-        }
-        // diagonal Gram sub-block partials over this wave's channels
-        if constexpr (P == Prec::Mixed) {
-          if (fast16) {
-            // narrow decay: fp16 operands, one MFMA per 8 channels for each of M and A
-#pragma unroll
-            for (int t = 0; t < CPL / 8; ++t) {
-              half8 qh, kh, rh;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                qh[j] = (_Float16)qL[8 * t + j];
-                kh[j] = (_Float16)kL[8 * t + j];
-                rh[j] = (_Float16)kR[8 * t + j];
-              }
-              accQd = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, rh, accQd, 0, 0, 0);
-              accKd = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, rh, accKd, 0, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+              qh[j] = (_Float16)qh_[8 * t + j];
+              kh[j] = (_Float16)kh_[8 * t + j];
+              rh[j] = (_Float16)rh_[8 * t + j];
             }
-          } else {
-            // wide decay: M on the fp32 matrix core; A in bf16 (range), one MFMA per 8 channels
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j], kR[j], accQd, 0, 0, 0);
-#pragma unroll
-            for (int t = 0; t < CPL / 8; ++t) {
-              bf16x8 kh, bh8;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                kh[j] = (__bf16)kL[8 * t + j];
-                bh8[j] = (__bf16)kR[8 * t + j];
-              }
-              accKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh8, accKd, 0, 0, 0);
-            }
+            accQd = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, rh, accQd, 0, 0, 0);
+            accKd = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, rh, accKd, 0, 0, 0);
           }
         } else {
+          // wide decay: M on the fp32 matrix core; A in bf16 (range), one MFMA per 8 channels
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) {
-            accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qL[j], kR[j], accQd, 0, 0, 0);
-            accKd = __builtin_amdgcn_mfma_f32_16x16x4f32(kL[j], kR[j], accKd, 0, 0, 0);
+          for (int j = 0; j < GC; ++j) accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qh_[j], rh_[j], accQd, 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < GC / 8; ++t) {
+            bf16x8 kh, bh8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              kh[j] = (__bf16)kh_[8 * t + j];
+              bh8[j] = (__bf16)rh_[8 * t + j];
+            }
+            accKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh8, accKd, 0, 0, 0);
           }
         }
-        if (ep == 0 && lg == 0) sBE[e_row] = bcur;
+      } else {
+#pragma unroll
+        for (int j = 0; j < GC; ++j) {
+          accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qh_[j], rh_[j], accQd, 0, 0, 0);
+          accKd = __builtin_amdgcn_mfma_f32_16x16x4f32(kh_[j], rh_[j], accKd, 0, 0, 0);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < GR::QW; ++i) {
-        retire(gbuf.q[i]);
-        retire(gbuf.k[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < CPL / 4; ++i) retire(gbuf.la[i]);
-      retire(gbuf.b);
-#pragma unroll
-      for (int i = 0; i < VR::VW; ++i) retire(vbuf.v[i]);
     }
+  };
+  // the value / beta part; it also retires every loaded register of the chunk
+  auto gate_v = [&]() {
+    wave = wave0;
+    asm volatile("" : "+s"(wave));
+    refresh_lane();
+    v_row = tid / VPR;
+    v_c0 = 8 * (tid % VPR);
+    const int eR = e_act ? row_block_of<NB>(wave) : 0;
+    if (v_act) {
+      float vv[8];
+      unpack<InT>(vbuf.v, vv, 8);
+      store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
+      store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
+    }
+    if (e_act && (wave & 1) == 0 && lg == 0) sBE[16 * eR + lr] = gbuf.b;
+#pragma unroll
+    for (int i = 0; i < GR::QW; ++i) {
+      retire(gbuf.q[i]);
+      retire(gbuf.k[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CPL / 4; ++i) retire(gbuf.la[i]);
+    retire(gbuf.b);
+#pragma unroll
+    for (int i = 0; i < VR::VW; ++i) retire(vbuf.v[i]);
+  };
+  auto gate_a = [&]() {
+    static_for<0, GH>(gate_part);
+    gate_v();
   };
   auto store_rb = [&]() {
     const int x = fresh_lane();
@@ -666,7 +684,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   };
   if (nchunks > 0) {
     load_chunk(t_begin, chunk_len(0));
-    gate_a(0);
+    gate_a();
     store_rb();
   }
   for (int64_t ch = 0; ch < nchunks; ++ch) {
@@ -1013,6 +1031,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         }
       }
     }
+    // first part of the next chunk's gate stage (writes only BH, read after the next barrier)
+    if constexpr (GH > 1) gate_part(std::integral_constant<int, 0>{});
     __syncthreads();  // ------------------------------------------------------------- B_e
 
     // ================= U = Tb Y ; O = Qg S ; next chunk's gate stage =================
@@ -1034,7 +1054,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
       }
     });
-    gate_a(ch + 1);
+    gate_part(std::integral_constant<int, GH - 1>{});  // the only part when GH == 1
+    gate_v();
 #pragma unroll
     for (int s = 0; s < U_SLOTS; ++s) {
       const int id = wave + NW * s;
