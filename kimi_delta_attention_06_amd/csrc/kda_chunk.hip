@@ -439,9 +439,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   GR gbuf;
   VR vbuf;
   // The next chunk's inputs are loaded in four groups (q; k; the log-decay; v and beta),
-  // each issued after a different barrier: every CU reaches a barrier at about the same
-  // time, and one large group per chunk would be a device-wide burst that saturates HBM
-  // and stalls instruction issue while the rest of the chunk leaves it idle.
+  // issued in different stages: every CU runs the same stage at about the same time, and
+  // one large group per chunk would be a device-wide burst that saturates HBM and stalls
+  // instruction issue while the rest of the chunk leaves it idle.
   // Each group is a raw buffer load whose descriptor covers the chunk's valid rows of this
   // head: rows past the chunk's length (and every row past the last chunk) read as zero
   // in hardware, so the loads need no branch and no zero fill.
@@ -702,10 +702,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     const int e_cb = ep * (DK / 2) + CPL * lg;
 
     __syncthreads();  // ------------------------------------------------------------- B_a
-    // Next-chunk loads and gate stage run unconditionally: past the last chunk the length is
-    // <= 0, every lane's load is masked off and the gate stage writes only dead LDS.  With no
-    // path that skips them, no load is still pending where its registers are reloaded.
-    load_qk1(q, gbuf.q, c_begin + C, chunk_len(ch + 1));
 
     // ================= per-channel block factors (once per chunk) =================
     // With bh_J = e^{s_J/2} (<= 1), for row block R and channel c:
@@ -744,8 +740,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
       sGM[tid] = g;
     }
+    // Next-chunk loads (and the next gate stage) run unconditionally: past the last chunk
+    // the length is <= 0 and every load reads zero.  Each group is issued as a wave finishes
+    // a stage's work rather than right after a barrier, so the device's requests spread out.
+    load_qk1(q, gbuf.q, c_begin + C, chunk_len(ch + 1));
     __syncthreads();  // ------------------------------------------------------------- B_f1
-    load_qk1(k, gbuf.k, c_begin + C, chunk_len(ch + 1));
 
     // ================= gate stage, part b: off-diagonal Gram, state operands =================
     f32x4 accQo[NB > 1 ? NB - 1 : 1], accKo[NB > 1 ? NB - 1 : 1];
@@ -817,8 +816,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         sPT[(base + 1) * 64 + l] = make_float4(accKd[0], accKd[1], accKd[2], accKd[3]);
       }
     }
+    load_qk1(k, gbuf.k, c_begin + C, chunk_len(ch + 1));
     __syncthreads();  // ------------------------------------------------------------- B_b
-    load_la(c_begin + C, chunk_len(ch + 1));
 
     // ===== Gram reduction by one wave of each row block, in parallel with the inverse of
     //       that block's diagonal sub-block of A by the other =====
@@ -885,6 +884,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         store4(blk + lr * LDA + 4 * lg, xr[0], xr[1], xr[2], xr[3]);
       }
     }
+    load_la(c_begin + C, chunk_len(ch + 1));
     __syncthreads();  // ------------------------------------------------------------- B_c
     load_vb(c_begin + C, chunk_len(ch + 1));
 
@@ -1084,9 +1084,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
       }
     });
-    o_begin = c_begin;
-    o_len = Lc;
-    store_pending();
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
@@ -1097,6 +1094,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
       }
     }
+    o_begin = c_begin;
+    o_len = Lc;
+    store_pending();
     write_ST();
     // prefix-cache checkpoint: the state after p tokens of this sequence, p a multiple of
     // ckpt_every, goes to slot (sequence start + p) / ckpt_every - 1 (distinct for every
