@@ -8,10 +8,11 @@ pass (B*T tokens, all 32 heads).  The same pass with state checkpoints every 512
 tokens is timed and reported under "checkpointed".  In the same run the decode/replay state update
 (256 sequences x 32 heads, fp32 state, 1 and 8 tokens) and the replay + verify
 variant (8 tokens, per-sequence commit counts) are timed and reported under
-"decode" (HBM GB/s against the 8 TB/s peak), and the fp64 CPU oracle is
-timed on a bounded sample of the chunk workload ("cpu_baseline").
+"decode" (HBM GB/s against the 8 TB/s peak); one chunked pass over a single
+1M-token sequence x 32 heads is timed and reported under "long_context"; and the
+fp64 CPU oracle is timed on a bounded sample of the chunk workload ("cpu_baseline").
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-long-context] [--copy-calibration]
 Prints exactly one JSON line on stdout.  --copy-calibration adds three launches of a
 plain elementwise copy of known size (1 GiB read, 1 GiB written) after the timed
 region, so that hardware byte counters (FETCH_SIZE / WRITE_SIZE) taken over the
@@ -128,8 +129,10 @@ def copy_calibration(dev, nbytes=1 << 30):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults: ~25 ms of warm-up launches (clocks settle) and ~90 ms timed on the chunk kernel
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-long-context", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -237,6 +240,29 @@ def main():
         % (n_writing, dw.n_seqs, v_ms, v_gbs, 100 * v_gbs / HBM_PEAK_GBS))
     del v_inp, v_o
 
+    # ---------------- long context: one 1M-token sequence x 32 heads (32 chains) ----------------
+    long_context = None
+    if not args.no_long_context:
+        lw = kda_inputs.LONG_CONTEXT
+        log("generating %s inputs" % lw.name)
+        l_inp = kda_inputs.make_chunk_inputs(lw, device=dev)
+        l_o = torch.empty(lw.total_tokens, lw.n_heads, lw.dv, dtype=torch.float32, device=dev)
+        l_hT = torch.empty(1, lw.n_heads, lw.dk, lw.dv, dtype=torch.float32, device=dev)
+
+        def lstep():
+            kda.chunk_fwd(l_inp["q"], l_inp["k"], l_inp["v"], l_inp["log_alpha"], l_inp["beta"], h0=None,
+                          chunk_size=lw.chunk_size, o=l_o, hT=l_hT)
+
+        l_ms = time_launches(lstep, 3, 1, stream)
+        l_tok = lw.total_tokens / (l_ms * 1e-3)
+        l_bytes = lw.total_tokens * lw.n_heads * BYTES_PER_TOKEN_HEAD + lw.n_heads * lw.dk * lw.dv * 4
+        long_context = {"workload": lw.name, "tokens": lw.total_tokens, "heads": lw.n_heads, "ms_per_step": round(l_ms, 3),
+                        "tokens_per_s": round(l_tok, 1),
+                        "algorithmic_GB/s": round(l_bytes / (l_ms * 1e-3) / 1e9, 1)}
+        log("long context (%d tokens x %d heads): %.2f ms/launch, %.2f M tokens/s"
+            % (lw.total_tokens, lw.n_heads, l_ms, l_tok / 1e6))
+        del l_inp, l_o, l_hT
+
     result = {
         "metric": METRIC,
         "value": round(tok_s, 1),
@@ -260,6 +286,7 @@ def main():
                  "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": alg_flops},
         "checkpointed": checkpointed,
         "decode": decode,
+        "long_context": long_context,
         "wall_s_timed_region": round(t_wall, 3),
     }
     if args.copy_calibration:
