@@ -42,6 +42,7 @@
 #ifndef KDA_H_
 #define KDA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -121,6 +122,47 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
                                       int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
                                       int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
                                       int32_t ckpt_every, float* ckpt, void* stream);
+
+/*
+ * kda_chunk_fwd_split - kda_chunk_fwd in two passes, for inputs with few
+ * (sequence, head) chains such as one long sequence.
+ *
+ * The chunkwise form separates work inside a chunk (decay, Gram matrices, the
+ * UT inverse) from the propagation of the state across chunks ("Kimi K3 model
+ * structure (7)", Q&A on the training/prefill kernel; the same page lists
+ * in-device context parallelism among KDA's execution forms).  Pass 1 does the
+ * in-chunk work for every chunk of every head at once, in parallel over the
+ * whole sequence, and writes each chunk's state-free operands to `workspace`;
+ * pass 2 walks the chunks of each chain with the state, reading them.  Results
+ * equal kda_chunk_fwd's up to rounding (the same operand precisions).
+ *
+ * Same arguments and results as kda_chunk_fwd, plus:
+ *
+ *   workspace        device scratch of at least the size that
+ *                    kda_chunk_fwd_split_workspace_size returns for the same
+ *                    sizes; 16-byte aligned; must not overlap any other buffer.
+ *                    Its contents are undefined before and after the call.
+ *   workspace_bytes  its size in bytes
+ *
+ * Supported: as kda_chunk_fwd with qkv_dtype BF16 only (KDA_ERR_UNSUPPORTED
+ * otherwise).  Errors: as kda_chunk_fwd, plus KDA_ERR_INVALID_ARGUMENT for a
+ * NULL, misaligned, too small or overlapping workspace when tokens exist.
+ */
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta, const float* h0, const int32_t* cu_seqlens, int32_t n_seqs,
+                               int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk_size,
+                               kda_dtype qkv_dtype, float* o, float* hT, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * kda_chunk_fwd_split_workspace_size - bytes of workspace kda_chunk_fwd_split
+ * needs: (total_tokens / chunk_size + n_seqs + 1) * n_heads tiles of the
+ * per-chunk operands (66,304 B each for dk = 128, chunk 64).  Writes *bytes.
+ * Errors: KDA_ERR_INVALID_ARGUMENT (NULL bytes, negative or zero sizes, bad
+ * dtype), KDA_ERR_UNSUPPORTED (a combination kda_chunk_fwd_split does not take).
+ */
+kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                              int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, size_t* bytes);
 
 /*
  * kda_recurrent_step - decode / draft-replay state update.

@@ -17,13 +17,14 @@ recurrent_verify also takes n_commit [N] int32 (tokens whose updates are kept).
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "recurrent_step", "recurrent_verify", "KDAError"]
+__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "chunk_fwd_split", "recurrent_step", "recurrent_verify", "KDAError"]
 
 
 class KDAError(RuntimeError):
@@ -79,6 +80,17 @@ def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: in
     return o, hT
 
 
+def chunk_fwd_split(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: int = 64,
+                    output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                    hT: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """`chunk_fwd` as two passes (bf16 inputs): the in-chunk work of every chunk in parallel, then the
+    state pass; for inputs with few (sequence, head) chains.  `workspace` (uint8, at least the size the
+    library reports) is allocated when not given.  Returns (o, hT)."""
+    o, hT, _ = _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, 0, None,
+                      split=True, workspace=workspace)
+    return o, hT
+
+
 def chunk_fwd_checkpointed(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: int = 64,
                            ckpt_every: int = 512, output_final_state: bool = True,
                            o: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None,
@@ -89,7 +101,8 @@ def chunk_fwd_checkpointed(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, c
                   int(ckpt_every), ckpt)
 
 
-def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, ckpt_every, ckpt):
+def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, ckpt_every, ckpt,
+           split=False, workspace=None):
     lib = _lib.load()
     batched = q.dim() == 4
     if batched:
@@ -135,7 +148,20 @@ def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_st
     else:
         hT = None
     stream = torch.cuda.current_stream(dev).cuda_stream
-    if ckpt_every == 0:
+    if split:
+        need = ctypes.c_size_t(0)
+        rc = lib.kda_chunk_fwd_split_workspace_size(n_seqs, T_total, H, dk, dv, int(chunk_size), code,
+                                                    ctypes.byref(need))
+        _check(rc, "kda_chunk_fwd_split_workspace_size")
+        if workspace is None:
+            workspace = torch.empty(max(int(need.value), 16), dtype=torch.uint8, device=dev)
+        else:
+            workspace = _dev(workspace, "workspace", torch.uint8, dev)
+        rc = lib.kda_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                                     _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code, _ptr(o),
+                                     _ptr(hT), _ptr(workspace), workspace.numel(), stream)
+        _check(rc, "kda_chunk_fwd_split")
+    elif ckpt_every == 0:
         rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
                                _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code, _ptr(o),
                                _ptr(hT), stream)

@@ -21,7 +21,7 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
                                const float* beta, const float* h0, const int32_t* cu_seqlens, int32_t n_seqs,
                                int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk_size,
                                kda_dtype qkv_dtype, float* o, float* hT, int32_t ckpt_every, float* ckpt,
-                               void* stream) {
+                               bool split, void* ws, size_t ws_bytes, void* stream) {
   if (n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0 || chunk_size <= 0)
     return KDA_ERR_INVALID_ARGUMENT;
   // checkpoints: ckpt_every > 0 and a multiple of the chunk size; ckpt holds
@@ -79,6 +79,27 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   if (!dims_ok(dk) || !dims_ok(dv)) return KDA_ERR_UNSUPPORTED;
   const bool bf16 = qkv_dtype == KDA_DTYPE_BF16;
   if (!kda::chunk_fwd_supported(dk, dv, chunk_size, bf16)) return KDA_ERR_UNSUPPORTED;
+  if (split) {
+    if (!bf16) return KDA_ERR_UNSUPPORTED;
+    const size_t need = kda::chunk_split_workspace_bytes(total_tokens, n_seqs, n_heads, dk, chunk_size);
+    if (n_seqs > 0 && total_tokens > 0) {
+      if (!ws || !aligned16(ws) || ws_bytes < need) return KDA_ERR_INVALID_ARGUMENT;
+      // the workspace must not overlap any input or output
+      const char* wb = (const char*)ws;
+      const char* we = wb + need;
+      const size_t esz = 2;
+      struct R { const void* p; size_t n; } bufs[] = {
+          {q, (size_t)total_tokens * n_heads * dk * esz}, {k, (size_t)total_tokens * n_heads * dk * esz},
+          {v, (size_t)total_tokens * n_heads * dv * esz}, {log_alpha, (size_t)total_tokens * n_heads * dk * 4},
+          {beta, (size_t)total_tokens * n_heads * 4}, {o, (size_t)total_tokens * n_heads * dv * 4},
+          {h0, h0 ? (size_t)n_seqs * n_heads * dk * dv * 4 : 0}, {hT, hT ? (size_t)n_seqs * n_heads * dk * dv * 4 : 0},
+          {cu_seqlens, cu_seqlens ? (size_t)(n_seqs + 1) * 4 : 0}};
+      for (const R& r : bufs) {
+        const char* b = (const char*)r.p;
+        if (r.n && b < we && wb < b + r.n) return KDA_ERR_INVALID_ARGUMENT;
+      }
+    }
+  }
   if (n_seqs == 0) return KDA_OK;
 
   kda::ChunkArgs a;
@@ -86,6 +107,10 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT; a.ckpt = ckpt; a.ckpt_every = ckpt ? ckpt_every : 1;
   a.n_seqs = n_seqs; a.n_heads = n_heads; a.dk = dk; a.dv = dv; a.chunk_size = chunk_size;
   a.total_tokens = total_tokens; a.seq_len = seq_len; a.bf16 = bf16; a.stream = stream;
+  if (split) {
+    if (total_tokens == 0) return kda::launch_chunk_fwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;  // hT only
+    return kda::launch_chunk_fwd_split(a, ws) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+  }
   return kda::launch_chunk_fwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -95,7 +120,28 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
                          void* stream) {
   return chunk_common(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, chunk_size,
-                      qkv_dtype, o, hT, 0, nullptr, stream);
+                      qkv_dtype, o, hT, 0, nullptr, false, nullptr, 0, stream);
+}
+
+kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                              int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, size_t* bytes) {
+  if (!bytes || n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0 || chunk_size <= 0)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (qkv_dtype != KDA_DTYPE_F32 && qkv_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (!dims_ok(dk) || !dims_ok(dv) || qkv_dtype != KDA_DTYPE_BF16 ||
+      !kda::chunk_fwd_supported(dk, dv, chunk_size, true))
+    return KDA_ERR_UNSUPPORTED;
+  *bytes = kda::chunk_split_workspace_bytes(total_tokens, n_seqs, n_heads, dk, chunk_size);
+  return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta, const float* h0, const int32_t* cu_seqlens, int32_t n_seqs,
+                               int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk_size,
+                               kda_dtype qkv_dtype, float* o, float* hT, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return chunk_common(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, chunk_size,
+                      qkv_dtype, o, hT, 0, nullptr, true, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -105,7 +151,7 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
                                       int32_t ckpt_every, float* ckpt, void* stream) {
   if (ckpt_every <= 0) return KDA_ERR_INVALID_ARGUMENT;
   return chunk_common(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, chunk_size,
-                      qkv_dtype, o, hT, ckpt_every, ckpt, stream);
+                      qkv_dtype, o, hT, ckpt_every, ckpt, false, nullptr, 0, stream);
 }
 
 static kda_status recurrent_common(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -292,12 +292,15 @@ __device__ __forceinline__ void unpack(const uint4* w, float* out, int n) {
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <int C, int DK, int BV, Prec P, typename InT>
+// PREP = false: the fused forward.  PREP = true: the intra-chunk part only, for a group of
+// `cpg` consecutive chunks of one (sequence, head) per workgroup; each chunk's state-free
+// operands go to workspace slot (sequence start / C + sequence + chunk) (see write_ws).
+template <int C, int DK, int BV, Prec P, typename InT, bool PREP>
 __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* h0,
     const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT, float* __restrict__ ckpt,
-    int ckpt_every, int n_chains, int H, int DV, int64_t seq_len) {
+    int ckpt_every, int n_chains, int H, int DV, int64_t seq_len, void* __restrict__ ws, int cpg) {
   using L = Lay<C, DK, BV, P>;
   using T = typename L::T;
   constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
@@ -333,11 +336,18 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   T* sUT = reinterpret_cast<T*>(smem + L::UT);
 
   // ---- (sequence, head, value tile); the value tiles of one chain share an XCD
-  const int ntile = DV / BV;
+  // (prep: (sequence, head, chunk group))
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, qd = bid >> 3;
-  const int tile = qd % ntile;
-  const int chain = (qd / ntile) * 8 + xcd;
+  int chain, tile = 0, grp = 0;
+  if constexpr (PREP) {
+    chain = bid % n_chains;
+    grp = bid / n_chains;
+  } else {
+    const int ntile = DV / BV;
+    const int xcd = bid & 7, qd = bid >> 3;
+    tile = qd % ntile;
+    chain = (qd / ntile) * 8 + xcd;
+  }
   if (chain >= n_chains) return;
   const int n = chain / H, h = chain - n * H;
   const int j0 = tile * BV;
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   for (int s = 0; s < S_SLOTS; ++s) {
     const int id = wave + NW * s;
     Sacc[s] = zero4();
-    if (id < NA * NJ && h0p) {
+    if (!PREP && id < NA * NJ && h0p) {
       const int a = id % NA, j = id / NA;
 #pragma unroll
       for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr];
@@ -397,7 +407,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
   };
-  write_ST();
+  if constexpr (!PREP) write_ST();
 
   // ---- gate-stage map: waves (R = wave/2, p = wave%2) for 2*NB waves
   const bool e_act = 2 * NB >= NW || wave0 < 2 * NB;
@@ -426,6 +436,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   };
 
   const int64_t nchunks = (t_end - t_begin + C - 1) / C;
+  int64_t ch_lo = 0, ch_hi = nchunks;
+  if constexpr (PREP) {
+    ch_lo = (int64_t)grp * cpg;
+    ch_hi = ch_lo + cpg < nchunks ? ch_lo + cpg : nchunks;
+    if (ch_lo >= ch_hi) return;
+  }
 
   using GR = GateRegs<InT, CPL>;
   using VR = VRegs<InT>;
@@ -477,7 +493,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
                               Lc > 0 ? (uint32_t)Lc * (uint32_t)(H * DV * sizeof(InT)) : 0u);
     gbuf.b = buf_load4(rb_, ld_off_b);
 #pragma unroll
-    for (int i = 0; i < VR::VW; ++i) vbuf.v[i] = buf_load16(rv, v_off + 16 * i);
+    for (int i = 0; i < VR::VW; ++i) vbuf.v[i] = PREP ? make_uint4(0, 0, 0, 0) : buf_load16(rv, v_off + 16 * i);
   };
   auto load_chunk = [&](int64_t cb, int Lc) {
     load_qk1(q, gbuf.q, cb, Lc);
@@ -502,6 +518,34 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
       }
+    }
+  };
+  // Workspace tile of one (chunk, head), 16-byte units in this order: Qg [C][DK], Kg [C][DK],
+  // Kd^T [DK][C], strict M [C][C], T Diag(beta) [C][C] (all T), then q.k [C] and e^{g_last}
+  // [DK] (fp32).  Slot of chunk j of the sequence starting at token t0: t0 / C + n + j.
+  auto write_ws = [&](int64_t chn) {
+    constexpr int U8 = 16 / (int)sizeof(T);
+    constexpr int NQ = C * DK / U8, NKD = DK * C / U8, NAQ = C * C / U8, NDQ = C / 4, NGM = DK / 4;
+    constexpr int NU = 2 * NQ + NKD + 2 * NAQ + NDQ + NGM;
+    const int64_t slot = t_begin / C + n + chn;
+    uint4* dst = reinterpret_cast<uint4*>(ws) + ((size_t)slot * H + h) * NU;
+    for (int i = tid; i < NU; i += NT) {
+      const void* src;
+      if (i < 2 * NQ) {
+        const int ii = i < NQ ? i : i - NQ;
+        src = (i < NQ ? sQG : sKG) + (ii / (DK / U8)) * LDD + (ii % (DK / U8)) * U8;
+      } else if (i < 2 * NQ + NKD) {
+        const int ii = i - 2 * NQ;
+        src = sKDT + (ii / (C / U8)) * LDC + (ii % (C / U8)) * U8;
+      } else if (i < 2 * NQ + NKD + 2 * NAQ) {
+        const int ii0 = i - 2 * NQ - NKD, ii = ii0 < NAQ ? ii0 : ii0 - NAQ;
+        src = (ii0 < NAQ ? sAQ : sTB) + (ii / (C / U8)) * LDC + (ii % (C / U8)) * U8;
+      } else if (i < NU - NGM) {
+        src = sDQ + 4 * (i - (NU - NGM - NDQ));
+      } else {
+        src = sGM + 4 * (i - (NU - NGM));
+      }
+      dst[i] = *reinterpret_cast<const uint4*>(src);
     }
   };
   auto store_pending = [&]() {
@@ -651,7 +695,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     v_row = tid / VPR;
     v_c0 = 8 * (tid % VPR);
     const int eR = e_act ? row_block_of<NB>(wave) : 0;
-    if (v_act) {
+    if (!PREP && v_act) {
       float vv[8];
       unpack<InT>(vbuf.v, vv, 8);
       store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
@@ -682,12 +726,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       for (int j = 0; j < CPL; j += 4) store4(dst + j, rbv[j], rbv[j + 1], rbv[j + 2], rbv[j + 3]);
     }
   };
-  if (nchunks > 0) {
-    load_chunk(t_begin, chunk_len(0));
+  if (ch_hi > ch_lo) {
+    load_chunk(t_begin + ch_lo * C, chunk_len(ch_lo));
     gate_a();
     store_rb();
   }
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
+  for (int64_t ch = ch_lo; ch < ch_hi; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
     const int Lc = chunk_len(ch);
     // Wave-dependent LDS offsets are cheap scalar arithmetic; an opaque copy of the
@@ -964,7 +1008,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(vv[i] - ks[i]);
       };
-      if constexpr (NB % 2 == 0 && NJ % 2 == 0) {
+      if constexpr (PREP) {
+        // no state here: Y is formed by the state kernel
+      } else if constexpr (NB % 2 == 0 && NJ % 2 == 0) {
         constexpr int NYB = (NB / 2) * (NJ / 2);
         static_for<0, (NYB + NH - 1) / NH>([&](auto sc) {
           constexpr int s = decltype(sc)::value;
@@ -1035,41 +1081,323 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     if constexpr (GH > 1) gate_part(std::integral_constant<int, 0>{});
     __syncthreads();  // ------------------------------------------------------------- B_e
 
-    // ================= U = Tb Y ; O = Qg S ; next chunk's gate stage =================
-    // The products are issued first; the next chunk's gate stage (vector ALU) runs while
-    // they complete.  It writes V, BH and beta, none of which is read after the barrier
-    // above; the loads it consumes were issued two stages ago.
-    f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
+    if constexpr (PREP) {
+      // the chunk's state-free operands to its workspace slot, beside the next gate stage
+      write_ws(ch);
+      gate_part(std::integral_constant<int, GH - 1>{});  // the only part when GH == 1
+      gate_v();
+      __syncthreads();  // (prep) the right base is stored after this barrier
+      store_rb();
+    } else {
+      // ================= U = Tb Y ; O = Qg S ; next chunk's gate stage =================
+      // The products are issued first; the next chunk's gate stage (vector ALU) runs while
+      // they complete.  It writes V, BH and beta, none of which is read after the barrier
+      // above; the loads it consumes were issued two stages ago.
+      f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
+      static_for<0, U_SLOTS>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
+                                       : CK / KS;
+        const int id = wave + NW * s;
+        Uacc[s] = zero4();
+        Oacc[s] = zero4();
+        if ((NB * NJ) % NW == 0 || id < NB * NJ) {
+          int R, j;
+          uo_tile(s, R, j);
+          mma_lds<T, KS, steps>(Uacc[s], sYT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
+          mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
+        }
+      });
+      gate_part(std::integral_constant<int, GH - 1>{});  // the only part when GH == 1
+      gate_v();
+  #pragma unroll
+      for (int s = 0; s < U_SLOTS; ++s) {
+        const int id = wave + NW * s;
+        if ((NB * NJ) % NW == 0 || id < NB * NJ) {
+          int R, j;
+          uo_tile(s, R, j);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(Uacc[s][i]);
+        }
+      }
+      __syncthreads();  // ------------------------------------------------------------- B_f
+      store_rb();
+
+      // ================= O += M U ; S <- e^{g} S + Kd^T U =================
+      static_for<0, U_SLOTS>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
+                                       : CK / KS;
+        const int id = wave + NW * s;
+        if ((NB * NJ) % NW == 0 || id < NB * NJ) {
+          int R, j;
+          uo_tile(s, R, j);
+          mma_lds<T, KS, steps>(Oacc[s], sUT + 16 * j * LDC, LDC, sAQ + 16 * R * LDC, LDC);
+          const float dq = sDQ[16 * R + lr];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
+        }
+      });
+  #pragma unroll
+      for (int s = 0; s < S_SLOTS; ++s) {
+        const int id = wave + NW * s;
+        if ((NA * NJ) % NW == 0 || id < NA * NJ) {
+          const int a = id % NA, j = id / NA;
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
+          mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
+        }
+      }
+      o_begin = c_begin;
+      o_len = Lc;
+      store_pending();
+      write_ST();
+      // prefix-cache checkpoint: the state after p tokens of this sequence, p a multiple of
+      // ckpt_every, goes to slot (sequence start + p) / ckpt_every - 1 (distinct for every
+      // checkpoint of every packed sequence)
+      if (ckpt && (c_begin + Lc - t_begin) % ckpt_every == 0) {
+        const int64_t slot = (c_begin + Lc) / ckpt_every - 1;
+        store_state(ckpt + ((size_t)slot * H + h) * DK * DV);
+      }
+    }
+  }
+
+  if (!PREP && hT) store_state(hT + (size_t)chain * DK * DV);
+}
+
+// ---------------------------------------------------------------------------
+// State-only kernel of the split path.  Per (sequence, head, value tile) it walks the
+// chunks in order with the fp32 master state in accumulator registers:
+//   Y = V - Kg S,  U = (T Diag beta) Y,  O = Qg S + M U + diag(q.k) U,  S <- Diag(gamma) S + Kd^T U,
+// reading each chunk's state-free operands from the workspace tile the prep pass wrote
+// (same units and order as write_ws).  The next chunk's tile is loaded into registers
+// while the current one is used and moved to LDS after its last read.
+// ---------------------------------------------------------------------------
+template <int C, int DK, int BV>
+struct SLay {
+  static constexpr int KS = 32, PD = 8, NB = C / 16;
+  static constexpr int CK = ((C + KS - 1) / KS) * KS;
+  static constexpr int LDD = DK + PD, LDC = CK + PD, LDV = BV + PD;
+  static constexpr size_t ST = 0;                                   // S^T [BV][LDD]
+  static constexpr size_t QG = ST + al16(size_t(BV) * LDD * 2);     // Qg [C][LDD]
+  static constexpr size_t KG = QG + al16(size_t(C) * LDD * 2);      // Kg [C][LDD]
+  static constexpr size_t KDT = KG + al16(size_t(C) * LDD * 2);     // Kd^T [DK][LDC]
+  static constexpr size_t AQ = KDT + al16(size_t(DK) * LDC * 2);    // strict M [C][LDC]
+  static constexpr size_t TB = AQ + al16(size_t(C) * LDC * 2);      // T Diag(beta) [C][LDC]
+  static constexpr size_t DQ = TB + al16(size_t(C) * LDC * 2);      // q.k [C] fp32
+  static constexpr size_t GM = DQ + al16(size_t(C) * 4);            // e^{g_last} [DK] fp32
+  static constexpr size_t VR = GM + al16(size_t(DK) * 4);           // V [C][LDV]
+  static constexpr size_t YT = VR + al16(size_t(C) * LDV * 2);      // Y^T [BV][LDC]
+  static constexpr size_t UT = YT + al16(size_t(BV) * LDC * 2);     // U^T [BV][LDC]
+  static constexpr size_t TOTAL = UT + al16(size_t(BV) * LDC * 2);
+  // workspace tile in 16-byte units
+  static constexpr int NQ = C * DK / 8, NKD = DK * C / 8, NAQ = C * C / 8, NDQ = C / 4, NGM = DK / 4;
+  static constexpr int NU = 2 * NQ + NKD + 2 * NAQ + NDQ + NGM;
+};
+
+template <int C, int DK, int BV, typename InT>
+__global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
+    const uint4* __restrict__ ws, const InT* __restrict__ v, const float* h0,
+    const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT,
+    int n_chains, int H, int DV, int64_t seq_len) {
+  using L = SLay<C, DK, BV>;
+  using T = _Float16;
+  constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
+  constexpr int LDD = L::LDD, LDC = L::LDC, LDV = L::LDV;
+  constexpr int NA = DK / 16, NJ = BV / 16, VPR = BV / 8;
+  constexpr int NQ = L::NQ, NKD = L::NKD, NAQ = L::NAQ, NDQ = L::NDQ, NGM = L::NGM, NU = L::NU;
+  constexpr int PF = (NU + NT - 1) / NT;
+  static_assert(sizeof(InT) == 2 && C * VPR <= NT, "bf16 values, one 16-byte load per lane");
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* sST = reinterpret_cast<T*>(smem + L::ST);
+  T* sQG = reinterpret_cast<T*>(smem + L::QG);
+  T* sKG = reinterpret_cast<T*>(smem + L::KG);
+  T* sKDT = reinterpret_cast<T*>(smem + L::KDT);
+  T* sAQ = reinterpret_cast<T*>(smem + L::AQ);
+  T* sTB = reinterpret_cast<T*>(smem + L::TB);
+  float* sDQ = reinterpret_cast<float*>(smem + L::DQ);
+  float* sGM = reinterpret_cast<float*>(smem + L::GM);
+  T* sV = reinterpret_cast<T*>(smem + L::VR);
+  T* sYT = reinterpret_cast<T*>(smem + L::YT);
+  T* sUT = reinterpret_cast<T*>(smem + L::UT);
+
+  const int ntile = DV / BV;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, qd = bid >> 3;
+  const int tile = qd % ntile;
+  const int chain = (qd / ntile) * 8 + xcd;
+  if (chain >= n_chains) return;
+  const int n = chain / H, h = chain - n * H;
+  const int j0 = tile * BV;
+  int64_t t_begin, t_end;
+  if (cu_seqlens) {
+    t_begin = cu_seqlens[n];
+    t_end = cu_seqlens[n + 1];
+  } else {
+    t_begin = (int64_t)n * seq_len;
+    t_end = t_begin + seq_len;
+  }
+  const int64_t nchunks = (t_end - t_begin + C - 1) / C;
+  auto chunk_len = [&](int64_t ch) -> int {
+    const int64_t rem = t_end - (t_begin + ch * C);
+    return (int)(rem < C ? rem : C);
+  };
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l = lane_id(), lr = l & 15, lg = l >> 4;
+
+  // zero once: the padded token columns (C .. CK) of the token-contiguous operands stay zero
+  for (int i = tid; i < int((L::VR - L::KDT) / 2); i += NT) sKDT[i] = (T)0.f;
+  for (int i = tid; i < int((L::TOTAL - L::YT) / 2); i += NT) sYT[i] = (T)0.f;
+
+  constexpr int S_SLOTS = (NA * NJ + NW - 1) / NW;
+  f32x4 Sacc[S_SLOTS];
+  const float* h0p = h0 ? h0 + (size_t)chain * DK * DV : nullptr;
+#pragma unroll
+  for (int s = 0; s < S_SLOTS; ++s) {
+    const int id = wave + NW * s;
+    Sacc[s] = zero4();
+    if (id < NA * NJ && h0p) {
+      const int a = id % NA, j = id / NA;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr];
+    }
+  }
+  auto write_ST = [&]() {
+#pragma unroll
+    for (int s = 0; s < S_SLOTS; ++s) {
+      const int id = wave + NW * s;
+      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
+        const int a = id % NA, j = id / NA;
+        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
+      }
+    }
+  };
+  auto store_state = [&](float* sp) {
+#pragma unroll
+    for (int s = 0; s < S_SLOTS; ++s) {
+      const int id = wave + NW * s;
+      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
+        const int a = id % NA, j = id / NA;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
+      }
+    }
+  };
+
+  constexpr int U_SLOTS = (NB * NJ + NW - 1) / NW;
+  constexpr bool UO_SPLIT = NB == 4 && NJ == 4 && NW == 8;
+  auto uo_tile = [&](int s, int& R, int& j) {
+    if constexpr (UO_SPLIT) {
+      R = 2 * s + (wave >> 2);
+      j = wave & 3;
+    } else {
+      const int id = wave + NW * s;
+      R = id % NB;
+      j = id / NB;
+    }
+  };
+
+  // next chunk's workspace tile and value rows, in registers
+  uint4 pf[PF], pv;
+  const bool v_act = C * VPR >= NT || tid < C * VPR;
+  const int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
+  auto load_tiles = [&](int64_t chn) {
+    const bool ok = chn < nchunks;
+    const int64_t slot = t_begin / C + n + chn;
+    const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * NU, ok ? (uint32_t)NU * 16u : 0u);
+#pragma unroll
+    for (int p = 0; p < PF; ++p) pf[p] = buf_load16(rs, (uint32_t)(tid + p * NT) * 16u);
+    const int Lc = ok ? chunk_len(chn) : 0;
+    const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + j0,
+                              Lc > 0 ? (uint32_t)Lc * (uint32_t)(H * DV * 2) : 0u);
+    pv = buf_load16(rv, (uint32_t)(v_row * H * DV + v_c0) * 2u);
+  };
+  auto store_tiles = [&]() {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int i = tid + p * NT;
+      if (NU % NT == 0 || i < NU) {
+        void* dst;
+        if (i < 2 * NQ) {
+          const int ii = i < NQ ? i : i - NQ;
+          dst = (i < NQ ? sQG : sKG) + (ii / (DK / 8)) * LDD + (ii % (DK / 8)) * 8;
+        } else if (i < 2 * NQ + NKD) {
+          const int ii = i - 2 * NQ;
+          dst = sKDT + (ii / (C / 8)) * LDC + (ii % (C / 8)) * 8;
+        } else if (i < 2 * NQ + NKD + 2 * NAQ) {
+          const int ii0 = i - 2 * NQ - NKD, ii = ii0 < NAQ ? ii0 : ii0 - NAQ;
+          dst = (ii0 < NAQ ? sAQ : sTB) + (ii / (C / 8)) * LDC + (ii % (C / 8)) * 8;
+        } else if (i < NU - NGM) {
+          dst = sDQ + 4 * (i - (NU - NGM - NDQ));
+        } else {
+          dst = sGM + 4 * (i - (NU - NGM));
+        }
+        *reinterpret_cast<uint4*>(dst) = pf[p];
+      }
+    }
+    if (v_act) {
+      const uint4* pw = &pv;
+      float vv[8];
+      unpack<InT>(pw, vv, 8);
+      store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
+      store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
+    }
+  };
+
+  __syncthreads();  // zero fill before the first tile
+  write_ST();
+  if (nchunks > 0) {
+    load_tiles(0);
+    store_tiles();
+  }
+  __syncthreads();
+
+  f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    const int64_t c_begin = t_begin + ch * C;
+    const int Lc = chunk_len(ch);
+    load_tiles(ch + 1);
+
+    // Y = V - Kg S (to Y^T) and O = Qg S
+#pragma unroll
+    for (int s = 0; s < U_SLOTS; ++s) {
+      const int id = wave + NW * s;
+      Oacc[s] = zero4();
+      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
+        int R, j;
+        uo_tile(s, R, j);
+        f32x4 ks = zero4();
+        mma_lds<T, KS, DK / KS>(ks, sST + 16 * j * LDD, LDD, sKG + 16 * R * LDD, LDD);
+        mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
+        const float4 v4 = load4(sV + (16 * R + lr) * LDV + 16 * j + 4 * lg);
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)(vv[i] - ks[i]);
+      }
+    }
+    __syncthreads();
+
+    // U = (T Diag beta) Y (to U^T)
     static_for<0, U_SLOTS>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
       constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
                                      : CK / KS;
       const int id = wave + NW * s;
       Uacc[s] = zero4();
-      Oacc[s] = zero4();
       if ((NB * NJ) % NW == 0 || id < NB * NJ) {
         int R, j;
         uo_tile(s, R, j);
         mma_lds<T, KS, steps>(Uacc[s], sYT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
-        mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)Uacc[s][i];
       }
     });
-    gate_part(std::integral_constant<int, GH - 1>{});  // the only part when GH == 1
-    gate_v();
-#pragma unroll
-    for (int s = 0; s < U_SLOTS; ++s) {
-      const int id = wave + NW * s;
-      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        int R, j;
-        uo_tile(s, R, j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(Uacc[s][i]);
-      }
-    }
-    __syncthreads();  // ------------------------------------------------------------- B_f
-    store_rb();
+    __syncthreads();
 
-    // ================= O += M U ; S <- e^{g} S + Kd^T U =================
+    // O += M U + diag(q.k) U, stored; S <- Diag(gamma) S + Kd^T U
     static_for<0, U_SLOTS>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
       constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
@@ -1080,8 +1408,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         uo_tile(s, R, j);
         mma_lds<T, KS, steps>(Oacc[s], sUT + 16 * j * LDC, LDC, sAQ + 16 * R * LDC, LDC);
         const float dq = sDQ[16 * R + lr];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
+        const int r = 16 * R + lr;
+        if (r < Lc) {
+          float* op = o + ((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + 4 * lg;
+          *reinterpret_cast<float4*>(op) = make_float4(Oacc[s][0] + dq * Uacc[s][0], Oacc[s][1] + dq * Uacc[s][1],
+                                                       Oacc[s][2] + dq * Uacc[s][2], Oacc[s][3] + dq * Uacc[s][3]);
+        }
       }
     });
 #pragma unroll
@@ -1094,49 +1426,105 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
       }
     }
-    o_begin = c_begin;
-    o_len = Lc;
-    store_pending();
+    __syncthreads();  // every read of this chunk's tile and of S^T is done
     write_ST();
-    // prefix-cache checkpoint: the state after p tokens of this sequence, p a multiple of
-    // ckpt_every, goes to slot (sequence start + p) / ckpt_every - 1 (distinct for every
-    // checkpoint of every packed sequence)
-    if (ckpt && (c_begin + Lc - t_begin) % ckpt_every == 0) {
-      const int64_t slot = (c_begin + Lc) / ckpt_every - 1;
-      store_state(ckpt + ((size_t)slot * H + h) * DK * DV);
-    }
+    store_tiles();
+    __syncthreads();
   }
-
   if (hT) store_state(hT + (size_t)chain * DK * DV);
 }
 
 // ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
-template <int C, int DK, int BV, Prec P, typename InT>
-static hipError_t launch_one(const ChunkArgs& a) {
-  constexpr size_t lds = lds_bytes<C, DK, BV, P>();
-  static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = chunk_fwd_kernel<C, DK, BV, P, InT>;
-  // the dynamic-LDS limit is a per-device attribute: set it once per device (one bit
-  // each, thread-safe); devices past the 64th set it on every launch
-  static std::atomic<uint64_t> attr_done{0};
+// The dynamic-LDS limit is a per-device attribute of each kernel: set it once per device
+// (one bit each in the kernel's own flag word, thread-safe); devices past the 64th set it
+// on every launch.
+static hipError_t set_lds_limit(const void* kern, size_t lds, std::atomic<uint64_t>& done) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
-  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if (bit) attr_done.fetch_or(bit, std::memory_order_release);
+    if (bit) done.fetch_or(bit, std::memory_order_release);
   }
+  return hipSuccess;
+}
+
+template <int C, int DK, int BV, Prec P, typename InT>
+static hipError_t launch_one(const ChunkArgs& a) {
+  constexpr size_t lds = lds_bytes<C, DK, BV, P>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = chunk_fwd_kernel<C, DK, BV, P, InT, false>;
+  static std::atomic<uint64_t> attr_done{0};
+  hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
+  if (e != hipSuccess) return e;
   const int n_chains = a.n_seqs * a.n_heads;
   const int ntile = a.dv / BV;
   const int grid = ((n_chains + 7) / 8) * 8 * ntile;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q, (const InT*)a.k,
                      (const InT*)a.v, a.log_alpha, a.beta, a.h0, a.cu_seqlens, a.o, a.hT, a.ckpt, a.ckpt_every,
-                     n_chains, a.n_heads, a.dv, a.seq_len);
+                     n_chains, a.n_heads, a.dv, a.seq_len, nullptr, 0);
   return hipGetLastError();
+}
+
+static int pick_bv(int n_chains, int dv, int max_bv);
+
+// ---- split path: prep pass (intra-chunk operands to the workspace), then the state pass
+template <int C, int DK>
+constexpr size_t split_tile_bytes() { return size_t(SLay<C, DK, 16>::NU) * 16; }
+
+// upper bound on chunks per sequence, known on the host without reading cu_seqlens
+static int64_t max_chunks_per_seq(const ChunkArgs& a) {
+  const int64_t len = a.cu_seqlens ? a.total_tokens : a.seq_len;
+  return (len + a.chunk_size - 1) / a.chunk_size;
+}
+
+template <int C, int DK, int BV, typename InT>
+static hipError_t launch_split(const ChunkArgs& a, void* ws) {
+  const int n_chains = a.n_seqs * a.n_heads;
+  {
+    constexpr size_t lds = lds_bytes<C, DK, 16, Prec::Mixed>();
+    auto kern = chunk_fwd_kernel<C, DK, 16, Prec::Mixed, InT, true>;
+    static std::atomic<uint64_t> attr_done{0};
+    hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
+    if (e != hipSuccess) return e;
+    // chunks per workgroup: about 8 workgroups per CU over the whole input, 4 to 64 chunks
+    const int64_t mc = max_chunks_per_seq(a);
+    int64_t cpg = ((int64_t)n_chains * mc) / 2048;
+    cpg = cpg < 4 ? 4 : (cpg > 64 ? 64 : cpg);
+    const int64_t groups = (mc + cpg - 1) / cpg;
+    const int64_t grid = (int64_t)n_chains * (groups > 0 ? groups : 1);
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q,
+                       (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, nullptr, a.cu_seqlens, nullptr, nullptr,
+                       nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    constexpr size_t lds = SLay<C, DK, BV>::TOTAL;
+    static_assert(lds <= 160 * 1024, "LDS budget");
+    auto kern = chunk_state_kernel<C, DK, BV, InT>;
+    static std::atomic<uint64_t> attr_done{0};
+    hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
+    if (e != hipSuccess) return e;
+    const int ntile = a.dv / BV;
+    const int grid = ((n_chains + 7) / 8) * 8 * ntile;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, (hipStream_t)a.stream, (const uint4*)ws, (const InT*)a.v,
+                       a.h0, a.cu_seqlens, a.o, a.hT, n_chains, a.n_heads, a.dv, a.seq_len);
+    return hipGetLastError();
+  }
+}
+
+template <int C, int DK, typename InT>
+static hipError_t dispatch_split_bv(const ChunkArgs& a, void* ws) {
+  const int bv = pick_bv(a.n_seqs * a.n_heads, a.dv, 64);
+  if (bv == 64) return launch_split<C, DK, 64, InT>(a, ws);
+  if (bv == 32) return launch_split<C, DK, 32, InT>(a, ws);
+  return launch_split<C, DK, 16, InT>(a, ws);
 }
 
 // value-tile width: the widest that still gives at least one workgroup per CU
@@ -1181,6 +1569,34 @@ bool chunk_fwd_supported(int dk, int dv, int chunk_size, bool bf16) {
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return false;
   if (!bf16 && dk == 128 && chunk_size == 64) return false;
   return true;
+}
+
+size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int chunk_size) {
+  using namespace chunkk;
+  size_t tile = 0;
+  if (dk == 128) {
+    tile = chunk_size == 64 ? split_tile_bytes<64, 128>() : chunk_size == 32 ? split_tile_bytes<32, 128>()
+                                                                             : split_tile_bytes<16, 128>();
+  } else {
+    tile = chunk_size == 64 ? split_tile_bytes<64, 64>() : chunk_size == 32 ? split_tile_bytes<32, 64>()
+                                                                            : split_tile_bytes<16, 64>();
+  }
+  // slots: sequence start / C + sequence index + chunk index < total_tokens / C + n_seqs + 1
+  const size_t slots = (size_t)(total_tokens / chunk_size) + (size_t)n_seqs + 1;
+  return slots * (size_t)n_heads * tile;
+}
+
+hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws) {
+  using namespace chunkk;
+  if (!a.bf16 || !chunk_fwd_supported(a.dk, a.dv, a.chunk_size, a.bf16)) return hipErrorInvalidValue;
+  if (a.dk == 128) {
+    if (a.chunk_size == 64) return dispatch_split_bv<64, 128, bf16_t>(a, ws);
+    if (a.chunk_size == 32) return dispatch_split_bv<32, 128, bf16_t>(a, ws);
+    return dispatch_split_bv<16, 128, bf16_t>(a, ws);
+  }
+  if (a.chunk_size == 64) return dispatch_split_bv<64, 64, bf16_t>(a, ws);
+  if (a.chunk_size == 32) return dispatch_split_bv<32, 64, bf16_t>(a, ws);
+  return dispatch_split_bv<16, 64, bf16_t>(a, ws);
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {

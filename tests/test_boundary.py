@@ -19,7 +19,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_checkpointed", "kda_recurrent_step",
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_checkpointed", "kda_chunk_fwd_split",
+                          "kda_chunk_fwd_split_workspace_size", "kda_recurrent_step",
                           "kda_recurrent_verify", "kda_status_string", "kda_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -118,3 +119,43 @@ def test_chunk_fwd_checkpointed_rejects(kw, code):
 def test_chunk_fwd_checkpointed_without_slots_accepts_null():
     # no tokens: no checkpoint slot exists, so ckpt may be NULL
     assert ckpt_call(N=0, T=0, q=None, k=None, v=None, la=None, b=None, o=None, ck=None) == 0
+
+
+def ws_size(N=1, T=64, H=2, dk=128, dv=128, C=64, dt=_lib.KDA_DTYPE_BF16, out=True):
+    b = ctypes.c_size_t(0)
+    rc = lib.kda_chunk_fwd_split_workspace_size(N, T, H, dk, dv, C, dt, ctypes.byref(b) if out else None)
+    return rc, b.value
+
+
+def test_split_workspace_size():
+    rc, n = ws_size()
+    # (64 / 64 + 1 + 1) slots x 2 heads x 66,304-byte tiles (dk 128, chunk 64)
+    assert rc == 0 and n == 3 * 2 * 66304
+    assert ws_size(T=1 << 20, N=1, H=32)[1] == ((1 << 20) // 64 + 2) * 32 * 66304
+    assert ws_size(dt=_lib.KDA_DTYPE_F32)[0] == 2
+    assert ws_size(dk=96)[0] == 2
+    assert ws_size(out=False)[0] == 1
+    assert ws_size(H=0)[0] == 1
+
+
+def split_call(**kw):
+    a = dict(q=P, k=P, v=P, la=P, b=P, h0=None, cu=None, N=1, T=64, H=2, dk=128, dv=128, C=64,
+             dt=_lib.KDA_DTYPE_BF16, o=P * 8, hT=None, ws=P * 64, wsb=1 << 22)
+    a.update(kw)
+    return lib.kda_chunk_fwd_split(a["q"], a["k"], a["v"], a["la"], a["b"], a["h0"], a["cu"], a["N"], a["T"],
+                                   a["H"], a["dk"], a["dv"], a["C"], a["dt"], a["o"], a["hT"], a["ws"], a["wsb"],
+                                   None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=None), 1), (dict(ws=P * 64 + 4), 1), (dict(wsb=1000), 1),
+    (dict(ws=P * 8), 1),  # workspace overlaps o
+    (dict(ws=P), 1),      # workspace overlaps the inputs
+    (dict(dt=_lib.KDA_DTYPE_F32), 2), (dict(dk=96), 2), (dict(C=48), 2), (dict(q=None), 1),
+])
+def test_chunk_fwd_split_rejects(kw, code):
+    assert split_call(**kw) == code
+
+
+def test_chunk_fwd_split_empty_batch_is_a_no_op():
+    assert split_call(N=0, T=0, q=None, k=None, v=None, la=None, b=None, o=None, ws=None, wsb=0) == 0
