@@ -1179,7 +1179,9 @@ struct SLay {
   static constexpr int CK = ((C + KS - 1) / KS) * KS;
   static constexpr int LDD = DK + PD, LDC = CK + PD, LDV = BV + PD;
   static constexpr size_t ST = 0;                                   // S^T [BV][LDD]
-  static constexpr size_t QG = ST + al16(size_t(BV) * LDD * 2);     // Qg [C][LDD]
+  static constexpr size_t T0 = ST + al16(size_t(BV) * LDD * 2);     // chunk tile buffer(s)
+  // offsets inside a chunk tile buffer
+  static constexpr size_t QG = 0;                                   // Qg [C][LDD]
   static constexpr size_t KG = QG + al16(size_t(C) * LDD * 2);      // Kg [C][LDD]
   static constexpr size_t KDT = KG + al16(size_t(C) * LDD * 2);     // Kd^T [DK][LDC]
   static constexpr size_t AQ = KDT + al16(size_t(DK) * LDC * 2);    // strict M [C][LDC]
@@ -1187,8 +1189,12 @@ struct SLay {
   static constexpr size_t DQ = TB + al16(size_t(C) * LDC * 2);      // q.k [C] fp32
   static constexpr size_t GM = DQ + al16(size_t(C) * 4);            // e^{g_last} [DK] fp32
   static constexpr size_t VR = GM + al16(size_t(DK) * 4);           // V [C][LDV]
-  static constexpr size_t YT = VR + al16(size_t(C) * LDV * 2);      // Y^T [BV][LDC]
-  static constexpr size_t UT = YT + al16(size_t(BV) * LDC * 2);     // U^T [BV][LDC]
+  static constexpr size_t TILE = VR + al16(size_t(C) * LDV * 2);
+  static constexpr size_t YU = 2 * al16(size_t(BV) * LDC * 2);      // Y^T and U^T [BV][LDC]
+  // two tile buffers when they fit: the next chunk's tile is written while this one is used
+  static constexpr bool DB = T0 + 2 * TILE + YU <= 160 * 1024;
+  static constexpr size_t YT = T0 + (DB ? 2 : 1) * TILE;
+  static constexpr size_t UT = YT + al16(size_t(BV) * LDC * 2);
   static constexpr size_t TOTAL = UT + al16(size_t(BV) * LDC * 2);
   // workspace tile in 16-byte units
   static constexpr int NQ = C * DK / 8, NKD = DK * C / 8, NAQ = C * C / 8, NDQ = C / 4, NGM = DK / 4;
@@ -1210,17 +1216,25 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
   static_assert(sizeof(InT) == 2 && C * VPR <= NT, "bf16 values, one 16-byte load per lane");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr bool DB = L::DB;
   T* sST = reinterpret_cast<T*>(smem + L::ST);
-  T* sQG = reinterpret_cast<T*>(smem + L::QG);
-  T* sKG = reinterpret_cast<T*>(smem + L::KG);
-  T* sKDT = reinterpret_cast<T*>(smem + L::KDT);
-  T* sAQ = reinterpret_cast<T*>(smem + L::AQ);
-  T* sTB = reinterpret_cast<T*>(smem + L::TB);
-  float* sDQ = reinterpret_cast<float*>(smem + L::DQ);
-  float* sGM = reinterpret_cast<float*>(smem + L::GM);
-  T* sV = reinterpret_cast<T*>(smem + L::VR);
   T* sYT = reinterpret_cast<T*>(smem + L::YT);
   T* sUT = reinterpret_cast<T*>(smem + L::UT);
+  // the chunk tile in use (buffer ch & 1 with two buffers)
+  T *sQG, *sKG, *sKDT, *sAQ, *sTB, *sV;
+  float *sDQ, *sGM;
+  auto use_buf = [&](int b) {
+    unsigned char* t = smem + L::T0 + (size_t)b * L::TILE;
+    sQG = reinterpret_cast<T*>(t + L::QG);
+    sKG = reinterpret_cast<T*>(t + L::KG);
+    sKDT = reinterpret_cast<T*>(t + L::KDT);
+    sAQ = reinterpret_cast<T*>(t + L::AQ);
+    sTB = reinterpret_cast<T*>(t + L::TB);
+    sDQ = reinterpret_cast<float*>(t + L::DQ);
+    sGM = reinterpret_cast<float*>(t + L::GM);
+    sV = reinterpret_cast<T*>(t + L::VR);
+  };
+  use_buf(0);
 
   const int ntile = DV / BV;
   const int bid = blockIdx.x;
@@ -1249,8 +1263,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
   const int l = lane_id(), lr = l & 15, lg = l >> 4;
 
   // zero once: the padded token columns (C .. CK) of the token-contiguous operands stay zero
-  for (int i = tid; i < int((L::VR - L::KDT) / 2); i += NT) sKDT[i] = (T)0.f;
-  for (int i = tid; i < int((L::TOTAL - L::YT) / 2); i += NT) sYT[i] = (T)0.f;
+  for (int i = tid; i < int((L::TOTAL - L::T0) / 2); i += NT) reinterpret_cast<T*>(smem + L::T0)[i] = (T)0.f;
 
   constexpr int S_SLOTS = (NA * NJ + NW - 1) / NW;
   f32x4 Sacc[S_SLOTS];
@@ -1304,17 +1317,24 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
   uint4 pf[PF], pv;
   const bool v_act = C * VPR >= NT || tid < C * VPR;
   const int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
-  auto load_tiles = [&](int64_t chn) {
+  // loads of units [p0, p1) of the tile of chunk chn (and of its value rows with the last
+  // group): the tile goes out in three groups, one per stage, so the device's requests
+  // do not all leave right after one barrier
+  auto load_tiles = [&](int64_t chn, int p0, int p1) {
     const bool ok = chn < nchunks;
     const int64_t slot = t_begin / C + n + chn;
     const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * NU, ok ? (uint32_t)NU * 16u : 0u);
 #pragma unroll
-    for (int p = 0; p < PF; ++p) pf[p] = buf_load16(rs, (uint32_t)(tid + p * NT) * 16u);
-    const int Lc = ok ? chunk_len(chn) : 0;
-    const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + j0,
-                              Lc > 0 ? (uint32_t)Lc * (uint32_t)(H * DV * 2) : 0u);
-    pv = buf_load16(rv, (uint32_t)(v_row * H * DV + v_c0) * 2u);
+    for (int p = 0; p < PF; ++p)
+      if (p >= p0 && p < p1) pf[p] = buf_load16(rs, (uint32_t)(tid + p * NT) * 16u);
+    if (p1 == PF) {
+      const int Lc = ok ? chunk_len(chn) : 0;
+      const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + j0,
+                                Lc > 0 ? (uint32_t)Lc * (uint32_t)(H * DV * 2) : 0u);
+      pv = buf_load16(rv, (uint32_t)(v_row * H * DV + v_c0) * 2u);
+    }
   };
+  constexpr int PG1 = PF / 3, PG2 = 2 * PF / 3;
   auto store_tiles = [&]() {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
@@ -1345,21 +1365,35 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
       store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
       store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
     }
+    // every loaded register is used on every path (see retire), so no load is still
+    // pending where the next chunk reuses its registers
+#pragma unroll
+    for (int p = 0; p < PF; ++p) retire(pf[p]);
+    retire(pv);
   };
 
   __syncthreads();  // zero fill before the first tile
   write_ST();
   if (nchunks > 0) {
-    load_tiles(0);
+    load_tiles(0, 0, PF);
     store_tiles();
   }
+  if constexpr (DB) load_tiles(1, 0, PF);  // chunk 1's tile waits in registers
   __syncthreads();
 
   f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
     const int Lc = chunk_len(ch);
-    load_tiles(ch + 1);
+    // the tile loaded next: chunk ch+2 with two buffers (chunk ch+1 goes from registers to the
+    // other buffer now), else chunk ch+1 (to LDS after this chunk's last read)
+    const int64_t chl = DB ? ch + 2 : ch + 1;
+    if constexpr (DB) {
+      use_buf((int)((ch + 1) & 1));
+      store_tiles();
+      use_buf((int)(ch & 1));
+    }
+    load_tiles(chl, 0, PG1);
 
     // Y = V - Kg S (to Y^T) and O = Qg S
 #pragma unroll
@@ -1380,6 +1414,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
     }
     __syncthreads();
 
+    load_tiles(chl, PG1, PG2);
     // U = (T Diag beta) Y (to U^T)
     static_for<0, U_SLOTS>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
@@ -1397,6 +1432,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
     });
     __syncthreads();
 
+    load_tiles(chl, PG2, PF);
     // O += M U + diag(q.k) U, stored; S <- Diag(gamma) S + Kd^T U
     static_for<0, U_SLOTS>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
@@ -1426,10 +1462,15 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
         mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
       }
     }
-    __syncthreads();  // every read of this chunk's tile and of S^T is done
-    write_ST();
-    store_tiles();
-    __syncthreads();
+    if constexpr (DB) {
+      write_ST();
+      __syncthreads();
+    } else {
+      __syncthreads();  // every read of this chunk's tile and of S^T is done
+      write_ST();
+      store_tiles();
+      __syncthreads();
+    }
   }
   if (hT) store_state(hT + (size_t)chain * DK * DV);
 }
