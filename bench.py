@@ -9,7 +9,8 @@ tokens is timed and reported under "checkpointed".  In the same run the decode/r
 (256 sequences x 32 heads, fp32 state, 1 and 8 tokens) and the replay + verify
 variant (8 tokens, per-sequence commit counts) are timed and reported under
 "decode" (HBM GB/s against the 8 TB/s peak); one chunked pass over a single
-1M-token sequence x 32 heads is timed and reported under "long_context"; and the
+1M-token sequence x 32 heads is timed, fused and split (kda_chunk_fwd_split), and
+reported under "long_context"; and the
 fp64 CPU oracle is timed on a bounded sample of the chunk workload ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-long-context] [--copy-calibration]
@@ -253,15 +254,28 @@ def main():
             kda.chunk_fwd(l_inp["q"], l_inp["k"], l_inp["v"], l_inp["log_alpha"], l_inp["beta"], h0=None,
                           chunk_size=lw.chunk_size, o=l_o, hT=l_hT)
 
-        l_ms = time_launches(lstep, 3, 1, stream)
-        l_tok = lw.total_tokens / (l_ms * 1e-3)
+        l_ws = None
+
+        def lstep_split():
+            kda.chunk_fwd_split(l_inp["q"], l_inp["k"], l_inp["v"], l_inp["log_alpha"], l_inp["beta"], h0=None,
+                                chunk_size=lw.chunk_size, o=l_o, hT=l_hT, workspace=l_ws)
+
         l_bytes = lw.total_tokens * lw.n_heads * BYTES_PER_TOKEN_HEAD + lw.n_heads * lw.dk * lw.dv * 4
-        long_context = {"workload": lw.name, "tokens": lw.total_tokens, "heads": lw.n_heads, "ms_per_step": round(l_ms, 3),
-                        "tokens_per_s": round(l_tok, 1),
-                        "algorithmic_GB/s": round(l_bytes / (l_ms * 1e-3) / 1e9, 1)}
-        log("long context (%d tokens x %d heads): %.2f ms/launch, %.2f M tokens/s"
-            % (lw.total_tokens, lw.n_heads, l_ms, l_tok / 1e6))
-        del l_inp, l_o, l_hT
+        long_context = {"workload": lw.name, "tokens": lw.total_tokens, "heads": lw.n_heads}
+        for leg, fn in (("fused", lstep), ("split", lstep_split)):
+            if leg == "split":
+                l_ws = torch.empty(kda.chunk_fwd_split_workspace_bytes(lw.n_seqs, lw.total_tokens, lw.n_heads, lw.dk,
+                                                                       lw.dv, lw.chunk_size),
+                                   dtype=torch.uint8, device=dev)
+            l_ms = time_launches(fn, 3, 1, stream)
+            l_tok = lw.total_tokens / (l_ms * 1e-3)
+            long_context[leg] = {"ms_per_step": round(l_ms, 3), "tokens_per_s": round(l_tok, 1),
+                                 "algorithmic_GB/s": round(l_bytes / (l_ms * 1e-3) / 1e9, 1)}
+            log("long context, %s (%d tokens x %d heads): %.2f ms/launch, %.2f M tokens/s"
+                % (leg, lw.total_tokens, lw.n_heads, l_ms, l_tok / 1e6))
+        if l_ws is not None:
+            long_context["split"]["workspace_bytes"] = l_ws.numel()
+        del l_inp, l_o, l_hT, l_ws
 
     result = {
         "metric": METRIC,

@@ -24,7 +24,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "chunk_fwd_split", "recurrent_step", "recurrent_verify", "KDAError"]
+__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "chunk_fwd_split", "chunk_fwd_split_workspace_bytes",
+           "recurrent_step", "recurrent_verify", "KDAError"]
 
 
 class KDAError(RuntimeError):
@@ -89,6 +90,17 @@ def chunk_fwd_split(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_si
     o, hT, _ = _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, 0, None,
                       split=True, workspace=workspace)
     return o, hT
+
+
+def chunk_fwd_split_workspace_bytes(n_seqs: int, total_tokens: int, n_heads: int, dk: int, dv: int,
+                                    chunk_size: int = 64) -> int:
+    """Bytes of workspace `chunk_fwd_split` needs for bf16 inputs of these sizes."""
+    need = ctypes.c_size_t(0)
+    rc = _lib.load().kda_chunk_fwd_split_workspace_size(int(n_seqs), int(total_tokens), int(n_heads), int(dk),
+                                                        int(dv), int(chunk_size), _lib.KDA_DTYPE_BF16,
+                                                        ctypes.byref(need))
+    _check(rc, "kda_chunk_fwd_split_workspace_size")
+    return int(need.value)
 
 
 def chunk_fwd_checkpointed(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: int = 64,
