@@ -7,7 +7,9 @@ HIP library never does, and this package never imports the HIP path.
 
 Pins: the oracle is checked against closed forms, exact rational arithmetic,
 finite-difference gradients and brute-force dense unrolling in
-``tests/test_oracle_*.py``; no function here is "parity unpinned".
+``tests/test_oracle_*.py``; the backward (`kda_bwd`) against central finite
+differences of the pinned forward and the chain rule across a sequence split;
+no function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -47,6 +49,10 @@ def _load():
             lib.kda_oracle_fwd.argtypes = [ctypes.c_void_p] * 7 + [
                 ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+            lib.kda_oracle_bwd.restype = ctypes.c_int
+            lib.kda_oracle_bwd.argtypes = [ctypes.c_void_p] * 7 + [
+                ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 8 + [
+                ctypes.c_int]
             lib.kda_oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -135,3 +141,34 @@ def kda_recurrent_verify(q, k, v, log_alpha, beta, S, n_commit, n_threads: int =
     take = lambda x: np.concatenate([x[i, :c[i]] for i in range(N)], axis=0)
     _, S_new = kda_fwd(take(q), take(k), take(v), take(la), take(be), S, cu, n_threads)
     return o, S_new
+
+
+def kda_bwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, do=None, dhT=None, n_threads: int = 0):
+    """Oracle backward (reverse mode of `kda_fwd`, written out in ``kda_oracle.c``).
+
+    Gradients of  sum_t o_t . do_t + sum hT . dhT  with respect to q, k, v, log_alpha, beta and h0.
+    Shapes as `kda_fwd`; do: [T, H, dv]; dhT: [N, H, dk, dv] or None (zeros).
+    Returns a dict of float64 arrays: dq, dk, dlog_alpha [T, H, dk]; dv [T, H, dv]; dbeta [T, H];
+    dh0 [N, H, dk, dv].
+    """
+    q, k, v, la, be, h0, do, dhT = (_f32(x) for x in (q, k, v, log_alpha, beta, h0, do, dhT))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert do is not None and do.shape == (T, H, dv)
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        if hasattr(cu_seqlens, "detach"):
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    N = len(cu) - 1
+    if dhT is not None:
+        assert dhT.shape == (N, H, dk, dv)
+    out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)),
+               dlog_alpha=np.zeros((T, H, dk)), dbeta=np.zeros((T, H)), dh0=np.zeros((N, H, dk, dv)))
+    rc = _load().kda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(h0), _ptr(cu), N, T, H, dk, dv,
+                                _ptr(do), _ptr(dhT), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), int(n_threads))
+    if rc != 0:
+        raise ValueError("kda oracle (backward) rejected its arguments (rc=%d)" % rc)
+    return out

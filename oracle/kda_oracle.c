@@ -151,3 +151,148 @@ int kda_oracle_max_threads(void) {
   return 1;
 #endif
 }
+
+/*
+ * Reverse mode of the same recurrence (the backward pass), plain and slow: for every
+ * (sequence, head) the forward states S_0 = h0, S_1 .. S_L are kept, then the adjoint
+ * dS runs backwards from dS_L = dhT.  Token t (with P = Diag(alpha_t) S_{t-1},
+ * u = P^T k_t, delta = beta_t (v_t - u), S_t = P + k_t delta^T, o_t = S_t^T q_t) gives:
+ *   dS      += q_t do_t^T                      (read-out)
+ *   dq_t     = S_t do_t
+ *   ddelta   = dS^T k_t                        (S_t = P + k delta^T)
+ *   dk_t     = dS delta
+ *   dv_t     = beta_t ddelta,   dbeta_t = ddelta . (v_t - u),   du = -beta_t ddelta
+ *   dP       = dS + k_t du^T,   dk_t    += P du                  (u = P^T k)
+ *   dlog_alpha_t[c] = sum_j dP[c][j] P[c][j]                     (P = Diag(e^{log alpha}) S_{t-1})
+ *   dS       = Diag(alpha_t) dP                 (adjoint of S_{t-1})
+ * and dh0 = dS after the first token.  The loss these are gradients of is
+ * sum_t o_t . do_t + sum hT . dhT.
+ *
+ * do_: [T, H, dv] fp32; dhT: [N, H, dk, dv] fp32 or NULL (zeros).  Outputs fp64: dq, dk_out,
+ * dla [T, H, dk]; dv_out [T, H, dv]; dbeta [T, H]; dh0 [N, H, dk, dv] or NULL.
+ * Memory: (longest sequence + 1) * dk * dv doubles per thread.  Returns 0, or -1.
+ */
+int kda_oracle_bwd(const float *q, const float *k, const float *v, const float *log_alpha,
+                   const float *beta, const float *h0, const int64_t *cu_seqlens, int n_seqs,
+                   int64_t total_tokens, int n_heads, int dk, int dv, const float *do_,
+                   const float *dhT, double *dq, double *dk_out, double *dv_out, double *dla,
+                   double *dbeta, double *dh0, int n_threads) {
+  if (!q || !k || !v || !log_alpha || !beta || !cu_seqlens || !do_ || !dq || !dk_out || !dv_out || !dla ||
+      !dbeta)
+    return -1;
+  if (n_seqs < 0 || n_heads <= 0 || dk <= 0 || dv <= 0 || total_tokens < 0) return -1;
+  if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] != total_tokens) return -1;
+  int64_t maxlen = 0;
+  for (int n = 0; n < n_seqs; ++n) {
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    if (cu_seqlens[n + 1] - cu_seqlens[n] > maxlen) maxlen = cu_seqlens[n + 1] - cu_seqlens[n];
+  }
+  int nt = 1;
+#ifdef _OPENMP
+  nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+#endif
+  const int64_t pairs = (int64_t)n_seqs * n_heads;
+  const size_t DD = (size_t)dk * dv;
+  int err = 0;
+
+#pragma omp parallel num_threads(nt)
+  {
+    double *St = (double *)malloc(sizeof(double) * DD * (size_t)(maxlen + 1));
+    double *dS = (double *)malloc(sizeof(double) * DD);
+    double *P = (double *)malloc(sizeof(double) * DD);
+    double *a = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *dl = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *dd = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *du = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!St || !dS || !P || !a || !u || !dl || !dd || !du) {
+#pragma omp atomic write
+      err = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t pair = 0; pair < pairs; ++pair) {
+        const int n = (int)(pair / n_heads), h = (int)(pair % n_heads);
+        const int64_t t0 = cu_seqlens[n], L = cu_seqlens[n + 1] - cu_seqlens[n];
+        const float *h0p = h0 ? h0 + ((size_t)n * n_heads + h) * DD : NULL;
+        for (size_t i = 0; i < DD; ++i) St[i] = h0p ? (double)h0p[i] : 0.0;
+        /* forward, keeping every state */
+        for (int64_t s = 0; s < L; ++s) {
+          const int64_t t = t0 + s;
+          const float *kt = k + ((size_t)t * n_heads + h) * dk;
+          const float *vt = v + ((size_t)t * n_heads + h) * dv;
+          const float *lat = log_alpha + ((size_t)t * n_heads + h) * dk;
+          const double bt = (double)beta[(size_t)t * n_heads + h];
+          const double *Sp = St + (size_t)s * DD;
+          double *Sn = St + (size_t)(s + 1) * DD;
+          for (int c = 0; c < dk; ++c) {
+            const double ac = exp((double)lat[c]);
+            for (int j = 0; j < dv; ++j) P[(size_t)c * dv + j] = ac * Sp[(size_t)c * dv + j];
+          }
+          for (int j = 0; j < dv; ++j) u[j] = 0.0;
+          for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) u[j] += (double)kt[c] * P[(size_t)c * dv + j];
+          for (int j = 0; j < dv; ++j) dl[j] = bt * ((double)vt[j] - u[j]); /* delta */
+          for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) Sn[(size_t)c * dv + j] = P[(size_t)c * dv + j] + (double)kt[c] * dl[j];
+        }
+        /* backward */
+        const float *dhTp = dhT ? dhT + ((size_t)n * n_heads + h) * DD : NULL;
+        for (size_t i = 0; i < DD; ++i) dS[i] = dhTp ? (double)dhTp[i] : 0.0;
+        for (int64_t s = L - 1; s >= 0; --s) {
+          const int64_t t = t0 + s;
+          const size_t ik = ((size_t)t * n_heads + h) * dk, iv = ((size_t)t * n_heads + h) * dv;
+          const float *qt = q + ik, *kt = k + ik, *lat = log_alpha + ik, *vt = v + iv, *dot = do_ + iv;
+          const double bt = (double)beta[(size_t)t * n_heads + h];
+          const double *Sp = St + (size_t)s * DD, *Sn = St + (size_t)(s + 1) * DD;
+          for (int c = 0; c < dk; ++c) {
+            a[c] = exp((double)lat[c]);
+            for (int j = 0; j < dv; ++j) P[(size_t)c * dv + j] = a[c] * Sp[(size_t)c * dv + j];
+          }
+          for (int j = 0; j < dv; ++j) u[j] = 0.0;
+          for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) u[j] += (double)kt[c] * P[(size_t)c * dv + j];
+          for (int j = 0; j < dv; ++j) dl[j] = bt * ((double)vt[j] - u[j]); /* delta */
+          /* read-out */
+          for (int c = 0; c < dk; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+              dS[(size_t)c * dv + j] += (double)qt[c] * (double)dot[j];
+              acc += Sn[(size_t)c * dv + j] * (double)dot[j];
+            }
+            dq[ik + c] = acc;
+          }
+          /* write: S_t = P + k delta^T */
+          for (int j = 0; j < dv; ++j) dd[j] = 0.0;
+          for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) dd[j] += dS[(size_t)c * dv + j] * (double)kt[c];
+          double db = 0.0;
+          for (int j = 0; j < dv; ++j) {
+            dv_out[iv + j] = bt * dd[j];
+            db += dd[j] * ((double)vt[j] - u[j]);
+            du[j] = -bt * dd[j];
+          }
+          dbeta[(size_t)t * n_heads + h] = db;
+          for (int c = 0; c < dk; ++c) {
+            double g = 0.0, gP = 0.0, gl = 0.0;
+            for (int j = 0; j < dv; ++j) {
+              const double dSc = dS[(size_t)c * dv + j];
+              g += dSc * dl[j];
+              gP += P[(size_t)c * dv + j] * du[j];
+              const double dP = dSc + (double)kt[c] * du[j];
+              gl += dP * P[(size_t)c * dv + j];
+              dS[(size_t)c * dv + j] = a[c] * dP; /* adjoint of S_{t-1} */
+            }
+            dk_out[ik + c] = g + gP;
+            dla[ik + c] = gl;
+          }
+        }
+        if (dh0) {
+          double *d0 = dh0 + ((size_t)n * n_heads + h) * DD;
+          for (size_t i = 0; i < DD; ++i) d0[i] = dS[i];
+        }
+      }
+    }
+    free(St); free(dS); free(P); free(a); free(u); free(dl); free(dd); free(du);
+  }
+  return err ? -1 : 0;
+}
