@@ -165,6 +165,49 @@ kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_toke
                                               int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, size_t* bytes);
 
 /*
+ * kda_bwd - backward pass of the recurrence (reverse mode).
+ *
+ * Training needs the gradients of KDA beyond the published inference forward
+ * ("Kimi K3 NPU Training", conclusions, item 1, and the NPU operator-support
+ * table, KDA backward row).  For the same inputs as kda_chunk_fwd and the
+ * cotangents `dout` of o and `dhT` of the final states, writes the gradients of
+ *     sum_t o_t . dout_t + sum_n hT_n . dhT_n
+ * with respect to q, k, v, log_alpha, beta and h0.  The forward states are
+ * recomputed (fp32, token by token): the kernel keeps the state at the start of
+ * every 64-token segment in `workspace` and the per-token states of one segment
+ * per (sequence, head).
+ *
+ *   q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads,
+ *   dk, dv, qkv_dtype    as kda_chunk_fwd (no chunk size: the pass is token-serial)
+ *   dout        device fp32 [total_tokens, n_heads, dv]
+ *   dhT         device fp32 [n_seqs, n_heads, dk, dv] or NULL (zeros)
+ *   dq, dk_out, dlog_alpha   device fp32 [total_tokens, n_heads, dk]
+ *   dv_out      device fp32 [total_tokens, n_heads, dv]
+ *   dbeta       device fp32 [total_tokens, n_heads]
+ *   dh0         device fp32 [n_seqs, n_heads, dk, dv] or NULL (not written)
+ *   workspace   device scratch of at least kda_bwd_workspace_size bytes; contents
+ *               undefined before and after the call
+ *
+ * Outputs and the workspace must not overlap any input or each other.  All
+ * pointers 16-byte aligned.  Supported: dk, dv in {64, 128}; qkv_dtype F32 or
+ * BF16.  Errors as kda_chunk_fwd, plus KDA_ERR_INVALID_ARGUMENT for a missing,
+ * small or overlapping workspace or overlapping outputs.
+ */
+kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                   const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t n_heads,
+                   int32_t dk, int32_t dv, kda_dtype qkv_dtype, const float* dout, const float* dhT, float* dq,
+                   float* dk_out, float* dv_out, float* dlog_alpha, float* dbeta, float* dh0, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * kda_bwd_workspace_size - bytes of workspace kda_bwd needs:
+ * (total_tokens / 64 + n_seqs + 1 + 64 * n_seqs) * n_heads * dk * dv * 4.
+ * Errors: KDA_ERR_INVALID_ARGUMENT (NULL bytes, bad sizes), KDA_ERR_UNSUPPORTED (dk, dv).
+ */
+kda_status kda_bwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv,
+                                  size_t* bytes);
+
+/*
  * kda_recurrent_step - decode / draft-replay state update.
  *
  * For each of n_seqs sequences, applies n_tokens consecutive tokens to the

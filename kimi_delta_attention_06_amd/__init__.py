@@ -25,7 +25,7 @@ import torch
 from . import _lib
 
 __all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "chunk_fwd_split", "chunk_fwd_split_workspace_bytes",
-           "recurrent_step", "recurrent_verify", "KDAError"]
+           "backward", "backward_workspace_bytes", "recurrent_step", "recurrent_verify", "KDAError"]
 
 
 class KDAError(RuntimeError):
@@ -195,6 +195,78 @@ def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_st
     if batched:
         o = o.view(B, T, H, dv)
     return o, hT, ckpt
+
+
+def backward(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=None,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients of sum(o * do) + sum(hT * dhT) for the forward of `chunk_fwd` on the same inputs.
+
+    q, k, v, log_alpha, beta, h0, cu_seqlens as `chunk_fwd` (packed [T, H, d] or batched [B, T, H, d]);
+    do like o; dhT like hT (None: zeros).  `workspace` (uint8, at least `backward_workspace_bytes`) is
+    allocated when not given.  Returns a dict: dq, dk, dv, dlog_alpha (shapes of their inputs), dbeta,
+    dh0 [N, H, dk, dv].
+    """
+    lib = _lib.load()
+    batched = q.dim() == 4
+    if batched:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens requires packed [T, H, d] inputs")
+        B, Tb = q.shape[0], q.shape[1]
+        flat = lambda x: x.reshape(B * Tb, *x.shape[2:]) if x is not None else None
+        q, k, v, log_alpha, beta, do = (flat(x) for x in (q, k, v, log_alpha, beta, do))
+        n_seqs = B
+    dev = q.device
+    q, k, v = _dev(q, "q", device=dev), _dev(k, "k", device=dev), _dev(v, "v", device=dev)
+    code = _dtype_code(q, k, v)
+    log_alpha = _dev(log_alpha, "log_alpha", torch.float32, dev)
+    beta = _dev(beta, "beta", torch.float32, dev)
+    do = _dev(do, "do", torch.float32, dev)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [T, H, dk] and v [T, H, dv]")
+    T_total, H, dk = q.shape
+    dv = v.shape[2]
+    if log_alpha.shape != q.shape or beta.shape != (T_total, H) or do.shape != v.shape:
+        raise ValueError("expected log_alpha [T, H, dk], beta [T, H] and do [T, H, dv]")
+    if cu_seqlens is not None:
+        cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        n_seqs = cu_seqlens.numel() - 1
+    elif not batched:
+        n_seqs = 1 if T_total > 0 else 0
+    h0 = _dev(h0, "h0", torch.float32, dev)
+    dhT = _dev(dhT, "dhT", torch.float32, dev)
+    for name, x in (("h0", h0), ("dhT", dhT)):
+        if x is not None and tuple(x.shape) != (n_seqs, H, dk, dv):
+            raise ValueError("%s must be [N, H, dk, dv] = %s" % (name, (n_seqs, H, dk, dv)))
+    out = dict(dq=torch.empty(T_total, H, dk, dtype=torch.float32, device=dev),
+               dk=torch.empty(T_total, H, dk, dtype=torch.float32, device=dev),
+               dv=torch.empty(T_total, H, dv, dtype=torch.float32, device=dev),
+               dlog_alpha=torch.empty(T_total, H, dk, dtype=torch.float32, device=dev),
+               dbeta=torch.empty(T_total, H, dtype=torch.float32, device=dev),
+               dh0=torch.empty(n_seqs, H, dk, dv, dtype=torch.float32, device=dev))
+    need = backward_workspace_bytes(n_seqs, T_total, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        workspace = _dev(workspace, "workspace", torch.uint8, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), n_seqs,
+                     T_total, H, dk, dv, code, _ptr(do), _ptr(dhT), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                     _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
+                     workspace.numel(), stream)
+    _check(rc, "kda_bwd")
+    if batched:
+        for key in ("dq", "dk", "dv", "dlog_alpha", "dbeta"):
+            out[key] = out[key].view(B, Tb, *out[key].shape[1:])
+    return out
+
+
+def backward_workspace_bytes(n_seqs: int, total_tokens: int, n_heads: int, dk: int, dv: int) -> int:
+    """Bytes of workspace `backward` needs."""
+    need = ctypes.c_size_t(0)
+    rc = _lib.load().kda_bwd_workspace_size(int(n_seqs), int(total_tokens), int(n_heads), int(dk), int(dv),
+                                            ctypes.byref(need))
+    _check(rc, "kda_bwd_workspace_size")
+    return int(need.value)
 
 
 def _recurrent(fn_name, q, k, v, log_alpha, beta, S, n_commit, o):

@@ -154,6 +154,71 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
                       qkv_dtype, o, hT, ckpt_every, ckpt, false, nullptr, 0, stream);
 }
 
+kda_status kda_bwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv,
+                                  size_t* bytes) {
+  if (!bytes || n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (!dims_ok(dk) || !dims_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  *bytes = kda::bwd_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv);
+  return KDA_OK;
+}
+
+kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                   const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t n_heads,
+                   int32_t dk, int32_t dv, kda_dtype qkv_dtype, const float* dout, const float* dhT, float* dq,
+                   float* dk_out, float* dv_out, float* dlog_alpha, float* dbeta, float* dh0, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (qkv_dtype != KDA_DTYPE_F32 && qkv_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (n_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (total_tokens > 0 &&
+      (!q || !k || !v || !log_alpha || !beta || !dout || !dq || !dk_out || !dv_out || !dlog_alpha || !dbeta))
+    return KDA_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, h0, cu_seqlens, dout, dhT, dq, dk_out, dv_out, dlog_alpha,
+                        dbeta, dh0, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_INVALID_ARGUMENT;
+  int64_t seq_len = 0;
+  if (!cu_seqlens && n_seqs > 0) {
+    if (total_tokens % n_seqs != 0) return KDA_ERR_INVALID_ARGUMENT;
+    seq_len = total_tokens / n_seqs;
+  }
+  if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)n_seqs * n_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (!dims_ok(dk) || !dims_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return KDA_OK;
+  const size_t need = kda::bwd_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARGUMENT;
+  // every output (and the workspace) must not overlap any input or any other output
+  const size_t esz = qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+  const size_t T = (size_t)total_tokens, Hh = (size_t)n_heads, st = (size_t)n_seqs * n_heads * dk * dv * 4;
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{q, T * Hh * dk * esz}, {k, T * Hh * dk * esz}, {v, T * Hh * dv * esz},
+                   {log_alpha, T * Hh * dk * 4}, {beta, T * Hh * 4}, {h0, h0 ? st : 0},
+                   {cu_seqlens, cu_seqlens ? (size_t)(n_seqs + 1) * 4 : 0}, {dout, T * Hh * dv * 4},
+                   {dhT, dhT ? st : 0}};
+  const R outs[] = {{dq, T * Hh * dk * 4}, {dk_out, T * Hh * dk * 4}, {dv_out, T * Hh * dv * 4},
+                    {dlog_alpha, T * Hh * dk * 4}, {dbeta, T * Hh * 4}, {dh0, dh0 ? st : 0},
+                    {workspace, need}};
+  auto overlap = [](const R& a, const R& b) {
+    const char* pa = (const char*)a.p;
+    const char* pb = (const char*)b.p;
+    return a.n && b.n && pa < pb + b.n && pb < pa + a.n;
+  };
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const R& r : ins)
+      if (overlap(outs[i], r)) return KDA_ERR_INVALID_ARGUMENT;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j])) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  kda::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0; a.cu_seqlens = cu_seqlens;
+  a.dout = dout; a.dhT = dhT; a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dlog_alpha = dlog_alpha;
+  a.dbeta = dbeta; a.dh0 = dh0; a.ws = workspace; a.n_seqs = n_seqs; a.n_heads = n_heads; a.dk_dim = dk;
+  a.dv_dim = dv; a.total_tokens = total_tokens; a.seq_len = seq_len; a.bf16 = qkv_dtype == KDA_DTYPE_BF16;
+  a.stream = stream;
+  return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 static kda_status recurrent_common(const void* q, const void* k, const void* v, const float* log_alpha,
                                    const float* beta, float* S_inout, const int32_t* n_commit, bool need_commit,
                                    int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv,

@@ -26,4 +26,20 @@ __device__ __forceinline__ T wave_xor(T x, int mask) {
   return __shfl_xor(x, mask, kWave);
 }
 
+// sum over the 16 lanes of each DPP row, returned to every lane of the row
+template <int N>
+__device__ __forceinline__ float row_shr_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 | N, 0xf,
+                                                                       0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x = row_shr_add<1>(x);
+  x = row_shr_add<2>(x);
+  x = row_shr_add<4>(x);
+  x = row_shr_add<8>(x);
+  // lane 15 of the row now holds the total: DPP row_newbcast:15
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x15f, 0xf, 0xf,
+                                                                false));
+}
+
 }  // namespace kda

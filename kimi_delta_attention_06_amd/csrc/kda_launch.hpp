@@ -39,7 +39,34 @@ struct ChunkArgs {
   void* stream;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const float* beta;
+  const float* h0;           // may be null
+  const int32_t* cu_seqlens; // may be null (equal lengths)
+  const float* dout;         // cotangent of o
+  const float* dhT;          // cotangent of hT, may be null
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dlog_alpha;
+  float* dbeta;
+  float* dh0;                // may be null
+  void* ws;                  // bwd_workspace_bytes(...) bytes
+  int n_seqs, n_heads, dk_dim, dv_dim;
+  int64_t total_tokens;
+  int64_t seq_len;
+  bool bf16;
+  void* stream;
+};
+
 hipError_t launch_recurrent_step(const RecurrentArgs& a);
+// Backward pass (token-recurrent, fp32 state and gradients).
+hipError_t launch_bwd(const BwdArgs& a);
+size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 // Split path (bf16 only): intra-chunk pass into `ws`, then the state pass.
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws);
