@@ -201,7 +201,8 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log
 
 /*
  * kda_bwd_workspace_size - bytes of workspace kda_bwd needs:
- * (total_tokens / 64 + n_seqs + 1 + 64 * n_seqs) * n_heads * dk * dv * 4.
+ * (total_tokens / 64 + n_seqs + 1 + 64 * n_seqs) * n_heads * dk * dv * 4 (states)
+ * + (3 * dk + 1) * total_tokens * n_heads * 4 rounded up to 16 (partial gradients).
  * Errors: KDA_ERR_INVALID_ARGUMENT (NULL bytes, bad sizes), KDA_ERR_UNSUPPORTED (dk, dv).
  */
 kda_status kda_bwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv,

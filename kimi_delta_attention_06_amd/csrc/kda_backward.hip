@@ -15,9 +15,12 @@
 // training needs beyond the published inference forward ("Kimi K3 NPU Training",
 // conclusions, item 1, and the NPU operator-support table, KDA backward row).
 //
-// One workgroup per (sequence, head), DV/16 waves, with the decode kernel's thread map:
-// lane l of wave w holds rows rg = l & 15, rg + 16, ... and value columns
-// [16 w + 4 (l >> 4), +4).  Column reductions (over rows: u, dd) stay in the wave
+// Two workgroups per (sequence, head), each owning half of the value columns (the
+// columns of S evolve independently), DV/32 waves each, with the decode kernel's thread
+// map: lane l of wave w holds rows rg = l & 15, rg + 16, ... and value columns
+// [j0 + 16 w + 4 (l >> 4), +4).  The row gradients of the second half go to the
+// workspace and are added to the first half's by a small kernel (a two-term sum, so the
+// result does not depend on which half finishes first).  Column reductions (over rows: u, dd) stay in the wave
 // (in-lane, then a DPP row sum); row reductions (over columns: dq, dk, dlog a, db) are
 // summed across the wave's four column groups with lane shuffles and across waves
 // through LDS once per batch of kB tokens.
@@ -27,33 +30,49 @@
 // segments backwards, recomputes the segment's per-token states into a per-chain
 // scratch (`tok`), then runs the adjoint over the segment.  Every thread reads back only
 // the state entries it wrote itself.
+#include <atomic>
+
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
-constexpr int kBwdB = 4;    // tokens per staged batch
+constexpr int kBwdB = 8;    // tokens per staged batch
 constexpr int kBwdL = 64;   // tokens per recomputed segment (a multiple of kBwdB)
 
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(DV * 4) void bwd_kernel(
+__global__ __launch_bounds__(DV * 2) void bwd_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* __restrict__ h0,
     const int32_t* __restrict__ cu_seqlens, const float* __restrict__ dout, const float* __restrict__ dhT,
     float* __restrict__ dq, float* __restrict__ dk_out, float* __restrict__ dv_out, float* __restrict__ dla,
     float* __restrict__ dbeta, float* __restrict__ dh0, float* __restrict__ ckpt, float* __restrict__ tok,
-    int H, int64_t seq_len) {
-  constexpr int NTH = DV * 4, NWV = DV / 16, RPT = DK / 16;
+    float* __restrict__ part, int H, int64_t seq_len, int64_t total_tokens) {
+  constexpr int NTH = DV * 2, NWV = DV / 32, RPT = DK / 16;
   constexpr int B = kBwdB, L = kBwdL;
   static_assert(DV % 16 == 0 && DK % 16 == 0 && L % B == 0, "thread map");
 
-  __shared__ float s_q[B][DK], s_k[B][DK], s_a[B][DK];
-  __shared__ float s_v[B][DV], s_do[B][DV], s_b[B];
-  __shared__ float s_red[B][NWV][3][DK];  // per-wave row partials of dq, dk, dlog a
-  __shared__ float s_redb[B][NWV];        // per-wave partials of db
+  // dynamic LDS: staged token inputs, then the per-wave row partials of dq, dk, dlog a and db
+  extern __shared__ __attribute__((aligned(16))) float smem_b[];
+  float(*s_q)[DK] = reinterpret_cast<float(*)[DK]>(smem_b);
+  float(*s_k)[DK] = reinterpret_cast<float(*)[DK]>(smem_b + B * DK);
+  float(*s_a)[DK] = reinterpret_cast<float(*)[DK]>(smem_b + 2 * B * DK);
+  float(*s_v)[DV] = reinterpret_cast<float(*)[DV]>(smem_b + 3 * B * DK);
+  float(*s_do)[DV] = reinterpret_cast<float(*)[DV]>(smem_b + 3 * B * DK + B * DV);
+  float* s_b = smem_b + 3 * B * DK + 2 * B * DV;
+  float(*s_red)[NWV][3][DK] = reinterpret_cast<float(*)[NWV][3][DK]>(smem_b + 3 * B * DK + 2 * B * DV + B);
+  float(*s_redb)[NWV] = reinterpret_cast<float(*)[NWV]>(smem_b + 3 * B * DK + 2 * B * DV + B + B * NWV * 3 * DK);
 
-  const int chain = blockIdx.x;
+  const int chain = blockIdx.x >> 1, half = blockIdx.x & 1;
   const int n = chain / H, h = chain - n * H;
+  // the second half's row gradients: partial dq, dk, dlog a [3][T][H][DK] and db [T][H]
+  if (half) {
+    const size_t TH = (size_t)total_tokens * H;
+    dq = part;
+    dk_out = part + TH * DK;
+    dla = part + 2 * TH * DK;
+    dbeta = part + 3 * TH * DK;
+  }
   int64_t t_begin, t_end;
   if (cu_seqlens) {
     t_begin = cu_seqlens[n];
@@ -67,7 +86,7 @@ __global__ __launch_bounds__(DV * 4) void bwd_kernel(
 
   const int t = threadIdx.x;
   const int lane = t % kWave, wave = t / kWave;
-  const int rg = lane & 15, c0 = 16 * wave + 4 * (lane >> 4);
+  const int rg = lane & 15, c0 = half * (DV / 2) + 16 * wave + 4 * (lane >> 4);
   constexpr size_t SD = (size_t)DK * DV;
 
   // state at the start of segment s: slot t_begin / L + n + s (distinct for any packing)
@@ -92,8 +111,8 @@ __global__ __launch_bounds__(DV * 4) void bwd_kernel(
       s_a[j][c] = expf(log_alpha[off]);
       if (rev) s_q[j][c] = to_f32(q[off]);
     }
-    for (int idx = t; idx < cnt * DV; idx += NTH) {
-      const int j = idx / DV, c = idx - j * DV;
+    for (int idx = t; idx < cnt * (DV / 2); idx += NTH) {
+      const int j = idx / (DV / 2), c = half * (DV / 2) + idx - j * (DV / 2);
       const size_t off = ((size_t)(t0 + j) * H + h) * DV + c;
       s_v[j][c] = to_f32(v[off]);
       if (rev) s_do[j][c] = dout[off];
@@ -169,10 +188,18 @@ __global__ __launch_bounds__(DV * 4) void bwd_kernel(
       __syncthreads();
       stage(t0, cnt, true);
       __syncthreads();
+      float4 Sn[RPT];  // S_{t-1} of the batch's last token, loaded ahead
+      {
+        const int64_t it = t0 + cnt - 1 - sb;
+        load_state(it > 0 ? tok_base + (size_t)(it - 1) * SD : ckpt_at(s), Sn);
+      }
       for (int j = cnt - 1; j >= 0; --j) {
         const int64_t it = t0 + j - sb;  // token index inside the segment
         float4 Sp[RPT];                  // S_{t-1}; P = Diag(a_t) S_{t-1} is formed on the fly
-        load_state(it > 0 ? tok_base + (size_t)(it - 1) * SD : ckpt_at(s), Sp);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) Sp[i] = Sn[i];
+        // the next (earlier) token's S_{t-2}, in flight during this token's work
+        if (j > 0) load_state(it > 1 ? tok_base + (size_t)(it - 2) * SD : ckpt_at(s), Sn);
         float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -257,21 +284,59 @@ __global__ __launch_bounds__(DV * 4) void bwd_kernel(
   if (dh0) store_state(dh0 + (size_t)chain * SD, dS);
 }
 
+// second-half row gradients added to the first half's: x[i] += p[i]
+__global__ void bwd_add_kernel(float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dla,
+                               float* __restrict__ db, const float* __restrict__ part, int64_t nk, int64_t nb) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t j = i; j < nk; j += stride) {
+    dq[j] += part[j];
+    dk[j] += part[nk + j];
+    dla[j] += part[2 * nk + j];
+  }
+  for (int64_t j = i; j < nb; j += stride) db[j] += part[3 * nk + j];
+}
+
 size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv) {
   const size_t sd = (size_t)dk * dv * sizeof(float);
   const size_t ck = ((size_t)(total_tokens / kBwdL) + (size_t)n_seqs + 1) * (size_t)n_heads * sd;
   const size_t tk = (size_t)n_seqs * n_heads * kBwdL * sd;
-  return ck + tk;
+  const size_t th = (size_t)total_tokens * n_heads;
+  const size_t pt = (3 * th * dk + th) * sizeof(float);
+  return ck + tk + ((pt + 15) & ~size_t(15));
 }
 
 template <int DK, int DV, typename InT>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   float* ck = (float*)a.ws;
   float* tk = ck + ((size_t)(a.total_tokens / kBwdL) + (size_t)a.n_seqs + 1) * a.n_heads * DK * DV;
-  hipLaunchKernelGGL((bwd_kernel<DK, DV, InT>), dim3((unsigned)((int64_t)a.n_seqs * a.n_heads)), dim3(DV * 4), 0,
+  float* pt = tk + (size_t)a.n_seqs * a.n_heads * kBwdL * DK * DV;
+  constexpr int NWV = DV / 32;
+  constexpr size_t lds = sizeof(float) * ((size_t)3 * kBwdB * DK + 2 * kBwdB * DV + kBwdB + (size_t)kBwdB * NWV * 3 * DK +
+                                          kBwdB * NWV);
+  static std::atomic<uint64_t> attr_done{0};
+  {
+    int dev = 0;
+    hipError_t e0 = hipGetDevice(&dev);
+    if (e0 != hipSuccess) return e0;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+    if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+      e0 = hipFuncSetAttribute((const void*)bwd_kernel<DK, DV, InT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds);
+      if (e0 != hipSuccess) return e0;
+      if (bit) attr_done.fetch_or(bit, std::memory_order_release);
+    }
+  }
+  hipLaunchKernelGGL((bwd_kernel<DK, DV, InT>), dim3((unsigned)((int64_t)a.n_seqs * a.n_heads * 2)), dim3(DV * 2), lds,
                      (hipStream_t)a.stream, (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta,
-                     a.h0, a.cu_seqlens, a.dout, a.dhT, a.dq, a.dk, a.dv, a.dlog_alpha, a.dbeta, a.dh0, ck, tk,
-                     a.n_heads, a.seq_len);
+                     a.h0, a.cu_seqlens, a.dout, a.dhT, a.dq, a.dk, a.dv, a.dlog_alpha, a.dbeta, a.dh0, ck, tk, pt,
+                     a.n_heads, a.seq_len, a.total_tokens);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nk = a.total_tokens * a.n_heads * DK, nb = a.total_tokens * a.n_heads;
+  const int64_t blocks = (nk + 255) / 256 < 4096 ? (nk + 255) / 256 : 4096;
+  hipLaunchKernelGGL(bwd_add_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, (hipStream_t)a.stream,
+                     a.dq, a.dk, a.dlog_alpha, a.dbeta, (const float*)pt, nk, nb);
   return hipGetLastError();
 }
 

@@ -175,8 +175,9 @@ def bwd_call(**kw):
 def test_bwd_workspace_size():
     b = ctypes.c_size_t(0)
     assert lib.kda_bwd_workspace_size(1, 64, 2, 128, 128, ctypes.byref(b)) == 0
-    # (64 / 64 + 1 + 1) checkpoint slots + 64 token states per chain, x 2 heads x 64 KiB
-    assert b.value == (3 + 64) * 2 * 128 * 128 * 4
+    # (64 / 64 + 1 + 1) checkpoint slots + 64 token states per chain, x 2 heads x 64 KiB,
+    # + partial row gradients of the second column half: (3 * 128 + 1) x 64 tokens x 2 heads, fp32
+    assert b.value == (3 + 64) * 2 * 128 * 128 * 4 + (3 * 128 + 1) * 64 * 2 * 4
     assert lib.kda_bwd_workspace_size(1, 64, 2, 96, 128, ctypes.byref(b)) == 2
     assert lib.kda_bwd_workspace_size(1, 64, 2, 128, 128, None) == 1
 
