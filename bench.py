@@ -12,6 +12,7 @@ variant (8 tokens, per-sequence commit counts) are timed and reported under
 1M-token sequence x 32 heads is timed, fused and split (kda_chunk_fwd_split), and
 reported under "long_context"; and the
 fp64 CPU oracle is timed on a bounded sample of the chunk workload ("cpu_baseline").
+The backward pass (kda_bwd) on the Kimi-Linear layer is timed under "backward".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-long-context] [--copy-calibration]
 Prints exactly one JSON line on stdout.  --copy-calibration adds three launches of a
@@ -241,6 +242,22 @@ def main():
         % (n_writing, dw.n_seqs, v_ms, v_gbs, 100 * v_gbs / HBM_PEAK_GBS))
     del v_inp, v_o
 
+    # ---------------- backward pass on the Kimi-Linear layer ----------------
+    b_do = torch.randn(w.total_tokens, w.n_heads, w.dv, generator=torch.Generator(device=dev).manual_seed(77),
+                       device=dev)
+    b_ws = torch.empty(kda.backward_workspace_bytes(w.n_seqs, w.total_tokens, w.n_heads, w.dk, w.dv),
+                       dtype=torch.uint8, device=dev)
+
+    def bstep():
+        kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], b_do, cu_seqlens=inp["cu_seqlens"],
+                     workspace=b_ws)
+
+    b_ms = time_launches(bstep, 5, 1, stream)
+    backward = {"workload": w.name, "ms_per_step": round(b_ms, 3), "tokens_per_s": round(tokens / (b_ms * 1e-3), 1),
+                "workspace_bytes": b_ws.numel(), "kind": "token-recurrent fp32 (kda_bwd)"}
+    log("backward (kda_bwd) on %s: %.3f ms/call, %.2f M tokens/s" % (w.name, b_ms, tokens / (b_ms * 1e-3) / 1e6))
+    del b_do, b_ws
+
     # ---------------- long context: one 1M-token sequence x 32 heads (32 chains) ----------------
     long_context = None
     if not args.no_long_context:
@@ -301,6 +318,7 @@ def main():
         "checkpointed": checkpointed,
         "decode": decode,
         "long_context": long_context,
+        "backward": backward,
         "wall_s_timed_region": round(t_wall, 3),
     }
     if args.copy_calibration:
