@@ -6,6 +6,8 @@ HIP kernels.  PyTorch provides device memory and the current stream.
 
     o, hT = chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size=64)
     o, hT, ckpt = chunk_fwd_checkpointed(..., ckpt_every=512)  # + states every 512 tokens
+    o, hT = chunk_fwd_split(...)                          # two passes, for few (sequence, head) chains
+    g = backward(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=None)  # dq, dk, dv, ...
     o = recurrent_step(q, k, v, log_alpha, beta, S)      # updates S in place
     o = recurrent_verify(q, k, v, log_alpha, beta, S, n_commit)  # commits a prefix per sequence
 

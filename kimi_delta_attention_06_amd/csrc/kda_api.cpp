@@ -284,6 +284,6 @@ const char* kda_status_string(kda_status s) {
   return "KDA_ERR_UNKNOWN";
 }
 
-int32_t kda_version(void) { return 100; }
+int32_t kda_version(void) { return 110; }
 
 }  // extern "C"
