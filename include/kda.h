@@ -165,20 +165,21 @@ kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_toke
                                               int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, size_t* bytes);
 
 /*
- * kda_bwd - backward pass of the recurrence (reverse mode).
+ * kda_bwd - backward pass of the recurrence (reverse mode), chunkwise.
  *
  * Training needs the gradients of KDA beyond the published inference forward
  * ("Kimi K3 NPU Training", conclusions, item 1, and the NPU operator-support
  * table, KDA backward row).  For the same inputs as kda_chunk_fwd and the
  * cotangents `dout` of o and `dhT` of the final states, writes the gradients of
  *     sum_t o_t . dout_t + sum_n hT_n . dhT_n
- * with respect to q, k, v, log_alpha, beta and h0.  The forward states are
- * recomputed (fp32, token by token): the kernel keeps the state at the start of
- * every 64-token segment in `workspace` and the per-token states of one segment
- * per (sequence, head).
+ * with respect to q, k, v, log_alpha, beta and h0.  Reverse mode of the chunk
+ * form in 16-token chunks, every product in fp32: the forward stores the state
+ * entering every chunk in `workspace`, a reverse pass over each sequence's chunks
+ * stores the cotangent of the state leaving every chunk, and a parallel pass forms
+ * each chunk's gradients from the two.
  *
  *   q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads,
- *   dk, dv, qkv_dtype    as kda_chunk_fwd (no chunk size: the pass is token-serial)
+ *   dk, dv, qkv_dtype    as kda_chunk_fwd (the chunk size is fixed at 16)
  *   dout        device fp32 [total_tokens, n_heads, dv]
  *   dhT         device fp32 [n_seqs, n_heads, dk, dv] or NULL (zeros)
  *   dq, dk_out, dlog_alpha   device fp32 [total_tokens, n_heads, dk]
@@ -190,8 +191,11 @@ kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_toke
  *
  * Outputs and the workspace must not overlap any input or each other.  All
  * pointers 16-byte aligned.  Supported: dk, dv in {64, 128}; qkv_dtype F32 or
- * BF16.  Errors as kda_chunk_fwd, plus KDA_ERR_INVALID_ARGUMENT for a missing,
- * small or overlapping workspace or overlapping outputs.
+ * BF16.  Precondition not checked on the device: every 16-token chunk (counted
+ * from each sequence start) decays by less than 120 nats per channel
+ * (sum(log_alpha) > -120); kda_bwd_recurrent has no such bound.  Errors as
+ * kda_chunk_fwd, plus KDA_ERR_INVALID_ARGUMENT for a missing, small or
+ * overlapping workspace or overlapping outputs.
  */
 kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
                    const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t n_heads,
@@ -201,12 +205,36 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log
 
 /*
  * kda_bwd_workspace_size - bytes of workspace kda_bwd needs:
- * (total_tokens / 64 + n_seqs + 1 + 64 * n_seqs) * n_heads * dk * dv * 4 (states)
- * + (3 * dk + 1) * total_tokens * n_heads * 4 rounded up to 16 (partial gradients).
+ * (2 * (total_tokens / 16) + n_seqs + 1) * n_heads * dk * dv * 4.
  * Errors: KDA_ERR_INVALID_ARGUMENT (NULL bytes, bad sizes), KDA_ERR_UNSUPPORTED (dk, dv).
  */
 kda_status kda_bwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv,
                                   size_t* bytes);
+
+/*
+ * kda_bwd_recurrent - the same gradients as kda_bwd, token by token.
+ *
+ * Differentiates the recurrence one token at a time in fp32 (the reverse mode of
+ * the per-token update, the same passage as kda_bwd): the state at the start of
+ * every 64-token segment is kept in `workspace`, each segment's per-token states are
+ * recomputed into it, and the adjoint runs backwards over them.  No decay bound;
+ * much slower than kda_bwd on long sequences.  Arguments, outputs and errors as
+ * kda_bwd, with kda_bwd_recurrent_workspace_size bytes of workspace.
+ */
+kda_status kda_bwd_recurrent(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                             const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                             int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype, const float* dout,
+                             const float* dhT, float* dq, float* dk_out, float* dv_out, float* dlog_alpha,
+                             float* dbeta, float* dh0, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_bwd_recurrent_workspace_size - bytes of workspace kda_bwd_recurrent needs:
+ * (total_tokens / 64 + n_seqs + 1 + 64 * n_seqs) * n_heads * dk * dv * 4 (states)
+ * + (3 * dk + 1) * total_tokens * n_heads * 4 rounded up to 16 (partial gradients).
+ * Errors: KDA_ERR_INVALID_ARGUMENT (NULL bytes, bad sizes), KDA_ERR_UNSUPPORTED (dk, dv).
+ */
+kda_status kda_bwd_recurrent_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                            int32_t dv, size_t* bytes);
 
 /*
  * kda_recurrent_step - decode / draft-replay state update.

@@ -8,6 +8,7 @@ HIP kernels.  PyTorch provides device memory and the current stream.
     o, hT, ckpt = chunk_fwd_checkpointed(..., ckpt_every=512)  # + states every 512 tokens
     o, hT = chunk_fwd_split(...)                          # two passes, for few (sequence, head) chains
     g = backward(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=None)  # dq, dk, dv, ...
+    g = backward(..., method="recurrent")                # token by token, no decay bound
     o = recurrent_step(q, k, v, log_alpha, beta, S)      # updates S in place
     o = recurrent_verify(q, k, v, log_alpha, beta, S, n_commit)  # commits a prefix per sequence
 
@@ -200,14 +201,17 @@ def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_st
 
 
 def backward(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=None,
-             workspace: Optional[torch.Tensor] = None):
+             workspace: Optional[torch.Tensor] = None, method: str = "chunk"):
     """Gradients of sum(o * do) + sum(hT * dhT) for the forward of `chunk_fwd` on the same inputs.
 
     q, k, v, log_alpha, beta, h0, cu_seqlens as `chunk_fwd` (packed [T, H, d] or batched [B, T, H, d]);
     do like o; dhT like hT (None: zeros).  `workspace` (uint8, at least `backward_workspace_bytes`) is
-    allocated when not given.  Returns a dict: dq, dk, dv, dlog_alpha (shapes of their inputs), dbeta,
-    dh0 [N, H, dk, dv].
+    allocated when not given.  method "chunk" (kda_bwd, 16-token chunks on the fp32 matrix core) or
+    "recurrent" (kda_bwd_recurrent, token by token, no decay bound).  Returns a dict: dq, dk, dv,
+    dlog_alpha (shapes of their inputs), dbeta, dh0 [N, H, dk, dv].
     """
+    if method not in ("chunk", "recurrent"):
+        raise ValueError("method must be 'chunk' or 'recurrent'")
     lib = _lib.load()
     batched = q.dim() == 4
     if batched:
@@ -245,29 +249,32 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=None,
                dlog_alpha=torch.empty(T_total, H, dk, dtype=torch.float32, device=dev),
                dbeta=torch.empty(T_total, H, dtype=torch.float32, device=dev),
                dh0=torch.empty(n_seqs, H, dk, dv, dtype=torch.float32, device=dev))
-    need = backward_workspace_bytes(n_seqs, T_total, H, dk, dv)
+    need = backward_workspace_bytes(n_seqs, T_total, H, dk, dv, method)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     else:
         workspace = _dev(workspace, "workspace", torch.uint8, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), n_seqs,
-                     T_total, H, dk, dv, code, _ptr(do), _ptr(dhT), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                     _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
-                     workspace.numel(), stream)
-    _check(rc, "kda_bwd")
+    name = "kda_bwd" if method == "chunk" else "kda_bwd_recurrent"
+    rc = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+                            n_seqs, T_total, H, dk, dv, code, _ptr(do), _ptr(dhT), _ptr(out["dq"]), _ptr(out["dk"]),
+                            _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dh0"]),
+                            _ptr(workspace), workspace.numel(), stream)
+    _check(rc, name)
     if batched:
         for key in ("dq", "dk", "dv", "dlog_alpha", "dbeta"):
             out[key] = out[key].view(B, Tb, *out[key].shape[1:])
     return out
 
 
-def backward_workspace_bytes(n_seqs: int, total_tokens: int, n_heads: int, dk: int, dv: int) -> int:
-    """Bytes of workspace `backward` needs."""
+def backward_workspace_bytes(n_seqs: int, total_tokens: int, n_heads: int, dk: int, dv: int,
+                             method: str = "chunk") -> int:
+    """Bytes of workspace `backward` needs with this method."""
     need = ctypes.c_size_t(0)
-    rc = _lib.load().kda_bwd_workspace_size(int(n_seqs), int(total_tokens), int(n_heads), int(dk), int(dv),
-                                            ctypes.byref(need))
-    _check(rc, "kda_bwd_workspace_size")
+    name = "kda_bwd_workspace_size" if method == "chunk" else "kda_bwd_recurrent_workspace_size"
+    rc = getattr(_lib.load(), name)(int(n_seqs), int(total_tokens), int(n_heads), int(dk), int(dv),
+                                    ctypes.byref(need))
+    _check(rc, name)
     return int(need.value)
 
 

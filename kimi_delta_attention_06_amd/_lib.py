@@ -30,6 +30,10 @@ SIGNATURES = {
     "kda_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
                                _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "kda_bwd_workspace_size": (ctypes.c_int, [_I32, _I64, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "kda_bwd_recurrent": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
+                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "kda_bwd_recurrent_workspace_size": (ctypes.c_int, [_I32, _I64, _I32, _I32, _I32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]),
     "kda_recurrent_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                           ctypes.c_int, _P, _P]),
     "kda_recurrent_verify": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,

@@ -25,7 +25,7 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
-SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_backward.hip"]
+SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_backward.hip", "kda_backward_chunk.hip"]
 
 
 def _compile(src: str, extra) -> str:

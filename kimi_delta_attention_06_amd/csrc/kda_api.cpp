@@ -154,19 +154,35 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
                       qkv_dtype, o, hT, ckpt_every, ckpt, false, nullptr, 0, stream);
 }
 
-kda_status kda_bwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv,
-                                  size_t* bytes) {
+static size_t bwd_ws_bytes(bool chunk, int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv) {
+  return chunk ? kda::bwd_chunk_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv)
+               : kda::bwd_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv);
+}
+
+static kda_status bwd_ws_common(bool chunk, int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                int32_t dv, size_t* bytes) {
   if (!bytes || n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
   if (!dims_ok(dk) || !dims_ok(dv)) return KDA_ERR_UNSUPPORTED;
-  *bytes = kda::bwd_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv);
+  *bytes = bwd_ws_bytes(chunk, total_tokens, n_seqs, n_heads, dk, dv);
   return KDA_OK;
 }
 
-kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
-                   const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t n_heads,
-                   int32_t dk, int32_t dv, kda_dtype qkv_dtype, const float* dout, const float* dhT, float* dq,
-                   float* dk_out, float* dv_out, float* dlog_alpha, float* dbeta, float* dh0, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+kda_status kda_bwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv,
+                                  size_t* bytes) {
+  return bwd_ws_common(true, n_seqs, total_tokens, n_heads, dk, dv, bytes);
+}
+
+kda_status kda_bwd_recurrent_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                            int32_t dv, size_t* bytes) {
+  return bwd_ws_common(false, n_seqs, total_tokens, n_heads, dk, dv, bytes);
+}
+
+static kda_status bwd_common(bool chunk, const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* h0, const int32_t* cu_seqlens, int32_t n_seqs,
+                             int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype,
+                             const float* dout, const float* dhT, float* dq, float* dk_out, float* dv_out,
+                             float* dlog_alpha, float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   if (n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
   if (qkv_dtype != KDA_DTYPE_F32 && qkv_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
   if (n_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -186,7 +202,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log
   if ((int64_t)n_seqs * n_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   if (!dims_ok(dk) || !dims_ok(dv)) return KDA_ERR_UNSUPPORTED;
   if (n_seqs == 0) return KDA_OK;
-  const size_t need = kda::bwd_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv);
+  const size_t need = bwd_ws_bytes(chunk, total_tokens, n_seqs, n_heads, dk, dv);
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID_ARGUMENT;
   // every output (and the workspace) must not overlap any input or any other output
   const size_t esz = qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
@@ -216,7 +232,26 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log
   a.dbeta = dbeta; a.dh0 = dh0; a.ws = workspace; a.n_seqs = n_seqs; a.n_heads = n_heads; a.dk_dim = dk;
   a.dv_dim = dv; a.total_tokens = total_tokens; a.seq_len = seq_len; a.bf16 = qkv_dtype == KDA_DTYPE_BF16;
   a.stream = stream;
-  return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+  return (chunk ? kda::launch_bwd_chunk(a) : kda::launch_bwd(a)) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                   const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t n_heads,
+                   int32_t dk, int32_t dv, kda_dtype qkv_dtype, const float* dout, const float* dhT, float* dq,
+                   float* dk_out, float* dv_out, float* dlog_alpha, float* dbeta, float* dh0, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return bwd_common(true, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, qkv_dtype,
+                    dout, dhT, dq, dk_out, dv_out, dlog_alpha, dbeta, dh0, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_bwd_recurrent(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                             const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                             int32_t n_heads, int32_t dk, int32_t dv, kda_dtype qkv_dtype, const float* dout,
+                             const float* dhT, float* dq, float* dk_out, float* dv_out, float* dlog_alpha,
+                             float* dbeta, float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(false, q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv,
+                    qkv_dtype, dout, dhT, dq, dk_out, dv_out, dlog_alpha, dbeta, dh0, workspace, workspace_bytes,
+                    stream);
 }
 
 static kda_status recurrent_common(const void* q, const void* k, const void* v, const float* log_alpha,

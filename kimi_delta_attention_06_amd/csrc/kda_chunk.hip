@@ -577,8 +577,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   // diagonal Gram's MMA k-steps), then the value / beta part.  The parts of chunk c+1 run
   // beside chunk c's latency-bound MMA stages: part 0 with the inverse levels, the rest
   // with the U / O products.
-  constexpr int GH = (P == Prec::Mixed ? CPL >= 16 : CPL >= 8) ? 2 : 1;
+  constexpr int GH = ((P == Prec::Mixed ? CPL >= 16 : CPL >= 8) && (CPL / 2) * (int)sizeof(InT) % 16 == 0) ? 2 : 1;
   constexpr int GC = CPL / GH;
+  static_assert(GC * (int)sizeof(InT) % 16 == 0, "a gate part unpacks whole 16-byte input words");
   auto gate_part = [&](auto hc) {
     constexpr int hh = decltype(hc)::value;
     // Wave-dependent LDS offsets are cheap scalar arithmetic; an opaque copy of the
@@ -1638,6 +1639,15 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws) {
   if (a.chunk_size == 64) return dispatch_split_bv<64, 64, bf16_t>(a, ws);
   if (a.chunk_size == 32) return dispatch_split_bv<32, 64, bf16_t>(a, ws);
   return dispatch_split_bv<16, 64, bf16_t>(a, ws);
+}
+
+hipError_t launch_chunk_fwd_f32(const ChunkArgs& a) {
+  using namespace chunkk;
+  if (a.chunk_size != 16 || !chunk_fwd_supported(a.dk, a.dv, 16, false)) return hipErrorInvalidValue;
+  if (a.bf16) {
+    return a.dk == 128 ? dispatch_bv<16, 128, 64, Prec::F32, bf16_t>(a) : dispatch_bv<16, 64, 64, Prec::F32, bf16_t>(a);
+  }
+  return a.dk == 128 ? dispatch_bv<16, 128, 64, Prec::F32, float>(a) : dispatch_bv<16, 64, 64, Prec::F32, float>(a);
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {

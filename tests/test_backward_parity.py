@@ -1,9 +1,10 @@
-"""kda_bwd (HIP, token-recurrent fp32 backward) against the fp64 oracle's reverse mode.
+"""kda_bwd (HIP, chunkwise fp32 matrix-core backward) and kda_bwd_recurrent (HIP, token by
+token, fp32) against the fp64 oracle's reverse mode.
 
-The kernel evaluates the adjoint recurrence in fp32 from inputs that are exact in fp32
-(bf16 inputs widen exactly), so its error is fp32 rounding accumulated over a sequence:
-tolerance max |err| <= 1e-3 * RMS(ref) for every gradient (dq, dk, dv, dlog_alpha, dbeta,
-dh0) separately, for fp32 and bf16 inputs alike.
+Both evaluate the adjoint in fp32 from inputs that are exact in fp32 (bf16 inputs widen
+exactly), so their error is fp32 rounding accumulated over a sequence: tolerance
+max |err| <= 1e-3 * RMS(ref) for every gradient (dq, dk, dv, dlog_alpha, dbeta, dh0)
+separately, for fp32 and bf16 inputs alike.
 """
 import numpy as np
 import pytest
@@ -32,10 +33,10 @@ def check(g, ref):
         assert err <= TOL * rms, (key, err, rms)
 
 
-def run(inp, do, dhT):
+def run(inp, do, dhT, method="chunk"):
     import kimi_delta_attention_06_amd as kda
     g = kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do, h0=inp["h0"],
-                     cu_seqlens=inp["cu_seqlens"], dhT=dhT)
+                     cu_seqlens=inp["cu_seqlens"], dhT=dhT, method=method)
     torch.cuda.synchronize()
     return g
 
@@ -55,25 +56,53 @@ def cotangents(inp, seed, with_dhT=True):
     return do, dhT
 
 
+METHODS = ["chunk", "recurrent"]
+
+
+@pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
-def test_backward_small_varlen(dtype, dk, dv):
-    """Sequences across several 64-token segments with ragged tails, an empty and a 1-token one,
-    nonzero h0 and dhT."""
+def test_backward_small_varlen(method, dtype, dk, dv):
+    """Sequences across several chunks and 64-token segments with ragged tails and unaligned
+    starts, an empty and a 1-token one, nonzero h0 and dhT."""
     lens = [150, 0, 1, 64, 97, 33]
-    print("backward: %s dk=%d dv=%d lens=%s" % (dtype, dk, dv, lens), flush=True)
+    print("backward %s: %s dk=%d dv=%d lens=%s" % (method, dtype, dk, dv, lens), flush=True)
     inp = kda_inputs.make_custom_chunk_inputs(lens, 3, dk, dv, dtype, h0_std=0.02, seed=21 + dk + dv, device="cuda")
     do, dhT = cotangents(inp, 5 + dk)
+    check(run(inp, do, dhT, method), ref(inp, do, dhT))
+
+
+@pytest.mark.parametrize("method", METHODS)
+def test_backward_without_initial_or_final_state(method):
+    inp = kda_inputs.make_custom_chunk_inputs([130, 7], 2, 128, 128, torch.bfloat16, seed=8, device="cuda")
+    do, _ = cotangents(inp, 9, with_dhT=False)
+    check(run(inp, do, None, method), ref(inp, do, None))
+
+
+@pytest.mark.parametrize("lens", [[16], [15], [17, 16, 48, 3]])
+def test_backward_chunk_boundaries(lens):
+    """Lengths at, below and past the 16-token chunk: full, ragged and single-row chunks."""
+    print("backward chunk: lens=%s" % (lens,), flush=True)
+    inp = kda_inputs.make_custom_chunk_inputs(lens, 2, 128, 128, torch.bfloat16, h0_std=0.02, seed=len(lens),
+                                              device="cuda")
+    do, dhT = cotangents(inp, 3)
     check(run(inp, do, dhT), ref(inp, do, dhT))
 
 
-def test_backward_without_initial_or_final_state():
-    inp = kda_inputs.make_custom_chunk_inputs([130, 7], 2, 128, 128, torch.bfloat16, seed=8, device="cuda")
-    do, _ = cotangents(inp, 9, with_dhT=False)
-    check(run(inp, do, None), ref(inp, do, None))
+def test_backward_chunk_strong_decay():
+    """Gate law x5: about 4 nats per token and channel on average, ~65 per 16-token chunk and
+    ~105 at most (inside the 120-nat bound), so the balanced Gram operands span up to ~e^52."""
+    inp = kda_inputs.make_custom_chunk_inputs([200, 45], 2, 128, 128, torch.bfloat16, gate_scale=5.0, h0_std=0.02,
+                                              seed=77, device="cuda")
+    la = inp["log_alpha"].double()
+    print("backward chunk strong decay: mean log a %.2f, min over 16 tokens %.1f" %
+          (float(la.mean()), float(la[:16].sum(0).min())), flush=True)
+    do, dhT = cotangents(inp, 4)
+    check(run(inp, do, dhT), ref(inp, do, dhT))
 
 
-def test_backward_kimi_linear_layer_two_heads():
+@pytest.mark.parametrize("method", METHODS)
+def test_backward_kimi_linear_layer_two_heads(method):
     """The Kimi-Linear-shaped layer (B=4, T=4096, d=128) on 2 of its 32 heads, gate law x0.1."""
     w = kda_inputs.KIMI_LINEAR_LAYER
     inp = kda_inputs.make_chunk_inputs(w, device="cuda")
@@ -83,5 +112,5 @@ def test_backward_kimi_linear_layer_two_heads():
     sub["cu_seqlens"] = inp["cu_seqlens"]
     del inp
     do, dhT = cotangents(sub, 11)
-    print("backward: Kimi-Linear layer, heads 3 and 17, B=4 T=4096", flush=True)
-    check(run(sub, do, dhT), ref(sub, do, dhT))
+    print("backward %s: Kimi-Linear layer, heads 3 and 17, B=4 T=4096" % method, flush=True)
+    check(run(sub, do, dhT, method), ref(sub, do, dhT))

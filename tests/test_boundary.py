@@ -21,6 +21,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_checkpointed", "kda_chunk_fwd_split",
                           "kda_chunk_fwd_split_workspace_size", "kda_bwd", "kda_bwd_workspace_size",
+                          "kda_bwd_recurrent", "kda_bwd_recurrent_workspace_size",
                           "kda_recurrent_step",
                           "kda_recurrent_verify", "kda_status_string", "kda_version"}
     for n in names:
@@ -162,26 +163,37 @@ def test_chunk_fwd_split_empty_batch_is_a_no_op():
     assert split_call(N=0, T=0, q=None, k=None, v=None, la=None, b=None, o=None, ws=None, wsb=0) == 0
 
 
-def bwd_call(**kw):
+def bwd_call(fn="kda_bwd", **kw):
     a = dict(q=P, k=P, v=P, la=P, b=P, h0=None, cu=None, N=1, T=64, H=2, dk=128, dv=128, dt=_lib.KDA_DTYPE_BF16,
              do=P, dhT=None, dq=P * 8, dkk=P * 9, dvv=P * 10, dla=P * 11, db=P * 12, dh0=None, ws=P * 64,
              wsb=1 << 24)
     a.update(kw)
-    return lib.kda_bwd(a["q"], a["k"], a["v"], a["la"], a["b"], a["h0"], a["cu"], a["N"], a["T"], a["H"], a["dk"],
-                       a["dv"], a["dt"], a["do"], a["dhT"], a["dq"], a["dkk"], a["dvv"], a["dla"], a["db"], a["dh0"],
-                       a["ws"], a["wsb"], None)
+    return getattr(lib, fn)(a["q"], a["k"], a["v"], a["la"], a["b"], a["h0"], a["cu"], a["N"], a["T"], a["H"],
+                            a["dk"], a["dv"], a["dt"], a["do"], a["dhT"], a["dq"], a["dkk"], a["dvv"], a["dla"],
+                            a["db"], a["dh0"], a["ws"], a["wsb"], None)
 
 
 def test_bwd_workspace_size():
     b = ctypes.c_size_t(0)
     assert lib.kda_bwd_workspace_size(1, 64, 2, 128, 128, ctypes.byref(b)) == 0
-    # (64 / 64 + 1 + 1) checkpoint slots + 64 token states per chain, x 2 heads x 64 KiB,
-    # + partial row gradients of the second column half: (3 * 128 + 1) x 64 tokens x 2 heads, fp32
-    assert b.value == (3 + 64) * 2 * 128 * 128 * 4 + (3 * 128 + 1) * 64 * 2 * 4
+    # states entering the 64 / 16 chunks + state cotangents of (64 / 16 + 1 + 1) chunk slots,
+    # x 2 heads x 64 KiB
+    assert b.value == (4 + 6) * 2 * 128 * 128 * 4
     assert lib.kda_bwd_workspace_size(1, 64, 2, 96, 128, ctypes.byref(b)) == 2
     assert lib.kda_bwd_workspace_size(1, 64, 2, 128, 128, None) == 1
 
 
+def test_bwd_recurrent_workspace_size():
+    b = ctypes.c_size_t(0)
+    assert lib.kda_bwd_recurrent_workspace_size(1, 64, 2, 128, 128, ctypes.byref(b)) == 0
+    # (64 / 64 + 1 + 1) checkpoint slots + 64 token states per chain, x 2 heads x 64 KiB,
+    # + partial row gradients of the second column half: (3 * 128 + 1) x 64 tokens x 2 heads, fp32
+    assert b.value == (3 + 64) * 2 * 128 * 128 * 4 + (3 * 128 + 1) * 64 * 2 * 4
+    assert lib.kda_bwd_recurrent_workspace_size(1, 64, 2, 96, 128, ctypes.byref(b)) == 2
+    assert lib.kda_bwd_recurrent_workspace_size(1, 64, 2, 128, 128, None) == 1
+
+
+@pytest.mark.parametrize("fn", ["kda_bwd", "kda_bwd_recurrent"])
 @pytest.mark.parametrize("kw,code", [
     (dict(ws=None), 1), (dict(wsb=1000), 1), (dict(ws=P * 64 + 4), 1), (dict(do=None), 1), (dict(dq=None), 1),
     (dict(dq=P), 1),          # an output overlaps the inputs
@@ -189,10 +201,11 @@ def test_bwd_workspace_size():
     (dict(ws=P * 10), 1),     # the workspace overlaps an output
     (dict(dt=5), 1), (dict(dk=96), 2), (dict(T=63, N=2), 1), (dict(N=0, T=5), 1),
 ])
-def test_bwd_rejects(kw, code):
-    assert bwd_call(**kw) == code
+def test_bwd_rejects(fn, kw, code):
+    assert bwd_call(fn, **kw) == code
 
 
-def test_bwd_empty_batch_is_a_no_op():
-    assert bwd_call(N=0, T=0, q=None, k=None, v=None, la=None, b=None, do=None, dq=None, dkk=None, dvv=None,
+@pytest.mark.parametrize("fn", ["kda_bwd", "kda_bwd_recurrent"])
+def test_bwd_empty_batch_is_a_no_op(fn):
+    assert bwd_call(fn, N=0, T=0, q=None, k=None, v=None, la=None, b=None, do=None, dq=None, dkk=None, dvv=None,
                     dla=None, db=None, ws=None, wsb=0) == 0
