@@ -12,7 +12,7 @@ variant (8 tokens, per-sequence commit counts) are timed and reported under
 1M-token sequence x 32 heads is timed, fused and split (kda_chunk_fwd_split), and
 reported under "long_context"; and the
 fp64 CPU oracle is timed on a bounded sample of the chunk workload ("cpu_baseline").
-The backward pass (kda_bwd) on the Kimi-Linear layer is timed under "backward".
+The backward pass (kda_bwd, chunkwise) on the Kimi-Linear layer is timed under "backward".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-long-context] [--copy-calibration]
 Prints exactly one JSON line on stdout.  --copy-calibration adds three launches of a
@@ -254,7 +254,7 @@ def main():
 
     b_ms = time_launches(bstep, 5, 1, stream)
     backward = {"workload": w.name, "ms_per_step": round(b_ms, 3), "tokens_per_s": round(tokens / (b_ms * 1e-3), 1),
-                "workspace_bytes": b_ws.numel(), "kind": "token-recurrent fp32 (kda_bwd)"}
+                "workspace_bytes": b_ws.numel(), "kind": "chunkwise fp32 matrix-core reverse mode (kda_bwd)"}
     log("backward (kda_bwd) on %s: %.3f ms/call, %.2f M tokens/s" % (w.name, b_ms, tokens / (b_ms * 1e-3) / 1e6))
     del b_do, b_ws
 
