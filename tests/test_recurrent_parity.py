@@ -4,7 +4,8 @@ Workload: 256 sequences x 32 heads, dk = dv = 128, fp32 state ~ N(0, 0.02^2),
 one decode token or a replay of 8 draft tokens, bf16 q/k/v (q, k unit-norm),
 per-channel log_alpha = -softplus(N(0,1)), beta = sigmoid(N(0,1)).
 Tolerance (bf16 inputs): max |err| <= 2e-2 * RMS(reference), for o and for the
-updated state separately; fp32 inputs: max |err| <= 1e-4.
+updated state separately; fp32 inputs: max |err| <= 1e-4.  Token counts up to 5 run
+the rows16 thread map and 6 to 8 the groups map, so both are covered on every shape.
 """
 import numpy as np
 import pytest
@@ -33,7 +34,7 @@ def run_case(n_tokens, n_seqs=None, dk=128, dv=128, dtype=torch.bfloat16, seed=N
     return o, inp["S"], o_ref, S_ref
 
 
-@pytest.mark.parametrize("n_tokens", [1, 8])
+@pytest.mark.parametrize("n_tokens", [1, 6, 8])
 def test_decode_workload_matches_oracle(n_tokens):
     print("decode 256x32 d128 n_tokens=%d" % n_tokens, flush=True)
     o, S, o_ref, S_ref = run_case(n_tokens)
@@ -46,7 +47,7 @@ def test_decode_workload_matches_oracle(n_tokens):
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128)])
-@pytest.mark.parametrize("n_tokens", [1, 3, 8])
+@pytest.mark.parametrize("n_tokens", [1, 3, 5, 6, 8])
 def test_decode_shapes_fp32_inputs(dk, dv, n_tokens):
     o, S, o_ref, S_ref = run_case(n_tokens, n_seqs=5, dk=dk, dv=dv, dtype=torch.float32, seed=77 + n_tokens)
     eo, _ = errs(o, o_ref)
@@ -112,7 +113,7 @@ def test_verify_commits_per_sequence_prefix():
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128)])
-@pytest.mark.parametrize("n_tokens", [1, 5])
+@pytest.mark.parametrize("n_tokens", [1, 5, 6, 8])
 def test_verify_shapes_fp32_inputs(dk, dv, n_tokens):
     commit = [n_tokens, 0, 1, n_tokens - 1, 3]
     o, S, o_ref, S_ref, _ = run_verify(n_tokens, commit, dk=dk, dv=dv, dtype=torch.float32, seed=5 + n_tokens)
