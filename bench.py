@@ -43,6 +43,7 @@ BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 512
 # lower-triangular intra-chunk products (A, M, W, Ut, M U); the UT inverse is not counted.
 FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_kimi_linear_layer_pmc.txt")
+SQ_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_kimi_linear_layer_sq_counters.txt")
 CHUNK_SRC = os.path.join(ROOT, "kimi_delta_attention_06_amd", "csrc", "kda_chunk.hip")
 
 
@@ -55,12 +56,12 @@ def src_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per launch measured by rocprofv3 counters for the current kernel source, else None."""
-    if not os.path.exists(PMC_SUMMARY):
+def profile_value(path, key):
+    """A figure from a rocprofv3 counter summary, if it was taken on the current kernel source, else None."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(PMC_SUMMARY) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
@@ -68,9 +69,14 @@ def traffic_from_profile():
     if vals.get("kernel_source_sha256_16") != src_hash(CHUNK_SRC):
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def traffic_from_profile():
+    """HBM bytes per launch measured by rocprofv3 counters for the current kernel source, else None."""
+    return profile_value(PMC_SUMMARY, "hbm_bytes_per_launch")
 
 
 def time_launches(fn, steps, warmup, stream):
@@ -314,7 +320,10 @@ def main():
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
                      "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": alg_flops},
+                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": alg_flops,
+                 # rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs) and VALU busy of the same kernel
+                 "counter_busy_frac": profile_value(SQ_SUMMARY, "mfma_busy_frac"),
+                 "counter_valu_busy_frac": profile_value(SQ_SUMMARY, "valu_busy_frac")},
         "checkpointed": checkpointed,
         "decode": decode,
         "long_context": long_context,
