@@ -94,6 +94,31 @@ def time_launches(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per launch
 
 
+def launch_spread(fn, n, stream):
+    """Per-launch times (ms) from an event pair around each of n launches: p10, median, p90."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    pick = lambda f: t[min(n - 1, int(round(f * (n - 1))))]
+    return {"p10_ms": round(pick(0.1), 5), "median_ms": round(pick(0.5), 5), "p90_ms": round(pick(0.9), 5),
+            "launches": n}
+
+
+def copy_bandwidth(dev, stream, nbytes=1 << 30):
+    """GB/s of a plain device copy (torch copy_ of nbytes fp32: nbytes read + nbytes written)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    ms = time_launches(lambda: dst.copy_(src), 20, 5, stream)
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(inp, n_seqs):
     """fp64 oracle on the first `n_seqs` sequences of the workload, all heads (whole sequences)."""
     import oracle
@@ -188,6 +213,11 @@ def main():
     tflops = alg_flops / (ms * 1e-3) / 1e12
     log("chunk_fwd: %.4f ms/launch, %.1f M tokens/s, %.0f GB/s algorithmic, %.1f TFLOP/s algorithmic"
         % (ms, tok_s / 1e6, gbs, tflops))
+    spread = launch_spread(step, 50, stream)
+    log("chunk_fwd per-launch spread: p10 %.4f, median %.4f, p90 %.4f ms" % (spread["p10_ms"], spread["median_ms"],
+                                                                         spread["p90_ms"]))
+    copy_gbs = copy_bandwidth(dev, stream)
+    log("device copy (1 GiB each way): %.0f GB/s" % copy_gbs)
 
     # ---------------- the same pass with 512-token state checkpoints ----------------
     ck_every = 512
@@ -221,6 +251,7 @@ def main():
         d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
         decode["n%d" % n_tok] = {"ms_per_step": round(d_ms, 5), "GB/s": round(d_gbs, 1),
                                  "frac_of_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4),
+                                 "frac_of_copy": round(d_gbs / copy_gbs, 4),
                                  "tokens_per_s": round(dw.n_seqs * n_tok / (d_ms * 1e-3), 1),
                                  "bytes_per_step": d_bytes}
         log("recurrent_step n=%d: %.4f ms, %.0f GB/s (%.1f%% of peak)" % (n_tok, d_ms, d_gbs, 100 * d_gbs / HBM_PEAK_GBS))
@@ -242,7 +273,7 @@ def main():
     v_bytes = (dw.n_seqs + n_writing) * state_bytes + dw.n_seqs * 8 * dw.n_heads * BYTES_PER_TOKEN_HEAD
     v_gbs = v_bytes / (v_ms * 1e-3) / 1e9
     decode["verify_n8"] = {"ms_per_step": round(v_ms, 5), "GB/s": round(v_gbs, 1),
-                           "frac_of_hbm_peak": round(v_gbs / HBM_PEAK_GBS, 4),
+                           "frac_of_hbm_peak": round(v_gbs / HBM_PEAK_GBS, 4), "frac_of_copy": round(v_gbs / copy_gbs, 4),
                            "sequences_committing": n_writing, "bytes_per_step": v_bytes}
     log("recurrent_verify n=8 (%d of %d sequences commit): %.4f ms, %.0f GB/s (%.1f%% of peak)"
         % (n_writing, dw.n_seqs, v_ms, v_gbs, 100 * v_gbs / HBM_PEAK_GBS))
@@ -292,8 +323,10 @@ def main():
                                    dtype=torch.uint8, device=dev)
             l_ms = time_launches(fn, 3, 1, stream)
             l_tok = lw.total_tokens / (l_ms * 1e-3)
+            n_chunks = -(-lw.seq_len // lw.chunk_size)
             long_context[leg] = {"ms_per_step": round(l_ms, 3), "tokens_per_s": round(l_tok, 1),
-                                 "algorithmic_GB/s": round(l_bytes / (l_ms * 1e-3) / 1e9, 1)}
+                                 "algorithmic_GB/s": round(l_bytes / (l_ms * 1e-3) / 1e9, 1),
+                                 "us_per_serial_chunk_step": round(l_ms * 1e3 / n_chunks, 3)}
             log("long context, %s (%d tokens x %d heads): %.2f ms/launch, %.2f M tokens/s"
                 % (leg, lw.total_tokens, lw.n_heads, l_ms, l_tok / 1e6))
         if l_ws is not None:
@@ -318,7 +351,9 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                     "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": alg_bytes},
+                     "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": alg_bytes,
+                     "copy_GB/s": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4)},
+        "launch_spread": spread,
         "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": alg_flops,
                  # rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs) and VALU busy of the same kernel
