@@ -118,6 +118,18 @@ template <> struct Vec<bf16_t> {
   }
 };
 
+// 16 bytes of input (8 bf16 or 4 fp32 values), widened to fp32 at d
+__device__ __forceinline__ void widen16(float* d, const uint4& x, bf16_t) {
+  float2 f;
+  f = bf16x2_to_f32x2(x.x); d[0] = f.x; d[1] = f.y;
+  f = bf16x2_to_f32x2(x.y); d[2] = f.x; d[3] = f.y;
+  f = bf16x2_to_f32x2(x.z); d[4] = f.x; d[5] = f.y;
+  f = bf16x2_to_f32x2(x.w); d[6] = f.x; d[7] = f.y;
+}
+__device__ __forceinline__ void widen16(float* d, const uint4& x, float) {
+  d[0] = __uint_as_float(x.x); d[1] = __uint_as_float(x.y); d[2] = __uint_as_float(x.z); d[3] = __uint_as_float(x.w);
+}
+
 // The per-chunk operands both kernels form (LDS, fp32).
 template <int DK>
 struct Intra {
@@ -281,16 +293,63 @@ __global__ __launch_bounds__(NT) void bwd_ds_kernel(const InT* __restrict__ q, c
   }
   const int64_t slot0 = start / C + n;
 
-  for (int64_t j = nch - 1; j >= 0; --j) {
-    const int64_t t0 = start + C * j;
-    const int Lc = (int)(len - C * j < C ? len - C * j : C);
-    in.load(q, k, la, beta, t0, Lc, H, h);
-    for (int e = threadIdx.x; e < C * BV / 4; e += NT) {
-      const int i = e / (BV / 4), c = (e - i * (BV / 4)) * 4;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < Lc) x = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + v0 + c);
-      *reinterpret_cast<float4*>(sDO + i * LDO + c) = x;
+  // The inputs of the next chunk (in reverse order) are loaded into registers while the
+  // current one is processed: q, k (16 bytes per item), log a and dO (float4), beta.
+  constexpr int VE = Vec<InT>::N, NV = C * DK / VE;
+  constexpr int IQK = (2 * NV + NT - 1) / NT, ILA = (C * DK / 4 + NT - 1) / NT, IDO = (C * BV / 4 + NT - 1) / NT;
+  uint4 rqk[IQK];
+  float4 rla[ILA], rdo[IDO];
+  float rb = 0.f;
+  auto fetch = [&](int64_t jj) {
+    const int64_t t0 = start + C * jj;
+    const int Lc = (int)(len - C * jj < C ? len - C * jj : C);
+#pragma unroll
+    for (int it = 0; it < IQK; ++it) {
+      const int e = threadIdx.x + NT * it, which = e / NV, ee = e - which * NV;
+      const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
+      rqk[it] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < 2 * NV && i < Lc)
+        rqk[it] = *reinterpret_cast<const uint4*>((which ? k : q) + ((size_t)(t0 + i) * H + h) * DK + c);
     }
+#pragma unroll
+    for (int it = 0; it < ILA; ++it) {
+      const int e = threadIdx.x + NT * it, i = e / (DK / 4), c = (e - i * (DK / 4)) * 4;
+      rla[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < C * DK / 4 && i < Lc) rla[it] = *reinterpret_cast<const float4*>(la + ((size_t)(t0 + i) * H + h) * DK + c);
+    }
+#pragma unroll
+    for (int it = 0; it < IDO; ++it) {
+      const int e = threadIdx.x + NT * it, i = e / (BV / 4), c = (e - i * (BV / 4)) * 4;
+      rdo[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < C * BV / 4 && i < Lc)
+        rdo[it] = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + v0 + c);
+    }
+    rb = (int)threadIdx.x < Lc ? beta[(size_t)(t0 + threadIdx.x) * H + h] : 0.f;
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int it = 0; it < IQK; ++it) {
+      const int e = threadIdx.x + NT * it, which = e / NV, ee = e - which * NV;
+      const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
+      if (e < 2 * NV) widen16((which ? in.k : in.q) + i * LDK + c, rqk[it], InT{});
+    }
+#pragma unroll
+    for (int it = 0; it < ILA; ++it) {
+      const int e = threadIdx.x + NT * it, i = e / (DK / 4), c = (e - i * (DK / 4)) * 4;
+      if (e < C * DK / 4) *reinterpret_cast<float4*>(in.g + i * LDK + c) = rla[it];
+    }
+#pragma unroll
+    for (int it = 0; it < IDO; ++it) {
+      const int e = threadIdx.x + NT * it, i = e / (BV / 4), c = (e - i * (BV / 4)) * 4;
+      if (e < C * BV / 4) *reinterpret_cast<float4*>(sDO + i * LDO + c) = rdo[it];
+    }
+    if (threadIdx.x < C) in.b[threadIdx.x] = rb;
+  };
+  if (nch > 0) fetch(nch - 1);
+
+  for (int64_t j = nch - 1; j >= 0; --j) {
+    put();
+    if (j > 0) fetch(j - 1);
     {
       float* dst = dsw + ((size_t)(slot0 + j) * H + h) * DK * DV;
 #pragma unroll
@@ -420,6 +479,18 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   const float* dSC = dsw + ((size_t)slot * H + h) * DK * DV;
   const int w = threadIdx.x / kWave, l = lane();
 
+  // S and dS' columns of value tile tv, in registers: the next tile's are in flight while
+  // the current one is worked on (the first tile's beside the chunk's input loads)
+  float4 pS[UPT], pD[UPT];
+  auto fetch = [&](int tv) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int e = threadIdx.x + NT * u, c = e / (BV / 4), c4 = (e - c * (BV / 4)) * 4;
+      pS[u] = S0 ? *reinterpret_cast<const float4*>(S0 + (size_t)c * DV + tv * BV + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      pD[u] = *reinterpret_cast<const float4*>(dSC + (size_t)c * DV + tv * BV + c4);
+    }
+  };
+  fetch(0);
   in.load(q, k, la, beta, t0, Lc, H, h);
   for (int e = threadIdx.x; e < C * DV / 4; e += NT) {
     const int i = e / (DV / 4), c = (e - i * (DV / 4)) * 4;
@@ -446,13 +517,12 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {  // stage S and dS' columns [vb, vb + BV)
       const int e = threadIdx.x + NT * u, c = e / (BV / 4), c4 = (e - c * (BV / 4)) * 4;
-      float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (S0) s4 = *reinterpret_cast<const float4*>(S0 + (size_t)c * DV + vb + c4);
-      const float4 d4 = *reinterpret_cast<const float4*>(dSC + (size_t)c * DV + vb + c4);
+      const float4 s4 = pS[u], d4 = pD[u];
       *reinterpret_cast<float4*>(sS + c * LDB + c4) = s4;
       *reinterpret_cast<float4*>(sD + c * LDB + c4) = d4;
       gs[u] += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
     }
+    if (tv + 1 < NTV) fetch(tv + 1);
     __syncthreads();
     {  // partial Kg S (waves 0-3) and Kc dS' (waves 4-7) over one half of the channels
       const int vt = w & 1, kh = (w >> 1) & 1;
