@@ -9,8 +9,8 @@ tokens is timed and reported under "checkpointed".  In the same run the decode/r
 (256 sequences x 32 heads, fp32 state, 1 and 8 tokens) and the replay + verify
 variant (8 tokens, per-sequence commit counts) are timed and reported under
 "decode" (HBM GB/s against the 8 TB/s peak); one chunked pass over a single
-1M-token sequence x 32 heads is timed, fused and split (kda_chunk_fwd_split), and
-reported under "long_context"; and the
+1M-token sequence x 32 heads is timed, fused and split (kda_chunk_fwd_split), 1 warm-up + 5 timed
+launches each, and reported under "long_context"; and the
 fp64 CPU oracle is timed on a bounded sample of the chunk workload ("cpu_baseline").
 The backward pass (kda_bwd, chunkwise) on the Kimi-Linear layer is timed under "backward".
 
@@ -247,12 +247,13 @@ def main():
                                o=d_o)
 
         d_ms = time_launches(dstep, max(args.steps, 20), args.warmup, stream)
+        d_spread = launch_spread(dstep, 50, stream)
         d_bytes = 2 * dw.n_seqs * dw.n_heads * dw.dk * dw.dv * 4 + dw.n_seqs * n_tok * dw.n_heads * BYTES_PER_TOKEN_HEAD
         d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
         decode["n%d" % n_tok] = {"ms_per_step": round(d_ms, 5), "GB/s": round(d_gbs, 1),
                                  "frac_of_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4),
                                  "frac_of_copy": round(d_gbs / copy_gbs, 4),
-                                 "tokens_per_s": round(dw.n_seqs * n_tok / (d_ms * 1e-3), 1),
+                                 "tokens_per_s": round(dw.n_seqs * n_tok / (d_ms * 1e-3), 1), "launch_spread": d_spread,
                                  "bytes_per_step": d_bytes}
         log("recurrent_step n=%d: %.4f ms, %.0f GB/s (%.1f%% of peak)" % (n_tok, d_ms, d_gbs, 100 * d_gbs / HBM_PEAK_GBS))
         del d_inp, d_o
@@ -321,7 +322,7 @@ def main():
                 l_ws = torch.empty(kda.chunk_fwd_split_workspace_bytes(lw.n_seqs, lw.total_tokens, lw.n_heads, lw.dk,
                                                                        lw.dv, lw.chunk_size),
                                    dtype=torch.uint8, device=dev)
-            l_ms = time_launches(fn, 3, 1, stream)
+            l_ms = time_launches(fn, 5, 1, stream)
             l_tok = lw.total_tokens / (l_ms * 1e-3)
             n_chunks = -(-lw.seq_len // lw.chunk_size)
             long_context[leg] = {"ms_per_step": round(l_ms, 3), "tokens_per_s": round(l_tok, 1),
