@@ -133,8 +133,12 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
  * in-device context parallelism among KDA's execution forms).  Pass 1 does the
  * in-chunk work for every chunk of every head at once, in parallel over the
  * whole sequence, and writes each chunk's state-free operands to `workspace`;
- * pass 2 walks the chunks of each chain with the state, reading them.  Results
- * equal kda_chunk_fwd's up to rounding (the same operand precisions).
+ * pass 2 walks the chunks of each chain with the state, reading them.  When the
+ * state pass fits on half of the CUs (chains x dv/32 <= 128) and the longest
+ * sequence has at least 128 chunks, the chunks are cut into 2 to 16 ranges and
+ * each launch runs pass 2 over one range beside pass 1 over the next, with the
+ * state handed between ranges through the workspace.  Results equal
+ * kda_chunk_fwd's up to rounding (the same operand precisions).
  *
  * Same arguments and results as kda_chunk_fwd, plus:
  *
@@ -157,7 +161,8 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
 /*
  * kda_chunk_fwd_split_workspace_size - bytes of workspace kda_chunk_fwd_split
  * needs: (total_tokens / chunk_size + n_seqs + 1) * n_heads tiles of the
- * per-chunk operands (66,304 B each for dk = 128, chunk 64).  Writes *bytes.
+ * per-chunk operands (66,304 B each for dk = 128, chunk 64), then
+ * n_seqs * n_heads fp32 dk x dv states.  Writes *bytes.
  * Errors: KDA_ERR_INVALID_ARGUMENT (NULL bytes, negative or zero sizes, bad
  * dtype), KDA_ERR_UNSUPPORTED (a combination kda_chunk_fwd_split does not take).
  */

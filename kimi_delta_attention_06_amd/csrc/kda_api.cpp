@@ -81,7 +81,7 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   if (!kda::chunk_fwd_supported(dk, dv, chunk_size, bf16)) return KDA_ERR_UNSUPPORTED;
   if (split) {
     if (!bf16) return KDA_ERR_UNSUPPORTED;
-    const size_t need = kda::chunk_split_workspace_bytes(total_tokens, n_seqs, n_heads, dk, chunk_size);
+    const size_t need = kda::chunk_split_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv, chunk_size);
     if (n_seqs > 0 && total_tokens > 0) {
       if (!ws || !aligned16(ws) || ws_bytes < need) return KDA_ERR_INVALID_ARGUMENT;
       // the workspace must not overlap any input or output
@@ -131,7 +131,7 @@ kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_toke
   if (!dims_ok(dk) || !dims_ok(dv) || qkv_dtype != KDA_DTYPE_BF16 ||
       !kda::chunk_fwd_supported(dk, dv, chunk_size, true))
     return KDA_ERR_UNSUPPORTED;
-  *bytes = kda::chunk_split_workspace_bytes(total_tokens, n_seqs, n_heads, dk, chunk_size);
+  *bytes = kda::chunk_split_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv, chunk_size);
   return KDA_OK;
 }
 

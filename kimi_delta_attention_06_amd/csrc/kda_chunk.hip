@@ -295,12 +295,39 @@ __device__ __forceinline__ void unpack(const uint4* w, float* out, int n) {
 // PREP = false: the fused forward.  PREP = true: the intra-chunk part only, for a group of
 // `cpg` consecutive chunks of one (sequence, head) per workgroup; each chunk's state-free
 // operands go to workspace slot (sequence start / C + sequence + chunk) (see write_ws).
-template <int C, int DK, int BV, Prec P, typename InT, bool PREP>
+// Pipelined split (PIPE_BV > 0, in-chunk mode only): the first n_state_blocks workgroups
+// run the state pass over chunks [ch_begin, ch_end) with value tiles of PIPE_BV columns
+// (chunk_state_body, defined below), the others the in-chunk pass over the chunk groups
+// from grp0 on.
+struct PipeArgs {
+  int n_state_blocks, grp0;
+  int64_t ch_begin, ch_end;
+  const float* h0;
+  float *o, *hT, *carry;
+};
+
+template <int C, int DK, int BV, typename InT>
+__device__ __forceinline__ void chunk_state_body(const uint4* __restrict__ ws, const InT* __restrict__ v,
+                                                 const float* h0, const int32_t* __restrict__ cu_seqlens,
+                                                 float* __restrict__ o, float* hT, int n_chains, int H, int DV,
+                                                 int64_t seq_len, int bid, int64_t ch_begin, int64_t ch_end,
+                                                 float* carry);
+
+template <int C, int DK, int BV, Prec P, typename InT, bool PREP, int PIPE_BV = 0>
 __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* h0,
     const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT, float* __restrict__ ckpt,
-    int ckpt_every, int n_chains, int H, int DV, int64_t seq_len, void* __restrict__ ws, int cpg) {
+    int ckpt_every, int n_chains, int H, int DV, int64_t seq_len, void* __restrict__ ws, int cpg, PipeArgs pa) {
+  static_assert(PIPE_BV == 0 || PREP, "the pipelined mode pairs the state pass with the in-chunk pass");
+  if constexpr (PIPE_BV > 0) {
+    if ((int)blockIdx.x < pa.n_state_blocks) {
+      chunk_state_body<C, DK, PIPE_BV, InT>(reinterpret_cast<const uint4*>(ws), v, pa.h0, cu_seqlens, pa.o, pa.hT,
+                                            n_chains, H, DV, seq_len, (int)blockIdx.x, pa.ch_begin, pa.ch_end,
+                                            pa.carry);
+      return;
+    }
+  }
   using L = Lay<C, DK, BV, P>;
   using T = typename L::T;
   constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
@@ -337,11 +364,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 
   // ---- (sequence, head, value tile); the value tiles of one chain share an XCD
   // (prep: (sequence, head, chunk group))
-  const int bid = blockIdx.x;
+  const int bid = (int)blockIdx.x - (PIPE_BV > 0 ? pa.n_state_blocks : 0);
   int chain, tile = 0, grp = 0;
   if constexpr (PREP) {
     chain = bid % n_chains;
-    grp = bid / n_chains;
+    grp = bid / n_chains + (PIPE_BV > 0 ? pa.grp0 : 0);
   } else {
     const int ntile = DV / BV;
     const int xcd = bid & 7, qd = bid >> 3;
@@ -1202,11 +1229,14 @@ struct SLay {
   static constexpr int NU = 2 * NQ + NKD + 2 * NAQ + NDQ + NGM;
 };
 
+// Chunks [ch_begin, ch_end) of every chain (clipped to the chain's length).  The state
+// enters from h0 (or zeros) when ch_begin is 0, else from `carry`; it leaves to hT when
+// the chain's last chunk is in the range, else to `carry` ([n_chains][DK][DV] fp32).
 template <int C, int DK, int BV, typename InT>
-__global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
+__device__ __forceinline__ void chunk_state_body(
     const uint4* __restrict__ ws, const InT* __restrict__ v, const float* h0,
     const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT,
-    int n_chains, int H, int DV, int64_t seq_len) {
+    int n_chains, int H, int DV, int64_t seq_len, int bid, int64_t ch_begin, int64_t ch_end, float* carry) {
   using L = SLay<C, DK, BV>;
   using T = _Float16;
   constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
@@ -1238,7 +1268,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
   use_buf(0);
 
   const int ntile = DV / BV;
-  const int bid = blockIdx.x;
   const int xcd = bid & 7, qd = bid >> 3;
   const int tile = qd % ntile;
   const int chain = (qd / ntile) * 8 + xcd;
@@ -1254,6 +1283,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
     t_end = t_begin + seq_len;
   }
   const int64_t nchunks = (t_end - t_begin + C - 1) / C;
+  if (ch_begin > 0 && ch_begin >= nchunks) return;  // the chain ended in an earlier range
+  const int64_t ch_stop = ch_end < nchunks ? ch_end : nchunks;
   auto chunk_len = [&](int64_t ch) -> int {
     const int64_t rem = t_end - (t_begin + ch * C);
     return (int)(rem < C ? rem : C);
@@ -1268,7 +1299,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
 
   constexpr int S_SLOTS = (NA * NJ + NW - 1) / NW;
   f32x4 Sacc[S_SLOTS];
-  const float* h0p = h0 ? h0 + (size_t)chain * DK * DV : nullptr;
+  const float* h0p = ch_begin > 0 ? carry + (size_t)chain * DK * DV : (h0 ? h0 + (size_t)chain * DK * DV : nullptr);
 #pragma unroll
   for (int s = 0; s < S_SLOTS; ++s) {
     const int id = wave + NW * s;
@@ -1322,7 +1353,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
   // group): the tile goes out in three groups, one per stage, so the device's requests
   // do not all leave right after one barrier
   auto load_tiles = [&](int64_t chn, int p0, int p1) {
-    const bool ok = chn < nchunks;
+    const bool ok = chn < ch_stop;
     const int64_t slot = t_begin / C + n + chn;
     const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * NU, ok ? (uint32_t)NU * 16u : 0u);
 #pragma unroll
@@ -1375,24 +1406,24 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
 
   __syncthreads();  // zero fill before the first tile
   write_ST();
-  if (nchunks > 0) {
-    load_tiles(0, 0, PF);
+  if (ch_begin < ch_stop) {
+    load_tiles(ch_begin, 0, PF);
     store_tiles();
   }
-  if constexpr (DB) load_tiles(1, 0, PF);  // chunk 1's tile waits in registers
+  if constexpr (DB) load_tiles(ch_begin + 1, 0, PF);  // the next chunk's tile waits in registers
   __syncthreads();
 
   f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
+  for (int64_t ch = ch_begin; ch < ch_stop; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
     const int Lc = chunk_len(ch);
     // the tile loaded next: chunk ch+2 with two buffers (chunk ch+1 goes from registers to the
     // other buffer now), else chunk ch+1 (to LDS after this chunk's last read)
     const int64_t chl = DB ? ch + 2 : ch + 1;
     if constexpr (DB) {
-      use_buf((int)((ch + 1) & 1));
+      use_buf((int)((ch - ch_begin + 1) & 1));
       store_tiles();
-      use_buf((int)(ch & 1));
+      use_buf((int)((ch - ch_begin) & 1));
     }
     load_tiles(chl, 0, PG1);
 
@@ -1473,8 +1504,22 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
       __syncthreads();
     }
   }
-  if (hT) store_state(hT + (size_t)chain * DK * DV);
+  if (ch_stop == nchunks) {
+    if (hT) store_state(hT + (size_t)chain * DK * DV);
+  } else {
+    store_state(carry + (size_t)chain * DK * DV);
+  }
 }
+
+template <int C, int DK, int BV, typename InT>
+__global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
+    const uint4* __restrict__ ws, const InT* __restrict__ v, const float* h0,
+    const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT,
+    int n_chains, int H, int DV, int64_t seq_len) {
+  chunk_state_body<C, DK, BV, InT>(ws, v, h0, cu_seqlens, o, hT, n_chains, H, DV, seq_len, (int)blockIdx.x, 0,
+                                   INT64_MAX, nullptr);
+}
+
 
 // ---------------------------------------------------------------------------
 // Host-side dispatch
@@ -1508,7 +1553,7 @@ static hipError_t launch_one(const ChunkArgs& a) {
   const int grid = ((n_chains + 7) / 8) * 8 * ntile;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q, (const InT*)a.k,
                      (const InT*)a.v, a.log_alpha, a.beta, a.h0, a.cu_seqlens, a.o, a.hT, a.ckpt, a.ckpt_every,
-                     n_chains, a.n_heads, a.dv, a.seq_len, nullptr, 0);
+                     n_chains, a.n_heads, a.dv, a.seq_len, nullptr, 0, PipeArgs{});
   return hipGetLastError();
 }
 
@@ -1522,6 +1567,69 @@ constexpr size_t split_tile_bytes() { return size_t(SLay<C, DK, 16>::NU) * 16; }
 static int64_t max_chunks_per_seq(const ChunkArgs& a) {
   const int64_t len = a.cu_seqlens ? a.total_tokens : a.seq_len;
   return (len + a.chunk_size - 1) / a.chunk_size;
+}
+
+// Pipelined split (chunk_fwd_kernel with PIPE_BV): value tiles of 32 columns, so that a few
+// chains' state pass takes at most 128 CUs, and 2 to 16 ranges of at least 64 chunks.
+constexpr int kPipeBV = 32;
+static bool split_pipelined(const ChunkArgs& a, int64_t max_chunks, int& n_ranges) {
+  const int64_t state_blocks = (int64_t)((a.n_seqs * a.n_heads + 7) / 8) * 8 * (a.dv / kPipeBV);
+  n_ranges = (int)(max_chunks / 64 < 16 ? max_chunks / 64 : 16);
+  return state_blocks <= 128 && n_ranges >= 2;
+}
+
+template <int C, int DK, typename InT>
+static hipError_t launch_split_pipelined(const ChunkArgs& a, void* ws, float* carry, int64_t mc, int n_ranges) {
+  const int n_chains = a.n_seqs * a.n_heads;
+  const int state_blocks = ((n_chains + 7) / 8) * 8 * (a.dv / kPipeBV);
+  // range length in chunks: a multiple of the in-chunk pass's group size cpg (16 groups per range)
+  int64_t rl = (mc + n_ranges - 1) / n_ranges;
+  int64_t cpg = (rl + 15) / 16;
+  cpg = cpg < 4 ? 4 : (cpg > 64 ? 64 : cpg);
+  rl = ((rl + cpg - 1) / cpg) * cpg;
+  const int64_t groups = rl / cpg;
+  const int64_t nr = (mc + rl - 1) / rl;
+  if ((int64_t)n_chains * groups + state_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // first range's in-chunk pass on its own
+  {
+    constexpr size_t lds = lds_bytes<C, DK, 16, Prec::Mixed>();
+    auto kern = chunk_fwd_kernel<C, DK, 16, Prec::Mixed, InT, true>;
+    static std::atomic<uint64_t> attr_done{0};
+    hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(n_chains * groups)), dim3(NT), lds, (hipStream_t)a.stream,
+                       (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, nullptr, a.cu_seqlens,
+                       nullptr, nullptr, nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg, PipeArgs{});
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // then per range r: the state pass over range r beside the in-chunk pass over range r + 1
+  constexpr size_t lds_p = lds_bytes<C, DK, 16, Prec::Mixed>(), lds_s = SLay<C, DK, kPipeBV>::TOTAL;
+  constexpr size_t lds = lds_p > lds_s ? lds_p : lds_s;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = chunk_fwd_kernel<C, DK, 16, Prec::Mixed, InT, true, kPipeBV>;
+  static std::atomic<uint64_t> attr_done{0};
+  hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
+  if (e != hipSuccess) return e;
+  for (int64_t r = 0; r < nr; ++r) {
+    const bool next = r + 1 < nr;
+    const int64_t grid = state_blocks + (next ? (int64_t)n_chains * groups : 0);
+    PipeArgs pa{};
+    pa.n_state_blocks = state_blocks;
+    pa.grp0 = (int)((r + 1) * groups);
+    pa.ch_begin = r * rl;
+    pa.ch_end = next ? (r + 1) * rl : INT64_MAX;
+    pa.h0 = a.h0;
+    pa.o = a.o;
+    pa.hT = a.hT;
+    pa.carry = carry;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q,
+                       (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, nullptr, a.cu_seqlens, nullptr, nullptr,
+                       nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg, pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int C, int DK, int BV, typename InT>
@@ -1542,7 +1650,7 @@ static hipError_t launch_split(const ChunkArgs& a, void* ws) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q,
                        (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, nullptr, a.cu_seqlens, nullptr, nullptr,
-                       nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg);
+                       nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg, PipeArgs{});
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1562,7 +1670,10 @@ static hipError_t launch_split(const ChunkArgs& a, void* ws) {
 }
 
 template <int C, int DK, typename InT>
-static hipError_t dispatch_split_bv(const ChunkArgs& a, void* ws) {
+static hipError_t dispatch_split_bv(const ChunkArgs& a, void* ws, float* carry) {
+  const int64_t mc = max_chunks_per_seq(a);
+  int n_ranges = 0;
+  if (split_pipelined(a, mc, n_ranges)) return launch_split_pipelined<C, DK, InT>(a, ws, carry, mc, n_ranges);
   const int bv = pick_bv(a.n_seqs * a.n_heads, a.dv, 64);
   if (bv == 64) return launch_split<C, DK, 64, InT>(a, ws);
   if (bv == 32) return launch_split<C, DK, 32, InT>(a, ws);
@@ -1613,7 +1724,8 @@ bool chunk_fwd_supported(int dk, int dv, int chunk_size, bool bf16) {
   return true;
 }
 
-size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int chunk_size) {
+// per-chunk tiles, then one fp32 state per chain for the pipelined path's hand-over between ranges
+static size_t split_tiles_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int chunk_size) {
   using namespace chunkk;
   size_t tile = 0;
   if (dk == 128) {
@@ -1628,17 +1740,24 @@ size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads
   return slots * (size_t)n_heads * tile;
 }
 
+size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv, int chunk_size) {
+  return split_tiles_bytes(total_tokens, n_seqs, n_heads, dk, chunk_size) +
+         (size_t)n_seqs * n_heads * dk * dv * sizeof(float);
+}
+
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws) {
   using namespace chunkk;
   if (!a.bf16 || !chunk_fwd_supported(a.dk, a.dv, a.chunk_size, a.bf16)) return hipErrorInvalidValue;
+  float* carry = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
+                                          split_tiles_bytes(a.total_tokens, a.n_seqs, a.n_heads, a.dk, a.chunk_size));
   if (a.dk == 128) {
-    if (a.chunk_size == 64) return dispatch_split_bv<64, 128, bf16_t>(a, ws);
-    if (a.chunk_size == 32) return dispatch_split_bv<32, 128, bf16_t>(a, ws);
-    return dispatch_split_bv<16, 128, bf16_t>(a, ws);
+    if (a.chunk_size == 64) return dispatch_split_bv<64, 128, bf16_t>(a, ws, carry);
+    if (a.chunk_size == 32) return dispatch_split_bv<32, 128, bf16_t>(a, ws, carry);
+    return dispatch_split_bv<16, 128, bf16_t>(a, ws, carry);
   }
-  if (a.chunk_size == 64) return dispatch_split_bv<64, 64, bf16_t>(a, ws);
-  if (a.chunk_size == 32) return dispatch_split_bv<32, 64, bf16_t>(a, ws);
-  return dispatch_split_bv<16, 64, bf16_t>(a, ws);
+  if (a.chunk_size == 64) return dispatch_split_bv<64, 64, bf16_t>(a, ws, carry);
+  if (a.chunk_size == 32) return dispatch_split_bv<32, 64, bf16_t>(a, ws, carry);
+  return dispatch_split_bv<16, 64, bf16_t>(a, ws, carry);
 }
 
 hipError_t launch_chunk_fwd_f32(const ChunkArgs& a) {

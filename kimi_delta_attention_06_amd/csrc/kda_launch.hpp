@@ -77,7 +77,7 @@ hipError_t launch_chunk_fwd_f32(const ChunkArgs& a);
 // Split path (bf16 only): intra-chunk pass into `ws`, then the state pass.
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws);
 // Workspace bytes the split path needs for these sizes.
-size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int chunk_size);
+size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv, int chunk_size);
 // True if the chunk kernel has an instantiation for these parameters.
 bool chunk_fwd_supported(int dk, int dv, int chunk_size, bool bf16);
 

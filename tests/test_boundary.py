@@ -131,9 +131,10 @@ def ws_size(N=1, T=64, H=2, dk=128, dv=128, C=64, dt=_lib.KDA_DTYPE_BF16, out=Tr
 
 def test_split_workspace_size():
     rc, n = ws_size()
-    # (64 / 64 + 1 + 1) slots x 2 heads x 66,304-byte tiles (dk 128, chunk 64)
-    assert rc == 0 and n == 3 * 2 * 66304
-    assert ws_size(T=1 << 20, N=1, H=32)[1] == ((1 << 20) // 64 + 2) * 32 * 66304
+    # (64 / 64 + 1 + 1) slots x 2 heads x 66,304-byte tiles (dk 128, chunk 64), then one fp32
+    # 128 x 128 state per (sequence, head) for the hand-over between chunk ranges
+    assert rc == 0 and n == 3 * 2 * 66304 + 1 * 2 * 128 * 128 * 4
+    assert ws_size(T=1 << 20, N=1, H=32)[1] == ((1 << 20) // 64 + 2) * 32 * 66304 + 32 * 128 * 128 * 4
     assert ws_size(dt=_lib.KDA_DTYPE_F32)[0] == 2
     assert ws_size(dk=96)[0] == 2
     assert ws_size(out=False)[0] == 1

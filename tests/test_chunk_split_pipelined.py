@@ -1,0 +1,53 @@
+"""kda_chunk_fwd_split on inputs with few (sequence, head) chains and long sequences, where
+the state pass runs over ranges of chunks beside the next range's in-chunk pass, against
+the fp64 oracle and against the fused kda_chunk_fwd.
+
+Shapes are chosen so that the state pass needs at most 128 workgroups (chains x dv/32)
+and the longest sequence has at least 128 chunks (two or more ranges).  Tolerances as in
+test_chunk_split: bf16 inputs, max |err| <= 2e-2 * RMS(ref) against the oracle, and
+max |diff| <= 1e-4 * RMS(ref) against the fused kernel.
+"""
+import pytest
+import torch
+
+import kda_inputs
+from test_chunk_parity import check_bf16
+from test_chunk_split import check_same, ref, run_fused, run_split
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("lens,H,dk,dv,C", [
+    ([16384], 4, 128, 128, 64),          # 256 chunks: four ranges of 64
+    ([9000, 3000, 70, 0], 2, 128, 128, 64),  # sequences ending in different ranges, one empty
+    ([5000, 4097], 3, 64, 64, 32),       # dk = dv = 64, chunk 32
+    ([8200], 8, 128, 64, 16),            # dv = 64, chunk 16: 513 chunks
+])
+def test_split_pipelined_against_oracle_and_fused(lens, H, dk, dv, C):
+    print("split pipelined: lens=%s H=%d dk=%d dv=%d C=%d" % (lens, H, dk, dv, C), flush=True)
+    inp = kda_inputs.make_custom_chunk_inputs(lens, H, dk, dv, torch.bfloat16, h0_std=0.02, seed=sum(lens) + H,
+                                              device="cuda")
+    o, hT = run_split(inp, chunk_size=C)
+    o_ref, h_ref = ref(inp)
+    check_bf16(o, hT, o_ref, h_ref)
+    of, hf = run_fused(inp, chunk_size=C)
+    check_same(o, of, o_ref, "o")
+    check_same(hT, hf, h_ref, "hT")
+
+
+def test_split_pipelined_final_state_in_place_and_absent():
+    """hT aliasing h0 (each chain reads h0 in the first range and writes hT in the range where it
+    ends), and hT not requested (the hand-over between ranges goes through the workspace)."""
+    import kimi_delta_attention_06_amd as kda
+    inp = kda_inputs.make_custom_chunk_inputs([12000, 600], 2, 128, 128, torch.bfloat16, h0_std=0.02, seed=41,
+                                              device="cuda")
+    o_ref, h_ref = ref(inp)
+    h = inp["h0"].clone()
+    o, _ = kda.chunk_fwd_split(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], h0=h,
+                               cu_seqlens=inp["cu_seqlens"], chunk_size=64, hT=h)
+    torch.cuda.synchronize()
+    check_bf16(o, h, o_ref, h_ref)
+    o2, _ = kda.chunk_fwd_split(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], h0=inp["h0"],
+                                cu_seqlens=inp["cu_seqlens"], chunk_size=64, output_final_state=False)
+    torch.cuda.synchronize()
+    check_same(o2, o, o_ref, "o")
