@@ -61,6 +61,17 @@
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
+// The host code below is in two parts, each built into its own object so that each
+// can take its own instruction-scheduling flags: the fused forward (every PREP = false
+// instantiation) and the split path (the in-chunk, pipelined and state passes).  A
+// plain compile builds both.
+#ifndef KDA_CHUNK_FUSED
+#define KDA_CHUNK_FUSED 1
+#endif
+#ifndef KDA_CHUNK_SPLIT
+#define KDA_CHUNK_SPLIT 1
+#endif
+
 namespace kda {
 namespace chunkk {
 
@@ -1540,6 +1551,7 @@ static hipError_t set_lds_limit(const void* kern, size_t lds, std::atomic<uint64
   return hipSuccess;
 }
 
+#if KDA_CHUNK_FUSED
 template <int C, int DK, int BV, Prec P, typename InT>
 static hipError_t launch_one(const ChunkArgs& a) {
   constexpr size_t lds = lds_bytes<C, DK, BV, P>();
@@ -1557,9 +1569,11 @@ static hipError_t launch_one(const ChunkArgs& a) {
   return hipGetLastError();
 }
 
+#endif  // KDA_CHUNK_FUSED
 static int pick_bv(int n_chains, int dv, int max_bv);
 
 // ---- split path: prep pass (intra-chunk operands to the workspace), then the state pass
+#if KDA_CHUNK_SPLIT
 template <int C, int DK>
 constexpr size_t split_tile_bytes() { return size_t(SLay<C, DK, 16>::NU) * 16; }
 
@@ -1680,6 +1694,7 @@ static hipError_t dispatch_split_bv(const ChunkArgs& a, void* ws, float* carry) 
   return launch_split<C, DK, 16, InT>(a, ws);
 }
 
+#endif  // KDA_CHUNK_SPLIT
 // value-tile width: the widest that still gives at least one workgroup per CU
 static int pick_bv(int n_chains, int dv, int max_bv) {
   for (int bv = max_bv; bv >= 16; bv /= 2)
@@ -1687,6 +1702,7 @@ static int pick_bv(int n_chains, int dv, int max_bv) {
   return 16;
 }
 
+#if KDA_CHUNK_FUSED
 template <int C, int DK, int MAXBV, Prec P, typename InT>
 static hipError_t dispatch_bv(const ChunkArgs& a) {
   const int bv = pick_bv(a.n_seqs * a.n_heads, a.dv, MAXBV);
@@ -1715,8 +1731,10 @@ static hipError_t dispatch_c(const ChunkArgs& a) {
   return hipErrorInvalidValue;
 }
 
+#endif  // KDA_CHUNK_FUSED
 }  // namespace chunkk
 
+#if KDA_CHUNK_FUSED
 bool chunk_fwd_supported(int dk, int dv, int chunk_size, bool bf16) {
   if (!((dk == 64 || dk == 128) && (dv == 64 || dv == 128))) return false;
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return false;
@@ -1724,6 +1742,9 @@ bool chunk_fwd_supported(int dk, int dv, int chunk_size, bool bf16) {
   return true;
 }
 
+#endif  // KDA_CHUNK_FUSED
+
+#if KDA_CHUNK_SPLIT
 // per-chunk tiles, then one fp32 state per chain for the pipelined path's hand-over between ranges
 static size_t split_tiles_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int chunk_size) {
   using namespace chunkk;
@@ -1760,6 +1781,9 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws) {
   return dispatch_split_bv<16, 64, bf16_t>(a, ws, carry);
 }
 
+#endif  // KDA_CHUNK_SPLIT
+
+#if KDA_CHUNK_FUSED
 hipError_t launch_chunk_fwd_f32(const ChunkArgs& a) {
   using namespace chunkk;
   if (a.chunk_size != 16 || !chunk_fwd_supported(a.dk, a.dv, 16, false)) return hipErrorInvalidValue;
@@ -1777,5 +1801,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a) {
   }
   return a.dk == 128 ? dispatch_c<128, Prec::F32, float>(a) : dispatch_c<64, Prec::F32, float>(a);
 }
+
+#endif  // KDA_CHUNK_FUSED
 
 }  // namespace kda
