@@ -12,7 +12,8 @@ variant (8 tokens, per-sequence commit counts) are timed and reported under
 1M-token sequence x 32 heads is timed, fused and split (kda_chunk_fwd_split), 1 warm-up + 5 timed
 launches each, and reported under "long_context"; and the
 fp64 CPU oracle is timed on a bounded sample of the chunk workload ("cpu_baseline").
-The backward pass (kda_bwd, chunkwise) on the Kimi-Linear layer is timed under "backward".
+The backward pass (kda_bwd, chunkwise) on the Kimi-Linear layer is timed under "backward", and
+the tiny fp32 and varlen packed chunked workloads under "other_workloads".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-long-context] [--copy-calibration]
 Prints exactly one JSON line on stdout.  --copy-calibration adds three launches of a
@@ -296,6 +297,26 @@ def main():
     log("backward (kda_bwd) on %s: %.3f ms/call, %.2f M tokens/s" % (w.name, b_ms, tokens / (b_ms * 1e-3) / 1e6))
     del b_do, b_ws
 
+    # ---------------- the other chunked workloads, timed as well ----------------
+    # tiny fp32 (256 tokens x 2 heads x 64 dims, chunk 16: launch-bound) and varlen packed
+    # (32,768 tokens in 8 sequences x 32 heads, nonzero h0)
+    other = {}
+    for ow in (kda_inputs.TINY_FP32, kda_inputs.VARLEN_PACKED):
+        o_inp = kda_inputs.make_chunk_inputs(ow, device=dev)
+        o_o = torch.empty(ow.total_tokens, ow.n_heads, ow.dv, dtype=torch.float32, device=dev)
+        o_h = torch.empty(ow.n_seqs, ow.n_heads, ow.dk, ow.dv, dtype=torch.float32, device=dev)
+
+        def ostep(o_inp=o_inp, o_o=o_o, o_h=o_h, ow=ow):
+            kda.chunk_fwd(o_inp["q"], o_inp["k"], o_inp["v"], o_inp["log_alpha"], o_inp["beta"], h0=o_inp["h0"],
+                          cu_seqlens=o_inp["cu_seqlens"], chunk_size=ow.chunk_size, o=o_o, hT=o_h)
+
+        o_ms = time_launches(ostep, 100, 20, stream)
+        o_bytes = ow.total_tokens * ow.n_heads * (3 * ow.dk * o_inp["q"].element_size() + 4 * ow.dk + 4 + 4 * ow.dv)
+        other[ow.name] = {"ms_per_step": round(o_ms, 5), "tokens_per_s": round(ow.total_tokens / (o_ms * 1e-3), 1),
+                          "algorithmic_GB/s": round(o_bytes / (o_ms * 1e-3) / 1e9, 1)}
+        log("%s: %.4f ms/launch, %.2f M tokens/s" % (ow.name, o_ms, ow.total_tokens / (o_ms * 1e-3) / 1e6))
+        del o_inp, o_o, o_h
+
     # ---------------- long context: one 1M-token sequence x 32 heads (32 chains) ----------------
     long_context = None
     if not args.no_long_context:
@@ -364,6 +385,7 @@ def main():
         "decode": decode,
         "long_context": long_context,
         "backward": backward,
+        "other_workloads": other,
         "wall_s_timed_region": round(t_wall, 3),
     }
     if args.copy_calibration:
