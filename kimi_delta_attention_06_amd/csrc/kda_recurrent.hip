@@ -18,128 +18,31 @@
 // after token c - 1 (not at all for c = 0); later tokens are drafts whose updates are
 // dropped.  Without counts, every token is committed.
 //
-// Two thread maps, chosen by the number of tokens per call:
-//
-// * rows16 (one token, or a short replay: state streaming): each wave owns 16
-//   value columns and all DK rows.  Lane l of wave w holds row group rg = l & 15
-//   (rows rg, rg + 16, ...) and columns [4 cg, 4 cg + 4) with cg = 4 w + (l >> 4),
-//   DV/16 waves per workgroup.  One state load instruction of a wave covers 16
-//   consecutive rows x 64 bytes.  A reduction over dk is in-lane over the lane's
-//   rows, then a DPP scan across the 16 lanes of a row and a DPP broadcast of lane 15.
-// * groups (longer replays, where the per-token vector work matters): a group of
-//   G = 8 consecutive lanes shares four value columns [4 cg, 4 cg + 4); lane rg of the
-//   group holds the DK / G contiguous key rows [rg DK/G, (rg + 1) DK/G) as float4s,
-//   DV/4 groups, 256 threads for DV = 128.  The per-row inputs are read from LDS as
-//   float4s, and a reduction is in-lane, then a 3-step DPP butterfly (quad swaps,
-//   half-row mirror) that leaves the sum in every lane of the group: about a quarter
-//   fewer vector instructions per token than rows16.
-//
-// In both, the reductions never leave the wave, so the token loop has no barrier,
-// and every HBM access of S is a float4 per lane.
+// Thread map: a group of G = 8 consecutive lanes shares four value columns
+// [4 cg, 4 cg + 4); lane rg of the group holds the DK / G contiguous key rows
+// [rg DK/G, (rg + 1) DK/G) as float4s, DV/4 groups (256 threads for DV = 128).  The
+// per-row inputs are read from LDS as float4s, and a reduction over dk is in-lane,
+// then a 3-step DPP butterfly (quad swaps, half-row mirror) that leaves the sum in
+// every lane of the group, so the token loop has no barrier.  Every HBM access of S is
+// a float4 per lane, read and written non-temporally: each state tile is touched once
+// per call, and streaming stores keep the written tiles from occupying the caches
+// (measured on 256 x 32 states of 128 x 128: 245 -> 215 us at 8 tokens).
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
 constexpr int kMaxReplay = 8;
-// Token counts up to this use the rows16 map, larger ones the groups map (measured on
-// the 256 x 32 x 128 x 128 decode workload: rows16 is faster up to 4 tokens, 3% slower
-// at 8 where the vector work no longer hides under the state traffic).
-constexpr int kRows16MaxTokens = 5;
 
-template <typename InT>
-__device__ __forceinline__ float ld_in(const InT* p, size_t i) {
-  return to_f32(p[i]);
+// State tiles are read once and written once per call: streaming (non-temporal) accesses.
+typedef float f32x4nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_state(const float* p) {
+  const f32x4nt x = __builtin_nontemporal_load(reinterpret_cast<const f32x4nt*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
 }
-
-template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(DV * 4) void recurrent_rows16_kernel(
-    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta, float* __restrict__ S,
-    float* __restrict__ o, const int32_t* __restrict__ n_commit, int n_tokens, int H) {
-  constexpr int NTH = DV * 4;  // DV/16 waves
-  constexpr int RPT = DK / 16;
-  static_assert(DV % 16 == 0 && DK % 16 == 0, "thread map");
-
-  __shared__ float s_q[kMaxReplay][DK];
-  __shared__ float s_k[kMaxReplay][DK];
-  __shared__ float s_a[kMaxReplay][DK];
-  __shared__ float s_v[kMaxReplay][DV];
-  __shared__ float s_b[kMaxReplay];
-  __shared__ float s_qk[kMaxReplay];
-
-  const int nh = blockIdx.x;  // sequence * H + head
-  const int n = nh / H, h = nh - n * H;
-  const int t = threadIdx.x;
-  const int lane = t % kWave, wave = t / kWave;
-  const int rg = lane & 15, cg = 4 * wave + (lane >> 4);
-
-  // tokens whose updates reach the stored state (clamped to [0, n_tokens])
-  int commit = n_tokens;
-  if (n_commit) commit = min(max(n_commit[n], 0), n_tokens);
-
-  float* Sp = S + (size_t)nh * DK * DV;
-  float4 st[RPT];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    st[i] = *reinterpret_cast<const float4*>(Sp + (size_t)(rg + 16 * i) * DV + cg * 4);
-
-  // Stage the token inputs (the state loads above are still in flight).
-  for (int idx = t; idx < n_tokens * DK; idx += NTH) {
-    const int tok = idx / DK, c = idx - tok * DK;
-    const size_t off = ((size_t)(n * n_tokens + tok) * H + h) * DK + c;
-    s_q[tok][c] = ld_in(q, off);
-    s_k[tok][c] = ld_in(k, off);
-    s_a[tok][c] = expf(log_alpha[off]);
-  }
-  for (int idx = t; idx < n_tokens * DV; idx += NTH) {
-    const int tok = idx / DV, j = idx - tok * DV;
-    s_v[tok][j] = ld_in(v, ((size_t)(n * n_tokens + tok) * H + h) * DV + j);
-  }
-  if (t < n_tokens) s_b[t] = beta[(size_t)(n * n_tokens + t) * H + h];
-  __syncthreads();
-  // q . k per token: wave w reduces tokens w, w + waves, ...
-  for (int tok = wave; tok < n_tokens; tok += NTH / kWave) {
-    float p = 0.f;
-    for (int c = lane; c < DK; c += kWave) p += s_q[tok][c] * s_k[tok][c];
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) p += wave_xor(p, m);
-    if (lane == 0) s_qk[tok] = p;
-  }
-  __syncthreads();
-
-  for (int tok = 0; tok < n_tokens; ++tok) {
-    float4 u = make_float4(0.f, 0.f, 0.f, 0.f), w = u;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + 16 * i;
-      const float a = s_a[tok][r], kr = s_k[tok][r], qr = s_q[tok][r];
-      st[i].x *= a; st[i].y *= a; st[i].z *= a; st[i].w *= a;
-      u.x += st[i].x * kr; u.y += st[i].y * kr; u.z += st[i].z * kr; u.w += st[i].w * kr;
-      w.x += st[i].x * qr; w.y += st[i].y * qr; w.z += st[i].z * qr; w.w += st[i].w * qr;
-    }
-    u.x = row_sum16(u.x); u.y = row_sum16(u.y); u.z = row_sum16(u.z); u.w = row_sum16(u.w);
-    w.x = row_sum16(w.x); w.y = row_sum16(w.y); w.z = row_sum16(w.z); w.w = row_sum16(w.w);
-    const float b = s_b[tok], qk = s_qk[tok];
-    const float4 vv = *reinterpret_cast<const float4*>(&s_v[tok][cg * 4]);
-    float4 d;
-    d.x = b * (vv.x - u.x); d.y = b * (vv.y - u.y); d.z = b * (vv.z - u.z); d.w = b * (vv.w - u.w);
-    if (rg == 0) {
-      float4 ot;
-      ot.x = w.x + qk * d.x; ot.y = w.y + qk * d.y; ot.z = w.z + qk * d.z; ot.w = w.w + qk * d.w;
-      *reinterpret_cast<float4*>(o + ((size_t)(n * n_tokens + tok) * H + h) * DV + cg * 4) = ot;
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const float kr = s_k[tok][rg + 16 * i];
-      st[i].x += kr * d.x; st[i].y += kr * d.y; st[i].z += kr * d.z; st[i].w += kr * d.w;
-    }
-    if (tok + 1 == commit) {
-#pragma unroll
-      for (int i = 0; i < RPT; ++i)
-        *reinterpret_cast<float4*>(Sp + (size_t)(rg + 16 * i) * DV + cg * 4) = st[i];
-    }
-  }
+__device__ __forceinline__ void st_state(float* p, const float4& v) {
+  const f32x4nt x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4nt*>(p));
 }
 
 template <int CTRL>
@@ -207,7 +110,7 @@ __global__ __launch_bounds__(DV / 4 * RG) void recurrent_group_kernel(
   float* Sp = S + (size_t)nh * DK * DV + (size_t)r0 * DV + cg * 4;
   float4 st[RPL];
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) st[i] = *reinterpret_cast<const float4*>(Sp + (size_t)i * DV);
+  for (int i = 0; i < RPL; ++i) st[i] = ld_state(Sp + (size_t)i * DV);
 
   // Stage the token inputs (the state loads above are still in flight).
   for (int idx = t; idx < n_tokens * (DK / VE); idx += NTH) {
@@ -279,7 +182,7 @@ __global__ __launch_bounds__(DV / 4 * RG) void recurrent_group_kernel(
     }
     if (tok + 1 == commit) {
 #pragma unroll
-      for (int i = 0; i < RPL; ++i) *reinterpret_cast<float4*>(Sp + (size_t)i * DV) = st[i];
+      for (int i = 0; i < RPL; ++i) st_state(Sp + (size_t)i * DV, st[i]);
     }
   }
 }
@@ -287,16 +190,10 @@ __global__ __launch_bounds__(DV / 4 * RG) void recurrent_group_kernel(
 template <int DK, int DV, typename InT>
 static hipError_t launch_rec(const RecurrentArgs& a) {
   const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_heads));
-  if (a.n_tokens <= kRows16MaxTokens) {
-    hipLaunchKernelGGL((recurrent_rows16_kernel<DK, DV, InT>), grid, dim3(DV * 4), 0, (hipStream_t)a.stream,
-                       (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, a.S, a.o,
-                       a.n_commit, a.n_tokens, a.n_heads);
-  } else {
-    constexpr int G = 8;
-    hipLaunchKernelGGL((recurrent_group_kernel<DK, DV, G, InT>), grid, dim3(DV / 4 * G), 0, (hipStream_t)a.stream,
-                       (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, a.S, a.o,
-                       a.n_commit, a.n_tokens, a.n_heads);
-  }
+  constexpr int G = 8;
+  hipLaunchKernelGGL((recurrent_group_kernel<DK, DV, G, InT>), grid, dim3(DV / 4 * G), 0, (hipStream_t)a.stream,
+                     (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, a.S, a.o, a.n_commit,
+                     a.n_tokens, a.n_heads);
   return hipGetLastError();
 }
 

@@ -4,8 +4,8 @@ Workload: 256 sequences x 32 heads, dk = dv = 128, fp32 state ~ N(0, 0.02^2),
 one decode token or a replay of 8 draft tokens, bf16 q/k/v (q, k unit-norm),
 per-channel log_alpha = -softplus(N(0,1)), beta = sigmoid(N(0,1)).
 Tolerance (bf16 inputs): max |err| <= 2e-2 * RMS(reference), for o and for the
-updated state separately; fp32 inputs: max |err| <= 1e-4.  Token counts up to 5 run
-the rows16 thread map and 6 to 8 the groups map, so both are covered on every shape.
+updated state separately; fp32 inputs: max |err| <= 1e-4.  Token counts 1, 3, 5, 6 and
+8 are covered on every (dk, dv) shape.
 """
 import numpy as np
 import pytest
