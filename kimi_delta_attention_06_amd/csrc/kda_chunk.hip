@@ -584,7 +584,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       } else {
         src = sGM + 4 * (i - (NU - NGM));
       }
-      dst[i] = *reinterpret_cast<const uint4*>(src);
+      // written once, read once by the state pass much later: a streaming store
+      typedef unsigned int u32x4w __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4w*>(src), reinterpret_cast<u32x4w*>(dst) + i);
     }
   };
   auto store_pending = [&]() {
@@ -1492,8 +1494,9 @@ __device__ __forceinline__ void chunk_state_body(
         const int r = 16 * R + lr;
         if (r < Lc) {
           float* op = o + ((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + 4 * lg;
-          *reinterpret_cast<float4*>(op) = make_float4(Oacc[s][0] + dq * Uacc[s][0], Oacc[s][1] + dq * Uacc[s][1],
-                                                       Oacc[s][2] + dq * Uacc[s][2], Oacc[s][3] + dq * Uacc[s][3]);
+          __builtin_nontemporal_store(f32x4{Oacc[s][0] + dq * Uacc[s][0], Oacc[s][1] + dq * Uacc[s][1],
+                                            Oacc[s][2] + dq * Uacc[s][2], Oacc[s][3] + dq * Uacc[s][3]},
+                                      reinterpret_cast<f32x4*>(op));
         }
       }
     });
