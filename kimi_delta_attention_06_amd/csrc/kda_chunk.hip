@@ -546,7 +546,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   f32x4 Opend[U_SLOTS];
   int64_t o_begin = 0;
   int o_len = 0;
-  // the fp32 master state of this value tile into a [DK][DV] row-major state (streaming stores)
+  // the fp32 master state of this value tile into a [DK][DV] row-major state
   auto store_state = [&](float* sp) {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
@@ -554,8 +554,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_nontemporal_store(Sacc[s][i], &sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr]);
+        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
       }
     }
   };
@@ -601,9 +600,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         // lane (token lr, column group lg) holds o[16R + lr][16j + 4lg .. +3]
         const int r = 16 * R + lr;
         const uint32_t off = ((uint32_t)r * hdv + (uint32_t)(16 * j + 4 * lg)) * 4u;
-        if (r < o_len)  // written once, read by no later stage: a streaming store
-          __builtin_nontemporal_store(f32x4{Opend[s][0], Opend[s][1], Opend[s][2], Opend[s][3]},
-                                      reinterpret_cast<f32x4*>(ob + off));
+        if (r < o_len)
+          *reinterpret_cast<float4*>(ob + off) = make_float4(Opend[s][0], Opend[s][1], Opend[s][2], Opend[s][3]);
       }
     }
   };
