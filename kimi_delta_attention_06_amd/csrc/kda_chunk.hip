@@ -1492,9 +1492,8 @@ __device__ __forceinline__ void chunk_state_body(
         const int r = 16 * R + lr;
         if (r < Lc) {
           float* op = o + ((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + 4 * lg;
-          __builtin_nontemporal_store(f32x4{Oacc[s][0] + dq * Uacc[s][0], Oacc[s][1] + dq * Uacc[s][1],
-                                            Oacc[s][2] + dq * Uacc[s][2], Oacc[s][3] + dq * Uacc[s][3]},
-                                      reinterpret_cast<f32x4*>(op));
+          *reinterpret_cast<float4*>(op) = make_float4(Oacc[s][0] + dq * Uacc[s][0], Oacc[s][1] + dq * Uacc[s][1],
+                                                       Oacc[s][2] + dq * Uacc[s][2], Oacc[s][3] + dq * Uacc[s][3]);
         }
       }
     });
