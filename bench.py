@@ -45,20 +45,26 @@ BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 512
 FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_kimi_linear_layer_pmc.txt")
 SQ_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_kimi_linear_layer_sq_counters.txt")
-CHUNK_SRC = os.path.join(ROOT, "kimi_delta_attention_06_amd", "csrc", "kda_chunk.hip")
+# the chunk kernel's code is fixed by its source and by the compiler flags the build gives it
+CHUNK_BUILD_FILES = [os.path.join(ROOT, "kimi_delta_attention_06_amd", "csrc", "kda_chunk.hip"),
+                     os.path.join(ROOT, "kimi_delta_attention_06_amd", "build.py")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def build_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def profile_value(path, key):
-    """A figure from a rocprofv3 counter summary, if it was taken on the current kernel source, else None."""
+    """A figure from a rocprofv3 counter summary, if it was taken on the current kernel source and build
+    flags, else None."""
     if not os.path.exists(path):
         return None
     vals = {}
@@ -67,7 +73,7 @@ def profile_value(path, key):
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != src_hash(CHUNK_SRC):
+    if vals.get("kernel_build_sha256_16") != build_hash(CHUNK_BUILD_FILES):
         return None
     try:
         return float(vals[key])
@@ -76,7 +82,7 @@ def profile_value(path, key):
 
 
 def traffic_from_profile():
-    """HBM bytes per launch measured by rocprofv3 counters for the current kernel source, else None."""
+    """HBM bytes per launch measured by rocprofv3 counters for the current kernel build, else None."""
     return profile_value(PMC_SUMMARY, "hbm_bytes_per_launch")
 
 

@@ -37,7 +37,11 @@
  * stream is synchronised.  Argument errors are detected on the host before any
  * launch and return a status with no side effects.  A launch failure reported
  * by the HIP runtime returns KDA_ERR_LAUNCH.  Nothing is printed and no C++
- * exception crosses this interface.
+ * exception crosses this interface.  The fused chunked-forward kernels
+ * (kda_chunk_fwd, kda_chunk_fwd_checkpointed, the forward launch inside kda_bwd,
+ * and kda_chunk_fwd_split on zero tokens) are built for XNACK off, the MI355X
+ * default; in a process with XNACK on they do not load and those calls return
+ * KDA_ERR_LAUNCH.
  */
 #ifndef KDA_H_
 #define KDA_H_
