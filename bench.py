@@ -178,7 +178,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
