@@ -180,3 +180,49 @@ def make_custom_chunk_inputs(lens, n_heads, dk, dv, dtype=torch.bfloat16, gate_s
         h0 = h0_std * torch.randn(len(lens), n_heads, dk, dv, generator=gen, device=device, dtype=torch.float32)
     return dict(q=q, k=k, v=v, log_alpha=la, beta=be, h0=h0,
                 cu_seqlens=torch.from_numpy(cu).to(device), lens=lens, seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# Adversarial inputs for edge-case tests (input construction only)
+# ---------------------------------------------------------------------------
+
+ADVERSARIAL_KINDS = ("wide_decay", "large_values", "small_values", "parallel_keys")
+
+
+def make_adversarial_chunk_inputs(kind: str, lens, n_heads, dk, dv, dtype=torch.bfloat16, seed=0,
+                                  device="cpu") -> dict:
+    """Draws as make_custom_chunk_inputs (h0 ~ N(0, 0.02^2)), then changes one aspect:
+
+    * wide_decay: log_alpha = -30 on the first third of the key channels (480 nats per 16 tokens:
+      the channel forgets everything every token) and exactly 0 on the second third;
+    * large_values: v ~ N(0, 2500^2) before the cast (|v| up to about 1e4) and h0 ~ N(0, 300^2);
+    * small_values: v ~ N(0, 1e-10) before the cast and h0 ~ N(0, 1e-14) (magnitudes near 1e-5
+      and 1e-7, below fp16's normal range);
+    * parallel_keys: beta = 1, and the keys of every 8 consecutive tokens are one unit direction
+      plus noise of 1e-3 per coordinate (renormalised), with every other key an exact repeat of
+      the one before.
+    """
+    if kind not in ADVERSARIAL_KINDS:
+        raise ValueError("unknown kind %r" % kind)
+    inp = make_custom_chunk_inputs(lens, n_heads, dk, dv, dtype=dtype, h0_std=0.02, seed=seed, device=device)
+    T = int(inp["cu_seqlens"][-1])
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 7919)
+    f32 = torch.float32
+    if kind == "wide_decay":
+        third = dk // 3
+        inp["log_alpha"][:, :, :third] = -30.0
+        inp["log_alpha"][:, :, third:2 * third] = 0.0
+    elif kind in ("large_values", "small_values"):
+        vs, hs = (2500.0, 300.0) if kind == "large_values" else (1e-5, 1e-7)
+        inp["v"] = (vs * torch.randn(T, n_heads, dv, generator=gen, device=device, dtype=f32)).to(dtype)
+        inp["h0"] = hs * torch.randn(len(lens), n_heads, dk, dv, generator=gen, device=device, dtype=f32)
+    else:
+        n_dir = (T + 7) // 8
+        base = torch.randn(n_dir, n_heads, dk, generator=gen, device=device, dtype=f32)
+        base = _unit_rows(base).repeat_interleave(8, dim=0)[:T]
+        k = _unit_rows(base + 1e-3 * torch.randn(T, n_heads, dk, generator=gen, device=device, dtype=f32))
+        k[1::2] = k[0::2][: k[1::2].shape[0]]
+        inp["k"] = k.to(dtype)
+        inp["beta"] = torch.ones(T, n_heads, device=device, dtype=f32)
+    return inp

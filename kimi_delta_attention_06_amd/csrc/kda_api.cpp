@@ -13,6 +13,17 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool dims_ok(int32_t d) { return d == 64 || d == 128; }
 
+// a byte range of one buffer (n == 0: absent)
+struct Range {
+  const void* p;
+  size_t n;
+};
+bool overlap(const Range& a, const Range& b) {
+  const char* pa = (const char*)a.p;
+  const char* pb = (const char*)b.p;
+  return a.n && b.n && pa < pb + b.n && pb < pa + a.n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,6 +84,19 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
       const char* b = (const char*)r.p;
       if (b < oe && ob < b + r.n) return KDA_ERR_INVALID_ARGUMENT;
     }
+  }
+  // hT is an output: it must not overlap o or an input, except that it may be h0 itself
+  // (in-place advance: every workgroup reads its h0 tile before it writes that hT tile)
+  if (hT && n_seqs > 0) {
+    const size_t esz = qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const size_t T = (size_t)total_tokens, Hh = (size_t)n_heads;
+    const Range h{hT, (size_t)n_seqs * n_heads * dk * dv * sizeof(float)};
+    const Range others[] = {{q, T * Hh * dk * esz}, {k, T * Hh * dk * esz}, {v, T * Hh * dv * esz},
+                            {log_alpha, T * Hh * dk * 4}, {beta, T * Hh * 4}, {o, T * Hh * dv * 4},
+                            {cu_seqlens, cu_seqlens ? (size_t)(n_seqs + 1) * 4 : 0},
+                            {h0 == hT ? nullptr : h0, h0 && h0 != hT ? h.n : 0}};
+    for (const Range& r : others)
+      if (overlap(h, r)) return KDA_ERR_INVALID_ARGUMENT;
   }
   if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // cu_seqlens is int32
   if ((int64_t)n_seqs * n_heads * 8 > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // grid: chains x value tiles
@@ -269,6 +293,17 @@ static kda_status recurrent_common(const void* q, const void* k, const void* v, 
   if (!dims_ok(dk) || !dims_ok(dv) || n_tokens > 8) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)n_seqs * n_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   if (n_seqs == 0) return KDA_OK;
+  // the state is read and written in place: it must not overlap the token inputs or the commit
+  // counts (o is checked below)
+  {
+    const size_t ntok = (size_t)n_seqs * n_tokens * n_heads;
+    const size_t esz = qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const Range st{S_inout, (size_t)n_seqs * n_heads * dk * dv * 4};
+    const Range ins[] = {{q, ntok * dk * esz}, {k, ntok * dk * esz}, {v, ntok * dv * esz}, {log_alpha, ntok * dk * 4},
+                         {beta, ntok * 4}, {n_commit, n_commit ? (size_t)n_seqs * 4 : 0}};
+    for (const Range& r : ins)
+      if (overlap(st, r)) return KDA_ERR_INVALID_ARGUMENT;
+  }
   // o must not overlap the state, the token inputs or the commit counts
   {
     const bool bf16 = qkv_dtype == KDA_DTYPE_BF16;
@@ -319,6 +354,6 @@ const char* kda_status_string(kda_status s) {
   return "KDA_ERR_UNKNOWN";
 }
 
-int32_t kda_version(void) { return 110; }
+int32_t kda_version(void) { return 10200; }
 
 }  // extern "C"

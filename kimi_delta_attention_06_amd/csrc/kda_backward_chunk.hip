@@ -34,8 +34,9 @@
 //
 // Decay balancing.  Gram products take their decay from the chunk midpoint m = g_L / 2:
 // left operands x_i e^{g_i - m}, right operands k_j e^{m - g_j}, each at most e^{|g_L|/2},
-// so a 16-token chunk may decay by up to ~120 nats per channel before the fp32
-// operands (times the values they scale) overflow.
+// on the matrix core.  A chunk that decays by more than 64 nats in some channel (where those
+// operands, times the values they scale, could leave the fp32 range) forms the Gram terms from
+// per-element factors e^{g_i - g_j} <= 1 instead, so any finite log a is taken.
 //
 // Three launches: (1) the forward chunk kernel in fp32 stores the state entering every
 // chunk (its checkpoint output at a 16-token spacing); (2) `bwd_ds_kernel` walks each
@@ -174,34 +175,65 @@ struct Intra {
     if (threadIdx.x < C) b[threadIdx.x] = (int)threadIdx.x < Lc ? bp[(size_t)(t0 + threadIdx.x) * H + h] : 0.f;
   }
 
-  // prefix sum of log a over the rows (one thread per channel) and e^{g_L}
-  __device__ void prefix() {
+  // Prefix sum of log a over the rows (one thread per channel) and e^{g_L}.  Each step is
+  // floored at -110 nats: e^{-110} is 0 in fp32 like e^{x} for every x below it, so the floor
+  // changes nothing an fp32 evaluation can represent, the sums stay finite for any finite log a,
+  // and differences of nearby sums keep their precision.  Returns true for a channel whose
+  // chunk decays by more than kBalancedNats.
+  static constexpr float kBalancedNats = 64.f;
+  __device__ bool prefix() {
     const int c = threadIdx.x;
+    bool wide = false;
     if (c < DK) {
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < C; ++i) {
-        s += g[i * LDK + c];
+        const float x = g[i * LDK + c];
+        s += x < -110.f ? -110.f : x;  // (a NaN stays NaN)
         g[i * LDK + c] = s;
       }
       el[c] = expf(s);
+      wide = !(s >= -kBalancedNats);
     }
+    return wide;
   }
 
-  // decay-scaled operands, every element
-  __device__ void scale() {
+  // Decay-scaled operands, every element.  `exact` (a chunk decaying by more than kBalancedNats
+  // in some channel): the midpoint-balanced Gram operands ql, kl, kr would overflow, so they are
+  // not formed and the Gram terms take their per-element factors instead (gram_exact and the
+  // exact branch of the gradient pass).
+  __device__ void scale(bool exact) {
     for (int e = threadIdx.x; e < C * DK; e += NT) {
       const int i = e / DK, c = e - i * DK, o = i * LDK + c;
       const float gi = g[o], gl = g[(C - 1) * LDK + c], m = 0.5f * gl;
-      const float e1 = expf(gi - m), e2 = expf(m - gi), eg = expf(gi), ec = expf(gl - gi);
+      const float eg = expf(gi), ec = expf(gl - gi);
       const float qv = q[o], kv = k[o];
-      ql[o] = qv * e1;
-      kl[o] = kv * e1;
-      kr[o] = kv * e2;
+      if (!exact) {
+        const float e1 = expf(gi - m), e2 = expf(m - gi);
+        ql[o] = qv * e1;
+        kl[o] = kv * e1;
+        kr[o] = kv * e2;
+      }
       qg[o] = qv * eg;
       kg[o] = kv * eg;
       kc[o] = kv * ec;
     }
+  }
+
+  // A and M from per-element decay factors e^{g_ic - g_jc} <= 1 (j <= i): one thread per
+  // (i, j) pair, threads 0 .. 255
+  __device__ void gram_exact() {
+    const int t = threadIdx.x, i = t >> 4, j = t & 15;
+    float a = 0.f, m = 0.f;
+    if (j <= i) {
+      for (int c = 0; c < DK; ++c) {
+        const float kj = k[j * LDK + c] * expf(fminf(g[i * LDK + c] - g[j * LDK + c], 0.f));
+        a = fmaf(k[i * LDK + c], kj, a);
+        m = fmaf(q[i * LDK + c], kj, m);
+      }
+    }
+    A[i * LDC + j] = j < i ? a : 0.f;
+    M[i * LDC + j] = m;
   }
 
   // wave 0: A (strictly lower), wave 1: M (lower with the diagonal)
@@ -361,11 +393,14 @@ __global__ __launch_bounds__(NT) void bwd_ds_kernel(const InT* __restrict__ q, c
       }
     }
     __syncthreads();
-    in.prefix();
+    const bool exact = __syncthreads_or(in.prefix());
+    in.scale(exact);
     __syncthreads();
-    in.scale();
-    __syncthreads();
-    if (w < 2) in.gram(w);
+    if (exact) {
+      if (w < 4) in.gram_exact();
+    } else if (w < 2) {
+      in.gram(w);
+    }
     {  // partial Kc dS' over one k-range: job w = (v-tile w % NVT, k-range w / NVT)
       const int vt = w % NVT, kq = w / NVT;
       f32x4 acc = zero4();
@@ -499,11 +534,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     *reinterpret_cast<float4*>(sDO + i * LDO + c) = x;
   }
   __syncthreads();
-  in.prefix();
+  const bool exact = __syncthreads_or(in.prefix());
+  in.scale(exact);
   __syncthreads();
-  in.scale();
-  __syncthreads();
-  if (w < 2) in.gram(w);
+  if (exact) {
+    if (w < 4) in.gram_exact();
+  } else if (w < 2) {
+    in.gram(w);
+  }
   __syncthreads();
   if (w == 0) in.inverse();
 
@@ -635,18 +673,56 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   float* sKCT = sD;  // [C][LDK]: k dKc e^{g_L - g}
   if (w < NCT) {
     const int ct = w;
-    f32x4 P = zero4(), R = zero4(), Pp = zero4(), Rp = zero4();
-    mma<1, LDC, 1, 1, LDK>(P, sDM, in.kr + 16 * ct);
-    mma<1, 1, LDC, 1, LDK>(R, sDM, in.ql + 16 * ct);
-    mma<1, LDC, 1, 1, LDK>(Pp, sDA, in.kr + 16 * ct);
-    mma<1, 1, LDC, 1, LDK>(Rp, sDA, in.kl + 16 * ct);
+    // Gram terms through the decay: P = (dM o E) K, R = (dM o E)^T Q, P' = (dA o E) K,
+    // R' = (dA o E)^T K, on the matrix core from the balanced operands, or per element
+    float pfa[4], rfa[4], ppfa[4], rpfa[4];
+    if (!exact) {
+      f32x4 P = zero4(), R = zero4(), Pp = zero4(), Rp = zero4();
+      mma<1, LDC, 1, 1, LDK>(P, sDM, in.kr + 16 * ct);
+      mma<1, 1, LDC, 1, LDK>(R, sDM, in.ql + 16 * ct);
+      mma<1, LDC, 1, 1, LDK>(Pp, sDA, in.kr + 16 * ct);
+      mma<1, 1, LDC, 1, LDK>(Rp, sDA, in.kl + 16 * ct);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * (l >> 4) + r, c = 16 * ct + (l & 15), o = i * LDK + c;
+        const float gi = in.g[o], m = 0.5f * in.g[(C - 1) * LDK + c];
+        const float e1 = expf(gi - m), e2 = expf(m - gi);
+        pfa[r] = e1 * P[r];
+        rfa[r] = e2 * R[r];
+        ppfa[r] = e1 * Pp[r];
+        rpfa[r] = e2 * Rp[r];
+      }
+    } else {
+      // dM is lower and dA strictly lower, so the factor of every entry they keep is <= 1 (the
+      // exponent is clamped at 0 where they are zero, so no inf meets a zero)
+      const int c = 16 * ct + (l & 15);
+      float gi[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        gi[r] = in.g[(4 * (l >> 4) + r) * LDK + c];
+        pfa[r] = rfa[r] = ppfa[r] = rpfa[r] = 0.f;
+      }
+      for (int y = 0; y < C; ++y) {
+        const float gy = in.g[y * LDK + c], ky = in.k[y * LDK + c], qy = in.q[y * LDK + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * (l >> 4) + r;
+          const float ef = expf(fminf(gi[r] - gy, 0.f)) * ky;  // row i, column y <= i
+          const float eb = expf(fminf(gy - gi[r], 0.f));       // row y >= i, column i
+          pfa[r] = fmaf(sDM[i * LDC + y], ef, pfa[r]);
+          ppfa[r] = fmaf(sDA[i * LDC + y], ef, ppfa[r]);
+          rfa[r] = fmaf(sDM[y * LDC + i] * eb, qy, rfa[r]);
+          rpfa[r] = fmaf(sDA[y * LDC + i] * eb, ky, rpfa[r]);
+        }
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * (l >> 4) + r, c = 16 * ct + (l & 15), o = i * LDK + c;
-      const float gi = in.g[o], gl = in.g[(C - 1) * LDK + c], m = 0.5f * gl;
-      const float e1 = expf(gi - m), e2 = expf(m - gi), eg = expf(gi), ec = expf(gl - gi);
+      const float gi = in.g[o], gl = in.g[(C - 1) * LDK + c];
+      const float eg = expf(gi), ec = expf(gl - gi);
       const float qv = in.q[o], kv = in.k[o];
-      const float pf = e1 * P[r], rf = e2 * R[r], ppf = e1 * Pp[r], rpf = e2 * Rp[r];
+      const float pf = pfa[r], rf = rfa[r], ppf = ppfa[r], rpf = rpfa[r];
       const float dqg = aQ[r], dkg = -aK[r], dkc = aC[r];
       const float dqv = dqg * eg + pf;
       const float dkv = dkg * eg + dkc * ec + rf + ppf + rpf;

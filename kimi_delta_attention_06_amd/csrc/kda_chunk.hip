@@ -176,6 +176,93 @@ __device__ __forceinline__ float scan16(float x) {
 constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
+// In log2 units: the balanced factors of a diagonal 16-token sub-block stay finite in fp32
+// while the block decays by at most 160 nats in every channel (see the gate stage).
+constexpr float kBalancedLimit = -230.83f;  // -160 nats
+// Per-token decay floor for the exact path, log2 units (about -111 nats): 2^-160 is 0 in fp32,
+// like 2^x for every x below it, so the floor changes nothing an fp32 recurrence can represent;
+// it keeps sums of 16 steps finite for any finite log alpha, and small enough that differences
+// of nearby sums keep their precision.
+constexpr float kStepFloor = -160.f;
+
+// Exact diagonal Gram sub-block for one channel part, for blocks whose decay is too wide for
+// the balanced factorisation.  Lane (column token i = lr, channel group lg) holds its token's q,
+// k and in-block cumulative decay cx (log2 units) for GC channels; every entry
+// X[r][i] = sum_c x_rc k_ic 2^{cx_rc - cx_ic} (i <= r) has a factor <= 1.  Row r's values come
+// from lane r of the same 16-lane row (same channels) by a DPP broadcast; the four channel
+// groups are then summed across rows, and each lane adds rows 4 lg .. 4 lg + 3 of column lr to
+// its accumulators (the 16x16 MFMA accumulator layout).  Rows go in two halves of 8 to bound
+// the live registers.
+template <int GC>
+__device__ __forceinline__ void gram_exact(const float* q, const float* k, const float* cx, int lr, int lg,
+                                           f32x4& accM, f32x4& accA) {
+  static_for<0, 2>([&](auto hc) {
+    constexpr int r0 = 8 * decltype(hc)::value;
+    float pm[8], pa[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pm[r] = pa[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GC; ++j) {
+      const float ci = cx[j], ki = k[j];
+      static_for<0, 8>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const float cr = row_bcast16<r0 + r>(cx[j]);
+        const float qr = row_bcast16<r0 + r>(q[j]);
+        const float kr = row_bcast16<r0 + r>(k[j]);
+        // r == lr gives cr - ci = 0 exactly; entries above the diagonal are selected away
+        const float t = (r0 + r >= lr) ? ki * __builtin_amdgcn_exp2f(cr - ci) : 0.f;
+        pm[r] = fmaf(qr, t, pm[r]);
+        pa[r] = fmaf(kr, t, pa[r]);
+      });
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      pm[r] += __shfl_xor(pm[r], 16, kWave);
+      pm[r] += __shfl_xor(pm[r], 32, kWave);
+      pa[r] += __shfl_xor(pa[r], 16, kWave);
+      pa[r] += __shfl_xor(pa[r], 32, kWave);
+    }
+    // lanes of groups 2 hc and 2 hc + 1 own rows r0 .. r0 + 3 and r0 + 4 .. r0 + 7
+    const bool lo = lg == 2 * decltype(hc)::value, hi = lg == 2 * decltype(hc)::value + 1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      accM[u] += lo ? pm[u] : (hi ? pm[4 + u] : 0.f);
+      accA[u] += lo ? pa[u] : (hi ? pa[4 + u] : 0.f);
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Range of the 16-bit state-step operands.  The state S and the values V enter the fp16
+// matrix products of a chunk (Y = V - Kg S, U = T Diag(b) Y, O = Qg S + M U, S' = g S + Kd^T U),
+// all linear in (V, S) jointly; a chunk whose largest |S| or |V| is outside [2^-6, 2^6) is
+// computed on copies scaled by a power of two 2^-e that brings it into [2^4, 2^5), and its o
+// and state update are scaled back by 2^e (exact in fp32).  So any finite v and h0 are taken,
+// and tiny ones keep their precision instead of flushing in fp16.
+// ---------------------------------------------------------------------------
+// |x| as a bit pattern: ordered like the magnitudes (NaN above inf above every finite value)
+__device__ __forceinline__ uint32_t mag_bits(float x) { return __float_as_uint(x) << 1; }
+// largest of the wave's lanes (each lane's value >= 0 as an unsigned pattern)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  const uint32_t a = __builtin_amdgcn_readlane(x, 15), b = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 47), d = __builtin_amdgcn_readlane(x, 63);
+  return max(max(a, b), max(c, d));
+}
+// Scale exponent e for a chunk whose largest magnitude has the pattern m (mag_bits): 0 inside
+// [2^-6, 2^6), for zero, inf and NaN (which then propagate unchanged); otherwise the scaled
+// largest magnitude lands in [2^4, 2^5), with 2^e and 2^-e kept normal.
+__device__ __forceinline__ int range_exponent(uint32_t m) {
+  const int E = (int)(m >> 24);  // biased exponent
+  if (m == 0 || E == 255 || (E >= 127 - 6 && E < 127 + 6)) return 0;
+  const int e = E - 127 - 4;
+  return e < -125 ? -125 : (e > 125 ? 125 : e);
+}
+__device__ __forceinline__ float pow2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
 // ---------------------------------------------------------------------------
 // LDS layout (bytes).  Regions with disjoint lifetimes share memory:
 //   RB (gate stage -> off-diagonal Gram) with YT (T stage -> U),
@@ -204,9 +291,10 @@ struct Lay {
   static constexpr size_t BE = AO + al16(size_t(NPAIR) * 16 * AOR * 4);   // beta [C]
   static constexpr size_t DQ = BE + al16(size_t(C) * 4);                  // q_r . k_r [C]
   static constexpr size_t GM = DQ + al16(size_t(C) * 4);                  // e^{g_last} [DK]
+  static constexpr size_t MX = GM + al16(size_t(DK) * 4);                 // per-wave largest magnitude [NW]
   // per chunk
   static constexpr int LDV = BV + PD;                   // [C][BV] rows (value columns)
-  static constexpr size_t QG = GM + al16(size_t(DK) * 4);                 // Qg [C][LDD]
+  static constexpr size_t QG = MX + al16(size_t(NW) * 4);                 // Qg [C][LDD]
   static constexpr size_t KG = QG + al16(size_t(C) * LDD * sizeof(T));    // Kg [C][LDD]
   static constexpr size_t KDT = KG + al16(size_t(C) * LDD * sizeof(T));   // Kd^T [DK][LDC]
   static constexpr size_t VR = KDT + al16(size_t(DK) * LDC * sizeof(T));  // V [C][LDV]
@@ -364,6 +452,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   float* sBE = reinterpret_cast<float*>(smem + L::BE);
   float* sDQ = reinterpret_cast<float*>(smem + L::DQ);
   float* sGM = reinterpret_cast<float*>(smem + L::GM);
+  uint32_t* sMX = reinterpret_cast<uint32_t*>(smem + L::MX);
   T* sQG = reinterpret_cast<T*>(smem + L::QG);
   T* sKG = reinterpret_cast<T*>(smem + L::KG);
   T* sKDT = reinterpret_cast<T*>(smem + L::KDT);
@@ -441,17 +530,36 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr];
     }
   }
-  auto write_ST = [&]() {
+  // The 16-bit copy of the state for the chunk's products, scaled by f (2^-e of the chunk's
+  // range exponent; exactly 1 unless the chunk is out of range, then the branch is taken)
+  auto write_ST = [&](auto scaled, float f) {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
-        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
+        f32x4 x = Sacc[s];
+        if constexpr (decltype(scaled)::value) x *= f;
+        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, x[0], x[1], x[2], x[3]);
       }
     }
   };
-  if constexpr (!PREP) write_ST();
+  // Range exponent of the chunk in flight (16-bit operands only; see range_exponent).
+  constexpr bool kRanged = P == Prec::Mixed && !PREP;
+  int sc_e = 0;
+  // largest |v| of this thread's values of the next chunk, as a mag_bits pattern
+  uint32_t v_mag = 0;
+  auto publish_range = [&]() {
+    if constexpr (kRanged) {
+      uint32_t m = v_mag;
+#pragma unroll
+      for (int s = 0; s < S_SLOTS; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, mag_bits(Sacc[s][i]));
+      m = wave_max_u32(m);
+      if (lane_id() == 0) sMX[wave0] = m;
+    }
+  };
 
   // ---- gate-stage map: waves (R = wave/2, p = wave%2) for 2*NB waves
   const bool e_act = 2 * NB >= NW || wave0 < 2 * NB;
@@ -498,6 +606,22 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   };
   GR gbuf;
   VR vbuf;
+  uint4 vkeep[VR::VW];
+#pragma unroll
+  for (int i = 0; i < VR::VW; ++i) vkeep[i] = make_uint4(0, 0, 0, 0);
+  // the chunk's values (held in vkeep) to LDS in the operand type, scaled like write_ST
+  auto write_V = [&](auto scaled, float f) {
+    if (!PREP && v_act) {
+      float vv[8];
+      unpack<InT>(vkeep, vv, 8);
+      if constexpr (decltype(scaled)::value) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vv[i] *= f;
+      }
+      store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
+      store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
+    }
+  };
   // The next chunk's inputs are loaded in four groups (q; k; the log-decay; v and beta),
   // issued in different stages: every CU runs the same stage at about the same time, and
   // one large group per chunk would be a device-wide burst that saturates HBM and stalls
@@ -671,11 +795,49 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       // When every channel of this part decays by less than 8 nats over the block, the
       // balanced operands stay within e^{+-4} of the inputs and fp16 represents them as
       // well as the off-diagonal operands; otherwise the part's diagonal products take
-      // the wide path.  The vote is wave-uniform.
+      // the wide path, and past 160 nats (where the balanced factors would overflow) the
+      // exact path.  The votes are wave-uniform.
       float smin = ss[0];
 #pragma unroll
       for (int j = 1; j < GC; ++j) smin = fminf(smin, ss[j]);
       [[maybe_unused]] const bool fast16 = __builtin_amdgcn_ballot_w64(!(smin > -11.5415603f)) == 0;  // 8 nats in log2 units
+      if (__builtin_amdgcn_ballot_w64(!(smin > kBalancedLimit)) != 0) {
+        // Exact path.  Operands referenced to the block start instead of its middle:
+        //   left q e^{c}, k e^{c} (<= 1), right base k e^{s - c} (<= 1), diagonal Gram from
+        //   per-element factors.  The block's own factor in the chunk tables is then 1, which
+        //   the stored decay e^{s} says by its sign bit (stored negated; -0 when it underflows).
+        float cx[GC];
+#pragma unroll
+        for (int j = 0; j < GC; ++j) {
+          const float x = la[j] * 1.4426950408889634f;
+          cx[j] = x < kStepFloor ? kStepFloor : x;  // (a NaN stays NaN)
+        }
+#pragma unroll
+        for (int j = 0; j < GC; ++j) cx[j] += shr16<1>(cx[j]);
+#pragma unroll
+        for (int j = 0; j < GC; ++j) cx[j] += shr16<2>(cx[j]);
+#pragma unroll
+        for (int j = 0; j < GC; ++j) cx[j] += shr16<4>(cx[j]);
+#pragma unroll
+        for (int j = 0; j < GC; ++j) cx[j] += shr16<8>(cx[j]);
+        gram_exact<GC>(qh_, kh_, cx, lr, lg, accQd, accKd);
+#pragma unroll
+        for (int j = 0; j < GC; ++j) {
+          const float sx = row_bcast16<15>(cx[j]);
+          const float eq = __builtin_amdgcn_exp2f(cx[j]);
+          const float kk = kh_[j];
+          qh_[j] *= eq;
+          kh_[j] = kk * eq;
+          rh_[j] = kk * __builtin_amdgcn_exp2f(sx - cx[j]);
+          bh_[j] = rh_[j];
+          ss[j] = -__builtin_amdgcn_exp2f(sx);
+        }
+        if (lr == 15) {
+#pragma unroll
+          for (int j = 0; j < GC; j += 4) store4(sBH + eR * DK + e_cb + j, ss[j], ss[j + 1], ss[j + 2], ss[j + 3]);
+        }
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < GC; ++j) {
         const float x = cc[j] - 0.5f * ss[j];
@@ -745,10 +907,25 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     v_c0 = 8 * (tid % VPR);
     const int eR = e_act ? row_block_of<NB>(wave) : 0;
     if (!PREP && v_act) {
-      float vv[8];
-      unpack<InT>(vbuf.v, vv, 8);
-      store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
-      store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
+      // the next chunk's values wait in registers until its range exponent is known (write_V)
+#pragma unroll
+      for (int i = 0; i < VR::VW; ++i) vkeep[i] = vbuf.v[i];
+      if constexpr (kRanged) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < VR::VW; ++i) {
+          const uint32_t w4[4] = {vbuf.v[i].x, vbuf.v[i].y, vbuf.v[i].z, vbuf.v[i].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if constexpr (sizeof(InT) == 2) {
+              m = max(m, max(w4[u] << 17, (w4[u] & 0xffff0000u) << 1));  // both bf16 halves
+            } else {
+              m = max(m, w4[u] << 1);
+            }
+          }
+        }
+        v_mag = m;
+      }
     }
     if (e_act && (wave & 1) == 0 && lg == 0) sBE[16 * eR + lr] = gbuf.b;
 #pragma unroll
@@ -779,7 +956,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     load_chunk(t_begin + ch_lo * C, chunk_len(ch_lo));
     gate_a();
     store_rb();
+    publish_range();
   }
+  // 2^-e and 2^e of the chunk's range exponent
+  float sc_dn = 1.f, sc_up = 1.f;
   for (int64_t ch = ch_lo; ch < ch_hi; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
     const int Lc = chunk_len(ch);
@@ -797,12 +977,33 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 
     __syncthreads();  // ------------------------------------------------------------- B_a
 
+    // ================= the chunk's range exponent and its 16-bit S and V copies =================
+    if constexpr (!PREP) {
+      if constexpr (kRanged) {
+        static_assert(NW == 8, "two 16-byte reads of the per-wave maxima");
+        const uint4 m0 = *reinterpret_cast<const uint4*>(sMX), m1 = *reinterpret_cast<const uint4*>(sMX + 4);
+        const uint32_t m = max(max(max(m0.x, m0.y), max(m0.z, m0.w)), max(max(m1.x, m1.y), max(m1.z, m1.w)));
+        sc_e = range_exponent(__builtin_amdgcn_readfirstlane(m));
+        sc_dn = pow2i(-sc_e);
+        sc_up = pow2i(sc_e);
+      }
+      if (sc_e == 0) {
+        write_ST(std::false_type{}, 1.f);
+        write_V(std::false_type{}, 1.f);
+      } else {
+        write_ST(std::true_type{}, sc_dn);
+        write_V(std::true_type{}, sc_dn);
+      }
+    }
+
     // ================= per-channel block factors (once per chunk) =================
     // With bh_J = e^{s_J/2} (<= 1), for row block R and channel c:
     //   pre_R  = bh_R prod_{J<R} bh_J^2 = e^{G_{R-1} + s_R/2}      Qg = qL pre, Kg = kL pre
     //   post_R = bh_R prod_{J>R} bh_J^2 = e^{g_last - G_R + s_R/2} Kd = kR post
     //   f_RI   = bh_R prod_{I<J<R} bh_J^2                          off-diagonal left factor (I < R)
     //   gamma  = prod_J bh_J^2 = e^{g_last}
+    // A block on the exact path stores -e^{s_J} instead: its operands are referenced to the
+    // block start, so its own factor is 1 and its squared factor is e^{s_J}.
     // Stored in the A/T region, which is free from the previous chunk's WY stage until
     // this chunk's Gram reduction.
     float* sFT = sAK;
@@ -810,8 +1011,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       float bh[NB], b2[NB];
 #pragma unroll
       for (int J = 0; J < NB; ++J) {
-        bh[J] = sBH[J * DK + tid];
-        b2[J] = bh[J] * bh[J];
+        const float x = sBH[J * DK + tid];
+        const bool exact = __float_as_uint(x) >> 31;
+        bh[J] = exact ? 1.f : x;
+        b2[J] = exact ? -x : x * x;
       }
       float g = 1.f;
 #pragma unroll
@@ -832,7 +1035,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         }
         g *= b2[R];
       }
-      sGM[tid] = g;
+      // (fused: e^{g_last} 2^-e, the state update's decay in the chunk's scaled units)
+      sGM[tid] = kRanged ? g * sc_dn : g;
     }
     // Next-chunk loads (and the next gate stage) run unconditionally: past the last chunk
     // the length is <= 0 and every load reads zero.  Each group is issued as a wave finishes
@@ -1186,6 +1390,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
           const float dq = sDQ[16 * R + lr];
   #pragma unroll
           for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
+          if (kRanged && sc_e != 0) Opend[s] *= sc_up;
         }
       });
   #pragma unroll
@@ -1196,12 +1401,13 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   #pragma unroll
           for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
           mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
+          if (kRanged && sc_e != 0) Sacc[s] *= sc_up;  // back to unscaled units
         }
       }
       o_begin = c_begin;
       o_len = Lc;
       store_pending();
-      write_ST();
+      publish_range();
       // prefix-cache checkpoint: the state after p tokens of this sequence, p a multiple of
       // ckpt_every, goes to slot (sequence start + p) / ckpt_every - 1 (distinct for every
       // checkpoint of every packed sequence)
@@ -1240,12 +1446,10 @@ struct SLay {
   static constexpr size_t GM = DQ + al16(size_t(C) * 4);            // e^{g_last} [DK] fp32
   static constexpr size_t VR = GM + al16(size_t(DK) * 4);           // V [C][LDV]
   static constexpr size_t TILE = VR + al16(size_t(C) * LDV * 2);
-  static constexpr size_t YU = 2 * al16(size_t(BV) * LDC * 2);      // Y^T and U^T [BV][LDC]
-  // two tile buffers when they fit: the next chunk's tile is written while this one is used
-  static constexpr bool DB = T0 + 2 * TILE + YU <= 160 * 1024;
-  static constexpr size_t YT = T0 + (DB ? 2 : 1) * TILE;
-  static constexpr size_t UT = YT + al16(size_t(BV) * LDC * 2);
-  static constexpr size_t TOTAL = UT + al16(size_t(BV) * LDC * 2);
+  static constexpr size_t YT = T0 + TILE;                           // Y^T [BV][LDC]
+  static constexpr size_t UT = YT + al16(size_t(BV) * LDC * 2);     // U^T [BV][LDC]
+  static constexpr size_t MX = UT + al16(size_t(BV) * LDC * 2);     // per-wave largest magnitude [NW]
+  static constexpr size_t TOTAL = MX + al16(size_t(NW) * 4);
   // workspace tile in 16-byte units
   static constexpr int NQ = C * DK / 8, NKD = DK * C / 8, NAQ = C * C / 8, NDQ = C / 4, NGM = DK / 4;
   static constexpr int NU = 2 * NQ + NKD + 2 * NAQ + NDQ + NGM;
@@ -1269,25 +1473,19 @@ __device__ __forceinline__ void chunk_state_body(
   static_assert(sizeof(InT) == 2 && C * VPR <= NT, "bf16 values, one 16-byte load per lane");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr bool DB = L::DB;
   T* sST = reinterpret_cast<T*>(smem + L::ST);
   T* sYT = reinterpret_cast<T*>(smem + L::YT);
   T* sUT = reinterpret_cast<T*>(smem + L::UT);
-  // the chunk tile in use (buffer ch & 1 with two buffers)
-  T *sQG, *sKG, *sKDT, *sAQ, *sTB, *sV;
-  float *sDQ, *sGM;
-  auto use_buf = [&](int b) {
-    unsigned char* t = smem + L::T0 + (size_t)b * L::TILE;
-    sQG = reinterpret_cast<T*>(t + L::QG);
-    sKG = reinterpret_cast<T*>(t + L::KG);
-    sKDT = reinterpret_cast<T*>(t + L::KDT);
-    sAQ = reinterpret_cast<T*>(t + L::AQ);
-    sTB = reinterpret_cast<T*>(t + L::TB);
-    sDQ = reinterpret_cast<float*>(t + L::DQ);
-    sGM = reinterpret_cast<float*>(t + L::GM);
-    sV = reinterpret_cast<T*>(t + L::VR);
-  };
-  use_buf(0);
+  uint32_t* sMX = reinterpret_cast<uint32_t*>(smem + L::MX);
+  unsigned char* tb = smem + L::T0;  // the chunk tile
+  T* sQG = reinterpret_cast<T*>(tb + L::QG);
+  T* sKG = reinterpret_cast<T*>(tb + L::KG);
+  T* sKDT = reinterpret_cast<T*>(tb + L::KDT);
+  T* sAQ = reinterpret_cast<T*>(tb + L::AQ);
+  T* sTB = reinterpret_cast<T*>(tb + L::TB);
+  float* sDQ = reinterpret_cast<float*>(tb + L::DQ);
+  float* sGM = reinterpret_cast<float*>(tb + L::GM);
+  T* sV = reinterpret_cast<T*>(tb + L::VR);
 
   const int ntile = DV / BV;
   const int xcd = bid & 7, qd = bid >> 3;
@@ -1317,7 +1515,7 @@ __device__ __forceinline__ void chunk_state_body(
   const int l = lane_id(), lr = l & 15, lg = l >> 4;
 
   // zero once: the padded token columns (C .. CK) of the token-contiguous operands stay zero
-  for (int i = tid; i < int((L::TOTAL - L::T0) / 2); i += NT) reinterpret_cast<T*>(smem + L::T0)[i] = (T)0.f;
+  for (int i = tid; i < int((L::MX - L::T0) / 2); i += NT) reinterpret_cast<T*>(smem + L::T0)[i] = (T)0.f;
 
   constexpr int S_SLOTS = (NA * NJ + NW - 1) / NW;
   f32x4 Sacc[S_SLOTS];
@@ -1332,13 +1530,16 @@ __device__ __forceinline__ void chunk_state_body(
       for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr];
     }
   }
-  auto write_ST = [&]() {
+  // the 16-bit state copy, scaled by f = 2^-e when the chunk is out of range (see range_exponent)
+  auto write_ST = [&](auto scaled, float f) {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
-        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
+        f32x4 x = Sacc[s];
+        if constexpr (decltype(scaled)::value) x *= f;
+        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, x[0], x[1], x[2], x[3]);
       }
     }
   };
@@ -1368,7 +1569,7 @@ __device__ __forceinline__ void chunk_state_body(
   };
 
   // next chunk's workspace tile and value rows, in registers
-  uint4 pf[PF], pv;
+  uint4 pf[PF], pv = make_uint4(0, 0, 0, 0);
   const bool v_act = C * VPR >= NT || tid < C * VPR;
   const int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
   // loads of units [p0, p1) of the tile of chunk chn (and of its value rows with the last
@@ -1389,7 +1590,8 @@ __device__ __forceinline__ void chunk_state_body(
     }
   };
   constexpr int PG1 = PF / 3, PG2 = 2 * PF / 3;
-  auto store_tiles = [&]() {
+  // the loaded tile to LDS; the values in the operand type, scaled like write_ST
+  auto store_tiles = [&](auto scaled, float f) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int i = tid + p * NT;
@@ -1416,6 +1618,10 @@ __device__ __forceinline__ void chunk_state_body(
       const uint4* pw = &pv;
       float vv[8];
       unpack<InT>(pw, vv, 8);
+      if constexpr (decltype(scaled)::value) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vv[i] *= f;
+      }
       store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
       store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
     }
@@ -1425,28 +1631,53 @@ __device__ __forceinline__ void chunk_state_body(
     for (int p = 0; p < PF; ++p) retire(pf[p]);
     retire(pv);
   };
+  // largest |S| and |v| of the next chunk over the wave, to LDS
+  auto publish_range = [&]() {
+    uint32_t m = 0;
+    if (v_act) {
+      const uint32_t w4[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m = max(m, max(w4[u] << 17, (w4[u] & 0xffff0000u) << 1));  // bf16 halves
+    }
+#pragma unroll
+    for (int s = 0; s < S_SLOTS; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, mag_bits(Sacc[s][i]));
+    m = wave_max_u32(m);
+    if (l == 0) sMX[wave] = m;
+  };
+  // after a barrier: the next chunk's range exponent from every wave's figure, then its state and
+  // tile to LDS
+  int sc_e = 0;
+  float sc_dn = 1.f, sc_up = 1.f;
+  auto stage_next = [&]() {
+    static_assert(NW == 8, "two 16-byte reads of the per-wave maxima");
+    const uint4 m0 = *reinterpret_cast<const uint4*>(sMX), m1 = *reinterpret_cast<const uint4*>(sMX + 4);
+    const uint32_t m = max(max(max(m0.x, m0.y), max(m0.z, m0.w)), max(max(m1.x, m1.y), max(m1.z, m1.w)));
+    sc_e = range_exponent(__builtin_amdgcn_readfirstlane(m));
+    sc_dn = pow2i(-sc_e);
+    sc_up = pow2i(sc_e);
+    if (sc_e == 0) {
+      write_ST(std::false_type{}, 1.f);
+      store_tiles(std::false_type{}, 1.f);
+    } else {
+      write_ST(std::true_type{}, sc_dn);
+      store_tiles(std::true_type{}, sc_dn);
+    }
+  };
 
   __syncthreads();  // zero fill before the first tile
-  write_ST();
-  if (ch_begin < ch_stop) {
-    load_tiles(ch_begin, 0, PF);
-    store_tiles();
-  }
-  if constexpr (DB) load_tiles(ch_begin + 1, 0, PF);  // the next chunk's tile waits in registers
+  load_tiles(ch_begin, 0, PF);
+  publish_range();
+  __syncthreads();
+  stage_next();
   __syncthreads();
 
   f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
   for (int64_t ch = ch_begin; ch < ch_stop; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
     const int Lc = chunk_len(ch);
-    // the tile loaded next: chunk ch+2 with two buffers (chunk ch+1 goes from registers to the
-    // other buffer now), else chunk ch+1 (to LDS after this chunk's last read)
-    const int64_t chl = DB ? ch + 2 : ch + 1;
-    if constexpr (DB) {
-      use_buf((int)((ch - ch_begin + 1) & 1));
-      store_tiles();
-      use_buf((int)((ch - ch_begin) & 1));
-    }
+    const int64_t chl = ch + 1;  // the tile loaded next, to LDS after this chunk's last read
     load_tiles(chl, 0, PG1);
 
     // Y = V - Kg S (to Y^T) and O = Qg S
@@ -1487,7 +1718,8 @@ __device__ __forceinline__ void chunk_state_body(
     __syncthreads();
 
     load_tiles(chl, PG2, PF);
-    // O += M U + diag(q.k) U, stored; S <- Diag(gamma) S + Kd^T U
+    // O += M U + diag(q.k) U, stored; S <- Diag(gamma) S + Kd^T U (in the chunk's scaled units,
+    // then back)
     static_for<0, U_SLOTS>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
       constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
@@ -1500,9 +1732,12 @@ __device__ __forceinline__ void chunk_state_body(
         const float dq = sDQ[16 * R + lr];
         const int r = 16 * R + lr;
         if (r < Lc) {
+          f32x4 ov;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = Oacc[s][i] + dq * Uacc[s][i];
+          if (sc_e != 0) ov *= sc_up;
           float* op = o + ((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + 4 * lg;
-          *reinterpret_cast<float4*>(op) = make_float4(Oacc[s][0] + dq * Uacc[s][0], Oacc[s][1] + dq * Uacc[s][1],
-                                                       Oacc[s][2] + dq * Uacc[s][2], Oacc[s][3] + dq * Uacc[s][3]);
+          *reinterpret_cast<float4*>(op) = make_float4(ov[0], ov[1], ov[2], ov[3]);
         }
       }
     });
@@ -1511,20 +1746,22 @@ __device__ __forceinline__ void chunk_state_body(
       const int id = wave + NW * s;
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
+        if (sc_e == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
-        mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
+          for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
+          mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i] * sc_dn;
+          mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
+          Sacc[s] *= sc_up;
+        }
       }
     }
-    if constexpr (DB) {
-      write_ST();
-      __syncthreads();
-    } else {
-      __syncthreads();  // every read of this chunk's tile and of S^T is done
-      write_ST();
-      store_tiles();
-      __syncthreads();
-    }
+    publish_range();
+    __syncthreads();  // every read of this chunk's tile and of S^T is done
+    stage_next();
+    __syncthreads();
   }
   if (ch_stop == nchunks) {
     if (hT) store_state(hT + (size_t)chain * DK * DV);
@@ -1737,6 +1974,12 @@ static hipError_t dispatch_c(const ChunkArgs& a) {
     if (a.chunk_size == 32) return dispatch_bv<32, DK, (DK == 128 ? 32 : 64), P, InT>(a);
     if constexpr (DK == 64) {
       if (a.chunk_size == 64) return dispatch_bv<64, DK, 32, P, InT>(a);
+    } else {
+      // fp32 operands of a 64-token chunk at dk = 128 (Qg, Kg, Kd^T, the right base: 32 KB each)
+      // do not fit the 160 KB of LDS beside the rest; the recurrence does not depend on the
+      // chunk size, so these run as 32-token chunks (checkpoint spacings, multiples of 64, are
+      // multiples of 32 as well)
+      if (a.chunk_size == 64) return dispatch_bv<32, DK, 32, P, InT>(a);
     }
   }
   return hipErrorInvalidValue;
@@ -1749,7 +1992,6 @@ static hipError_t dispatch_c(const ChunkArgs& a) {
 bool chunk_fwd_supported(int dk, int dv, int chunk_size, bool bf16) {
   if (!((dk == 64 || dk == 128) && (dv == 64 || dv == 128))) return false;
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return false;
-  if (!bf16 && dk == 128 && chunk_size == 64) return false;
   return true;
 }
 

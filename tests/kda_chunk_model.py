@@ -95,3 +95,69 @@ def chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size=64,
                 o[s:e, h] = O[:L]
             hT[n, h] = S
     return o, hT
+
+
+def gram_factored_f32(X, K, LA, sub=16, limit_nats=160.0):
+    """The decay-scaled Gram G[r, i] = sum_c X_rc K_ic exp(g_rc - g_ic) (i <= r) of one chunk,
+    evaluated in fp32 with the factorisation the chunk kernel uses (a model of its arithmetic,
+    for checking exponent ranges on the CPU).
+
+    g is the running sum of LA over the chunk's rows.  Rows are cut into sub-blocks of `sub`;
+    c is the in-sub-block cumulative decay and s its total per channel:
+      * a channel whose sub-block decays by at most `limit_nats` is balanced around the block's
+        middle: left X e^{c - s/2}, right K e^{s/2 - c}, both at most e^{|s|/2};
+      * a wider channel is referenced to the block start: left X e^{c} (<= 1) with the
+        diagonal sub-block formed element by element from e^{c_r - c_i} (<= 1);
+      * sub-block pairs R > I: left X_r e^{c_r} e^{G_{R-1} - G_I} (built from the stored
+        block factors), right K_i e^{s_I - c_i}, all <= 1.
+    Each step's decay is floored at 2^-160 (about -111 nats), as in the kernel.  Returns the
+    fp32 Gram (lower triangle incl. the diagonal; the upper part zero) and whether every
+    operand stayed finite.
+    """
+    f = np.float32
+    X, K = X.astype(f), K.astype(f)
+    l2 = f(1.4426950408889634)
+    cx_step = np.maximum(LA.astype(f) * l2, f(-160.0))
+    C, D = X.shape
+    nb = (C + sub - 1) // sub
+    lim = f(limit_nats) * l2
+    out = np.zeros((C, C), f)
+    finite = True
+    c_all, s_all, own, b2 = [], [], [], []
+    with np.errstate(over="ignore", invalid="ignore", under="ignore"):
+        for R in range(nb):
+            r0, r1 = R * sub, min(C, (R + 1) * sub)
+            c = np.cumsum(cx_step[r0:r1], axis=0, dtype=f)
+            s = c[-1]
+            exact = s < -lim
+            c_all.append(c)
+            s_all.append(s)
+            own.append(np.where(exact, f(1.0), np.exp2(s / 2)).astype(f))
+            b2.append(np.where(exact, np.exp2(s), np.exp2(s / 2) ** 2).astype(f))
+            # diagonal sub-block
+            left = np.where(exact, X[r0:r1] * np.exp2(c), X[r0:r1] * np.exp2(c - s / 2))
+            right = np.where(exact, f(0.0), K[r0:r1] * np.exp2(s / 2 - c))
+            finite &= bool(np.isfinite(left).all() and np.isfinite(right).all())
+            bal = np.where(exact, f(0.0), left) @ right.T
+            L = r1 - r0
+            ex = np.zeros((L, L), f)
+            for r in range(L):
+                for i in range(r + 1):
+                    e = np.exp2(np.minimum(c[r] - c[i], f(0.0)))
+                    ex[r, i] = np.sum(np.where(exact, X[r0 + r] * K[r0 + i] * e, f(0.0)), dtype=f)
+            out[r0:r1, r0:r1] = np.tril(bal + ex)
+        for R in range(nb):
+            r0, r1 = R * sub, min(C, (R + 1) * sub)
+            c, s = c_all[R], s_all[R]
+            exact = s < -lim
+            qL = np.where(exact, X[r0:r1] * np.exp2(c), X[r0:r1] * np.exp2(c - s / 2))
+            for I in range(R):
+                i0, i1 = I * sub, (I + 1) * sub
+                fac = own[R].copy()
+                for J in range(I + 1, R):
+                    fac = fac * b2[J]
+                left = qL * fac
+                right = K[i0:i1] * np.exp2(s_all[I] - c_all[I])
+                finite &= bool(np.isfinite(left).all() and np.isfinite(right).all())
+                out[r0:r1, i0:i1] = left @ right.T
+    return out, finite

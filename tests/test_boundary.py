@@ -63,6 +63,30 @@ def test_chunk_fwd_rejects(kw, code):
     assert chunk(**kw) == code
 
 
+@pytest.mark.parametrize("kw", [
+    dict(hT=P * 8),                    # hT overlaps o
+    dict(hT=P),                        # hT overlaps q
+    dict(hT=P * 2, la=P * 2 + 4096),   # hT overlaps log_alpha
+    dict(hT=P * 2, b=P * 2 + 256),     # hT overlaps beta
+    dict(hT=P * 2, h0=P * 2 + 4096),   # hT overlaps h0 without being h0
+    dict(hT=P * 2, cu=P * 2 + 64, T=64),  # hT overlaps cu_seqlens
+])
+def test_chunk_fwd_rejects_overlapping_final_state(kw):
+    assert chunk(**kw) == 1
+
+
+def test_chunk_fwd_split_and_checkpointed_reject_overlapping_final_state():
+    assert split_call(hT=P * 8) == 1
+    assert ckpt_call(hT=P) == 1
+
+
+def test_chunk_fwd_accepts_fp32_chunk64_at_dk128():
+    # fp32 with dk = 128 and 64-token chunks is in the supported set; with a misaligned o the call
+    # still fails validation (status 1, not 2), so nothing is launched
+    assert chunk(dt=_lib.KDA_DTYPE_F32, C=64, o=P * 8 + 4) == 1
+    assert chunk(dt=_lib.KDA_DTYPE_F32, C=64, dk=96) == 2
+
+
 def test_chunk_fwd_empty_batch_is_a_no_op():
     assert chunk(N=0, T=0, q=None, k=None, v=None, la=None, b=None, o=None) == 0
 
@@ -73,6 +97,17 @@ def test_chunk_fwd_empty_batch_is_a_no_op():
 ])
 def test_recurrent_step_rejects(kw, code):
     assert step(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [
+    dict(S=P),                 # the state overlaps q
+    dict(S=P * 2, k=P * 2 + 64),
+    dict(S=P * 2, v=P * 2 + 4096),
+    dict(S=P * 2, la=P * 2 + 65536),
+    dict(S=P * 2, b=P * 2 + 128),
+])
+def test_recurrent_step_rejects_state_overlapping_inputs(kw):
+    assert step(**kw) == 1
 
 
 def test_recurrent_step_zero_sequences_is_a_no_op():
@@ -93,6 +128,10 @@ def verify(**kw):
 ])
 def test_recurrent_verify_rejects(kw, code):
     assert verify(**kw) == code
+
+
+def test_recurrent_verify_rejects_state_overlapping_commit_counts():
+    assert verify(nc=P * 4 + 1024) == 1
 
 
 def test_recurrent_verify_zero_sequences_is_a_no_op():

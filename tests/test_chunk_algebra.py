@@ -64,3 +64,46 @@ def test_blocked_factorisation_survives_strong_decay():
     assert not np.isfinite(o_plain).all()
     o, hT = chunk_fwd(q, k, v, la, be, chunk_size=256, sub=16)
     assert rel(o, o_ref) < 1e-11 and rel(hT, h_ref) < 1e-11
+
+
+def _gram_ref(X, K, LA):
+    # the decay between rows i and r as the sum of the steps in between (not a difference of
+    # running sums, which a step of -1e30 would swamp)
+    LA = np.asarray(LA, np.float64)
+    C = X.shape[0]
+    out = np.zeros((C, C))
+    for r in range(C):
+        for i in range(r + 1):
+            out[r, i] = np.sum(X[r] * K[i] * np.exp(LA[i + 1:r + 1].sum(0)))
+    return out
+
+
+@pytest.mark.parametrize("law", ["wide", "mixed", "extreme"])
+def test_kernel_factorisation_stays_finite_for_any_decay(law):
+    """The chunk kernel's fp32 factorisation of the decay-scaled Gram (balanced sub-blocks up to
+    160 nats of decay, block-start references with per-element diagonal factors beyond) keeps
+    every operand finite and matches the fp64 Gram, where the balanced form alone overflows."""
+    from kda_chunk_model import gram_factored_f32
+    rng = np.random.default_rng({"wide": 31, "mixed": 32, "extreme": 33}[law])
+    C, D = 64, 48
+    X = rng.standard_normal((C, D)) / np.sqrt(D)
+    K = rng.standard_normal((C, D)) / np.sqrt(D)
+    LA = -np.log1p(np.exp(rng.standard_normal((C, D))))
+    if law == "wide":
+        LA[:, :16] = -30.0
+        LA[:, 16:32] = 0.0
+    elif law == "mixed":
+        LA[16:32, :8] = -12.5    # one 16-token block decaying by 200 nats (exact path)
+        LA[32:48, 8:16] = -9.0   # one by 144 nats (balanced, wide)
+        LA[:, 40:] = -1e-3
+    else:
+        LA[5:60:7, :10] = -1e30
+        LA[:, 10:12] = -3e3
+    ref = _gram_ref(X, K, LA)
+    out, finite = gram_factored_f32(X, K, LA)
+    assert finite
+    assert np.abs(out - ref).max() <= 2e-6 * max(1.0, np.abs(ref).max())
+    # the balanced form alone overflows once a block decays by more than ~177 nats
+    assert (LA.reshape(C // 16, 16, D).sum(1) < -177).any()
+    _, finite_bal = gram_factored_f32(X, K, LA, limit_nats=np.inf)
+    assert not finite_bal
