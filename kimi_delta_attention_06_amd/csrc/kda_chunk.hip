@@ -242,6 +242,38 @@ __device__ __forceinline__ void gram_exact(const float* q, const float* k, const
 // ---------------------------------------------------------------------------
 // |x| as a bit pattern: ordered like the magnitudes (NaN above inf above every finite value)
 __device__ __forceinline__ uint32_t mag_bits(float x) { return __float_as_uint(x) << 1; }
+// The largest mag_bits over fp32 values: the signed maximum of the raw patterns is the largest
+// non-negative value (if any), the unsigned maximum the negative value of largest magnitude (if
+// any); one integer max per value.
+template <int N>
+__device__ __forceinline__ uint32_t mag_max(const float* x) {
+  int32_t smax = INT32_MIN;
+  uint32_t umax = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    smax = max(smax, (int32_t)__float_as_uint(x[i]));
+    umax = max(umax, __float_as_uint(x[i]));
+  }
+  const uint32_t pos = smax < 0 ? 0u : (uint32_t)smax;
+  const uint32_t neg = (umax >> 31) ? (umax & 0x7fffffffu) : 0u;
+  return max(pos, neg) << 1;
+}
+// The largest mag_bits over the bf16 values packed in n 32-bit words: packed 16-bit maxima of the
+// magnitudes, then the larger half, as an fp32 pattern.
+__device__ __forceinline__ uint32_t mag_max_bf16(const uint32_t* w, int n) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7fff7fffu);
+  for (int i = 1; i < n; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+  return (uint32_t)max(m[0], m[1]) << 17;
+}
+// A mag_bits pattern of an unscaled value, expressed in units scaled by 2^-e (saturating; zero,
+// inf and NaN unchanged).
+__device__ __forceinline__ uint32_t mag_scaled(uint32_t m, int e) {
+  const int E = (int)(m >> 24);
+  if (m == 0 || E == 255) return m;
+  const int Es = E - e < 1 ? 1 : (E - e > 254 ? 254 : E - e);
+  return ((uint32_t)Es << 24) | (m & 0xffffffu);
+}
 // largest of the wave's lanes (each lane's value >= 0 as an unsigned pattern)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
@@ -252,13 +284,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   const uint32_t c = __builtin_amdgcn_readlane(x, 47), d = __builtin_amdgcn_readlane(x, 63);
   return max(max(a, b), max(c, d));
 }
-// Scale exponent e for a chunk whose largest magnitude has the pattern m (mag_bits): 0 inside
-// [2^-6, 2^6), for zero, inf and NaN (which then propagate unchanged); otherwise the scaled
-// largest magnitude lands in [2^4, 2^5), with 2^e and 2^-e kept normal.
-__device__ __forceinline__ int range_exponent(uint32_t m) {
-  const int E = (int)(m >> 24);  // biased exponent
-  if (m == 0 || E == 255 || (E >= 127 - 6 && E < 127 + 6)) return 0;
-  const int e = E - 127 - 4;
+// Range exponent e of a chunk from the largest |S| and |v| (pattern m, in the previous chunk's
+// scaled units 2^-e_prev): 0 while the largest true magnitude is inside [2^-6, 2^6) or zero;
+// otherwise the scaled largest magnitude lands in [2^4, 2^5), with 2^e and 2^-e kept normal.
+// With an inf or NaN present nothing can be kept in range (it propagates) and e_prev is kept.
+__device__ __forceinline__ int range_exponent(uint32_t m, int e_prev) {
+  const int Em = (int)(m >> 24);  // biased exponent
+  if (Em == 255) return e_prev;
+  if (m == 0) return 0;
+  const int E = Em - 127 + e_prev;
+  if (E >= -6 && E < 6) return 0;
+  const int e = E - 4;
   return e < -125 ? -125 : (e > 125 ? 125 : e);
 }
 __device__ __forceinline__ float pow2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
@@ -291,10 +327,11 @@ struct Lay {
   static constexpr size_t BE = AO + al16(size_t(NPAIR) * 16 * AOR * 4);   // beta [C]
   static constexpr size_t DQ = BE + al16(size_t(C) * 4);                  // q_r . k_r [C]
   static constexpr size_t GM = DQ + al16(size_t(C) * 4);                  // e^{g_last} [DK]
-  static constexpr size_t MX = GM + al16(size_t(DK) * 4);                 // per-wave largest magnitude [NW]
+  // per-wave words: largest |S|, largest |v|, exact-path vote [3][NW]
+  static constexpr size_t MX = GM + al16(size_t(DK) * 4);
   // per chunk
   static constexpr int LDV = BV + PD;                   // [C][BV] rows (value columns)
-  static constexpr size_t QG = MX + al16(size_t(NW) * 4);                 // Qg [C][LDD]
+  static constexpr size_t QG = MX + al16(size_t(3 * NW) * 4);             // Qg [C][LDD]
   static constexpr size_t KG = QG + al16(size_t(C) * LDD * sizeof(T));    // Kg [C][LDD]
   static constexpr size_t KDT = KG + al16(size_t(C) * LDD * sizeof(T));   // Kd^T [DK][LDC]
   static constexpr size_t VR = KDT + al16(size_t(DK) * LDC * sizeof(T));  // V [C][LDV]
@@ -530,32 +567,34 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr];
     }
   }
-  // The 16-bit copy of the state for the chunk's products, scaled by f (2^-e of the chunk's
-  // range exponent; exactly 1 unless the chunk is out of range, then the branch is taken)
-  auto write_ST = [&](auto scaled, float f) {
+  // The 16-bit copy of the state for the chunk's products.  In the 16-bit precision the fp32
+  // state is held in the chunk's scaled units 2^-e (see range_exponent): it is rescaled when e
+  // changes, and o, hT and the checkpoints are scaled back by 2^e.
+  auto write_ST = [&]() {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
-        f32x4 x = Sacc[s];
-        if constexpr (decltype(scaled)::value) x *= f;
-        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, x[0], x[1], x[2], x[3]);
+        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
       }
     }
   };
-  // Range exponent of the chunk in flight (16-bit operands only; see range_exponent).
+  // Range exponent of the chunk in flight (16-bit operands only).
   constexpr bool kRanged = P == Prec::Mixed && !PREP;
   int sc_e = 0;
+  float sc_dn = 1.f, sc_up = 1.f;  // 2^-e and 2^e
   // largest |v| of this thread's values of the next chunk, as a mag_bits pattern
   uint32_t v_mag = 0;
   auto publish_range = [&]() {
     if constexpr (kRanged) {
-      uint32_t m = v_mag;
+      float sv[4 * S_SLOTS];
 #pragma unroll
       for (int s = 0; s < S_SLOTS; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = max(m, mag_bits(Sacc[s][i]));
+        for (int i = 0; i < 4; ++i) sv[4 * s + i] = ((NA * NJ) % NW == 0 || wave + NW * s < NA * NJ) ? Sacc[s][i] : 0.f;
+      uint32_t m = mag_max<4 * S_SLOTS>(sv);
+      m = max(m, sc_e == 0 ? v_mag : mag_scaled(v_mag, sc_e));
       m = wave_max_u32(m);
       if (lane_id() == 0) sMX[wave0] = m;
     }
@@ -677,6 +716,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   int64_t o_begin = 0;
   int o_len = 0;
   // the fp32 master state of this value tile into a [DK][DV] row-major state
+  // (from the chunk's scaled units back to the state's own)
   auto store_state = [&](float* sp) {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
@@ -684,7 +724,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
+        for (int i = 0; i < 4; ++i)
+          sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = kRanged ? Sacc[s][i] * sc_up : Sacc[s][i];
       }
     }
   };
@@ -743,6 +784,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   // shares LDS with Y^T and is stored only after Y^T's last use.
   float qL[CPL], kL[CPL], kR[CPL], rbv[CPL];
   f32x4 accQd, accKd;
+  bool wide_ext = false;  // this wave's gate stage of the next chunk needs the exact path
   // Gate stage, part a, in GH channel parts of GC channels (each a whole number of the
   // diagonal Gram's MMA k-steps), then the value / beta part.  The parts of chunk c+1 run
   // beside chunk c's latency-bound MMA stages: part 0 with the inverse levels, the rest
@@ -763,6 +805,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     if constexpr (hh == 0) {
       accQd = zero4();
       accKd = zero4();
+      wide_ext = false;
     }
     float* const qh_ = qL + hh * GC;
     float* const kh_ = kL + hh * GC;
@@ -795,49 +838,14 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       // When every channel of this part decays by less than 8 nats over the block, the
       // balanced operands stay within e^{+-4} of the inputs and fp16 represents them as
       // well as the off-diagonal operands; otherwise the part's diagonal products take
-      // the wide path, and past 160 nats (where the balanced factors would overflow) the
-      // exact path.  The votes are wave-uniform.
+      // the wide path.  The vote is wave-uniform.
       float smin = ss[0];
 #pragma unroll
       for (int j = 1; j < GC; ++j) smin = fminf(smin, ss[j]);
       [[maybe_unused]] const bool fast16 = __builtin_amdgcn_ballot_w64(!(smin > -11.5415603f)) == 0;  // 8 nats in log2 units
-      if (__builtin_amdgcn_ballot_w64(!(smin > kBalancedLimit)) != 0) {
-        // Exact path.  Operands referenced to the block start instead of its middle:
-        //   left q e^{c}, k e^{c} (<= 1), right base k e^{s - c} (<= 1), diagonal Gram from
-        //   per-element factors.  The block's own factor in the chunk tables is then 1, which
-        //   the stored decay e^{s} says by its sign bit (stored negated; -0 when it underflows).
-        float cx[GC];
-#pragma unroll
-        for (int j = 0; j < GC; ++j) {
-          const float x = la[j] * 1.4426950408889634f;
-          cx[j] = x < kStepFloor ? kStepFloor : x;  // (a NaN stays NaN)
-        }
-#pragma unroll
-        for (int j = 0; j < GC; ++j) cx[j] += shr16<1>(cx[j]);
-#pragma unroll
-        for (int j = 0; j < GC; ++j) cx[j] += shr16<2>(cx[j]);
-#pragma unroll
-        for (int j = 0; j < GC; ++j) cx[j] += shr16<4>(cx[j]);
-#pragma unroll
-        for (int j = 0; j < GC; ++j) cx[j] += shr16<8>(cx[j]);
-        gram_exact<GC>(qh_, kh_, cx, lr, lg, accQd, accKd);
-#pragma unroll
-        for (int j = 0; j < GC; ++j) {
-          const float sx = row_bcast16<15>(cx[j]);
-          const float eq = __builtin_amdgcn_exp2f(cx[j]);
-          const float kk = kh_[j];
-          qh_[j] *= eq;
-          kh_[j] = kk * eq;
-          rh_[j] = kk * __builtin_amdgcn_exp2f(sx - cx[j]);
-          bh_[j] = rh_[j];
-          ss[j] = -__builtin_amdgcn_exp2f(sx);
-        }
-        if (lr == 15) {
-#pragma unroll
-          for (int j = 0; j < GC; j += 4) store4(sBH + eR * DK + e_cb + j, ss[j], ss[j + 1], ss[j + 2], ss[j + 3]);
-        }
-        return;
-      }
+      // Past 160 nats over the block the balanced factors overflow: the wave redoes its gate stage
+      // on the exact path (fix_exact) after the next barrier, out of this code's way.
+      wide_ext |= __builtin_amdgcn_ballot_w64(!(smin > kBalancedLimit)) != 0;
 #pragma unroll
       for (int j = 0; j < GC; ++j) {
         const float x = cc[j] - 0.5f * ss[j];
@@ -874,27 +882,27 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
             accKd = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, rh, accKd, 0, 0, 0);
           }
         } else {
-          // wide decay: M on the fp32 matrix core; A in bf16 (range), one MFMA per 8 channels
+            // wide decay: M on the fp32 matrix core; A in bf16 (range), one MFMA per 8 channels
 #pragma unroll
-          for (int j = 0; j < GC; ++j) accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qh_[j], rh_[j], accQd, 0, 0, 0);
+            for (int j = 0; j < GC; ++j) accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qh_[j], rh_[j], accQd, 0, 0, 0);
 #pragma unroll
-          for (int t = 0; t < GC / 8; ++t) {
-            bf16x8 kh, bh8;
+            for (int t = 0; t < GC / 8; ++t) {
+              bf16x8 kh, bh8;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              kh[j] = (__bf16)kh_[8 * t + j];
-              bh8[j] = (__bf16)rh_[8 * t + j];
+              for (int j = 0; j < 8; ++j) {
+                kh[j] = (__bf16)kh_[8 * t + j];
+                bh8[j] = (__bf16)rh_[8 * t + j];
+              }
+              accKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh8, accKd, 0, 0, 0);
             }
-            accKd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, bh8, accKd, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < GC; ++j) {
+            accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qh_[j], rh_[j], accQd, 0, 0, 0);
+            accKd = __builtin_amdgcn_mfma_f32_16x16x4f32(kh_[j], rh_[j], accKd, 0, 0, 0);
           }
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < GC; ++j) {
-          accQd = __builtin_amdgcn_mfma_f32_16x16x4f32(qh_[j], rh_[j], accQd, 0, 0, 0);
-          accKd = __builtin_amdgcn_mfma_f32_16x16x4f32(kh_[j], rh_[j], accKd, 0, 0, 0);
-        }
-      }
     }
   };
   // the value / beta part; it also retires every loaded register of the chunk
@@ -911,20 +919,13 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < VR::VW; ++i) vkeep[i] = vbuf.v[i];
       if constexpr (kRanged) {
-        uint32_t m = 0;
+        static_assert(sizeof(InT) == 2, "16-bit operands with bf16 inputs");
+        uint32_t w[4 * VR::VW];
 #pragma unroll
         for (int i = 0; i < VR::VW; ++i) {
-          const uint32_t w4[4] = {vbuf.v[i].x, vbuf.v[i].y, vbuf.v[i].z, vbuf.v[i].w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if constexpr (sizeof(InT) == 2) {
-              m = max(m, max(w4[u] << 17, (w4[u] & 0xffff0000u) << 1));  // both bf16 halves
-            } else {
-              m = max(m, w4[u] << 1);
-            }
-          }
+          w[4 * i] = vbuf.v[i].x; w[4 * i + 1] = vbuf.v[i].y; w[4 * i + 2] = vbuf.v[i].z; w[4 * i + 3] = vbuf.v[i].w;
         }
-        v_mag = m;
+        v_mag = mag_max_bf16(w, 4 * VR::VW);
       }
     }
     if (e_act && (wave & 1) == 0 && lg == 0) sBE[16 * eR + lr] = gbuf.b;
@@ -943,6 +944,62 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     static_for<0, GH>(gate_part);
     gate_v();
   };
+  // The gate stage of one part on the exact path, from the raw inputs in gbuf: operands
+  // referenced to the block start instead of its middle (left q e^{c}, k e^{c} <= 1, right base
+  // k e^{s - c} <= 1), the diagonal Gram from per-element factors.  The block's own factor in the
+  // chunk tables is then 1, which the stored decay e^{s} says by its sign bit (stored negated;
+  // -0 when it underflows).
+  auto exact_part = [&](auto hc) {
+    constexpr int hh = decltype(hc)::value;
+    const int eR = row_block_of<NB>(wave0);
+    const int e_cb = (wave0 & 1) * (DK / 2) + CPL * lg + hh * GC;
+    if constexpr (hh == 0) {
+      accQd = zero4();
+      accKd = zero4();
+    }
+    float* const qh_ = qL + hh * GC;
+    float* const kh_ = kL + hh * GC;
+    float* const rh_ = kR + hh * GC;
+    float* const bh_ = rbv + hh * GC;
+    unpack<InT>(gbuf.q + hh * (GR::QW / GH), qh_, GC);
+    unpack<InT>(gbuf.k + hh * (GR::QW / GH), kh_, GC);
+    float la[GC];
+#pragma unroll
+    for (int i = 0; i < GC / 4; ++i) {
+      const float4 x = gbuf.la[hh * (GC / 4) + i];
+      la[4 * i] = x.x; la[4 * i + 1] = x.y; la[4 * i + 2] = x.z; la[4 * i + 3] = x.w;
+    }
+    float cx[GC], ss[GC];
+#pragma unroll
+    for (int j = 0; j < GC; ++j) {
+      const float x = la[j] * 1.4426950408889634f;
+      cx[j] = x < kStepFloor ? kStepFloor : x;  // (a NaN stays NaN)
+    }
+#pragma unroll
+    for (int j = 0; j < GC; ++j) cx[j] += shr16<1>(cx[j]);
+#pragma unroll
+    for (int j = 0; j < GC; ++j) cx[j] += shr16<2>(cx[j]);
+#pragma unroll
+    for (int j = 0; j < GC; ++j) cx[j] += shr16<4>(cx[j]);
+#pragma unroll
+    for (int j = 0; j < GC; ++j) cx[j] += shr16<8>(cx[j]);
+    gram_exact<GC>(qh_, kh_, cx, lr, lg, accQd, accKd);
+#pragma unroll
+    for (int j = 0; j < GC; ++j) {
+      const float sx = row_bcast16<15>(cx[j]);
+      const float eq = __builtin_amdgcn_exp2f(cx[j]);
+      const float kk = kh_[j];
+      qh_[j] *= eq;
+      kh_[j] = kk * eq;
+      rh_[j] = kk * __builtin_amdgcn_exp2f(sx - cx[j]);
+      bh_[j] = rh_[j];
+      ss[j] = -__builtin_amdgcn_exp2f(sx);
+    }
+    if (lr == 15) {
+#pragma unroll
+      for (int j = 0; j < GC; j += 4) store4(sBH + eR * DK + e_cb + j, ss[j], ss[j + 1], ss[j + 2], ss[j + 3]);
+    }
+  };
   auto store_rb = [&]() {
     const int x = fresh_lane();
     const int eR = e_act ? row_block_of<NB>(wave0) : 0;
@@ -952,14 +1009,30 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       for (int j = 0; j < CPL; j += 4) store4(dst + j, rbv[j], rbv[j + 1], rbv[j + 2], rbv[j + 3]);
     }
   };
+  // A wave whose gate stage voted for the exact path reloads the chunk's q, k and log-decay and
+  // redoes its gate stage on that path (every part, so its partial Gram sums are consistent).
+  auto fix_exact = [&](int64_t cb, int Lc) {
+    refresh_lane();
+    load_qk1(q, gbuf.q, cb, Lc);
+    load_qk1(k, gbuf.k, cb, Lc);
+    load_la(cb, Lc);
+    static_for<0, GH>(exact_part);
+#pragma unroll
+    for (int i = 0; i < GR::QW; ++i) {
+      retire(gbuf.q[i]);
+      retire(gbuf.k[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CPL / 4; ++i) retire(gbuf.la[i]);
+    store_rb();
+  };
   if (ch_hi > ch_lo) {
     load_chunk(t_begin + ch_lo * C, chunk_len(ch_lo));
     gate_a();
     store_rb();
     publish_range();
+    if (lane_id() == 0) sMX[2 * NW + wave0] = wide_ext;
   }
-  // 2^-e and 2^e of the chunk's range exponent
-  float sc_dn = 1.f, sc_up = 1.f;
   for (int64_t ch = ch_lo; ch < ch_hi; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
     const int Lc = chunk_len(ch);
@@ -977,24 +1050,45 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 
     __syncthreads();  // ------------------------------------------------------------- B_a
 
-    // ================= the chunk's range exponent and its 16-bit S and V copies =================
-    if constexpr (!PREP) {
-      if constexpr (kRanged) {
-        static_assert(NW == 8, "two 16-byte reads of the per-wave maxima");
-        const uint4 m0 = *reinterpret_cast<const uint4*>(sMX), m1 = *reinterpret_cast<const uint4*>(sMX + 4);
-        const uint32_t m = max(max(max(m0.x, m0.y), max(m0.z, m0.w)), max(max(m1.x, m1.y), max(m1.z, m1.w)));
-        sc_e = range_exponent(__builtin_amdgcn_readfirstlane(m));
-        sc_dn = pow2i(-sc_e);
-        sc_up = pow2i(sc_e);
-      }
-      if (sc_e == 0) {
-        write_ST(std::false_type{}, 1.f);
-        write_V(std::false_type{}, 1.f);
-      } else {
-        write_ST(std::true_type{}, sc_dn);
-        write_V(std::true_type{}, sc_dn);
+    // ================= the exact path for blocks of extreme decay (rare) =================
+    {
+      static_assert(NW == 8, "16-byte reads of the per-wave words");
+      const uint4 f0 = *reinterpret_cast<const uint4*>(sMX + 2 * NW), f1 = *reinterpret_cast<const uint4*>(sMX + 2 * NW + 4);
+      if (__builtin_amdgcn_readfirstlane(f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w)) {
+        if (wide_ext) fix_exact(c_begin, Lc);
+        __syncthreads();
       }
     }
+
+    // ================= the chunk's range exponent and its 16-bit S and V copies =================
+    if constexpr (kRanged) {
+      static_assert(NW == 8, "16-byte reads of the per-wave maxima");
+      const uint4 a0 = *reinterpret_cast<const uint4*>(sMX), a1 = *reinterpret_cast<const uint4*>(sMX + 4);
+      const uint32_t m = max(max(max(a0.x, a0.y), max(a0.z, a0.w)), max(max(a1.x, a1.y), max(a1.z, a1.w)));
+      const int e = range_exponent(__builtin_amdgcn_readfirstlane(m), sc_e);
+      if (e != sc_e) {
+        // rescale the held state to the new units, in two steps (the shift may exceed 2^126)
+        const int d = sc_e - e, d1 = d / 2;
+        const float f1 = pow2i(d1), f2 = pow2i(d - d1);
+#pragma unroll
+        for (int s = 0; s < S_SLOTS; ++s) Sacc[s] = (Sacc[s] * f1) * f2;
+        sc_e = e;
+        sc_dn = pow2i(-e);
+        sc_up = pow2i(e);
+      }
+    }
+    // (waves past the factor stage's DK threads write their copies now, the others after it)
+    auto write_copies = [&]() {
+      if constexpr (!PREP) {
+        write_ST();
+        if (sc_e == 0) {
+          write_V(std::false_type{}, 1.f);
+        } else {
+          write_V(std::true_type{}, sc_dn);
+        }
+      }
+    };
+    if (tid >= DK) write_copies();
 
     // ================= per-channel block factors (once per chunk) =================
     // With bh_J = e^{s_J/2} (<= 1), for row block R and channel c:
@@ -1035,8 +1129,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         }
         g *= b2[R];
       }
-      // (fused: e^{g_last} 2^-e, the state update's decay in the chunk's scaled units)
-      sGM[tid] = kRanged ? g * sc_dn : g;
+      sGM[tid] = g;
+      write_copies();
     }
     // Next-chunk loads (and the next gate stage) run unconditionally: past the last chunk
     // the length is <= 0 and every load reads zero.  Each group is issued as a wave finishes
@@ -1342,6 +1436,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       gate_v();
       __syncthreads();  // (prep) the right base is stored after this barrier
       store_rb();
+      if (lane_id() == 0) sMX[2 * NW + wave0] = wide_ext;
     } else {
       // ================= U = Tb Y ; O = Qg S ; next chunk's gate stage =================
       // The products are issued first; the next chunk's gate stage (vector ALU) runs while
@@ -1389,8 +1484,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
           mma_lds<T, KS, steps>(Oacc[s], sUT + 16 * j * LDC, LDC, sAQ + 16 * R * LDC, LDC);
           const float dq = sDQ[16 * R + lr];
   #pragma unroll
-          for (int i = 0; i < 4; ++i) Opend[s][i] = Oacc[s][i] + dq * Uacc[s][i];
-          if (kRanged && sc_e != 0) Opend[s] *= sc_up;
+          for (int i = 0; i < 4; ++i) Opend[s][i] = (Oacc[s][i] + dq * Uacc[s][i]) * (kRanged ? sc_up : 1.f);
         }
       });
   #pragma unroll
@@ -1401,13 +1495,13 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   #pragma unroll
           for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
           mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
-          if (kRanged && sc_e != 0) Sacc[s] *= sc_up;  // back to unscaled units
         }
       }
       o_begin = c_begin;
       o_len = Lc;
       store_pending();
       publish_range();
+      if (lane_id() == 0) sMX[2 * NW + wave0] = wide_ext;
       // prefix-cache checkpoint: the state after p tokens of this sequence, p a multiple of
       // ckpt_every, goes to slot (sequence start + p) / ckpt_every - 1 (distinct for every
       // checkpoint of every packed sequence)
@@ -1448,7 +1542,7 @@ struct SLay {
   static constexpr size_t TILE = VR + al16(size_t(C) * LDV * 2);
   static constexpr size_t YT = T0 + TILE;                           // Y^T [BV][LDC]
   static constexpr size_t UT = YT + al16(size_t(BV) * LDC * 2);     // U^T [BV][LDC]
-  static constexpr size_t MX = UT + al16(size_t(BV) * LDC * 2);     // per-wave largest magnitude [NW]
+  static constexpr size_t MX = UT + al16(size_t(BV) * LDC * 2);     // per-wave largest |S|, |v| [NW]
   static constexpr size_t TOTAL = MX + al16(size_t(NW) * 4);
   // workspace tile in 16-byte units
   static constexpr int NQ = C * DK / 8, NKD = DK * C / 8, NAQ = C * C / 8, NDQ = C / 4, NGM = DK / 4;
@@ -1530,27 +1624,26 @@ __device__ __forceinline__ void chunk_state_body(
       for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr];
     }
   }
-  // the 16-bit state copy, scaled by f = 2^-e when the chunk is out of range (see range_exponent)
-  auto write_ST = [&](auto scaled, float f) {
+  // The 16-bit state copy.  The fp32 state is held in the chunk's scaled units 2^-e (see
+  // range_exponent); o, hT and the hand-over state are scaled back by 2^e.
+  auto write_ST = [&]() {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
-        f32x4 x = Sacc[s];
-        if constexpr (decltype(scaled)::value) x *= f;
-        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, x[0], x[1], x[2], x[3]);
+        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
       }
     }
   };
-  auto store_state = [&](float* sp) {
+  auto store_state = [&](float* sp, float f) {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s) {
       const int id = wave + NW * s;
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i];
+        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i] * f;
       }
     }
   };
@@ -1572,22 +1665,23 @@ __device__ __forceinline__ void chunk_state_body(
   uint4 pf[PF], pv = make_uint4(0, 0, 0, 0);
   const bool v_act = C * VPR >= NT || tid < C * VPR;
   const int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
-  // loads of units [p0, p1) of the tile of chunk chn (and of its value rows with the last
-  // group): the tile goes out in three groups, one per stage, so the device's requests
-  // do not all leave right after one barrier
+  // loads of units [p0, p1) of the tile of chunk chn (and of its value rows, first, with the
+  // first group: their magnitude is needed before the chunk's last barrier, and loads retire
+  // in order): the tile goes out in three groups, one per stage, so the device's requests do
+  // not all leave right after one barrier
   auto load_tiles = [&](int64_t chn, int p0, int p1) {
     const bool ok = chn < ch_stop;
-    const int64_t slot = t_begin / C + n + chn;
-    const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * NU, ok ? (uint32_t)NU * 16u : 0u);
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-      if (p >= p0 && p < p1) pf[p] = buf_load16(rs, (uint32_t)(tid + p * NT) * 16u);
-    if (p1 == PF) {
+    if (p0 == 0) {
       const int Lc = ok ? chunk_len(chn) : 0;
       const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + j0,
                                 Lc > 0 ? (uint32_t)Lc * (uint32_t)(H * DV * 2) : 0u);
       pv = buf_load16(rv, (uint32_t)(v_row * H * DV + v_c0) * 2u);
     }
+    const int64_t slot = t_begin / C + n + chn;
+    const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * NU, ok ? (uint32_t)NU * 16u : 0u);
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (p >= p0 && p < p1) pf[p] = buf_load16(rs, (uint32_t)(tid + p * NT) * 16u);
   };
   constexpr int PG1 = PF / 3, PG2 = 2 * PF / 3;
   // the loaded tile to LDS; the values in the operand type, scaled like write_ST
@@ -1631,37 +1725,44 @@ __device__ __forceinline__ void chunk_state_body(
     for (int p = 0; p < PF; ++p) retire(pf[p]);
     retire(pv);
   };
-  // largest |S| and |v| of the next chunk over the wave, to LDS
+  int sc_e = 0;
+  float sc_dn = 1.f, sc_up = 1.f;
+  // largest |S| and |v| of the next chunk (in the chunk's scaled units) over the wave, to LDS
   auto publish_range = [&]() {
-    uint32_t m = 0;
+    uint32_t mv = 0;
     if (v_act) {
       const uint32_t w4[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) m = max(m, max(w4[u] << 17, (w4[u] & 0xffff0000u) << 1));  // bf16 halves
+      mv = mag_max_bf16(w4, 4);
     }
+    float sv[4 * S_SLOTS];
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) m = max(m, mag_bits(Sacc[s][i]));
+      for (int i = 0; i < 4; ++i) sv[4 * s + i] = ((NA * NJ) % NW == 0 || wave + NW * s < NA * NJ) ? Sacc[s][i] : 0.f;
+    uint32_t m = max(mag_max<4 * S_SLOTS>(sv), sc_e == 0 ? mv : mag_scaled(mv, sc_e));
     m = wave_max_u32(m);
     if (l == 0) sMX[wave] = m;
   };
-  // after a barrier: the next chunk's range exponent from every wave's figure, then its state and
-  // tile to LDS
-  int sc_e = 0;
-  float sc_dn = 1.f, sc_up = 1.f;
+  // after a barrier: the next chunk's range exponent from every wave's figures (the held state
+  // is rescaled to its units when it changes), then its state and tile to LDS
   auto stage_next = [&]() {
-    static_assert(NW == 8, "two 16-byte reads of the per-wave maxima");
-    const uint4 m0 = *reinterpret_cast<const uint4*>(sMX), m1 = *reinterpret_cast<const uint4*>(sMX + 4);
-    const uint32_t m = max(max(max(m0.x, m0.y), max(m0.z, m0.w)), max(max(m1.x, m1.y), max(m1.z, m1.w)));
-    sc_e = range_exponent(__builtin_amdgcn_readfirstlane(m));
-    sc_dn = pow2i(-sc_e);
-    sc_up = pow2i(sc_e);
+    static_assert(NW == 8, "16-byte reads of the per-wave maxima");
+    const uint4 a0 = *reinterpret_cast<const uint4*>(sMX), a1 = *reinterpret_cast<const uint4*>(sMX + 4);
+    const uint32_t m = max(max(max(a0.x, a0.y), max(a0.z, a0.w)), max(max(a1.x, a1.y), max(a1.z, a1.w)));
+    const int e = range_exponent(__builtin_amdgcn_readfirstlane(m), sc_e);
+    if (e != sc_e) {
+      const int d = sc_e - e, d1 = d / 2;
+      const float f1 = pow2i(d1), f2 = pow2i(d - d1);
+#pragma unroll
+      for (int s = 0; s < S_SLOTS; ++s) Sacc[s] = (Sacc[s] * f1) * f2;
+      sc_e = e;
+      sc_dn = pow2i(-e);
+      sc_up = pow2i(e);
+    }
+    write_ST();
     if (sc_e == 0) {
-      write_ST(std::false_type{}, 1.f);
       store_tiles(std::false_type{}, 1.f);
     } else {
-      write_ST(std::true_type{}, sc_dn);
       store_tiles(std::true_type{}, sc_dn);
     }
   };
@@ -1734,8 +1835,7 @@ __device__ __forceinline__ void chunk_state_body(
         if (r < Lc) {
           f32x4 ov;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = Oacc[s][i] + dq * Uacc[s][i];
-          if (sc_e != 0) ov *= sc_up;
+          for (int i = 0; i < 4; ++i) ov[i] = (Oacc[s][i] + dq * Uacc[s][i]) * sc_up;
           float* op = o + ((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + 4 * lg;
           *reinterpret_cast<float4*>(op) = make_float4(ov[0], ov[1], ov[2], ov[3]);
         }
@@ -1746,16 +1846,9 @@ __device__ __forceinline__ void chunk_state_body(
       const int id = wave + NW * s;
       if ((NA * NJ) % NW == 0 || id < NA * NJ) {
         const int a = id % NA, j = id / NA;
-        if (sc_e == 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
-          mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i] * sc_dn;
-          mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
-          Sacc[s] *= sc_up;
-        }
+        for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
+        mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
       }
     }
     publish_range();
@@ -1764,9 +1857,9 @@ __device__ __forceinline__ void chunk_state_body(
     __syncthreads();
   }
   if (ch_stop == nchunks) {
-    if (hT) store_state(hT + (size_t)chain * DK * DV);
+    if (hT) store_state(hT + (size_t)chain * DK * DV, sc_up);
   } else {
-    store_state(carry + (size_t)chain * DK * DV);
+    store_state(carry + (size_t)chain * DK * DV, sc_up);
   }
 }
 
