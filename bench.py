@@ -1,21 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the KDA operator on one MI355X.
 
-Timed step: one kda_chunk_fwd pass over the Kimi-Linear-shaped KDA layer
-(B=4, T=4096, H=32, dk=dv=128, chunk 64, bf16 q/k/v, fp32 gates and state;
-seeded synthetic inputs already resident in HBM).  `value` is tokens/s of that
-pass (B*T tokens, all 32 heads).  The same pass with state checkpoints every 512
-tokens is timed and reported under "checkpointed".  In the same run the decode/replay state update
-(256 sequences x 32 heads, fp32 state, 1 and 8 tokens) and the replay + verify
-variant (8 tokens, per-sequence commit counts) are timed and reported under
-"decode" (HBM GB/s against the 8 TB/s peak); one chunked pass over a single
-1M-token sequence x 32 heads is timed, fused and split (kda_chunk_fwd_split), 1 warm-up + 5 timed
-launches each, and reported under "long_context"; and the
-fp64 CPU oracle is timed on a bounded sample of the chunk workload ("cpu_baseline").
-The backward pass (kda_bwd, chunkwise) on the Kimi-Linear layer is timed under "backward", and
-the tiny fp32 and varlen packed chunked workloads under "other_workloads".
+Timed step (the headline): one kda_chunk_fwd_split call over the long-context
+workload, one 1,048,576-token sequence x 32 heads, dk = dv = 128, chunk 64, bf16
+q/k/v, fp32 log-decay/beta/o/hT (seeded synthetic inputs already resident in HBM).
+`value` is tokens/s of that call.  Before the warm-up the same call runs for
+--settle-ms so that clocks have settled; then --warmup untimed calls and exactly
+--steps timed calls between two synchronisations.  Its roofline (HBM-bound) and the
+fp64 CPU oracle on the workload's two seeded heads (cpu_baseline) go on the line,
+with the max-error/RMS of o and hT on those heads.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-long-context] [--copy-calibration]
+The other workloads are legs under "legs", each timed with HIP events on the launch
+stream, with its own roofline or bandwidth, its error against the oracle on a seeded
+slice, and the oracle's own time on the host: the Kimi-Linear-shaped layer (fused,
+with 512-token checkpoints, and split), the tiny fp32 case, the varlen packed batch,
+the decode / replay state update (1 and 8 tokens) and replay + verify, the backward
+pass, and the long-context sequence through the fused kernel.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
+                       [--legs all|headline] [--no-cpu-baseline] [--copy-calibration]
 Prints exactly one JSON line on stdout.  --copy-calibration adds three launches of a
 plain elementwise copy of known size (1 GiB read, 1 GiB written) after the timed
 region, so that hardware byte counters (FETCH_SIZE / WRITE_SIZE) taken over the
@@ -36,6 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 METRIC = "KDA chunked-fwd tokens/s (H=32,d=128) + MFMA util; decode state-update GB/s"
+BF16_TOL, F32_TOL = 2e-2, 1e-4
 
 # Algorithmic model of one chunked-forward token-head (dk = dv = d = 128, chunk C = 64):
 # bytes: q, k, v bf16 (3 x 256) + log_alpha fp32 (512) + beta fp32 (4) + o fp32 (512)
@@ -43,9 +47,11 @@ BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 512
 # flops: 6 d^2 for the state products (W S, Qg S, Kd^T U) + C (3 dk + 2 dv) for the
 # lower-triangular intra-chunk products (A, M, W, Ut, M U); the UT inverse is not counted.
 FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_kimi_linear_layer_pmc.txt")
-SQ_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_kimi_linear_layer_sq_counters.txt")
-# the chunk kernel's code is fixed by its source and by the compiler flags the build gives it
+PROFILES = os.path.join(ROOT, "profiles")
+PMC_SUMMARY = os.path.join(PROFILES, "chunk_fwd_kimi_linear_layer_pmc.txt")
+SQ_SUMMARY = os.path.join(PROFILES, "chunk_fwd_kimi_linear_layer_sq_counters.txt")
+LC_PMC_SUMMARY = os.path.join(PROFILES, "chunk_fwd_split_long_context_pmc.txt")
+# the chunk kernels' code is fixed by their source and by the compiler flags the build gives them
 CHUNK_BUILD_FILES = [os.path.join(ROOT, "kimi_delta_attention_06_amd", "csrc", "kda_chunk.hip"),
                      os.path.join(ROOT, "kimi_delta_attention_06_amd", "build.py")]
 
@@ -81,9 +87,11 @@ def profile_value(path, key):
         return None
 
 
-def traffic_from_profile():
-    """HBM bytes per launch measured by rocprofv3 counters for the current kernel build, else None."""
-    return profile_value(PMC_SUMMARY, "hbm_bytes_per_launch")
+def chunk_alg_bytes(tokens, heads, n_seqs, d=128, h0=False, qkv_bytes=2):
+    """Algorithmic HBM bytes of one chunked-forward call: the token rows read and o written once,
+    hT written (and h0 read when present) once per (sequence, head)."""
+    per = 3 * d * qkv_bytes + 4 * d + 4 + 4 * d
+    return tokens * heads * per + n_seqs * heads * d * d * 4 * (2 if h0 else 1)
 
 
 def time_launches(fn, steps, warmup, stream):
@@ -99,6 +107,19 @@ def time_launches(fn, steps, warmup, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms per launch
+
+
+def settle(fn, ms, stream):
+    """Runs fn back to back for at least `ms` of wall time (at least once); returns the launch count."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0 or ms <= 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms:
+                return n
 
 
 def launch_spread(fn, n, stream):
@@ -126,32 +147,6 @@ def copy_bandwidth(dev, stream, nbytes=1 << 30):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(inp, n_seqs):
-    """fp64 oracle on the first `n_seqs` sequences of the workload, all heads (whole sequences)."""
-    import oracle
-    T = int(sum(inp["lens"][:n_seqs]))
-    sl = slice(0, T)
-    args = [inp[x][sl].cpu() for x in ("q", "k", "v", "log_alpha", "beta")]
-    cu = inp["cu_seqlens"][: n_seqs + 1].cpu()
-    nthreads = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    oracle.kda_fwd(*args, None, cu, n_threads=nthreads)
-    dt = time.perf_counter() - t0
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": "fp64 token-by-token oracle on %d of %d sequences (%d tokens x 32 heads), "
-                      "%.2f s wall on %d threads (%s); same token count convention as value"
-                      % (n_seqs, len(inp["lens"]), T, dt, nthreads, cpu)}
-
-
 def copy_calibration(dev, nbytes=1 << 30):
     """Three launches of a plain elementwise copy (y = -x, fp32) of `nbytes` each way."""
     import torch
@@ -166,15 +161,324 @@ def copy_calibration(dev, nbytes=1 << 30):
     return {"kernel": "elementwise neg (fp32)", "read_bytes_per_launch": nbytes, "write_bytes_per_launch": nbytes}
 
 
+def cpu_info():
+    threads = len(os.sched_getaffinity(0))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, cpu
+
+
+def errors(x, ref, tol=None, absolute=False):
+    """max|err| / RMS(ref) and RMS(err) / RMS(ref) of x (torch or numpy) against the fp64 reference."""
+    import numpy as np
+    x = x.detach().double().cpu().numpy() if hasattr(x, "detach") else np.asarray(x, dtype=np.float64)
+    x = x.reshape(ref.shape)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    d = x - ref
+    emax = float(np.abs(d).max()) if ref.size else 0.0
+    out = {"max_err_over_rms": round(emax / rms, 6) if rms else 0.0,
+           "rms_err_over_rms": round(float(np.sqrt(np.mean(d ** 2))) / rms, 7) if rms else 0.0}
+    if absolute:
+        out["max_abs_err"] = float("%.3e" % emax)
+    if tol is not None:
+        out["within_tolerance"] = bool(emax <= tol if absolute else emax <= tol * rms)
+    return out
+
+
+def timed_oracle(fn, *a, **kw):
+    t0 = time.perf_counter()
+    r = fn(*a, **kw)
+    return r, time.perf_counter() - t0
+
+
+# ---------------------------------------------------------------------------------------------
+# the headline: the long-context sequence through the split path
+# ---------------------------------------------------------------------------------------------
+def headline(args, dev, stream, copy_gbs):
+    import torch
+    import kda_inputs
+    import kimi_delta_attention_06_amd as kda
+
+    lw = kda_inputs.LONG_CONTEXT
+    log("generating %s inputs" % lw.name)
+    inp = kda_inputs.make_chunk_inputs(lw, device=dev)
+    o = torch.empty(lw.total_tokens, lw.n_heads, lw.dv, dtype=torch.float32, device=dev)
+    hT = torch.empty(1, lw.n_heads, lw.dk, lw.dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.chunk_fwd_split_workspace_bytes(lw.n_seqs, lw.total_tokens, lw.n_heads, lw.dk, lw.dv,
+                                                         lw.chunk_size), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.chunk_fwd_split(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], h0=None,
+                            chunk_size=lw.chunk_size, o=o, hT=hT, workspace=ws)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_settle = settle(step, args.settle_ms, stream)
+    settle_ms = (time.perf_counter() - t0) * 1e3
+    log("settle: %d calls in %.0f ms; timing %s split: %d warmup + %d steps" % (n_settle, settle_ms, lw.name,
+                                                                               args.warmup, args.steps))
+    t_wall0 = time.perf_counter()
+    ms = time_launches(step, args.steps, args.warmup, stream)
+    t_wall = time.perf_counter() - t_wall0
+    tok_s = lw.total_tokens / (ms * 1e-3)
+    alg_bytes = chunk_alg_bytes(lw.total_tokens, lw.n_heads, 1)
+    alg_flops = lw.total_tokens * lw.n_heads * FLOPS_PER_TOKEN_HEAD
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    tflops = alg_flops / (ms * 1e-3) / 1e12
+    n_chunks = -(-lw.seq_len // lw.chunk_size)
+    log("%s split: %.3f ms/call, %.2f M tokens/s, %.0f GB/s algorithmic (%.1f%% of HBM peak)"
+        % (lw.name, ms, tok_s / 1e6, gbs, 100 * gbs / HBM_PEAK_GBS))
+    spread = launch_spread(step, 3, stream)
+    res = {
+        "ms": ms, "tok_s": tok_s, "wall": t_wall, "settle_ms": settle_ms, "settle_launches": n_settle,
+        "config": {"workload": lw.name, "batch": 1, "seq_len": lw.seq_len, "heads": lw.n_heads, "dk": lw.dk,
+                   "dv": lw.dv, "chunk": lw.chunk_size, "tokens": lw.total_tokens, "path": "kda_chunk_fwd_split",
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": profile_value(LC_PMC_SUMMARY,
+                                                                                     "hbm_bytes_per_call"),
+                     "kernel": "split path: chunk_fwd_kernel in-chunk pass, then 16 launches of its pipelined "
+                               "mode (state pass over one chunk range beside the next range's in-chunk pass); "
+                               "one call = one step",
+                     "algorithmic_bytes_per_launch": alg_bytes, "copy_GB/s": round(copy_gbs, 1),
+                     "frac_of_copy": round(gbs / copy_gbs, 4)},
+        "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": alg_flops},
+        "launch_spread": spread,
+        "us_per_serial_chunk_step": round(ms * 1e3 / n_chunks, 3),
+        "workspace_bytes": ws.numel(),
+    }
+    # the fused kernel on the same inputs (value tiles of 16 columns)
+    fused = lambda: kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], h0=None,
+                                  chunk_size=lw.chunk_size, o=o, hT=hT)
+    f_ms = time_launches(fused, 3, 1, stream)
+    f_gbs = alg_bytes / (f_ms * 1e-3) / 1e9
+    res["fused_leg"] = {"ms_per_step": round(f_ms, 3), "tokens_per_s": round(lw.total_tokens / (f_ms * 1e-3), 1),
+                        "algorithmic_GB/s": round(f_gbs, 1), "frac_of_hbm_peak": round(f_gbs / HBM_PEAK_GBS, 4),
+                        "us_per_serial_chunk_step": round(f_ms * 1e3 / n_chunks, 3)}
+    log("%s fused: %.3f ms/call" % (lw.name, f_ms))
+    step()  # the split path's outputs for the parity check
+    torch.cuda.synchronize()
+    del ws
+    heads = kda_inputs.long_context_oracle_heads()
+    hs = torch.as_tensor(heads, device=dev)
+    sub = {k_: inp[k_].index_select(1, hs).cpu() for k_ in ("q", "k", "v", "log_alpha", "beta")}
+    o_s, h_s = o.index_select(1, hs).cpu(), hT.index_select(1, hs).cpu()
+    del inp, o, hT
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        import oracle
+        threads, cpu = cpu_info()
+        log("oracle on heads %s of %s (%d tokens) on %d threads" % ([int(x) for x in heads], lw.name, lw.total_tokens, threads))
+        (o_ref, h_ref), t_or = timed_oracle(oracle.kda_fwd, sub["q"], sub["k"], sub["v"], sub["log_alpha"],
+                                            sub["beta"], None, None, n_threads=threads)
+        res["parity"] = {"o": errors(o_s, o_ref, BF16_TOL), "hT": errors(h_s, h_ref, BF16_TOL),
+                         "tolerance_max_err_over_rms": BF16_TOL,
+                         "sample": "heads %s (seeded), all %d tokens" % ([int(x) for x in heads], lw.total_tokens)}
+        scale = lw.n_heads / len(heads)
+        res["cpu_baseline"] = {
+            "value": round(lw.total_tokens / (t_or * scale), 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "fp64 token-by-token oracle on %d of %d heads (%d tokens each), %.2f s wall on %d threads (%s); "
+                      "value extrapolated to all %d heads (x%.0f time)" % (len(heads), lw.n_heads, lw.total_tokens,
+                                                                          t_or, threads, cpu, lw.n_heads, scale),
+            "measured_s": round(t_or, 3), "heads_measured": len(heads), "extrapolated": True}
+        log("oracle: %.2f s; o max err/rms %.4f, hT %.4f" % (t_or, res["parity"]["o"]["max_err_over_rms"],
+                                                             res["parity"]["hT"]["max_err_over_rms"]))
+    return res
+
+
+# ---------------------------------------------------------------------------------------------
+# legs
+# ---------------------------------------------------------------------------------------------
+def leg_kimi_linear(args, dev, stream, copy_gbs, legs):
+    import torch
+    import kda_inputs
+    import kimi_delta_attention_06_amd as kda
+
+    w = kda_inputs.KIMI_LINEAR_LAYER
+    inp = kda_inputs.make_chunk_inputs(w, device=dev)
+    o = torch.empty(w.total_tokens, w.n_heads, w.dv, dtype=torch.float32, device=dev)
+    hT = torch.empty(w.n_seqs, w.n_heads, w.dk, w.dv, dtype=torch.float32, device=dev)
+    view = lambda x: x.view(w.n_seqs, -1, *x.shape[1:])
+    qb, kb, vb, lab, beb = (view(inp[x]) for x in ("q", "k", "v", "log_alpha", "beta"))
+
+    def step():
+        kda.chunk_fwd(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size, o=o, hT=hT)
+
+    ms = time_launches(step, 200, 50, stream)
+    alg_bytes = chunk_alg_bytes(w.total_tokens, w.n_heads, w.n_seqs)
+    alg_flops = w.total_tokens * w.n_heads * FLOPS_PER_TOKEN_HEAD
+    gbs, tflops = alg_bytes / (ms * 1e-3) / 1e9, alg_flops / (ms * 1e-3) / 1e12
+    leg = {"path": "kda_chunk_fwd (fused)", "ms_per_step": round(ms, 5),
+           "tokens_per_s": round(w.total_tokens / (ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": profile_value(PMC_SUMMARY,
+                                                                                        "hbm_bytes_per_launch"),
+                        "kernel": "chunk_fwd_kernel<64,128,64,Mixed,bf16>", "algorithmic_bytes_per_launch": alg_bytes,
+                        "frac_of_copy": round(gbs / copy_gbs, 4)},
+           "mfma": {"algorithmic_tflops": round(tflops, 2), "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "algorithmic_flops_per_launch": alg_flops,
+                    "counter_busy_frac": profile_value(SQ_SUMMARY, "mfma_busy_frac"),
+                    "counter_valu_busy_frac": profile_value(SQ_SUMMARY, "valu_busy_frac")},
+           "launch_spread": launch_spread(step, 50, stream)}
+    log("%s fused: %.4f ms, %.1f M tokens/s, %.1f%% of HBM peak" % (w.name, ms, w.total_tokens / ms / 1e3,
+                                                                    100 * gbs / HBM_PEAK_GBS))
+    ck_every = 512
+    ck = torch.empty(w.total_tokens // ck_every, w.n_heads, w.dk, w.dv, dtype=torch.float32, device=dev)
+    cstep = lambda: kda.chunk_fwd_checkpointed(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size,
+                                               ckpt_every=ck_every, o=o, hT=hT, ckpt=ck)
+    c_ms = time_launches(cstep, 200, 50, stream)
+    legs[w.name + " checkpointed"] = {"ckpt_every": ck_every, "ms_per_step": round(c_ms, 5),
+                                      "overhead_vs_plain": round(c_ms / ms - 1.0, 4),
+                                      "checkpoint_bytes_per_step": ck.numel() * 4}
+    del ck
+    ws = torch.empty(kda.chunk_fwd_split_workspace_bytes(w.n_seqs, w.total_tokens, w.n_heads, w.dk, w.dv),
+                     dtype=torch.uint8, device=dev)
+    sstep = lambda: kda.chunk_fwd_split(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size, o=o, hT=hT,
+                                        workspace=ws)
+    s_ms = time_launches(sstep, 100, 20, stream)
+    legs[w.name + " split"] = {"ms_per_step": round(s_ms, 5), "tokens_per_s": round(w.total_tokens / (s_ms * 1e-3), 1)}
+    del ws
+    # backward on the same inputs
+    b_do = torch.randn(w.total_tokens, w.n_heads, w.dv, generator=torch.Generator(device=dev).manual_seed(77),
+                       device=dev)
+    b_ws = torch.empty(kda.backward_workspace_bytes(w.n_seqs, w.total_tokens, w.n_heads, w.dk, w.dv),
+                       dtype=torch.uint8, device=dev)
+    bstep = lambda: kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], b_do,
+                                 cu_seqlens=inp["cu_seqlens"], workspace=b_ws)
+    b_ms = time_launches(bstep, 5, 1, stream)
+    legs[w.name + " backward"] = {"ms_per_step": round(b_ms, 3), "tokens_per_s": round(w.total_tokens / (b_ms * 1e-3), 1),
+                                  "workspace_bytes": b_ws.numel(),
+                                  "kind": "chunkwise fp32 matrix-core reverse mode (kda_bwd)"}
+    log("%s backward: %.3f ms" % (w.name, b_ms))
+    del b_do, b_ws
+    step()
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        import oracle
+        threads, _ = cpu_info()
+        (o_ref, h_ref), t_or = timed_oracle(oracle.kda_fwd, inp["q"], inp["k"], inp["v"], inp["log_alpha"],
+                                            inp["beta"], None, inp["cu_seqlens"], n_threads=threads)
+        leg["parity"] = {"o": errors(o, o_ref, BF16_TOL), "hT": errors(hT, h_ref, BF16_TOL),
+                         "sample": "all %d tokens x %d heads" % (w.total_tokens, w.n_heads)}
+        leg["cpu_oracle"] = {"seconds": round(t_or, 3), "tokens_per_s": round(w.total_tokens / t_or, 1),
+                             "threads": threads, "sample": "whole workload"}
+    legs[w.name] = leg
+
+
+def leg_chunk_other(args, dev, stream, legs):
+    """tiny fp32 (256 tokens x 2 heads x 64, chunk 16) and varlen packed (32,768 tokens, 8 sequences)."""
+    import torch
+    import kda_inputs
+    import kimi_delta_attention_06_amd as kda
+
+    for ow in (kda_inputs.TINY_FP32, kda_inputs.VARLEN_PACKED):
+        inp = kda_inputs.make_chunk_inputs(ow, device=dev)
+        o = torch.empty(ow.total_tokens, ow.n_heads, ow.dv, dtype=torch.float32, device=dev)
+        hT = torch.empty(ow.n_seqs, ow.n_heads, ow.dk, ow.dv, dtype=torch.float32, device=dev)
+        step = lambda: kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], h0=inp["h0"],
+                                     cu_seqlens=inp["cu_seqlens"], chunk_size=ow.chunk_size, o=o, hT=hT)
+        ms = time_launches(step, 100, 20, stream)
+        qb = inp["q"].element_size()
+        alg = chunk_alg_bytes(ow.total_tokens, ow.n_heads, ow.n_seqs, ow.dk, inp["h0"] is not None, qb)
+        leg = {"ms_per_step": round(ms, 5), "tokens_per_s": round(ow.total_tokens / (ms * 1e-3), 1),
+               "algorithmic_GB/s": round(alg / (ms * 1e-3) / 1e9, 1),
+               "frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if ow.dtype == torch.bfloat16:
+            ws = torch.empty(kda.chunk_fwd_split_workspace_bytes(ow.n_seqs, ow.total_tokens, ow.n_heads, ow.dk,
+                                                                 ow.dv), dtype=torch.uint8, device=dev)
+            sstep = lambda: kda.chunk_fwd_split(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                                h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], chunk_size=ow.chunk_size,
+                                                o=o, hT=hT, workspace=ws)
+            leg["split_ms_per_step"] = round(time_launches(sstep, 100, 20, stream), 5)
+            del ws
+        step()
+        torch.cuda.synchronize()
+        log("%s: %.4f ms" % (ow.name, ms))
+        if not args.no_cpu_baseline:
+            import oracle
+            threads, _ = cpu_info()
+            (o_ref, h_ref), t_or = timed_oracle(oracle.kda_fwd, inp["q"], inp["k"], inp["v"], inp["log_alpha"],
+                                                inp["beta"], inp["h0"], inp["cu_seqlens"], n_threads=threads)
+            fp32 = ow.dtype == torch.float32
+            tol = F32_TOL if fp32 else BF16_TOL
+            leg["parity"] = {"o": errors(o, o_ref, tol, absolute=fp32), "hT": errors(hT, h_ref, tol, absolute=fp32),
+                             "sample": "whole workload"}
+            leg["cpu_oracle"] = {"seconds": round(t_or, 4), "tokens_per_s": round(ow.total_tokens / t_or, 1),
+                                 "threads": threads, "sample": "whole workload"}
+        legs[ow.name] = leg
+        del inp, o, hT
+
+
+def leg_decode(args, dev, stream, copy_gbs, legs):
+    import torch
+    import kda_inputs
+    import kimi_delta_attention_06_amd as kda
+
+    dw = kda_inputs.DECODE_256x32
+    state_bytes = dw.n_seqs * dw.n_heads * dw.dk * dw.dv * 4
+    for n_tok in (1, 8):
+        d = kda_inputs.make_decode_inputs(dw, n_tok, device=dev)
+        S0 = d["S"].clone()
+        d_o = torch.empty(dw.n_seqs, n_tok, dw.n_heads, dw.dv, dtype=torch.float32, device=dev)
+        dstep = lambda: kda.recurrent_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S"], o=d_o)
+        d_ms = time_launches(dstep, max(args.steps, 100), 50, stream)
+        spread = launch_spread(dstep, 50, stream)
+        d_bytes = 2 * state_bytes + dw.n_seqs * n_tok * dw.n_heads * BYTES_PER_TOKEN_HEAD
+        d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
+        leg = {"ms_per_step": round(d_ms, 5), "GB/s": round(d_gbs, 1), "frac_of_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4),
+               "frac_of_copy": round(d_gbs / copy_gbs, 4), "tokens_per_s": round(dw.n_seqs * n_tok / (d_ms * 1e-3), 1),
+               "launch_spread": spread, "bytes_per_step": d_bytes}
+        log("recurrent_step n=%d: %.4f ms, %.0f GB/s (%.1f%% of peak)" % (n_tok, d_ms, d_gbs, 100 * d_gbs / HBM_PEAK_GBS))
+        if not args.no_cpu_baseline:
+            import oracle
+            threads, _ = cpu_info()
+            d["S"].copy_(S0)
+            kda.recurrent_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S"], o=d_o)
+            torch.cuda.synchronize()
+            (o_ref, S_ref), t_or = timed_oracle(oracle.kda_recurrent_step, d["q"], d["k"], d["v"], d["log_alpha"],
+                                                d["beta"], S0, n_threads=threads)
+            leg["parity"] = {"o": errors(d_o, o_ref, BF16_TOL), "S": errors(d["S"], S_ref, BF16_TOL),
+                             "sample": "all %d sequences x %d heads, one step from the seeded state" % (dw.n_seqs,
+                                                                                                       dw.n_heads)}
+            leg["cpu_oracle"] = {"seconds": round(t_or, 4), "tokens_per_s": round(dw.n_seqs * n_tok / t_or, 1),
+                                 "threads": threads, "sample": "one step, all sequences and heads"}
+        legs["%s n%d" % (dw.name, n_tok)] = leg
+        del d, d_o, S0
+    # replay + verify: 8 tokens, per-sequence commit counts drawn uniformly from 0..8 (seeded)
+    v = kda_inputs.make_decode_inputs(dw, 8, device=dev)
+    gen = torch.Generator().manual_seed(1005 + 7)
+    n_commit = torch.randint(0, 9, (dw.n_seqs,), generator=gen, dtype=torch.int32).to(dev)
+    v_o = torch.empty(dw.n_seqs, 8, dw.n_heads, dw.dv, dtype=torch.float32, device=dev)
+    vstep = lambda: kda.recurrent_verify(v["q"], v["k"], v["v"], v["log_alpha"], v["beta"], v["S"], n_commit, o=v_o)
+    v_ms = time_launches(vstep, max(args.steps, 100), 50, stream)
+    n_writing = int((n_commit > 0).sum().item())
+    v_bytes = (dw.n_seqs + n_writing) * dw.n_heads * dw.dk * dw.dv * 4 + dw.n_seqs * 8 * dw.n_heads * BYTES_PER_TOKEN_HEAD
+    v_gbs = v_bytes / (v_ms * 1e-3) / 1e9
+    legs[dw.name + " verify n8"] = {"ms_per_step": round(v_ms, 5), "GB/s": round(v_gbs, 1),
+                                    "frac_of_hbm_peak": round(v_gbs / HBM_PEAK_GBS, 4),
+                                    "frac_of_copy": round(v_gbs / copy_gbs, 4), "sequences_committing": n_writing,
+                                    "bytes_per_step": v_bytes}
+    log("recurrent_verify n=8 (%d of %d commit): %.4f ms, %.0f GB/s" % (n_writing, dw.n_seqs, v_ms, v_gbs))
+    del v, v_o
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # defaults: ~25 ms of warm-up launches (clocks settle) and ~90 ms timed on the chunk kernel
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--no-long-context", action="store_true")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=400.0)
+    ap.add_argument("--legs", choices=("all", "headline"), default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -183,222 +487,49 @@ def main():
         sys.exit(2)
 
     import torch
-    import kda_inputs
-    import kimi_delta_attention_06_amd as kda
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-
-    # ---------------- chunked forward, Kimi-Linear-shaped layer ----------------
-    w = kda_inputs.KIMI_LINEAR_LAYER
-    log("generating %s inputs" % w.name)
-    inp = kda_inputs.make_chunk_inputs(w, device=dev)
-    o = torch.empty(w.total_tokens, w.n_heads, w.dv, dtype=torch.float32, device=dev)
-    hT = torch.empty(w.n_seqs, w.n_heads, w.dk, w.dv, dtype=torch.float32, device=dev)
-
-    # fixed-length batch: pass [B, T, H, d] views (no cu_seqlens)
-    qb = inp["q"].view(w.n_seqs, -1, w.n_heads, w.dk)
-    kb = inp["k"].view(w.n_seqs, -1, w.n_heads, w.dk)
-    vb = inp["v"].view(w.n_seqs, -1, w.n_heads, w.dv)
-    lab = inp["log_alpha"].view(w.n_seqs, -1, w.n_heads, w.dk)
-    beb = inp["beta"].view(w.n_seqs, -1, w.n_heads)
-
-    def step():
-        kda.chunk_fwd(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size, o=o, hT=hT)
-
-    log("timing chunk_fwd: %d warmup + %d steps" % (args.warmup, args.steps))
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    ms = time_launches(step, args.steps, args.warmup, stream)
-    t_wall = time.perf_counter() - t_wall0
-    tokens = w.total_tokens
-    tok_s = tokens / (ms * 1e-3)
-    alg_bytes = tokens * w.n_heads * BYTES_PER_TOKEN_HEAD + w.n_seqs * w.n_heads * w.dk * w.dv * 4
-    alg_flops = tokens * w.n_heads * FLOPS_PER_TOKEN_HEAD
-    gbs = alg_bytes / (ms * 1e-3) / 1e9
-    tflops = alg_flops / (ms * 1e-3) / 1e12
-    log("chunk_fwd: %.4f ms/launch, %.1f M tokens/s, %.0f GB/s algorithmic, %.1f TFLOP/s algorithmic"
-        % (ms, tok_s / 1e6, gbs, tflops))
-    spread = launch_spread(step, 50, stream)
-    log("chunk_fwd per-launch spread: p10 %.4f, median %.4f, p90 %.4f ms" % (spread["p10_ms"], spread["median_ms"],
-                                                                         spread["p90_ms"]))
     copy_gbs = copy_bandwidth(dev, stream)
     log("device copy (1 GiB each way): %.0f GB/s" % copy_gbs)
 
-    # ---------------- the same pass with 512-token state checkpoints ----------------
-    ck_every = 512
-    ck = torch.empty(tokens // ck_every, w.n_heads, w.dk, w.dv, dtype=torch.float32, device=dev)
-
-    def cstep():
-        kda.chunk_fwd_checkpointed(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size, ckpt_every=ck_every,
-                                   o=o, hT=hT, ckpt=ck)
-
-    c_ms = time_launches(cstep, args.steps, args.warmup, stream)
-    ck_bytes = ck.numel() * 4
-    checkpointed = {"ckpt_every": ck_every, "ms_per_step": round(c_ms, 5),
-                    "overhead_vs_plain": round(c_ms / ms - 1.0, 4), "checkpoint_bytes_per_step": ck_bytes,
-                    "algorithmic_GB/s": round((alg_bytes + ck_bytes) / (c_ms * 1e-3) / 1e9, 1)}
-    log("chunk_fwd_checkpointed (every %d tokens): %.4f ms/launch (%+.1f%%)" % (ck_every, c_ms, 100 * (c_ms / ms - 1)))
-    del ck
-
-    # ---------------- decode / replay ----------------
-    dw = kda_inputs.DECODE_256x32
-    decode = {}
-    for n_tok in (1, 8):
-        d_inp = kda_inputs.make_decode_inputs(dw, n_tok, device=dev)
-        d_o = torch.empty(dw.n_seqs, n_tok, dw.n_heads, dw.dv, dtype=torch.float32, device=dev)
-
-        def dstep(d_inp=d_inp, d_o=d_o):
-            kda.recurrent_step(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["log_alpha"], d_inp["beta"], d_inp["S"],
-                               o=d_o)
-
-        d_ms = time_launches(dstep, max(args.steps, 20), args.warmup, stream)
-        d_spread = launch_spread(dstep, 50, stream)
-        d_bytes = 2 * dw.n_seqs * dw.n_heads * dw.dk * dw.dv * 4 + dw.n_seqs * n_tok * dw.n_heads * BYTES_PER_TOKEN_HEAD
-        d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
-        decode["n%d" % n_tok] = {"ms_per_step": round(d_ms, 5), "GB/s": round(d_gbs, 1),
-                                 "frac_of_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4),
-                                 "frac_of_copy": round(d_gbs / copy_gbs, 4),
-                                 "tokens_per_s": round(dw.n_seqs * n_tok / (d_ms * 1e-3), 1), "launch_spread": d_spread,
-                                 "bytes_per_step": d_bytes}
-        log("recurrent_step n=%d: %.4f ms, %.0f GB/s (%.1f%% of peak)" % (n_tok, d_ms, d_gbs, 100 * d_gbs / HBM_PEAK_GBS))
-        del d_inp, d_o
-
-    # replay + verify: 8 tokens, per-sequence commit counts drawn uniformly from 0..8 (seeded)
-    v_inp = kda_inputs.make_decode_inputs(dw, 8, device=dev)
-    gen = torch.Generator().manual_seed(1005 + 7)
-    n_commit = torch.randint(0, 9, (dw.n_seqs,), generator=gen, dtype=torch.int32).to(dev)
-    v_o = torch.empty(dw.n_seqs, 8, dw.n_heads, dw.dv, dtype=torch.float32, device=dev)
-
-    def vstep():
-        kda.recurrent_verify(v_inp["q"], v_inp["k"], v_inp["v"], v_inp["log_alpha"], v_inp["beta"], v_inp["S"],
-                             n_commit, o=v_o)
-
-    v_ms = time_launches(vstep, max(args.steps, 20), args.warmup, stream)
-    n_writing = int((n_commit > 0).sum().item())
-    state_bytes = dw.n_heads * dw.dk * dw.dv * 4
-    v_bytes = (dw.n_seqs + n_writing) * state_bytes + dw.n_seqs * 8 * dw.n_heads * BYTES_PER_TOKEN_HEAD
-    v_gbs = v_bytes / (v_ms * 1e-3) / 1e9
-    decode["verify_n8"] = {"ms_per_step": round(v_ms, 5), "GB/s": round(v_gbs, 1),
-                           "frac_of_hbm_peak": round(v_gbs / HBM_PEAK_GBS, 4), "frac_of_copy": round(v_gbs / copy_gbs, 4),
-                           "sequences_committing": n_writing, "bytes_per_step": v_bytes}
-    log("recurrent_verify n=8 (%d of %d sequences commit): %.4f ms, %.0f GB/s (%.1f%% of peak)"
-        % (n_writing, dw.n_seqs, v_ms, v_gbs, 100 * v_gbs / HBM_PEAK_GBS))
-    del v_inp, v_o
-
-    # ---------------- backward pass on the Kimi-Linear layer ----------------
-    b_do = torch.randn(w.total_tokens, w.n_heads, w.dv, generator=torch.Generator(device=dev).manual_seed(77),
-                       device=dev)
-    b_ws = torch.empty(kda.backward_workspace_bytes(w.n_seqs, w.total_tokens, w.n_heads, w.dk, w.dv),
-                       dtype=torch.uint8, device=dev)
-
-    def bstep():
-        kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], b_do, cu_seqlens=inp["cu_seqlens"],
-                     workspace=b_ws)
-
-    b_ms = time_launches(bstep, 5, 1, stream)
-    backward = {"workload": w.name, "ms_per_step": round(b_ms, 3), "tokens_per_s": round(tokens / (b_ms * 1e-3), 1),
-                "workspace_bytes": b_ws.numel(), "kind": "chunkwise fp32 matrix-core reverse mode (kda_bwd)"}
-    log("backward (kda_bwd) on %s: %.3f ms/call, %.2f M tokens/s" % (w.name, b_ms, tokens / (b_ms * 1e-3) / 1e6))
-    del b_do, b_ws
-
-    # ---------------- the other chunked workloads, timed as well ----------------
-    # tiny fp32 (256 tokens x 2 heads x 64 dims, chunk 16: launch-bound) and varlen packed
-    # (32,768 tokens in 8 sequences x 32 heads, nonzero h0)
-    other = {}
-    for ow in (kda_inputs.TINY_FP32, kda_inputs.VARLEN_PACKED):
-        o_inp = kda_inputs.make_chunk_inputs(ow, device=dev)
-        o_o = torch.empty(ow.total_tokens, ow.n_heads, ow.dv, dtype=torch.float32, device=dev)
-        o_h = torch.empty(ow.n_seqs, ow.n_heads, ow.dk, ow.dv, dtype=torch.float32, device=dev)
-
-        def ostep(o_inp=o_inp, o_o=o_o, o_h=o_h, ow=ow):
-            kda.chunk_fwd(o_inp["q"], o_inp["k"], o_inp["v"], o_inp["log_alpha"], o_inp["beta"], h0=o_inp["h0"],
-                          cu_seqlens=o_inp["cu_seqlens"], chunk_size=ow.chunk_size, o=o_o, hT=o_h)
-
-        o_ms = time_launches(ostep, 100, 20, stream)
-        o_bytes = ow.total_tokens * ow.n_heads * (3 * ow.dk * o_inp["q"].element_size() + 4 * ow.dk + 4 + 4 * ow.dv)
-        other[ow.name] = {"ms_per_step": round(o_ms, 5), "tokens_per_s": round(ow.total_tokens / (o_ms * 1e-3), 1),
-                          "algorithmic_GB/s": round(o_bytes / (o_ms * 1e-3) / 1e9, 1)}
-        log("%s: %.4f ms/launch, %.2f M tokens/s" % (ow.name, o_ms, ow.total_tokens / (o_ms * 1e-3) / 1e6))
-        del o_inp, o_o, o_h
-
-    # ---------------- long context: one 1M-token sequence x 32 heads (32 chains) ----------------
-    long_context = None
-    if not args.no_long_context:
-        lw = kda_inputs.LONG_CONTEXT
-        log("generating %s inputs" % lw.name)
-        l_inp = kda_inputs.make_chunk_inputs(lw, device=dev)
-        l_o = torch.empty(lw.total_tokens, lw.n_heads, lw.dv, dtype=torch.float32, device=dev)
-        l_hT = torch.empty(1, lw.n_heads, lw.dk, lw.dv, dtype=torch.float32, device=dev)
-
-        def lstep():
-            kda.chunk_fwd(l_inp["q"], l_inp["k"], l_inp["v"], l_inp["log_alpha"], l_inp["beta"], h0=None,
-                          chunk_size=lw.chunk_size, o=l_o, hT=l_hT)
-
-        l_ws = None
-
-        def lstep_split():
-            kda.chunk_fwd_split(l_inp["q"], l_inp["k"], l_inp["v"], l_inp["log_alpha"], l_inp["beta"], h0=None,
-                                chunk_size=lw.chunk_size, o=l_o, hT=l_hT, workspace=l_ws)
-
-        l_bytes = lw.total_tokens * lw.n_heads * BYTES_PER_TOKEN_HEAD + lw.n_heads * lw.dk * lw.dv * 4
-        long_context = {"workload": lw.name, "tokens": lw.total_tokens, "heads": lw.n_heads}
-        for leg, fn in (("fused", lstep), ("split", lstep_split)):
-            if leg == "split":
-                l_ws = torch.empty(kda.chunk_fwd_split_workspace_bytes(lw.n_seqs, lw.total_tokens, lw.n_heads, lw.dk,
-                                                                       lw.dv, lw.chunk_size),
-                                   dtype=torch.uint8, device=dev)
-            l_ms = time_launches(fn, 5, 1, stream)
-            l_tok = lw.total_tokens / (l_ms * 1e-3)
-            n_chunks = -(-lw.seq_len // lw.chunk_size)
-            long_context[leg] = {"ms_per_step": round(l_ms, 3), "tokens_per_s": round(l_tok, 1),
-                                 "algorithmic_GB/s": round(l_bytes / (l_ms * 1e-3) / 1e9, 1),
-                                 "us_per_serial_chunk_step": round(l_ms * 1e3 / n_chunks, 3)}
-            log("long context, %s (%d tokens x %d heads): %.2f ms/launch, %.2f M tokens/s"
-                % (leg, lw.total_tokens, lw.n_heads, l_ms, l_tok / 1e6))
-        if l_ws is not None:
-            long_context["split"]["workspace_bytes"] = l_ws.numel()
-        del l_inp, l_o, l_hT, l_ws
+    h = headline(args, dev, stream, copy_gbs)
+    legs = {"long-context-1m-bf16 fused": h.pop("fused_leg")}
+    if args.legs == "all":
+        leg_kimi_linear(args, dev, stream, copy_gbs, legs)
+        leg_chunk_other(args, dev, stream, legs)
+        leg_decode(args, dev, stream, copy_gbs, legs)
 
     result = {
         "metric": METRIC,
-        "value": round(tok_s, 1),
+        "value": round(h["tok_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(h["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.n_seqs, "seq_len": w.seq_len, "heads": w.n_heads,
-                   "dk": w.dk, "dv": w.dv, "chunk": w.chunk_size, "tokens": tokens,
-                   "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                     "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": alg_bytes,
-                     "copy_GB/s": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4)},
-        "launch_spread": spread,
-        "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": alg_flops,
-                 # rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs) and VALU busy of the same kernel
-                 "counter_busy_frac": profile_value(SQ_SUMMARY, "mfma_busy_frac"),
-                 "counter_valu_busy_frac": profile_value(SQ_SUMMARY, "valu_busy_frac")},
-        "checkpointed": checkpointed,
-        "decode": decode,
-        "long_context": long_context,
-        "backward": backward,
-        "other_workloads": other,
-        "wall_s_timed_region": round(t_wall, 3),
+        "config": h["config"],
+        "settle_ms": round(h["settle_ms"], 1),
+        "settle_launches": h["settle_launches"],
+        "roofline": h["roofline"],
+        "mfma": h["mfma"],
+        "launch_spread": h["launch_spread"],
+        "us_per_serial_chunk_step": h["us_per_serial_chunk_step"],
+        "workspace_bytes": h["workspace_bytes"],
+        "wall_s_timed_region": round(h["wall"], 3),
+        "legs": legs,
     }
+    for key in ("parity", "cpu_baseline"):
+        if key in h:
+            result[key] = h[key]
     if args.copy_calibration:
         result["copy_calibration"] = copy_calibration(dev)
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(result), flush=True)
 
 

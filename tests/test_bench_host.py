@@ -57,3 +57,23 @@ def test_build_hash_covers_source_and_flags(tmp_path):
     assert bench.build_hash([str(a), str(b)]) != h1
     names = [os.path.basename(x) for x in bench.CHUNK_BUILD_FILES]
     assert names == ["kda_chunk.hip", "build.py"]
+
+
+def test_algorithmic_bytes_of_the_workloads():
+    # long context: 1,048,576 tokens x 32 heads at 1,796 B per token-head + hT (32 x 64 KiB)
+    assert bench.chunk_alg_bytes(1 << 20, 32, 1) == (1 << 20) * 32 * 1796 + 32 * 128 * 128 * 4
+    assert abs(bench.chunk_alg_bytes(1 << 20, 32, 1) / 1e6 - 60265.9) < 0.1
+    # Kimi-Linear layer: 950.0 MB; varlen packed with h0 read and hT written: 1,916.8 MB
+    assert abs(bench.chunk_alg_bytes(16384, 32, 4) / 1e6 - 950.0) < 0.1
+    assert abs(bench.chunk_alg_bytes(32768, 32, 8, h0=True) / 1e6 - 1916.8) < 0.1
+    # fp32 q/k/v at d = 64: 3 x 256 + 256 + 4 + 256 bytes per token-head
+    assert bench.chunk_alg_bytes(256, 2, 1, d=64, qkv_bytes=4) == 256 * 2 * (3 * 256 + 256 + 4 + 256) + 2 * 64 * 64 * 4
+
+
+def test_error_ratios():
+    ref = np.array([[3.0, -4.0], [0.0, 0.0]])  # RMS 2.5
+    e = bench.errors(ref + np.array([[0.05, 0.0], [0.0, -0.02]]), ref, tol=0.02)
+    assert e["max_err_over_rms"] == 0.02 and e["within_tolerance"]
+    assert abs(e["rms_err_over_rms"] - np.sqrt((0.05 ** 2 + 0.02 ** 2) / 4) / 2.5) < 1e-7
+    e = bench.errors(ref + 1e-3, ref, tol=1e-4, absolute=True)
+    assert not e["within_tolerance"] and e["max_abs_err"] == 1e-3
