@@ -163,6 +163,30 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
                                void* stream);
 
 /*
+ * kda_chunk_fwd_split_noalloc - kda_chunk_fwd_split for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Instead of a caller workspace it uses a
+ * fixed array of KDA_NOALLOC_SCRATCH_BYTES in the library's device memory, one
+ * per GPU, held until the process ends; nothing is allocated on any call.
+ * Calls on one GPU share that array and the contents of the last call stay in
+ * it, so calls that overlap in time on one GPU (several streams or host
+ * threads) race and must not be made.  The first call on a device looks up that
+ * device's array address.
+ *
+ * Same arguments and results as kda_chunk_fwd_split without workspace and
+ * workspace_bytes.  Errors: as kda_chunk_fwd_split, plus KDA_ERR_UNSUPPORTED when
+ * the workspace these sizes need (kda_chunk_fwd_split_workspace_size) exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES, and KDA_ERR_LAUNCH when the array's address cannot
+ * be obtained.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                                       const float* beta, const float* h0, const int32_t* cu_seqlens,
+                                       int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                       int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
+                                       void* stream);
+
+/*
  * kda_chunk_fwd_split_workspace_size - bytes of workspace kda_chunk_fwd_split
  * needs: (total_tokens / chunk_size + n_seqs + 1) * n_heads tiles of the
  * per-chunk operands (66,304 B each for dk = 128, chunk 64), then

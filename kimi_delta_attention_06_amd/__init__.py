@@ -7,6 +7,7 @@ HIP kernels.  PyTorch provides device memory and the current stream.
     o, hT = chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size=64)
     o, hT, ckpt = chunk_fwd_checkpointed(..., ckpt_every=512)  # + states every 512 tokens
     o, hT = chunk_fwd_split(...)                          # two passes, for few (sequence, head) chains
+    o, hT = chunk_fwd_split_noalloc(...)                  # the same with the library's own workspace
     g = backward(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=None)  # dq, dk, dv, ...
     g = backward(..., method="recurrent")                # token by token, no decay bound
     o = recurrent_step(q, k, v, log_alpha, beta, S)      # updates S in place
@@ -27,7 +28,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "chunk_fwd_split", "chunk_fwd_split_workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "chunk_fwd_split", "chunk_fwd_split_noalloc",
+           "chunk_fwd_split_workspace_bytes",
            "backward", "backward_workspace_bytes", "recurrent_step", "recurrent_verify", "KDAError"]
 
 
@@ -92,6 +94,17 @@ def chunk_fwd_split(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_si
     library reports) is allocated when not given.  Returns (o, hT)."""
     o, hT, _ = _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, 0, None,
                       split=True, workspace=workspace)
+    return o, hT
+
+
+def chunk_fwd_split_noalloc(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: int = 64,
+                            output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                            hT: Optional[torch.Tensor] = None):
+    """`chunk_fwd_split` with the library's own per-GPU workspace (kda_chunk_fwd_split_noalloc): the C call
+    allocates nothing.  Pass preallocated `o` (and `hT`) to keep the whole call free of allocation, e.g. under
+    HIP graph capture.  Calls on one GPU share the workspace and must not overlap in time."""
+    o, hT, _ = _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, 0, None,
+                      split="noalloc")
     return o, hT
 
 
@@ -163,7 +176,12 @@ def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_st
     else:
         hT = None
     stream = torch.cuda.current_stream(dev).cuda_stream
-    if split:
+    if split == "noalloc":
+        rc = lib.kda_chunk_fwd_split_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                                             _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code,
+                                             _ptr(o), _ptr(hT), stream)
+        _check(rc, "kda_chunk_fwd_split_noalloc")
+    elif split:
         need = ctypes.c_size_t(0)
         rc = lib.kda_chunk_fwd_split_workspace_size(n_seqs, T_total, H, dk, dv, int(chunk_size), code,
                                                     ctypes.byref(need))

@@ -15,6 +15,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kda.h")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 KDA_DTYPE_F32, KDA_DTYPE_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 256 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 # Every function include/kda.h declares, with its ctypes signature.
 _P, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
@@ -25,6 +26,8 @@ SIGNATURES = {
                                                   _I32, ctypes.c_int, _P, _P, _I32, _P, _P]),
     "kda_chunk_fwd_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                            _I32, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]),
+    "kda_chunk_fwd_split_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
+                                                   _I32, ctypes.c_int, _P, _P, _P]),
     "kda_chunk_fwd_split_workspace_size": (ctypes.c_int, [_I32, _I64, _I32, _I32, _I32, _I32, ctypes.c_int,
                                                           ctypes.POINTER(ctypes.c_size_t)]),
     "kda_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, ctypes.c_int,

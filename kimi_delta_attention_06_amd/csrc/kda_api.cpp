@@ -5,7 +5,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kda_launch.hpp"
+
+// The workspace of kda_chunk_fwd_split_noalloc: one array per GPU in the library's device
+// memory.  Host code never uses its name as an address: each device's address is looked up
+// once with hipGetSymbolAddress (scratch_address) and that pointer goes to the kernels.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -24,6 +31,28 @@ bool overlap(const Range& a, const Range& b) {
   return a.n && b.n && pa < pb + b.n && pb < pa + a.n;
 }
 
+// The device address of `scratch` on the current device: looked up on the first call per device
+// (devices past the 64th look it up on every call).
+std::mutex scratch_mu;
+void* scratch_ptr[64] = {};
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (dev >= 0 && dev < 64 && scratch_ptr[dev]) {
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!p) return hipErrorInvalidSymbol;
+  if (dev >= 0 && dev < 64) scratch_ptr[dev] = p;
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -32,7 +61,7 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
                                const float* beta, const float* h0, const int32_t* cu_seqlens, int32_t n_seqs,
                                int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk_size,
                                kda_dtype qkv_dtype, float* o, float* hT, int32_t ckpt_every, float* ckpt,
-                               bool split, void* ws, size_t ws_bytes, void* stream) {
+                               bool split, void* ws, size_t ws_bytes, void* stream, bool noalloc = false) {
   if (n_seqs < 0 || total_tokens < 0 || n_heads <= 0 || dk <= 0 || dv <= 0 || chunk_size <= 0)
     return KDA_ERR_INVALID_ARGUMENT;
   // checkpoints: ckpt_every > 0 and a multiple of the chunk size; ckpt holds
@@ -106,6 +135,12 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   if (split) {
     if (!bf16) return KDA_ERR_UNSUPPORTED;
     const size_t need = kda::chunk_split_workspace_bytes(total_tokens, n_seqs, n_heads, dk, dv, chunk_size);
+    if (noalloc && n_seqs > 0 && total_tokens > 0) {
+      // the library's own array in place of a caller workspace
+      if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_UNSUPPORTED;
+      if (scratch_address(&ws) != hipSuccess) return KDA_ERR_LAUNCH;
+      ws_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
     if (n_seqs > 0 && total_tokens > 0) {
       if (!ws || !aligned16(ws) || ws_bytes < need) return KDA_ERR_INVALID_ARGUMENT;
       // the workspace must not overlap any input or output
@@ -166,6 +201,15 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
                                void* stream) {
   return chunk_common(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, chunk_size,
                       qkv_dtype, o, hT, 0, nullptr, true, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                                       const float* beta, const float* h0, const int32_t* cu_seqlens,
+                                       int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,
+                                       int32_t dv, int32_t chunk_size, kda_dtype qkv_dtype, float* o, float* hT,
+                                       void* stream) {
+  return chunk_common(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, chunk_size,
+                      qkv_dtype, o, hT, 0, nullptr, true, nullptr, 0, stream, true);
 }
 
 kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -20,7 +20,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_checkpointed", "kda_chunk_fwd_split",
-                          "kda_chunk_fwd_split_workspace_size", "kda_bwd", "kda_bwd_workspace_size",
+                          "kda_chunk_fwd_split_workspace_size", "kda_chunk_fwd_split_noalloc",
+                          "kda_bwd", "kda_bwd_workspace_size",
                           "kda_bwd_recurrent", "kda_bwd_recurrent_workspace_size",
                           "kda_recurrent_step",
                           "kda_recurrent_verify", "kda_status_string", "kda_version"}
@@ -249,3 +250,22 @@ def test_bwd_rejects(fn, kw, code):
 def test_bwd_empty_batch_is_a_no_op(fn):
     assert bwd_call(fn, N=0, T=0, q=None, k=None, v=None, la=None, b=None, do=None, dq=None, dkk=None, dvv=None,
                     dla=None, db=None, ws=None, wsb=0) == 0
+
+
+def noalloc_call(**kw):
+    a = dict(q=P, k=P, v=P, la=P, b=P, h0=None, cu=None, N=1, T=64, H=2, dk=128, dv=128, C=64,
+             dt=_lib.KDA_DTYPE_BF16, o=P * 8, hT=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_split_noalloc(a["q"], a["k"], a["v"], a["la"], a["b"], a["h0"], a["cu"], a["N"], a["T"],
+                                           a["H"], a["dk"], a["dv"], a["C"], a["dt"], a["o"], a["hT"], None)
+
+
+def test_noalloc_rejects_sizes_past_its_array():
+    # the workspace of 32 heads x (4096 / 64 + 2) chunk slots (66,304 B each) + 32 states fits in 256 MiB;
+    # 8,192 tokens do not
+    need = lambda T: ((T // 64) + 2) * 32 * 66304 + 32 * 128 * 128 * 4
+    assert need(4096) <= _lib.NOALLOC_SCRATCH_BYTES < need(8192)
+    assert noalloc_call(T=8192, H=32, o=1 << 40, q=1 << 36, k=1 << 36, v=1 << 36, la=1 << 37, b=1 << 38) == 2
+    assert noalloc_call(dt=_lib.KDA_DTYPE_F32) == 2
+    assert noalloc_call(q=None) == 1 and noalloc_call(o=P) == 1  # o overlaps q
+    assert noalloc_call(N=0, T=0, q=None, k=None, v=None, la=None, b=None, o=None) == 0
