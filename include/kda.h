@@ -21,16 +21,20 @@
  *   q, k       [T_total, H, dk]   token-major, heads inner (a fixed-length
  *                                  [B, T, H, d] tensor is the same memory)
  *   v          [T_total, H, dv]
- *   log_alpha  [T_total, H, dk]   fp32, finite, <= 0
+ *   log_alpha  [T_total, H, dk]   fp32, <= 0 (a gate in [0, 1]); any finite value
  *   beta       [T_total, H]       fp32, in [0, 1]
  *   o          [T_total, H, dv]   fp32 output
  *   h0, hT     [N, H, dk, dv]     fp32 states
  *   cu_seqlens [N + 1]            int32 offsets of packed sequences
  *
  * Ownership and threading.  The caller allocates and frees every buffer.  The
- * library allocates nothing, keeps no mutable global state and is safe to call
- * from several host threads.  All pointers except cu_seqlens-for-fixed-length,
- * h0 and hT are required.  Device pointers must be 16-byte aligned.
+ * library allocates no memory at run time and is safe to call from several host
+ * threads.  Its only mutable global state is set up once and never read back:
+ * one word per kernel that records, thread-safely, on which devices the kernel's
+ * LDS limit was raised, and the per-device address of the fixed device array of
+ * kda_chunk_fwd_split_noalloc (looked up under a lock).  All pointers except
+ * cu_seqlens-for-fixed-length, h0 and hT are required.  Device pointers must be
+ * 16-byte aligned.
  *
  * Asynchrony and errors.  Calls enqueue kernels on `stream` (a hipStream_t;
  * NULL is the default stream) and return at once; results are valid once the
@@ -86,11 +90,17 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
  *                hT may alias h0 (in-place advance); o must not alias any input.
  *
  * Supported: dk, dv in {64, 128}; chunk_size in {16, 32, 64}; qkv_dtype F32 or
- * BF16 (F32 supports chunk_size <= 32 when dk = dv = 128).  Other shapes return
- * KDA_ERR_UNSUPPORTED.  Preconditions not checked on the device: the decay over
- * any 16 consecutive tokens of a chunk satisfies sum(log_alpha) > -170 per
- * channel; with BF16 inputs the state, values and intermediate chunk results
- * stay below 6e4 in magnitude (fp16 matrix-core operands).
+ * BF16 (F32 with dk = 128 and chunk_size 64 runs in chunks of 32 tokens, which
+ * changes only the rounding).  Other shapes return KDA_ERR_UNSUPPORTED.
+ *
+ * Range.  Any finite log_alpha <= 0 and any bf16 magnitude of q, k, v and h0 are
+ * taken.  A token's log_alpha below -110.9 nats (-160 in base 2) counts as -110.9
+ * (a factor of 6.6e-49 is already 0 against any other term in fp32).  A 16-token
+ * block whose decay spread exceeds 160 nats forms its decayed Gram products
+ * element by element, exactly, instead of from factors balanced around the
+ * block's middle.  With BF16 inputs the state and values of each chunk are
+ * scaled by a power of two chosen per chunk to fit the fp16 matrix-core operands;
+ * o and hT are scaled back.  NaN inputs give NaN outputs where they reach.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                          const float* beta, const float* h0, const int32_t* cu_seqlens,
@@ -224,11 +234,12 @@ kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_toke
  *
  * Outputs and the workspace must not overlap any input or each other.  All
  * pointers 16-byte aligned.  Supported: dk, dv in {64, 128}; qkv_dtype F32 or
- * BF16.  Precondition not checked on the device: every 16-token chunk (counted
- * from each sequence start) decays by less than 120 nats per channel
- * (sum(log_alpha) > -120); kda_bwd_recurrent has no such bound.  Errors as
- * kda_chunk_fwd, plus KDA_ERR_INVALID_ARGUMENT for a missing, small or
- * overlapping workspace or overlapping outputs.
+ * BF16.  Any finite log_alpha <= 0: a token's log_alpha below -110 nats counts
+ * as -110, and a 16-token chunk that decays by more than 64 nats in some channel
+ * forms its decay factors element by element (exactly) instead of balanced
+ * around the chunk's middle.  Errors as kda_chunk_fwd, plus
+ * KDA_ERR_INVALID_ARGUMENT for a missing, small or overlapping workspace or
+ * overlapping outputs.
  */
 kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
                    const float* h0, const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t n_heads,
@@ -250,7 +261,8 @@ kda_status kda_bwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t 
  * Differentiates the recurrence one token at a time in fp32 (the reverse mode of
  * the per-token update, the same passage as kda_bwd): the state at the start of
  * every 64-token segment is kept in `workspace`, each segment's per-token states are
- * recomputed into it, and the adjoint runs backwards over them.  No decay bound;
+ * recomputed into it, and the adjoint runs backwards over them.  It shares none of
+ * kda_bwd's chunk algebra (a cross-check of it) and is
  * much slower than kda_bwd on long sequences.  Arguments, outputs and errors as
  * kda_bwd, with kda_bwd_recurrent_workspace_size bytes of workspace.
  */

@@ -91,7 +91,8 @@ def test_backward_chunk_boundaries(lens):
 
 def test_backward_chunk_strong_decay():
     """Gate law x5: about 4 nats per token and channel on average, ~65 per 16-token chunk and
-    ~105 at most (inside the 120-nat bound), so the balanced Gram operands span up to ~e^52."""
+    ~105 at most, so chunks fall on both sides of the 64-nat switch between decay factors
+    balanced around the chunk's middle and the exact elementwise ones."""
     inp = kda_inputs.make_custom_chunk_inputs([200, 45], 2, 128, 128, torch.bfloat16, gate_scale=5.0, h0_std=0.02,
                                               seed=77, device="cuda")
     la = inp["log_alpha"].double()
