@@ -427,6 +427,28 @@ __device__ __forceinline__ void unpack(const uint4* w, float* out, int n) {
 }
 
 // ---------------------------------------------------------------------------
+// Workspace tile of the split path: one chunk's state-free operands for one head, in
+// 16-byte units.  The fp16 matrices are stored in matrix-core fragment order: for a
+// [rows][K] matrix (K padded to a multiple of 32 with zeros), unit
+// ((rb * K/32 + s) * 64 + lane) holds row 16 rb + (lane & 15), elements
+// 32 s + 8 (lane >> 4) .. +7, so that the operand of one k-step for one 16-row block is
+// 1 KB of consecutive units, one per lane.  The two fp32 vectors follow in plain order.
+// ---------------------------------------------------------------------------
+template <int C, int DK>
+struct WsTile {
+  static constexpr int CK = ((C + 31) / 32) * 32;                    // token k-extent
+  static constexpr int NSD = DK / 32, NSC = CK / 32;                 // k-steps over channels / tokens
+  static constexpr int QG = 0;                                       // Qg   [C][DK]
+  static constexpr int KG = QG + C * DK / 8;                         // Kg   [C][DK]
+  static constexpr int KDT = KG + C * DK / 8;                        // Kd^T [DK][CK]
+  static constexpr int AQ = KDT + DK * CK / 8;                       // strict M [C][CK]
+  static constexpr int TB = AQ + C * CK / 8;                         // T Diag(beta) [C][CK]
+  static constexpr int DQ = TB + C * CK / 8;                         // q.k [C] fp32
+  static constexpr int GM = DQ + C / 4;                              // e^{g_last} [DK] fp32
+  static constexpr int NU = GM + DK / 4;
+};
+
+// ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
 // PREP = false: the fused forward.  PREP = true: the intra-chunk part only, for a group of
@@ -733,30 +755,35 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   // Kd^T [DK][C], strict M [C][C], T Diag(beta) [C][C] (all T), then q.k [C] and e^{g_last}
   // [DK] (fp32).  Slot of chunk j of the sequence starting at token t0: t0 / C + n + j.
   auto write_ws = [&](int64_t chn) {
-    constexpr int U8 = 16 / (int)sizeof(T);
-    constexpr int NQ = C * DK / U8, NKD = DK * C / U8, NAQ = C * C / U8, NDQ = C / 4, NGM = DK / 4;
-    constexpr int NU = 2 * NQ + NKD + 2 * NAQ + NDQ + NGM;
+    using W = WsTile<C, DK>;
+    static_assert(!PREP || sizeof(T) == 2, "fp16 operands");
     const int64_t slot = t_begin / C + n + chn;
-    uint4* dst = reinterpret_cast<uint4*>(ws) + ((size_t)slot * H + h) * NU;
-    for (int i = tid; i < NU; i += NT) {
-      const void* src;
-      if (i < 2 * NQ) {
-        const int ii = i < NQ ? i : i - NQ;
-        src = (i < NQ ? sQG : sKG) + (ii / (DK / U8)) * LDD + (ii % (DK / U8)) * U8;
-      } else if (i < 2 * NQ + NKD) {
-        const int ii = i - 2 * NQ;
-        src = sKDT + (ii / (C / U8)) * LDC + (ii % (C / U8)) * U8;
-      } else if (i < 2 * NQ + NKD + 2 * NAQ) {
-        const int ii0 = i - 2 * NQ - NKD, ii = ii0 < NAQ ? ii0 : ii0 - NAQ;
-        src = (ii0 < NAQ ? sAQ : sTB) + (ii / (C / U8)) * LDC + (ii % (C / U8)) * U8;
-      } else if (i < NU - NGM) {
-        src = sDQ + 4 * (i - (NU - NGM - NDQ));
+    uint4* dst = reinterpret_cast<uint4*>(ws) + ((size_t)slot * H + h) * W::NU;
+    for (int i = tid; i < W::NU; i += NT) {
+      // byte offset in LDS of unit i's source
+      uint32_t off;
+      bool pad = false;  // a k-unit past the chunk's tokens: zero
+      if (i < W::KDT) {
+        // Qg, Kg: rows are tokens, k runs over the key channels
+        const int ii = i < W::KG ? i : i - W::KG, f = ii >> 6, ln = ii & 63;
+        const int row = 16 * (f / W::NSD) + (ln & 15), k0 = 32 * (f % W::NSD) + 8 * (ln >> 4);
+        off = (uint32_t)(i < W::KG ? L::QG : L::KG) + (uint32_t)(row * LDD + k0) * 2u;
+      } else if (i < W::DQ) {
+        // Kd^T (rows: channels), M and T Diag(beta) (rows: tokens); k runs over the tokens
+        const int ii = i < W::AQ ? i - W::KDT : (i < W::TB ? i - W::AQ : i - W::TB), f = ii >> 6, ln = ii & 63;
+        const int row = 16 * (f / W::NSC) + (ln & 15), k0 = 32 * (f % W::NSC) + 8 * (ln >> 4);
+        pad = k0 >= C;
+        off = (uint32_t)(i < W::AQ ? L::KDT : (i < W::TB ? L::AQ : L::TB)) + (uint32_t)(row * LDC + (pad ? 0 : k0)) * 2u;
+      } else if (i < W::GM) {
+        off = (uint32_t)L::DQ + (uint32_t)(i - W::DQ) * 16u;
       } else {
-        src = sGM + 4 * (i - (NU - NGM));
+        off = (uint32_t)L::GM + (uint32_t)(i - W::GM) * 16u;
       }
       // written once, read once by the state pass much later: a streaming store
       typedef unsigned int u32x4w __attribute__((ext_vector_type(4)));
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4w*>(src), reinterpret_cast<u32x4w*>(dst) + i);
+      u32x4w val = *reinterpret_cast<const u32x4w*>(smem + off);
+      if (pad) val = u32x4w{0u, 0u, 0u, 0u};
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4w*>(dst) + i);
     }
   };
   auto store_pending = [&]() {
@@ -1519,34 +1546,25 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
 // State-only kernel of the split path.  Per (sequence, head, value tile) it walks the
 // chunks in order with the fp32 master state in accumulator registers:
 //   Y = V - Kg S,  U = (T Diag beta) Y,  O = Qg S + M U + diag(q.k) U,  S <- Diag(gamma) S + Kd^T U,
-// reading each chunk's state-free operands from the workspace tile the prep pass wrote
-// (same units and order as write_ws).  The next chunk's tile is loaded into registers
-// while the current one is used and moved to LDS after its last read.
+// reading each chunk's state-free operands from the workspace tile the prep pass wrote.
+// Those operands go from memory straight into the registers of the matrix-core products
+// (each wave loads the fragments of its own row blocks, one chunk ahead, right after the
+// products of this chunk that used the same registers); only the operands that depend on
+// the state (S^T, Y^T, U^T) pass through LDS.  Three barriers per chunk; the values go
+// from memory straight to registers in the layout of the Y product.  Each fragment is
+// loaded by exactly one wave (see the wave roles below): the vector memory path of the CU,
+// not its matrix cores, bounds this loop.
 // ---------------------------------------------------------------------------
 template <int C, int DK, int BV>
 struct SLay {
   static constexpr int KS = 32, PD = 8, NB = C / 16;
-  static constexpr int CK = ((C + KS - 1) / KS) * KS;
-  static constexpr int LDD = DK + PD, LDC = CK + PD, LDV = BV + PD;
+  static constexpr int CK = WsTile<C, DK>::CK;
+  static constexpr int LDD = DK + PD, LDC = CK + PD;
   static constexpr size_t ST = 0;                                   // S^T [BV][LDD]
-  static constexpr size_t T0 = ST + al16(size_t(BV) * LDD * 2);     // chunk tile buffer(s)
-  // offsets inside a chunk tile buffer
-  static constexpr size_t QG = 0;                                   // Qg [C][LDD]
-  static constexpr size_t KG = QG + al16(size_t(C) * LDD * 2);      // Kg [C][LDD]
-  static constexpr size_t KDT = KG + al16(size_t(C) * LDD * 2);     // Kd^T [DK][LDC]
-  static constexpr size_t AQ = KDT + al16(size_t(DK) * LDC * 2);    // strict M [C][LDC]
-  static constexpr size_t TB = AQ + al16(size_t(C) * LDC * 2);      // T Diag(beta) [C][LDC]
-  static constexpr size_t DQ = TB + al16(size_t(C) * LDC * 2);      // q.k [C] fp32
-  static constexpr size_t GM = DQ + al16(size_t(C) * 4);            // e^{g_last} [DK] fp32
-  static constexpr size_t VR = GM + al16(size_t(DK) * 4);           // V [C][LDV]
-  static constexpr size_t TILE = VR + al16(size_t(C) * LDV * 2);
-  static constexpr size_t YT = T0 + TILE;                           // Y^T [BV][LDC]
+  static constexpr size_t YT = ST + al16(size_t(BV) * LDD * 2);     // Y^T [BV][LDC]
   static constexpr size_t UT = YT + al16(size_t(BV) * LDC * 2);     // U^T [BV][LDC]
   static constexpr size_t MX = UT + al16(size_t(BV) * LDC * 2);     // per-wave largest |S|, |v| [NW]
   static constexpr size_t TOTAL = MX + al16(size_t(NW) * 4);
-  // workspace tile in 16-byte units
-  static constexpr int NQ = C * DK / 8, NKD = DK * C / 8, NAQ = C * C / 8, NDQ = C / 4, NGM = DK / 4;
-  static constexpr int NU = 2 * NQ + NKD + 2 * NAQ + NDQ + NGM;
 };
 
 // Chunks [ch_begin, ch_end) of every chain (clipped to the chain's length).  The state
@@ -1558,36 +1576,26 @@ __device__ __forceinline__ void chunk_state_body(
     const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT,
     int n_chains, int H, int DV, int64_t seq_len, int bid, int64_t ch_begin, int64_t ch_end, float* carry) {
   using L = SLay<C, DK, BV>;
+  using W = WsTile<C, DK>;
   using T = _Float16;
-  constexpr int KS = L::KS, NB = L::NB, CK = L::CK;
-  constexpr int LDD = L::LDD, LDC = L::LDC, LDV = L::LDV;
-  constexpr int NA = DK / 16, NJ = BV / 16, VPR = BV / 8;
-  constexpr int NQ = L::NQ, NKD = L::NKD, NAQ = L::NAQ, NDQ = L::NDQ, NGM = L::NGM, NU = L::NU;
-  constexpr int PF = (NU + NT - 1) / NT;
-  static_assert(sizeof(InT) == 2 && C * VPR <= NT, "bf16 values, one 16-byte load per lane");
+  constexpr int NB = L::NB, LDD = L::LDD, LDC = L::LDC, NSD = W::NSD, NSC = W::NSC;
+  constexpr int NA = DK / 16, NJ = BV / 16;
+  static_assert(sizeof(InT) == 2, "bf16 values");
+  static_assert(NW % NA == 0, "the state tiles of a wave share one row block of Kd^T");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* sST = reinterpret_cast<T*>(smem + L::ST);
   T* sYT = reinterpret_cast<T*>(smem + L::YT);
   T* sUT = reinterpret_cast<T*>(smem + L::UT);
   uint32_t* sMX = reinterpret_cast<uint32_t*>(smem + L::MX);
-  unsigned char* tb = smem + L::T0;  // the chunk tile
-  T* sQG = reinterpret_cast<T*>(tb + L::QG);
-  T* sKG = reinterpret_cast<T*>(tb + L::KG);
-  T* sKDT = reinterpret_cast<T*>(tb + L::KDT);
-  T* sAQ = reinterpret_cast<T*>(tb + L::AQ);
-  T* sTB = reinterpret_cast<T*>(tb + L::TB);
-  float* sDQ = reinterpret_cast<float*>(tb + L::DQ);
-  float* sGM = reinterpret_cast<float*>(tb + L::GM);
-  T* sV = reinterpret_cast<T*>(tb + L::VR);
 
   const int ntile = DV / BV;
   const int xcd = bid & 7, qd = bid >> 3;
-  const int tile = qd % ntile;
+  const int tl = qd % ntile;
   const int chain = (qd / ntile) * 8 + xcd;
   if (chain >= n_chains) return;
   const int n = chain / H, h = chain - n * H;
-  const int j0 = tile * BV;
+  const int j0 = tl * BV;
   int64_t t_begin, t_end;
   if (cu_seqlens) {
     t_begin = cu_seqlens[n];
@@ -1608,144 +1616,137 @@ __device__ __forceinline__ void chunk_state_body(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l = lane_id(), lr = l & 15, lg = l >> 4;
 
-  // zero once: the padded token columns (C .. CK) of the token-contiguous operands stay zero
-  for (int i = tid; i < int((L::MX - L::T0) / 2); i += NT) reinterpret_cast<T*>(smem + L::T0)[i] = (T)0.f;
+  // zero once: the padded token columns (C .. CK) of Y^T and U^T stay zero
+  for (int i = tid; i < int(L::TOTAL / 16); i += NT) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
 
   constexpr int S_SLOTS = (NA * NJ + NW - 1) / NW;
   f32x4 Sacc[S_SLOTS];
   const float* h0p = ch_begin > 0 ? carry + (size_t)chain * DK * DV : (h0 ? h0 + (size_t)chain * DK * DV : nullptr);
+  auto s_active = [&](int s) { return (NA * NJ) % NW == 0 || wave + NW * s < NA * NJ; };
+  const int sa = wave % NA;  // row block of every state tile of this wave: tile (sa, (wave + NW s) / NA)
 #pragma unroll
   for (int s = 0; s < S_SLOTS; ++s) {
-    const int id = wave + NW * s;
+    const int j = (wave + NW * s) / NA;
     Sacc[s] = zero4();
-    if (id < NA * NJ && h0p) {
-      const int a = id % NA, j = id / NA;
+    if (s_active(s) && h0p) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr];
+      for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * sa + 4 * lg + i) * DV + j0 + 16 * j + lr];
     }
   }
   // The 16-bit state copy.  The fp32 state is held in the chunk's scaled units 2^-e (see
   // range_exponent); o, hT and the hand-over state are scaled back by 2^e.
   auto write_ST = [&]() {
 #pragma unroll
-    for (int s = 0; s < S_SLOTS; ++s) {
-      const int id = wave + NW * s;
-      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
-        const int a = id % NA, j = id / NA;
-        store4(sST + (16 * j + lr) * LDD + 16 * a + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
+    for (int s = 0; s < S_SLOTS; ++s)
+      if (s_active(s)) {
+        const int j = (wave + NW * s) / NA;
+        store4(sST + (16 * j + lr) * LDD + 16 * sa + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
       }
-    }
   };
   auto store_state = [&](float* sp, float f) {
 #pragma unroll
-    for (int s = 0; s < S_SLOTS; ++s) {
-      const int id = wave + NW * s;
-      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
-        const int a = id % NA, j = id / NA;
+    for (int s = 0; s < S_SLOTS; ++s)
+      if (s_active(s)) {
+        const int j = (wave + NW * s) / NA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * a + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i] * f;
+        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * sa + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i] * f;
       }
-    }
   };
 
-  constexpr int U_SLOTS = (NB * NJ + NW - 1) / NW;
-  constexpr bool UO_SPLIT = NB == 4 && NJ == 4 && NW == 8;
-  auto uo_tile = [&](int s, int& R, int& j) {
-    if constexpr (UO_SPLIT) {
-      R = 2 * s + (wave >> 2);
-      j = wave & 3;
-    } else {
-      const int id = wave + NW * s;
-      R = id % NB;
-      j = id / NB;
-    }
-  };
+  // Wave roles: wave R < NB (an "O wave") owns token row block R of Qg S, U and O over all
+  // NJ value tiles; wave NB + R (a "K wave") owns row block R of Kg S and Y.  Every operand
+  // fragment of the workspace tile is then loaded by one wave only.
+  static_assert(2 * NB <= NW, "two waves per token row block");
+  const bool o_wave = wave < NB, k_wave = wave >= NB && wave < 2 * NB;
+  const int R = o_wave ? wave : wave - NB;
+  const int tri = (16 * R + 15) / 32 + 1;  // k-steps of T Diag(beta) and M that reach row block R
 
-  // next chunk's workspace tile and value rows, in registers
-  uint4 pf[PF], pv = make_uint4(0, 0, 0, 0);
-  const bool v_act = C * VPR >= NT || tid < C * VPR;
-  const int v_row = tid / VPR, v_c0 = 8 * (tid % VPR);
-  // loads of units [p0, p1) of the tile of chunk chn (and of its value rows, first, with the
-  // first group: their magnitude is needed before the chunk's last barrier, and loads retire
-  // in order): the tile goes out in three groups, one per stage, so the device's requests do
-  // not all leave right after one barrier
-  auto load_tiles = [&](int64_t chn, int p0, int p1) {
-    const bool ok = chn < ch_stop;
-    if (p0 == 0) {
-      const int Lc = ok ? chunk_len(chn) : 0;
-      const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + j0,
-                                Lc > 0 ? (uint32_t)Lc * (uint32_t)(H * DV * 2) : 0u);
-      pv = buf_load16(rv, (uint32_t)(v_row * H * DV + v_c0) * 2u);
-    }
+  // ---- the chunk's operand fragments, loaded into the registers of the products: Qg (O
+  // waves) or Kg (K waves) rows of block R; T Diag(beta), M and q.k rows of block R (O waves);
+  // Kd^T rows of block sa and e^{g_last} (every wave with a state tile).
+  // Every wave issues the same memory instructions in the same order; an access a wave does
+  // not need goes through a descriptor of no bytes (or past its end) and returns zero without
+  // touching memory, and a store there is dropped.  The memory counter then has one count on
+  // every path, so each wait covers exactly the loads of the chunk before.
+  half8 gq[NSD], tb[NSC], aq[NSC], kdt[NSC];
+  float dq = 0.f;
+  float4 gm = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto tile_rsrc = [&](int64_t chn, bool mine) {
+    const bool ok = chn < ch_stop && mine;
     const int64_t slot = t_begin / C + n + chn;
-    const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * NU, ok ? (uint32_t)NU * 16u : 0u);
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-      if (p >= p0 && p < p1) pf[p] = buf_load16(rs, (uint32_t)(tid + p * NT) * 16u);
+    return make_rsrc(ws + ((size_t)(chn < ch_stop ? slot : 0) * H + h) * W::NU, ok ? (uint32_t)W::NU * 16u : 0u);
   };
-  constexpr int PG1 = PF / 3, PG2 = 2 * PF / 3;
-  // the loaded tile to LDS; the values in the operand type, scaled like write_ST
-  auto store_tiles = [&](auto scaled, float f) {
+  auto frag = [&](__amdgpu_buffer_rsrc_t rs, int region, int f) {
+    return __builtin_bit_cast(half8, buf_load16(rs, (uint32_t)(region + 64 * f + l) * 16u));
+  };
+  constexpr uint32_t kPast = 0x7ffffff0u;  // an offset past the end of any tile
+  const int Rl = (o_wave || k_wave) ? R : 0;
+  auto load_gq = [&](int64_t chn) {
+    const auto rs = tile_rsrc(chn, o_wave || k_wave);
+    const int region = o_wave ? W::QG : W::KG;
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int i = tid + p * NT;
-      if (NU % NT == 0 || i < NU) {
-        void* dst;
-        if (i < 2 * NQ) {
-          const int ii = i < NQ ? i : i - NQ;
-          dst = (i < NQ ? sQG : sKG) + (ii / (DK / 8)) * LDD + (ii % (DK / 8)) * 8;
-        } else if (i < 2 * NQ + NKD) {
-          const int ii = i - 2 * NQ;
-          dst = sKDT + (ii / (C / 8)) * LDC + (ii % (C / 8)) * 8;
-        } else if (i < 2 * NQ + NKD + 2 * NAQ) {
-          const int ii0 = i - 2 * NQ - NKD, ii = ii0 < NAQ ? ii0 : ii0 - NAQ;
-          dst = (ii0 < NAQ ? sAQ : sTB) + (ii / (C / 8)) * LDC + (ii % (C / 8)) * 8;
-        } else if (i < NU - NGM) {
-          dst = sDQ + 4 * (i - (NU - NGM - NDQ));
-        } else {
-          dst = sGM + 4 * (i - (NU - NGM));
-        }
-        *reinterpret_cast<uint4*>(dst) = pf[p];
-      }
+    for (int st = 0; st < NSD; ++st) gq[st] = frag(rs, region, Rl * NSD + st);
+  };
+  auto load_tb = [&](int64_t chn) {
+    const auto rs = tile_rsrc(chn, o_wave);
+#pragma unroll
+    for (int st = 0; st < NSC; ++st)
+      tb[st] = __builtin_bit_cast(half8, buf_load16(rs, st < tri ? (uint32_t)(W::TB + 64 * (Rl * NSC + st) + l) * 16u : kPast));
+  };
+  auto load_aq = [&](int64_t chn) {
+    const auto rs = tile_rsrc(chn, o_wave);
+#pragma unroll
+    for (int st = 0; st < NSC; ++st)
+      aq[st] = __builtin_bit_cast(half8, buf_load16(rs, st < tri ? (uint32_t)(W::AQ + 64 * (Rl * NSC + st) + l) * 16u : kPast));
+    dq = buf_load4(rs, (uint32_t)W::DQ * 16u + (uint32_t)(16 * Rl + lr) * 4u);
+  };
+  auto load_kd = [&](int64_t chn) {
+    const auto rs = tile_rsrc(chn, s_active(0));
+#pragma unroll
+    for (int st = 0; st < NSC; ++st) kdt[st] = frag(rs, W::KDT, sa * NSC + st);
+    gm = __builtin_bit_cast(float4, buf_load16(rs, (uint32_t)W::GM * 16u + (uint32_t)(16 * sa + 4 * lg) * 4u));
+  };
+  // (every wave issues the loads; the descriptor of a wave other than a K wave has no bytes, so
+  // its loads return zeros without touching memory and need no branch)
+  uint2 vnx[NJ];
+  auto load_v = [&](int64_t chn) {
+    const bool ok = chn < ch_stop;
+    const int Lc = ok ? chunk_len(chn) : 0;
+    const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + j0,
+                              (k_wave && Lc > 0) ? (uint32_t)Lc * (uint32_t)(H * DV * 2) : 0u);
+    const int Rv = k_wave ? R : 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      typedef int i32x2 __attribute__((ext_vector_type(2)));
+      const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(
+          rv, (int)(((uint32_t)(16 * Rv + lr) * (uint32_t)(H * DV) + (uint32_t)(16 * j + 4 * lg)) * 2u), 0, 0);
+      vnx[j] = make_uint2((uint32_t)x[0], (uint32_t)x[1]);
     }
-    if (v_act) {
-      const uint4* pw = &pv;
-      float vv[8];
-      unpack<InT>(pw, vv, 8);
-      if constexpr (decltype(scaled)::value) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vv[i] *= f;
-      }
-      store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
-      store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
-    }
-    // every loaded register is used on every path (see retire), so no load is still
-    // pending where the next chunk reuses its registers
-#pragma unroll
-    for (int p = 0; p < PF; ++p) retire(pf[p]);
-    retire(pv);
   };
   int sc_e = 0;
   float sc_dn = 1.f, sc_up = 1.f;
   // largest |S| and |v| of the next chunk (in the chunk's scaled units) over the wave, to LDS
   auto publish_range = [&]() {
-    uint32_t mv = 0;
-    if (v_act) {
-      const uint32_t w4[4] = {pv.x, pv.y, pv.z, pv.w};
-      mv = mag_max_bf16(w4, 4);
+    uint32_t w[2 * NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      w[2 * j] = vnx[j].x;
+      w[2 * j + 1] = vnx[j].y;
     }
+    const uint32_t mv = mag_max_bf16(w, 2 * NJ);
     float sv[4 * S_SLOTS];
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * s + i] = ((NA * NJ) % NW == 0 || wave + NW * s < NA * NJ) ? Sacc[s][i] : 0.f;
+      for (int i = 0; i < 4; ++i) sv[4 * s + i] = s_active(s) ? Sacc[s][i] : 0.f;
     uint32_t m = max(mag_max<4 * S_SLOTS>(sv), sc_e == 0 ? mv : mag_scaled(mv, sc_e));
     m = wave_max_u32(m);
     if (l == 0) sMX[wave] = m;
   };
-  // after a barrier: the next chunk's range exponent from every wave's figures (the held state
-  // is rescaled to its units when it changes), then its state and tile to LDS
-  auto stage_next = [&]() {
+  // after the barrier that follows publish_range: the next chunk's range exponent from every
+  // wave's figure.  When it changes (rarely) the held state is rescaled to the new units and
+  // its 16-bit copy, already written in the old units, is written again.
+  auto settle_range = [&]() {
     static_assert(NW == 8, "16-byte reads of the per-wave maxima");
     const uint4 a0 = *reinterpret_cast<const uint4*>(sMX), a1 = *reinterpret_cast<const uint4*>(sMX + 4);
     const uint32_t m = max(max(max(a0.x, a0.y), max(a0.z, a0.w)), max(max(a1.x, a1.y), max(a1.z, a1.w)));
@@ -1758,103 +1759,124 @@ __device__ __forceinline__ void chunk_state_body(
       sc_e = e;
       sc_dn = pow2i(-e);
       sc_up = pow2i(e);
-    }
-    write_ST();
-    if (sc_e == 0) {
-      store_tiles(std::false_type{}, 1.f);
-    } else {
-      store_tiles(std::true_type{}, sc_dn);
+      write_ST();
+      __syncthreads();
     }
   };
 
-  __syncthreads();  // zero fill before the first tile
-  load_tiles(ch_begin, 0, PF);
+  load_gq(ch_begin);
+  load_tb(ch_begin);
+  load_aq(ch_begin);
+  load_kd(ch_begin);
+  load_v(ch_begin);
+  __syncthreads();  // zero fill before the first state copy
+  write_ST();
   publish_range();
   __syncthreads();
-  stage_next();
-  __syncthreads();
+  settle_range();
 
-  f32x4 Uacc[U_SLOTS], Oacc[U_SLOTS];
+  // acc: Qg S, then O (O waves) or Kg S (K waves); Uacc: U (O waves)
+  f32x4 acc[NJ], Uacc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = Uacc[j] = zero4();
   for (int64_t ch = ch_begin; ch < ch_stop; ++ch) {
     const int64_t c_begin = t_begin + ch * C;
     const int Lc = chunk_len(ch);
-    const int64_t chl = ch + 1;  // the tile loaded next, to LDS after this chunk's last read
-    load_tiles(chl, 0, PG1);
+    // this chunk's values (loaded during the previous chunk); the next chunk's are loaded now
+    uint2 vcur[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) vcur[j] = vnx[j];
+    load_v(ch + 1);
 
-    // Y = V - Kg S (to Y^T) and O = Qg S
+    // Qg S (O waves) or Kg S (K waves), then Y = V - Kg S (to Y^T)
+    if (o_wave || k_wave) {
 #pragma unroll
-    for (int s = 0; s < U_SLOTS; ++s) {
-      const int id = wave + NW * s;
-      Oacc[s] = zero4();
-      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        int R, j;
-        uo_tile(s, R, j);
-        f32x4 ks = zero4();
-        mma_lds<T, KS, DK / KS>(ks, sST + 16 * j * LDD, LDD, sKG + 16 * R * LDD, LDD);
-        mma_lds<T, KS, DK / KS>(Oacc[s], sST + 16 * j * LDD, LDD, sQG + 16 * R * LDD, LDD);
-        const float4 v4 = load4(sV + (16 * R + lr) * LDV + 16 * j + 4 * lg);
-        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+      for (int j = 0; j < NJ; ++j) acc[j] = zero4();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)(vv[i] - ks[i]);
-      }
+      for (int st = 0; st < NSD; ++st)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) mma_frag(acc[j], ld_frag(sST + (16 * j + lr) * LDD + 8 * lg + 32 * st), gq[st]);
     }
-    __syncthreads();
-
-    load_tiles(chl, PG1, PG2);
-    // U = (T Diag beta) Y (to U^T)
-    static_for<0, U_SLOTS>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
-                                     : CK / KS;
-      const int id = wave + NW * s;
-      Uacc[s] = zero4();
-      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        int R, j;
-        uo_tile(s, R, j);
-        mma_lds<T, KS, steps>(Uacc[s], sYT + 16 * j * LDC, LDC, sTB + 16 * R * LDC, LDC);
+    load_gq(ch + 1);
+    if (k_wave) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)Uacc[s][i];
-      }
-    });
-    __syncthreads();
-
-    load_tiles(chl, PG2, PF);
-    // O += M U + diag(q.k) U, stored; S <- Diag(gamma) S + Kd^T U (in the chunk's scaled units,
-    // then back)
-    static_for<0, U_SLOTS>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      constexpr int steps = UO_SPLIT ? ((32 * (s + 1) + KS - 1) / KS < CK / KS ? (32 * (s + 1) + KS - 1) / KS : CK / KS)
-                                     : CK / KS;
-      const int id = wave + NW * s;
-      if ((NB * NJ) % NW == 0 || id < NB * NJ) {
-        int R, j;
-        uo_tile(s, R, j);
-        mma_lds<T, KS, steps>(Oacc[s], sUT + 16 * j * LDC, LDC, sAQ + 16 * R * LDC, LDC);
-        const float dq = sDQ[16 * R + lr];
-        const int r = 16 * R + lr;
-        if (r < Lc) {
-          f32x4 ov;
+      for (int j = 0; j < NJ; ++j) {
+        const float2 v01 = bf16x2_to_f32x2(vcur[j].x), v23 = bf16x2_to_f32x2(vcur[j].y);
+        const float vv[4] = {v01.x, v01.y, v23.x, v23.y};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = (Oacc[s][i] + dq * Uacc[s][i]) * sc_up;
-          float* op = o + ((size_t)(c_begin + r) * H + h) * DV + j0 + 16 * j + 4 * lg;
-          *reinterpret_cast<float4*>(op) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        for (int i = 0; i < 4; ++i) {
+          // rounded to fp32, then to fp16, as in the fused forward (not in one step)
+          float y = vv[i] * sc_dn - acc[j][i];
+          asm volatile("" : "+v"(y));
+          sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)y;
         }
       }
-    });
+    }
+    __syncthreads();
+
+    // U = (T Diag beta) Y (to U^T)
+    if (o_wave) {
 #pragma unroll
-    for (int s = 0; s < S_SLOTS; ++s) {
-      const int id = wave + NW * s;
-      if ((NA * NJ) % NW == 0 || id < NA * NJ) {
-        const int a = id % NA, j = id / NA;
+      for (int j = 0; j < NJ; ++j) Uacc[j] = zero4();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Sacc[s][i] *= sGM[16 * a + 4 * lg + i];
-        mma_lds<T, KS, CK / KS>(Sacc[s], sKDT + 16 * a * LDC, LDC, sUT + 16 * j * LDC, LDC);
+      for (int st = 0; st < NSC; ++st)
+        if (st < tri) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) mma_frag(Uacc[j], ld_frag(sYT + (16 * j + lr) * LDC + 8 * lg + 32 * st), tb[st]);
+        }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sUT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)Uacc[j][i];
+    }
+    load_tb(ch + 1);
+    __syncthreads();
+
+    // O = Qg S + M U + diag(q.k) U, stored (O waves); S <- Diag(gamma) S + Kd^T U (in the
+    // chunk's scaled units)
+    if (o_wave) {
+#pragma unroll
+      for (int st = 0; st < NSC; ++st)
+        if (st < tri) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) mma_frag(acc[j], ld_frag(sUT + (16 * j + lr) * LDC + 8 * lg + 32 * st), aq[st]);
+        }
+    }
+    {
+      // o rows of the chunk (O waves; a store past the chunk's rows, or by another wave, is dropped)
+      const uint32_t hdv = (uint32_t)(H * DV);
+      const auto ro = make_rsrc(o + ((size_t)c_begin * H + h) * DV + j0, o_wave ? (uint32_t)Lc * hdv * 4u : 0u);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+        f32x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = (acc[j][i] + dq * Uacc[j][i]) * sc_up;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, ov), ro,
+                                               (int)(((uint32_t)(16 * Rl + lr) * hdv + (uint32_t)(16 * j + 4 * lg)) * 4u),
+                                               0, 0);
       }
     }
+    load_aq(ch + 1);
+#pragma unroll
+    for (int s = 0; s < S_SLOTS; ++s) {
+      if (s_active(s)) {
+        const int j = (wave + NW * s) / NA;
+        Sacc[s][0] *= gm.x;
+        Sacc[s][1] *= gm.y;
+        Sacc[s][2] *= gm.z;
+        Sacc[s][3] *= gm.w;
+        const T* pb = sUT + (16 * j + lr) * LDC + 8 * lg;
+#pragma unroll
+        for (int st = 0; st < NSC; ++st) mma_frag(Sacc[s], kdt[st], ld_frag(pb + 32 * st));
+      }
+    }
+    load_kd(ch + 1);
+    // S^T for the next chunk: every read of this chunk's S^T was before the first barrier
+    write_ST();
     publish_range();
-    __syncthreads();  // every read of this chunk's tile and of S^T is done
-    stage_next();
-    __syncthreads();
+    __syncthreads();  // S^T, every read of Y^T / U^T and the per-wave maxima
+    settle_range();
   }
   if (ch_stop == nchunks) {
     if (hT) store_state(hT + (size_t)chain * DK * DV, sc_up);
@@ -1916,7 +1938,7 @@ static int pick_bv(int n_chains, int dv, int max_bv);
 // ---- split path: prep pass (intra-chunk operands to the workspace), then the state pass
 #if KDA_CHUNK_SPLIT
 template <int C, int DK>
-constexpr size_t split_tile_bytes() { return size_t(SLay<C, DK, 16>::NU) * 16; }
+constexpr size_t split_tile_bytes() { return size_t(WsTile<C, DK>::NU) * 16; }
 
 // upper bound on chunks per sequence, known on the host without reading cu_seqlens
 static int64_t max_chunks_per_seq(const ChunkArgs& a) {
