@@ -667,22 +667,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   };
   GR gbuf;
   VR vbuf;
-  uint4 vkeep[VR::VW];
-#pragma unroll
-  for (int i = 0; i < VR::VW; ++i) vkeep[i] = make_uint4(0, 0, 0, 0);
-  // the chunk's values (held in vkeep) to LDS in the operand type, scaled like write_ST
-  auto write_V = [&](auto scaled, float f) {
-    if (!PREP && v_act) {
-      float vv[8];
-      unpack<InT>(vkeep, vv, 8);
-      if constexpr (decltype(scaled)::value) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vv[i] *= f;
-      }
-      store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
-      store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
-    }
-  };
   // The next chunk's inputs are loaded in four groups (q; k; the log-decay; v and beta),
   // issued in different stages: every CU runs the same stage at about the same time, and
   // one large group per chunk would be a device-wide burst that saturates HBM and stalls
@@ -942,11 +926,18 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     v_c0 = 8 * (tid % VPR);
     const int eR = e_act ? row_block_of<NB>(wave) : 0;
     if (!PREP && v_act) {
-      // the next chunk's values wait in registers until its range exponent is known (write_V)
-#pragma unroll
-      for (int i = 0; i < VR::VW; ++i) vkeep[i] = vbuf.v[i];
       if constexpr (kRanged) {
-        static_assert(sizeof(InT) == 2, "16-bit operands with bf16 inputs");
+        // the next chunk's values to LDS as they are (bf16): the chunk's range factor is
+        // applied where Y is formed, after its exponent is known
+        static_assert(sizeof(InT) == 2 && sizeof(T) == 2 && VR::VW == 1, "8 bf16 values per thread");
+        *reinterpret_cast<uint4*>(sV + v_row * LDV + v_c0) = vbuf.v[0];
+      } else {
+        float vv[8];
+        unpack<InT>(vbuf.v, vv, 8);
+        store4(sV + v_row * LDV + v_c0, vv[0], vv[1], vv[2], vv[3]);
+        store4(sV + v_row * LDV + v_c0 + 4, vv[4], vv[5], vv[6], vv[7]);
+      }
+      if constexpr (kRanged) {
         uint32_t w[4 * VR::VW];
 #pragma unroll
         for (int i = 0; i < VR::VW; ++i) {
@@ -1087,7 +1078,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       }
     }
 
-    // ================= the chunk's range exponent and its 16-bit S and V copies =================
+    // ================= the chunk's range exponent and its 16-bit state copy =================
     if constexpr (kRanged) {
       static_assert(NW == 8, "16-byte reads of the per-wave maxima");
       const uint4 a0 = *reinterpret_cast<const uint4*>(sMX), a1 = *reinterpret_cast<const uint4*>(sMX + 4);
@@ -1104,16 +1095,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
         sc_up = pow2i(e);
       }
     }
-    // (waves past the factor stage's DK threads write their copies now, the others after it)
+    // (waves past the factor stage's DK threads write their copy now, the others after it)
     auto write_copies = [&]() {
-      if constexpr (!PREP) {
-        write_ST();
-        if (sc_e == 0) {
-          write_V(std::false_type{}, 1.f);
-        } else {
-          write_V(std::true_type{}, sc_dn);
-        }
-      }
+      if constexpr (!PREP) write_ST();
     };
     if (tid >= DK) write_copies();
 
@@ -1378,10 +1362,22 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       // transposed (token contiguous) as the operand of U = T Diag(beta) Y.  With even tile
       // counts a wave takes a 2x2 block of tiles, so each operand fragment feeds two products.
       auto y_store = [&](int R, int j, const f32x4& ks) {
-        const float4 v4 = load4(sV + (16 * R + lr) * LDV + 16 * j + 4 * lg);
-        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+        if constexpr (kRanged) {
+#pragma clang fp contract(off)
+          // v (bf16 in LDS) in the chunk's scaled units; Y rounded to fp32, then to fp16 (no
+          // fused multiply-add: the product is exact, and one rounding straight to fp16 is
+          // what contraction would give)
+          const uint2 w = *reinterpret_cast<const uint2*>(sV + (16 * R + lr) * LDV + 16 * j + 4 * lg);
+          const float2 v01 = bf16x2_to_f32x2(w.x), v23 = bf16x2_to_f32x2(w.y);
+          const float vv[4] = {v01.x, v01.y, v23.x, v23.y};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(vv[i] - ks[i]);
+          for (int i = 0; i < 4; ++i) sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)(vv[i] * sc_dn - ks[i]);
+        } else {
+          const float4 v4 = load4(sV + (16 * R + lr) * LDV + 16 * j + 4 * lg);
+          const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = cvt<T>(vv[i] - ks[i]);
+        }
       };
       if constexpr (PREP) {
         // no state here: Y is formed by the state kernel
@@ -1799,17 +1795,14 @@ __device__ __forceinline__ void chunk_state_body(
     }
     load_gq(ch + 1);
     if (k_wave) {
+#pragma clang fp contract(off)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const float2 v01 = bf16x2_to_f32x2(vcur[j].x), v23 = bf16x2_to_f32x2(vcur[j].y);
         const float vv[4] = {v01.x, v01.y, v23.x, v23.y};
+        // rounded to fp32, then to fp16, as in the fused forward (not in one step)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // rounded to fp32, then to fp16, as in the fused forward (not in one step)
-          float y = vv[i] * sc_dn - acc[j][i];
-          asm volatile("" : "+v"(y));
-          sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)y;
-        }
+        for (int i = 0; i < 4; ++i) sYT[(16 * j + 4 * lg + i) * LDC + 16 * R + lr] = (T)(vv[i] * sc_dn - acc[j][i]);
       }
     }
     __syncthreads();

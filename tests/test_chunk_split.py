@@ -2,13 +2,10 @@
 against the fp64 oracle, and against the fused kda_chunk_fwd on the same inputs.
 
 Tolerance against the oracle: bf16 inputs, max |err| <= 2e-2 * RMS(ref) for o and hT
-separately.  Against the fused kernel: max |diff| <= 1e-4 * RMS(ref) on inputs where both
-paths see the same operands, so that only the order of fp32 accumulation may differ.  The one
-operand they hold differently is v: the fused kernel keeps its copy of v (in the chunk's
-power-of-two scaled units) in fp16, where a bf16 value below 2^-17 (an fp16 subnormal with
-fewer bits) is rounded, while the state pass of the split path keeps v in fp32.  The inputs
-of the split-versus-fused comparisons therefore carry no |v| below 2^-13 (lift_tiny_values);
-every other test compares the split path with the oracle alone.
+separately.  Against the fused kernel: max |diff| <= 1e-4 * RMS(ref): both paths round the
+same operands at the same points (v in fp32 in the chunk's power-of-two units, Y to fp32 and
+then fp16, U, S and the in-chunk operands to fp16), so only the order of fp32 accumulation
+may differ.
 """
 import numpy as np
 import pytest
@@ -21,15 +18,6 @@ from test_chunk_parity import check_bf16, report, to64
 pytestmark = pytest.mark.gpu
 
 SAME_TOL = 1e-4
-
-
-def lift_tiny_values(inp, floor=2.0 ** -13):
-    """|v| below `floor` raised to `floor` (sign kept), in place: the values keep their scale
-    (these tests run in the unscaled band), so bf16 v is then exact in fp16 as well."""
-    v = inp["v"]
-    tiny = v.abs() < floor
-    v[tiny] = torch.where(v[tiny] < 0, -floor, floor).to(v.dtype)
-    return inp
 
 
 def run_split(inp, chunk_size=None, h0="inp", workspace=None):
@@ -67,8 +55,8 @@ def test_split_small_varlen_bf16(C, dk, dv):
     """Several chunks with ragged tails, empty and 1-token sequences, nonzero h0."""
     lens = [150, 0, 1, 64, 97, 33]
     print("split: small varlen bf16 C=%d dk=%d dv=%d lens=%s" % (C, dk, dv, lens), flush=True)
-    inp = lift_tiny_values(kda_inputs.make_custom_chunk_inputs(lens, 3, dk, dv, torch.bfloat16, h0_std=0.02,
-                                                               seed=11 + C + dk, device="cuda"))
+    inp = kda_inputs.make_custom_chunk_inputs(lens, 3, dk, dv, torch.bfloat16, h0_std=0.02, seed=11 + C + dk,
+                                              device="cuda")
     o, hT = run_split(inp, chunk_size=C)
     o_ref, h_ref = ref(inp)
     check_bf16(o, hT, o_ref, h_ref)
@@ -122,7 +110,7 @@ def test_split_workspace_reused_with_smaller_input():
 def test_split_kimi_linear_layer_workload():
     """B=4, T=4096, H=32, dk=dv=128, chunk 64: against the oracle and the fused kernel."""
     print("split: kimi-linear layer: B=4 T=4096 H=32 d=128 C=64", flush=True)
-    inp = lift_tiny_values(kda_inputs.make_chunk_inputs(kda_inputs.KIMI_LINEAR_LAYER, device="cuda"))
+    inp = kda_inputs.make_chunk_inputs(kda_inputs.KIMI_LINEAR_LAYER, device="cuda")
     o, hT = run_split(inp)
     o_ref, h_ref = ref(inp)
     check_bf16(o, hT, o_ref, h_ref)
