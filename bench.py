@@ -244,9 +244,9 @@ def headline(args, dev, stream, copy_gbs):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": profile_value(LC_PMC_SUMMARY,
                                                                                      "hbm_bytes_per_call"),
-                     "kernel": "split path: chunk_fwd_kernel in-chunk pass, then 16 launches of its pipelined "
-                               "mode (state pass over one chunk range beside the next range's in-chunk pass); "
-                               "one call = one step",
+                     "kernel": "split path: chunk_fwd_kernel's in-chunk pass over the first chunk range, then "
+                               "one launch per range of its pipelined mode (the state pass over range r beside "
+                               "the in-chunk pass over range r + 1; 32 ranges): one call = one step",
                      "algorithmic_bytes_per_launch": alg_bytes, "copy_GB/s": round(copy_gbs, 1),
                      "frac_of_copy": round(gbs / copy_gbs, 4)},
         "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,

@@ -149,7 +149,7 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
  * whole sequence, and writes each chunk's state-free operands to `workspace`;
  * pass 2 walks the chunks of each chain with the state, reading them.  When the
  * state pass fits on half of the CUs (chains x dv/32 <= 128) and the longest
- * sequence has at least 128 chunks, the chunks are cut into 2 to 16 ranges and
+ * sequence has at least 128 chunks, the chunks are cut into 2 to 32 ranges and
  * each launch runs pass 2 over one range beside pass 1 over the next, with the
  * state handed between ranges through the workspace.  Results equal
  * kda_chunk_fwd's up to rounding (the same operand precisions).

@@ -1940,11 +1940,11 @@ static int64_t max_chunks_per_seq(const ChunkArgs& a) {
 }
 
 // Pipelined split (chunk_fwd_kernel with PIPE_BV): value tiles of 32 columns, so that a few
-// chains' state pass takes at most 128 CUs, and 2 to 16 ranges of at least 64 chunks.
+// chains' state pass takes at most 128 CUs, and 2 to 32 ranges of at least 64 chunks.
 constexpr int kPipeBV = 32;
 static bool split_pipelined(const ChunkArgs& a, int64_t max_chunks, int& n_ranges) {
   const int64_t state_blocks = (int64_t)((a.n_seqs * a.n_heads + 7) / 8) * 8 * (a.dv / kPipeBV);
-  n_ranges = (int)(max_chunks / 64 < 16 ? max_chunks / 64 : 16);
+  n_ranges = (int)(max_chunks / 64 < 32 ? max_chunks / 64 : 32);
   return state_blocks <= 128 && n_ranges >= 2;
 }
 
