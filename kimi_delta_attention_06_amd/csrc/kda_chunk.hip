@@ -2044,7 +2044,10 @@ static hipError_t dispatch_split_bv(const ChunkArgs& a, void* ws, float* carry) 
   const int64_t mc = max_chunks_per_seq(a);
   int n_ranges = 0;
   if (split_pipelined(a, mc, n_ranges)) return launch_split_pipelined<C, DK, InT>(a, ws, carry, mc, n_ranges);
-  const int bv = pick_bv(a.n_seqs * a.n_heads, a.dv, 64);
+  // (a value tile as wide as dv when the chains alone fill the CUs: the state pass then runs
+  // in one round of workgroups instead of two)
+  const int bv = pick_bv(a.n_seqs * a.n_heads, a.dv, 128);
+  if (bv == 128) return launch_split<C, DK, 128, InT>(a, ws);
   if (bv == 64) return launch_split<C, DK, 64, InT>(a, ws);
   if (bv == 32) return launch_split<C, DK, 32, InT>(a, ws);
   return launch_split<C, DK, 16, InT>(a, ws);

@@ -65,6 +65,25 @@ def test_split_small_varlen_bf16(C, dk, dv):
     check_same(hT, hf, h_ref, "hT")
 
 
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_split_many_chains_one_tile_per_chain(C, dk):
+    """At least 256 (sequence, head) chains with dv = 128: the state pass takes the whole value
+    width in one workgroup per chain (ragged lengths, empty and 1-token sequences)."""
+    lens = [(37 * i) % 150 for i in range(40)]  # includes 0, 1-token and multi-chunk sequences
+    lens[3] = 1
+    H = 7  # 280 chains
+    print("split: many chains C=%d dk=%d H=%d lens %s" % (C, dk, H, lens[:8]), flush=True)
+    inp = kda_inputs.make_custom_chunk_inputs(lens, H, dk, 128, torch.bfloat16, h0_std=0.02, seed=200 + C + dk,
+                                              device="cuda")
+    o, hT = run_split(inp, chunk_size=C)
+    o_ref, h_ref = ref(inp)
+    check_bf16(o, hT, o_ref, h_ref)
+    of, hf = run_fused(inp, chunk_size=C)
+    check_same(o, of, o_ref, "o")
+    check_same(hT, hf, h_ref, "hT")
+
+
 @pytest.mark.parametrize("C", [16, 64])
 def test_split_narrow_decay(C):
     """Gate law x0.1: the fp16 path for every diagonal sub-block."""
