@@ -13,7 +13,8 @@ with the max-error/RMS of o and hT on those heads.
 The other workloads are legs under "legs", each timed with HIP events on the launch
 stream, with its own roofline or bandwidth, its error against the oracle on a seeded
 slice, and the oracle's own time on the host: the Kimi-Linear-shaped layer (fused,
-with 512-token checkpoints, and split), the tiny fp32 case, the varlen packed batch,
+with 512-token checkpoints, and split), the tiny fp32 case, the varlen packed batch (fused, split and the
+shape-chosen path of kda_chunk_fwd_auto),
 the decode / replay state update (1 and 8 tokens) and replay + verify, the backward
 pass, and the long-context sequence through the fused kernel.
 
@@ -399,6 +400,12 @@ def leg_chunk_other(args, dev, stream, legs):
                                                 h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], chunk_size=ow.chunk_size,
                                                 o=o, hT=hT, workspace=ws)
             leg["split_ms_per_step"] = round(time_launches(sstep, 100, 20, stream), 5)
+            astep = lambda: kda.chunk_fwd_auto(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                               h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], chunk_size=ow.chunk_size,
+                                               o=o, hT=hT, workspace=ws)
+            a_ms = time_launches(astep, 100, 20, stream)
+            leg["auto_ms_per_step"] = round(a_ms, 5)
+            leg["auto_tokens_per_s"] = round(ow.total_tokens / (a_ms * 1e-3), 1)
             del ws
         step()
         torch.cuda.synchronize()

@@ -173,6 +173,33 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
                                void* stream);
 
 /*
+ * kda_chunk_fwd_auto - the chunked forward on whichever path is faster for the
+ * input's shape: kda_chunk_fwd_split or kda_chunk_fwd (same results up to
+ * rounding).  The fused kernel fills the CUs with value tiles of 64 columns and
+ * redoes each chunk's in-chunk work once per tile; the split path does that work
+ * once per chunk and head but writes it to the workspace and reads it back.  With
+ * bf16 inputs, sequences of at least 4 chunks on average, and t64 = n_seqs *
+ * n_heads * dv / 64 fused value tiles, the split path is taken when t64 < 256
+ * (fewer chains than fill the CUs: the fused kernel would narrow its tiles and
+ * repeat the in-chunk work 4 to 8 times) or t64 >= 512 (two or more rounds of
+ * fused tiles, where the split path's state pass runs one round of full-width
+ * tiles); otherwise, and for fp32 inputs, the fused kernel.  Measured on MI355X at
+ * dk = dv = 128, chunk 64: 1M tokens x 32 heads 38 ms split vs 101 ms fused;
+ * 8 x 4,096 tokens x 32 heads 0.85 vs 0.94 ms; 4 x 4,096 x 32 heads 0.445 ms
+ * fused vs 0.46-0.48 ms split.
+ *
+ * Same arguments as kda_chunk_fwd_split.  The workspace is used only when the
+ * split path is taken (it may be NULL with workspace_bytes 0 otherwise); a caller
+ * that always passes kda_chunk_fwd_split_workspace_size bytes is always valid.
+ * Errors: as the path taken.
+ */
+kda_status kda_chunk_fwd_auto(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, const float* h0, const int32_t* cu_seqlens, int32_t n_seqs,
+                              int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk_size,
+                              kda_dtype qkv_dtype, float* o, float* hT, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * kda_chunk_fwd_split_noalloc - kda_chunk_fwd_split for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  Instead of a caller workspace it uses a

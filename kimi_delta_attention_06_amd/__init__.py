@@ -28,7 +28,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "chunk_fwd_split", "chunk_fwd_split_noalloc",
+__all__ = ["chunk_fwd", "chunk_fwd_checkpointed", "chunk_fwd_split", "chunk_fwd_split_noalloc", "chunk_fwd_auto",
            "chunk_fwd_split_workspace_bytes",
            "backward", "backward_workspace_bytes", "recurrent_step", "recurrent_verify", "KDAError"]
 
@@ -94,6 +94,17 @@ def chunk_fwd_split(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_si
     library reports) is allocated when not given.  Returns (o, hT)."""
     o, hT, _ = _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, 0, None,
                       split=True, workspace=workspace)
+    return o, hT
+
+
+def chunk_fwd_auto(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, chunk_size: int = 64,
+                   output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                   hT: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """The chunked forward on whichever of `chunk_fwd_split` and `chunk_fwd` is faster for the input's shape
+    (kda_chunk_fwd_auto; the rule is in kda.h).  `workspace` as for `chunk_fwd_split` (allocated when not
+    given and the input is bf16).  Returns (o, hT)."""
+    o, hT, _ = _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_state, o, hT, 0, None,
+                      split="auto", workspace=workspace)
     return o, hT
 
 
@@ -181,6 +192,12 @@ def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_st
                                              _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code,
                                              _ptr(o), _ptr(hT), stream)
         _check(rc, "kda_chunk_fwd_split_noalloc")
+    elif split == "auto" and code != _lib.KDA_DTYPE_BF16:
+        # (fp32 inputs: the fused kernel, no workspace)
+        rc = lib.kda_chunk_fwd_auto(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                                    _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code, _ptr(o),
+                                    _ptr(hT), None, 0, stream)
+        _check(rc, "kda_chunk_fwd_auto")
     elif split:
         need = ctypes.c_size_t(0)
         rc = lib.kda_chunk_fwd_split_workspace_size(n_seqs, T_total, H, dk, dv, int(chunk_size), code,
@@ -190,10 +207,12 @@ def _chunk(q, k, v, log_alpha, beta, h0, cu_seqlens, chunk_size, output_final_st
             workspace = torch.empty(max(int(need.value), 16), dtype=torch.uint8, device=dev)
         else:
             workspace = _dev(workspace, "workspace", torch.uint8, dev)
-        rc = lib.kda_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
-                                     _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code, _ptr(o),
-                                     _ptr(hT), _ptr(workspace), workspace.numel(), stream)
-        _check(rc, "kda_chunk_fwd_split")
+        fn, name = ((lib.kda_chunk_fwd_auto, "kda_chunk_fwd_auto") if split == "auto"
+                    else (lib.kda_chunk_fwd_split, "kda_chunk_fwd_split"))
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), n_seqs,
+                T_total, H, dk, dv, int(chunk_size), code, _ptr(o), _ptr(hT), _ptr(workspace), workspace.numel(),
+                stream)
+        _check(rc, name)
     elif ckpt_every == 0:
         rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
                                _ptr(cu_seqlens), n_seqs, T_total, H, dk, dv, int(chunk_size), code, _ptr(o),

@@ -26,6 +26,8 @@ SIGNATURES = {
                                                   _I32, ctypes.c_int, _P, _P, _I32, _P, _P]),
     "kda_chunk_fwd_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                            _I32, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]),
+    "kda_chunk_fwd_auto": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
+                                          _I32, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]),
     "kda_chunk_fwd_split_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                                    _I32, ctypes.c_int, _P, _P, _P]),
     "kda_chunk_fwd_split_workspace_size": (ctypes.c_int, [_I32, _I64, _I32, _I32, _I32, _I32, ctypes.c_int,

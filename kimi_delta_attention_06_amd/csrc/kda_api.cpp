@@ -203,6 +203,18 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
                       qkv_dtype, o, hT, 0, nullptr, true, workspace, workspace_bytes, stream);
 }
 
+kda_status kda_chunk_fwd_auto(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, const float* h0, const int32_t* cu_seqlens, int32_t n_seqs,
+                              int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk_size,
+                              kda_dtype qkv_dtype, float* o, float* hT, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const bool split = qkv_dtype == KDA_DTYPE_BF16 && n_heads > 0 && dv > 0 &&
+                     kda::chunk_fwd_prefers_split(n_seqs, n_heads, dv, chunk_size, total_tokens);
+  return chunk_common(q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads, dk, dv, chunk_size,
+                      qkv_dtype, o, hT, 0, nullptr, split, split ? workspace : nullptr, split ? workspace_bytes : 0,
+                      stream);
+}
+
 kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
                                        const float* beta, const float* h0, const int32_t* cu_seqlens,
                                        int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk,

@@ -2130,6 +2130,22 @@ size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads
          (size_t)n_seqs * n_heads * dk * dv * sizeof(float);
 }
 
+// Which forward path is faster for a bf16 input of this shape (measured on MI355X at
+// dk = dv = 128, chunk 64): the fused kernel fills the CUs with value tiles of 64 columns and
+// redoes the in-chunk work once per tile.  With fewer chains than that fills (a few long
+// sequences) its tiles narrow and the work is repeated 4-8 times (1M tokens x 32 heads: split
+// 37.7-38.8 ms, fused 101 ms); with enough chains for two or more rounds of those tiles the
+// split path's state pass runs one round of full-width tiles (8 x 4,096 tokens x 32 heads:
+// split 0.85 ms, fused 0.94 ms); in between (4 x 4,096 tokens x 32 heads: one round) the fused
+// kernel is faster (0.445 vs 0.46-0.48 ms).  Sequences shorter than 4 chunks on average stay
+// on the fused kernel (the workspace round trip is not repaid).
+bool chunk_fwd_prefers_split(int n_seqs, int n_heads, int dv, int chunk_size, int64_t total_tokens) {
+  if (n_seqs <= 0 || total_tokens <= 0) return false;
+  if (total_tokens / n_seqs < 4 * (int64_t)chunk_size) return false;
+  const int64_t tiles64 = (int64_t)n_seqs * n_heads * dv / 64;
+  return tiles64 < 256 || tiles64 >= 512;
+}
+
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws) {
   using namespace chunkk;
   if (!a.bf16 || !chunk_fwd_supported(a.dk, a.dv, a.chunk_size, a.bf16)) return hipErrorInvalidValue;

@@ -78,6 +78,8 @@ hipError_t launch_chunk_fwd_f32(const ChunkArgs& a);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws);
 // Workspace bytes the split path needs for these sizes.
 size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv, int chunk_size);
+// whether kda_chunk_fwd_auto takes the split path for a bf16 input of this shape
+bool chunk_fwd_prefers_split(int n_seqs, int n_heads, int dv, int chunk_size, int64_t total_tokens);
 // True if the chunk kernel has an instantiation for these parameters.
 bool chunk_fwd_supported(int dk, int dv, int chunk_size, bool bf16);
 

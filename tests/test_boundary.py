@@ -20,7 +20,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_checkpointed", "kda_chunk_fwd_split",
-                          "kda_chunk_fwd_split_workspace_size", "kda_chunk_fwd_split_noalloc",
+                          "kda_chunk_fwd_split_workspace_size", "kda_chunk_fwd_split_noalloc", "kda_chunk_fwd_auto",
                           "kda_bwd", "kda_bwd_workspace_size",
                           "kda_bwd_recurrent", "kda_bwd_recurrent_workspace_size",
                           "kda_recurrent_step",
@@ -188,6 +188,22 @@ def split_call(**kw):
     return lib.kda_chunk_fwd_split(a["q"], a["k"], a["v"], a["la"], a["b"], a["h0"], a["cu"], a["N"], a["T"],
                                    a["H"], a["dk"], a["dv"], a["C"], a["dt"], a["o"], a["hT"], a["ws"], a["wsb"],
                                    None)
+
+
+def test_chunk_fwd_auto_checks_the_workspace_on_the_split_path():
+    """Two sequences of 4 chunks x 2 heads: few chains, so the split path, whose workspace is checked on
+    the host (a missing, small or misaligned one is rejected before any launch)."""
+    def auto(**kw):
+        a = dict(q=P, k=P, v=P, la=P, b=P, h0=None, cu=None, N=2, T=512, H=2, dk=128, dv=128, C=64,
+                 dt=_lib.KDA_DTYPE_BF16, o=P * 8, hT=None, ws=P * 64, wsb=1 << 22)
+        a.update(kw)
+        return lib.kda_chunk_fwd_auto(a["q"], a["k"], a["v"], a["la"], a["b"], a["h0"], a["cu"], a["N"], a["T"],
+                                      a["H"], a["dk"], a["dv"], a["C"], a["dt"], a["o"], a["hT"], a["ws"], a["wsb"],
+                                      None)
+    assert auto(ws=None, wsb=0) == 1
+    assert auto(wsb=1000) == 1
+    assert auto(ws=P * 64 + 4) == 1
+    assert auto(dk=96, ws=None, wsb=0) == 2  # shape checks come first
 
 
 @pytest.mark.parametrize("kw,code", [

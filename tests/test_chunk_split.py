@@ -160,3 +160,27 @@ def test_split_long_context_workload_two_heads():
     torch.cuda.empty_cache()
     o_ref, h_ref = oracle.kda_fwd(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], None, None)
     check_bf16(o_s, h_s, o_ref, h_ref)
+
+
+@pytest.mark.parametrize("lens,H,path", [
+    ([600, 17, 400, 260], 2, "split"),      # 8 chains: the fused kernel would narrow its tiles
+    ([256] * 64, 2, "fused"),               # 128 chains of 4 chunks: one round of 64-column fused tiles
+    ([256] * 40 + [300, 212] * 12, 4, "split"),  # 256 chains: two rounds of fused tiles
+])
+def test_auto_takes_the_path_its_rule_names(lens, H, path):
+    """kda_chunk_fwd_auto: the same bits as the path the shape rule picks, against the oracle; the fused
+    choice runs without a workspace."""
+    import kimi_delta_attention_06_amd as kda
+    inp = kda_inputs.make_custom_chunk_inputs(lens, H, 128, 128, torch.bfloat16, h0_std=0.02, seed=len(lens) + H,
+                                              device="cuda")
+    args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
+    kw = dict(h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], chunk_size=64)
+    if path == "fused":
+        o_a, h_a = kda.chunk_fwd_auto(*args, workspace=torch.empty(0, dtype=torch.uint8, device="cuda"), **kw)
+        o_p, h_p = kda.chunk_fwd(*args, **kw)
+    else:
+        o_a, h_a = kda.chunk_fwd_auto(*args, **kw)
+        o_p, h_p = kda.chunk_fwd_split(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_p) and torch.equal(h_a, h_p)
+    check_bf16(o_a, h_a, *ref(inp))
