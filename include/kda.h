@@ -42,7 +42,7 @@
  * launch and return a status with no side effects.  A launch failure reported
  * by the HIP runtime returns KDA_ERR_LAUNCH.  Nothing is printed and no C++
  * exception crosses this interface.  The fused chunked-forward kernels
- * (kda_chunk_fwd, kda_chunk_fwd_checkpointed, the forward launch inside kda_bwd,
+ * (kda_chunk_fwd, kda_chunk_fwd_checkpointed
  * and kda_chunk_fwd_split on zero tokens) are built for XNACK off, the MI355X
  * default; in a process with XNACK on they do not load and those calls return
  * KDA_ERR_LAUNCH.
@@ -243,10 +243,11 @@ kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_toke
  * cotangents `dout` of o and `dhT` of the final states, writes the gradients of
  *     sum_t o_t . dout_t + sum_n hT_n . dhT_n
  * with respect to q, k, v, log_alpha, beta and h0.  Reverse mode of the chunk
- * form in 16-token chunks, every product in fp32: the forward stores the state
- * entering every chunk in `workspace`, a reverse pass over each sequence's chunks
- * stores the cotangent of the state leaving every chunk, and a parallel pass forms
- * each chunk's gradients from the two.
+ * form in 16-token chunks, every product in fp32: a parallel pass forms every
+ * chunk's state-free operands into `workspace`, a forward pass over each
+ * sequence's chunks stores the state entering every chunk, a reverse pass stores
+ * the cotangent of the state leaving every chunk, and a parallel pass forms each
+ * chunk's gradients from the three.
  *
  *   q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads,
  *   dk, dv, qkv_dtype    as kda_chunk_fwd (the chunk size is fixed at 16)
@@ -276,7 +277,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* log
 
 /*
  * kda_bwd_workspace_size - bytes of workspace kda_bwd needs:
- * (2 * (total_tokens / 16) + n_seqs + 1) * n_heads * dk * dv * 4.
+ * (total_tokens / 16 + n_seqs + 1) * n_heads * (2 * dk * dv + 65 * dk + 1044) * 4.
  * Errors: KDA_ERR_INVALID_ARGUMENT (NULL bytes, bad sizes), KDA_ERR_UNSUPPORTED (dk, dv).
  */
 kda_status kda_bwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t n_heads, int32_t dk, int32_t dv,

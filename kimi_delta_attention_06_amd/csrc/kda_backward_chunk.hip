@@ -38,11 +38,14 @@
 // operands, times the values they scale, could leave the fp32 range) forms the Gram terms from
 // per-element factors e^{g_i - g_j} <= 1 instead, so any finite log a is taken.
 //
-// Three launches: (1) the forward chunk kernel in fp32 stores the state entering every
-// chunk (its checkpoint output at a 16-token spacing); (2) `bwd_ds_kernel` walks each
-// (sequence, head, value tile) backwards over its chunks, keeping dS in registers and
-// storing the dS' of every chunk; (3) `bwd_grad_kernel` takes one (chunk, head) per
-// workgroup, all in parallel, and forms every gradient of the chunk from its S and dS'.
+// Four launches: (1) `bwd_prep_kernel`, one (chunk, head) per workgroup, all in parallel,
+// forms the chunk's state-free operands (g, Qg, Kg, Kc, A, M, T, T Diag(b), e_L) once and
+// writes them to the workspace; (2) `bwd_states_kernel` walks each (sequence, head, value
+// tile) forwards over its chunks with S in registers and stores the state entering every
+// chunk; (3) `bwd_ds_kernel` walks them backwards with dS in registers and stores the dS'
+// of every chunk; (4) `bwd_grad_kernel`, one (chunk, head) per workgroup, forms every
+// gradient of the chunk from its S, dS' and operands.  The two serial passes only run the
+// state-dependent products; every per-chunk operand they need is read, one chunk ahead.
 #include <atomic>
 
 #include "kda_common.hpp"
@@ -99,26 +102,6 @@ __device__ __forceinline__ void add_tile(f32x4& acc, const float* p, int ld) {
   for (int r = 0; r < 4; ++r) acc[r] += p[(4 * (l >> 4) + r) * ld + (l & 15)];
 }
 
-template <typename InT> struct Vec;
-template <> struct Vec<float> {
-  static constexpr int N = 4;
-  __device__ static void load(float* d, const float* s) {
-    const float4 x = *reinterpret_cast<const float4*>(s);
-    d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-  }
-};
-template <> struct Vec<bf16_t> {
-  static constexpr int N = 8;
-  __device__ static void load(float* d, const bf16_t* s) {
-    const uint4 x = *reinterpret_cast<const uint4*>(s);
-    float2 f;
-    f = bf16x2_to_f32x2(x.x); d[0] = f.x; d[1] = f.y;
-    f = bf16x2_to_f32x2(x.y); d[2] = f.x; d[3] = f.y;
-    f = bf16x2_to_f32x2(x.z); d[4] = f.x; d[5] = f.y;
-    f = bf16x2_to_f32x2(x.w); d[6] = f.x; d[7] = f.y;
-  }
-};
-
 // 16 bytes of input (8 bf16 or 4 fp32 values), widened to fp32 at d
 __device__ __forceinline__ void widen16(float* d, const uint4& x, bf16_t) {
   float2 f;
@@ -147,32 +130,42 @@ struct Intra {
     b = TB + C * LDC; el = b + C;
   }
 
-  // q, k, log a and b of rows t0 .. t0 + Lc - 1 (zeros past Lc)
+  // q, k, log a and b of rows t0 .. t0 + Lc - 1 (zeros past Lc): every load issued before the
+  // first is stored
   template <typename InT>
   __device__ void load(const InT* __restrict__ qp, const InT* __restrict__ kp, const float* __restrict__ lap,
                        const float* __restrict__ bp, int64_t t0, int Lc, int H, int h) {
-    constexpr int VE = Vec<InT>::N, NV = C * DK / VE;
-    for (int e = threadIdx.x; e < 2 * NV; e += NT) {
-      const int which = e / NV, ee = e - which * NV;
+    constexpr int VE = (int)(16 / sizeof(InT)), NQK = 2 * C * DK / VE, IQK = (NQK + NT - 1) / NT;
+    constexpr int NLA = C * DK / 4, ILA = (NLA + NT - 1) / NT;
+    const int tid = threadIdx.x;
+    uint4 rqk[IQK];
+    float4 rla[ILA];
+#pragma unroll
+    for (int it = 0; it < IQK; ++it) {
+      const int e = tid + NT * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
       const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
-      float x[VE];
-      if (i < Lc) {
-        Vec<InT>::load(x, (which ? kp : qp) + ((size_t)(t0 + i) * H + h) * DK + c);
-      } else {
-#pragma unroll
-        for (int u = 0; u < VE; ++u) x[u] = 0.f;
-      }
-      float* d = (which ? k : q) + i * LDK + c;
-#pragma unroll
-      for (int u = 0; u < VE; u += 4) *reinterpret_cast<float4*>(d + u) = make_float4(x[u], x[u + 1], x[u + 2], x[u + 3]);
+      rqk[it] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < NQK && i < Lc) rqk[it] = *reinterpret_cast<const uint4*>((which ? kp : qp) + ((size_t)(t0 + i) * H + h) * DK + c);
     }
-    for (int e = threadIdx.x; e < C * DK / 4; e += NT) {
-      const int i = e / (DK / 4), c = (e - i * (DK / 4)) * 4;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < Lc) x = *reinterpret_cast<const float4*>(lap + ((size_t)(t0 + i) * H + h) * DK + c);
-      *reinterpret_cast<float4*>(g + i * LDK + c) = x;
+#pragma unroll
+    for (int it = 0; it < ILA; ++it) {
+      const int e = tid + NT * it, i = e / (DK / 4), c = (e - i * (DK / 4)) * 4;
+      rla[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < NLA && i < Lc) rla[it] = *reinterpret_cast<const float4*>(lap + ((size_t)(t0 + i) * H + h) * DK + c);
     }
-    if (threadIdx.x < C) b[threadIdx.x] = (int)threadIdx.x < Lc ? bp[(size_t)(t0 + threadIdx.x) * H + h] : 0.f;
+    const float rb = tid < Lc ? bp[(size_t)(t0 + tid) * H + h] : 0.f;
+#pragma unroll
+    for (int it = 0; it < IQK; ++it) {
+      const int e = tid + NT * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
+      const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
+      if (e < NQK) widen16((which ? k : q) + i * LDK + c, rqk[it], InT{});
+    }
+#pragma unroll
+    for (int it = 0; it < ILA; ++it) {
+      const int e = tid + NT * it, i = e / (DK / 4), c = (e - i * (DK / 4)) * 4;
+      if (e < NLA) *reinterpret_cast<float4*>(g + i * LDK + c) = rla[it];
+    }
+    if (tid < C) b[tid] = rb;
   }
 
   // Prefix sum of log a over the rows (one thread per channel) and e^{g_L}.  Each step is
@@ -217,6 +210,19 @@ struct Intra {
       qg[o] = qv * eg;
       kg[o] = kv * eg;
       kc[o] = kv * ec;
+    }
+  }
+
+  // The midpoint-balanced operands ql, kl, kr alone (the same values as scale), from q, k, g
+  __device__ void scale_balanced() {
+    for (int e = threadIdx.x; e < C * DK; e += NT) {
+      const int i = e / DK, c = e - i * DK, o = i * LDK + c;
+      const float gi = g[o], m = 0.5f * g[(C - 1) * LDK + c];
+      const float e1 = expf(gi - m), e2 = expf(m - gi);
+      const float qv = q[o], kv = k[o];
+      ql[o] = qv * e1;
+      kl[o] = kv * e1;
+      kr[o] = kv * e2;
     }
   }
 
@@ -281,29 +287,189 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int64_t seq_
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// dS pass: one workgroup per (sequence, head, BV value columns), chunks in reverse order.
-// dS (DK x BV) lives in MFMA accumulators: wave w owns tiles tt = w + 8 u, c-tile tt % (DK/16),
-// v-tile tt / (DK/16).  Stores dS' of chunk j at workspace slot start/16 + n + j.
-template <int DK, int BV, typename InT>
-__global__ __launch_bounds__(NT) void bwd_ds_kernel(const InT* __restrict__ q, const InT* __restrict__ k,
-                                                    const float* __restrict__ la, const float* __restrict__ beta,
-                                                    const int32_t* __restrict__ cu, const float* __restrict__ dout,
-                                                    const float* __restrict__ dhT, float* __restrict__ dsw,
-                                                    float* __restrict__ dh0, int H, int DV, int64_t seq_len) {
-  using In = Intra<DK>;
-  constexpr int LDK = In::LDK, LDO = BV + 4;
-  constexpr int NVT = BV / 16, NCT = DK / 16, NTL = NCT * NVT, TPW = NTL / 8;
-  constexpr int KSPLIT = 8 / NVT, KR = DK / KSPLIT;
-  static_assert(NTL % 8 == 0 && 8 % NVT == 0 && KR % 16 == 0, "tiling");
+// The chunk slot of chunk j of sequence n is start_n / C + n + j: distinct for every chunk of
+// every packed sequence, below total_tokens / C + n_seqs + 1.  For a slot: its sequence (the
+// last n with start_n / C + n <= slot) and chunk; false for a slot no chunk maps to.
+__device__ __forceinline__ bool slot_chunk(const int32_t* cu, int n_seqs, int64_t seq_len, int slot, int& n,
+                                           int64_t& start, int64_t& len, int64_t& j) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int64_t st = cu ? (int64_t)cu[mid] : (int64_t)mid * seq_len;
+    if (st / C + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  n = lo;
+  seq_range(cu, n, seq_len, start, len);
+  j = (int64_t)slot - (start / C + n);
+  return j >= 0 && C * j < len;
+}
 
+// The operands the prep pass forms once per (chunk slot, head), fp32, in floats: Qg, Kg, Kc
+// and g (the floored prefix sums of log a) [C][DK]; A, M, T and T Diag(b) [C][C]; b [C];
+// e^{g_L} [DK]; the exact-path flag (0 or 1) padded to 16 bytes.  65 DK + 1044 floats.
+template <int DK>
+struct OpTile {
+  static constexpr int QG = 0, KG = QG + C * DK, KC = KG + C * DK, G = KC + C * DK;
+  static constexpr int A = G + C * DK, M = A + C * C, T = M + C * C, TB = T + C * C;
+  static constexpr int B = TB + C * C, EL = B + C, FLAG = EL + DK;
+  static constexpr int FLOATS = FLAG + 4;
+  static_assert(FLOATS == 65 * DK + 1044 && FLOATS % 4 == 0, "layout");
+};
+
+// States and state cotangents in the workspace are in matrix-core fragment order: the dk x dv
+// matrix is cut into 16 x 16 tiles (channel block ct, value block vt), tile vt * (DK / 16) + ct
+// at 256 floats each, in which lane l's four floats (channels 16 ct + 4 (l >> 4) + r, r = 0..3,
+// value 16 vt + (l & 15)) are consecutive at 4 l.  A wave moves a tile with one 16-byte access
+// per lane, and the tiles of a run of value blocks are contiguous.
+__device__ __forceinline__ size_t frag_off(int ct, int vt, int nct) {
+  return ((size_t)vt * nct + ct) * 256 + 4 * lane();
+}
+
+// An LDS tile written by some lanes of a wave and read by others of the same wave: the wave's
+// LDS accesses complete in order, so only the compiler must keep them in place.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------------------
+// Prep pass: one workgroup per (chunk slot, head), all in parallel.  Qg, Kg, Kc and g go from
+// registers to the workspace as they are formed; only what the Gram products and the inverse
+// read stays in LDS, with the balanced operands ql, kl formed over q, k (about 39 KB at
+// dk = 128: four workgroups per CU, so one workgroup's single-wave inverse overlaps the
+// others' work).
+template <int DK>
+struct PrepLay {
+  static constexpr int LDK = DK + 4;
+  static constexpr int FLOATS = 4 * C * LDK + 4 * C * LDC + C + DK;  // q|ql, k|kl, g, kr; A, M, T, TB; b; e_L
+};
+
+template <int DK, typename InT>
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(const InT* __restrict__ q, const InT* __restrict__ k,
+                                                      const float* __restrict__ la, const float* __restrict__ beta,
+                                                      const int32_t* __restrict__ cu, float* __restrict__ ops, int H,
+                                                      int64_t seq_len, int n_seqs) {
+  using In = Intra<DK>;
+  using O = OpTile<DK>;
+  constexpr int LDK = In::LDK, R4 = DK / 4;
   extern __shared__ __attribute__((aligned(16))) float smem[];
   In in(smem);
-  float* sDO = smem + In::FLOATS;     // [C][LDO]
-  float* sDST = sDO + C * LDO;        // [BV][LDK]: dS' transposed
-  float* sPart = sDST + BV * LDK;     // [8][C][LDC]
-  float* sDU = sPart + 8 * C * LDC;   // [C][LDO]
-  float* sNDY = sDU + C * LDO;        // [C][LDO]: -dY
+  // (Intra's layout re-pointed: the balanced left operands over q and k, the decayed forms
+  // not held; A, M, T, TB, b, e_L as in Intra, after four [C][LDK] matrices)
+  in.kr = in.g + C * LDK;
+  in.ql = in.q;
+  in.kl = in.k;
+  in.qg = in.kg = in.kc = nullptr;
+  in.A = in.kr + C * LDK;
+  in.M = in.A + C * LDC;
+  in.T = in.M + C * LDC;
+  in.TB = in.T + C * LDC;
+  in.b = in.TB + C * LDC;
+  in.el = in.b + C;
+  const int slot = blockIdx.x / H, h = blockIdx.x - slot * H;
+  int n;
+  int64_t start, len, j;
+  if (!slot_chunk(cu, n_seqs, seq_len, slot, n, start, len, j)) return;  // (whole workgroup)
+  const int64_t t0 = start + C * j;
+  const int Lc = (int)(len - C * j < C ? len - C * j : C);
+  const int w = threadIdx.x / kWave;
+  float* dst = ops + ((size_t)slot * H + h) * O::FLOATS;
+
+  in.load(q, k, la, beta, t0, Lc, H, h);
+  __syncthreads();
+  const bool exact = __syncthreads_or(in.prefix());
+  // decayed operands to the workspace, balanced ones (not on the exact path) in place
+  for (int e = threadIdx.x; e < C * R4; e += NT) {
+    const int i = e / R4, c = (e - i * R4) * 4, o = i * LDK + c;
+    const float4 gi = *reinterpret_cast<const float4*>(in.g + o);
+    const float4 gl = *reinterpret_cast<const float4*>(in.g + (C - 1) * LDK + c);
+    const float4 qv = *reinterpret_cast<const float4*>(in.q + o), kv = *reinterpret_cast<const float4*>(in.k + o);
+    const float g4[4] = {gi.x, gi.y, gi.z, gi.w}, l4[4] = {gl.x, gl.y, gl.z, gl.w};
+    const float q4[4] = {qv.x, qv.y, qv.z, qv.w}, k4[4] = {kv.x, kv.y, kv.z, kv.w};
+    float qg[4], kg[4], kc[4], ql[4], kl[4], kr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float eg = expf(g4[u]), ec = expf(l4[u] - g4[u]), m = 0.5f * l4[u];
+      qg[u] = q4[u] * eg;
+      kg[u] = k4[u] * eg;
+      kc[u] = k4[u] * ec;
+      if (!exact) {
+        const float e1 = expf(g4[u] - m), e2 = expf(m - g4[u]);
+        ql[u] = q4[u] * e1;
+        kl[u] = k4[u] * e1;
+        kr[u] = k4[u] * e2;
+      }
+    }
+    const int go = i * DK + c;
+    *reinterpret_cast<float4*>(dst + O::QG + go) = make_float4(qg[0], qg[1], qg[2], qg[3]);
+    *reinterpret_cast<float4*>(dst + O::KG + go) = make_float4(kg[0], kg[1], kg[2], kg[3]);
+    *reinterpret_cast<float4*>(dst + O::KC + go) = make_float4(kc[0], kc[1], kc[2], kc[3]);
+    *reinterpret_cast<float4*>(dst + O::G + go) = gi;
+    if (!exact) {
+      *reinterpret_cast<float4*>(in.ql + o) = make_float4(ql[0], ql[1], ql[2], ql[3]);
+      *reinterpret_cast<float4*>(in.kl + o) = make_float4(kl[0], kl[1], kl[2], kl[3]);
+      *reinterpret_cast<float4*>(in.kr + o) = make_float4(kr[0], kr[1], kr[2], kr[3]);
+    }
+  }
+  __syncthreads();
+  if (exact) {
+    if (w < 4) in.gram_exact();
+  } else if (w < 2) {
+    in.gram(w);
+  }
+  __syncthreads();
+  if (w == 0) in.inverse();
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e < 4 * C * C / 4) {  // A, M, T, T Diag(b)
+    const int m = e / (C * C / 4), i = (e / 4) % C, c = (e % 4) * 4;
+    *reinterpret_cast<float4*>(dst + O::A + m * C * C + i * C + c) =
+        *reinterpret_cast<const float4*>(in.A + m * C * LDC + i * LDC + c);
+  } else if (e < 4 * C * C / 4 + C / 4 + R4) {  // b, e^{g_L} (consecutive in both)
+    const int f = e - 4 * C * C / 4;
+    *reinterpret_cast<float4*>(dst + O::B + 4 * f) = *reinterpret_cast<const float4*>(in.b + 4 * f);
+  } else if (e == 4 * C * C / 4 + C / 4 + R4) {
+    *reinterpret_cast<float4*>(dst + O::FLAG) = make_float4(exact ? 1.f : 0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Serial passes: one workgroup per (sequence, head, BV value columns).  The DK x BV state (or
+// its cotangent) lives in MFMA accumulators: wave w owns tiles tt = w + 8 u, channel block
+// tt % (DK/16), value block tt / (DK/16).  A chunk's operands are read from its prep tile into
+// registers while the chunk before is processed, and put in LDS at the top of the chunk.
+template <int DK, int BV>
+struct SerialShape {
+  static constexpr int LDK = DK + 4, LDO = BV + 4;
+  static constexpr int NVT = BV / 16, NCT = DK / 16, NTL = NCT * NVT, TPW = NTL / 8;
+  static constexpr int KSPLIT = 8 / NVT, KR = DK / KSPLIT;  // the k-split of the DK-long products
+  static constexpr int R4 = DK / 4;
+  static_assert(NTL % 8 == 0 && 8 % NVT == 0 && KR % 16 == 0, "tiling");
+};
+
+// Forward states pass: S <- Diag(e_L) S + Kc^T U with U = T Diag(b) (V - Kg S), chunks in
+// order; stores the state entering chunk j (h0 or zeros for j = 0) at slot start/C + n + j.
+template <int DK, int BV, typename InT>
+__global__ __launch_bounds__(NT) void bwd_states_kernel(const InT* __restrict__ v, const float* __restrict__ h0,
+                                                        const int32_t* __restrict__ cu, const float* __restrict__ ops,
+                                                        float* __restrict__ sw, int H, int DV, int64_t seq_len) {
+  using O = OpTile<DK>;
+  using Sh = SerialShape<DK, BV>;
+  constexpr int LDK = Sh::LDK, LDO = Sh::LDO, NVT = Sh::NVT, NCT = Sh::NCT, TPW = Sh::TPW;
+  constexpr int KSPLIT = Sh::KSPLIT, KR = Sh::KR, R4 = Sh::R4;
+  constexpr int NKK = 2 * C * R4, IKK = (NKK + NT - 1) / NT;  // float4 of Kg and Kc (consecutive)
+  constexpr int NSM = C * C / 4 + R4;                          // T Diag(b), then e^{g_L}
+  constexpr int VE = (int)(16 / sizeof(InT)), NVI = C * BV / VE; // 16-byte items of the value tile
+  static_assert(NSM <= NT && NVI <= NT, "one small item per thread");
+
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float* sKG = smem;                   // [C][LDK]
+  float* sKC = sKG + C * LDK;          // [C][LDK]
+  float* sTB = sKC + C * LDK;          // [C][LDC]
+  float* sEL = sTB + C * LDC;          // [DK]
+  float* sV = sEL + DK;                // [C][LDO]
+  float* sST = sV + C * LDO;           // [BV][LDK]: S transposed
+  float* sPart = sST + BV * LDK;       // [8][C][LDC]
+  float* sY = sPart + 8 * C * LDC;     // [C][LDO]
+  float* sU = sY + C * LDO;            // [C][LDO]
 
   const int ntile = DV / BV;
   const int chain = blockIdx.x / ntile, tile = blockIdx.x - chain * ntile;
@@ -311,7 +477,152 @@ __global__ __launch_bounds__(NT) void bwd_ds_kernel(const InT* __restrict__ q, c
   int64_t start, len;
   seq_range(cu, n, seq_len, start, len);
   const int64_t nch = (len + C - 1) / C;
-  const int w = threadIdx.x / kWave, l = lane();
+  const int64_t slot0 = start / C + n;
+  const int tid = threadIdx.x, w = tid / kWave, l = lane();
+
+  f32x4 S[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tt = w + 8 * u, ct = tt % NCT, vt = tt / NCT;
+    const int crow = 16 * ct + 4 * (l >> 4), vcol = 16 * vt + (l & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[u][r] = h0 ? h0[((size_t)chain * DK + crow + r) * DV + v0 + vcol] : 0.f;
+    *reinterpret_cast<float4*>(sST + vcol * LDK + crow) = make_float4(S[u][0], S[u][1], S[u][2], S[u][3]);
+  }
+
+  float4 rkk[IKK], rsm = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint4 rv = make_uint4(0u, 0u, 0u, 0u);
+  auto fetch = [&](int64_t jj) {
+    const float* op = ops + ((size_t)(slot0 + jj) * H + h) * O::FLOATS;
+    const int64_t t0 = start + C * jj;
+    const int Lc = (int)(len - C * jj < C ? len - C * jj : C);
+#pragma unroll
+    for (int it = 0; it < IKK; ++it) {
+      const int e = tid + NT * it;
+      rkk[it] = e < NKK ? *reinterpret_cast<const float4*>(op + O::KG + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < C * C / 4) rsm = *reinterpret_cast<const float4*>(op + O::TB + 4 * tid);
+    else if (tid < NSM) rsm = *reinterpret_cast<const float4*>(op + O::EL + 4 * (tid - C * C / 4));
+    rv = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < NVI) {
+      const int i = tid / (BV / VE), c = (tid - i * (BV / VE)) * VE;
+      if (i < Lc) rv = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + i) * H + h) * DV + v0 + c);
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int it = 0; it < IKK; ++it) {
+      const int e = tid + NT * it;
+      if (e < NKK) {
+        const int m = e / (C * R4), ee = e - m * (C * R4), i = ee / R4, c = (ee - i * R4) * 4;
+        *reinterpret_cast<float4*>((m ? sKC : sKG) + i * LDK + c) = rkk[it];
+      }
+    }
+    if (tid < C * C / 4) *reinterpret_cast<float4*>(sTB + (tid / 4) * LDC + (tid % 4) * 4) = rsm;
+    else if (tid < NSM) *reinterpret_cast<float4*>(sEL + 4 * (tid - C * C / 4)) = rsm;
+    if (tid < NVI) {
+      const int i = tid / (BV / VE), c = (tid - i * (BV / VE)) * VE;
+      widen16(sV + i * LDO + c, rv, InT{});
+    }
+  };
+  if (nch > 0) fetch(0);
+
+  for (int64_t j = 0; j < nch; ++j) {
+    put();
+    if (j + 1 < nch) fetch(j + 1);
+    {  // the state entering chunk j
+      float* dst = sw + ((size_t)(slot0 + j) * H + h) * DK * DV;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int tt = w + 8 * u, ct = tt % NCT, vt = tt / NCT;
+        *reinterpret_cast<float4*>(dst + frag_off(ct, v0 / 16 + vt, NCT)) = make_float4(S[u][0], S[u][1], S[u][2], S[u][3]);
+      }
+    }
+    __syncthreads();
+    {  // partial Kg S over one k-range: job w = (value block w % NVT, k-range w / NVT)
+      const int vt = w % NVT, kq = w / NVT;
+      f32x4 acc = zero4();
+      mma<KR / 16, LDK, 1, LDK, 1>(acc, sKG + kq * KR, sST + 16 * vt * LDK + kq * KR);
+      store_tile(sPart + w * C * LDC, LDC, acc);
+    }
+    __syncthreads();
+    if (w >= 8 - NVT) {  // Y = V - Kg S, then U = T Diag(b) Y, one value block per wave
+      const int vt = w - (8 - NVT);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kq = 0; kq < KSPLIT; ++kq) add_tile(acc, sPart + (vt + kq * NVT) * C * LDC, LDC);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * (l >> 4) + r, col = 16 * vt + (l & 15);
+        sY[i * LDO + col] = sV[i * LDO + col] - acc[r];
+      }
+      wave_lds_order();
+      f32x4 u = zero4();
+      mma<1, LDC, 1, 1, LDO>(u, sTB, sY + 16 * vt);
+      store_tile(sU + 16 * vt, LDO, u);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {  // S <- Diag(e_L) S + Kc^T U
+      const int tt = w + 8 * u, ct = tt % NCT, vt = tt / NCT;
+      const int crow = 16 * ct + 4 * (l >> 4), vcol = 16 * vt + (l & 15);
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = sEL[crow + r] * S[u][r];
+      mma<1, 1, LDK, 1, LDO>(acc, sKC + 16 * ct, sU + 16 * vt);
+      S[u] = acc;
+      *reinterpret_cast<float4*>(sST + vcol * LDK + crow) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+  }
+}
+
+template <int DK, int BV>
+constexpr size_t states_lds_bytes() {
+  using Sh = SerialShape<DK, BV>;
+  return sizeof(float) * ((size_t)2 * C * Sh::LDK + C * LDC + DK + 3 * C * Sh::LDO + (size_t)BV * Sh::LDK +
+                          8 * C * LDC);
+}
+
+// dS pass: chunks in reverse order; stores dS' of chunk j (the cotangent of the state leaving
+// it) at slot start/C + n + j, and dh0.
+//   dU = M^T dO + Kc dS',  lambda = T^T dU,  dS = Diag(e_L) dS' + Qg^T dO - Kg^T Diag(b) lambda
+template <int DK, int BV>
+__global__ __launch_bounds__(NT) void bwd_ds_kernel(const int32_t* __restrict__ cu, const float* __restrict__ dout,
+                                                    const float* __restrict__ dhT, const float* __restrict__ ops,
+                                                    float* __restrict__ dsw, float* __restrict__ dh0, int H, int DV,
+                                                    int64_t seq_len) {
+  using O = OpTile<DK>;
+  using Sh = SerialShape<DK, BV>;
+  constexpr int LDK = Sh::LDK, LDO = Sh::LDO, NVT = Sh::NVT, NCT = Sh::NCT, TPW = Sh::TPW;
+  constexpr int KSPLIT = Sh::KSPLIT, KR = Sh::KR, R4 = Sh::R4;
+  constexpr int NBIG = 3 * C * R4, IBIG = (NBIG + NT - 1) / NT;  // float4 of Qg, Kg, Kc (consecutive)
+  constexpr int NMT = 2 * C * C / 4, NSM = NMT + C / 4 + R4;      // M, T (consecutive), then b, e^{g_L}
+  constexpr int NDO = C * BV / 4;
+  static_assert(NSM <= NT && NDO <= NT, "one small item per thread");
+
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float* sQG = smem;                   // [C][LDK]
+  float* sKG = sQG + C * LDK;
+  float* sKC = sKG + C * LDK;
+  float* sM = sKC + C * LDK;           // [C][LDC]
+  float* sT = sM + C * LDC;            // [C][LDC]
+  float* sB = sT + C * LDC;            // [C]
+  float* sEL = sB + C;                 // [DK]
+  float* sDO = sEL + DK;               // [C][LDO]
+  float* sDST = sDO + C * LDO;         // [BV][LDK]: dS' transposed
+  float* sPart = sDST + BV * LDK;      // [8][C][LDC]
+  float* sDU = sPart + 8 * C * LDC;    // [C][LDO]
+  float* sNDY = sDU + C * LDO;         // [C][LDO]: -dY
+
+  const int ntile = DV / BV;
+  const int chain = blockIdx.x / ntile, tile = blockIdx.x - chain * ntile;
+  const int n = chain / H, h = chain - n * H, v0 = tile * BV;
+  int64_t start, len;
+  seq_range(cu, n, seq_len, start, len);
+  const int64_t nch = (len + C - 1) / C;
+  const int64_t slot0 = start / C + n;
+  const int tid = threadIdx.x, w = tid / kWave, l = lane();
 
   f32x4 ds[TPW];
 #pragma unroll
@@ -323,109 +634,77 @@ __global__ __launch_bounds__(NT) void bwd_ds_kernel(const InT* __restrict__ q, c
       ds[u][r] = dhT ? dhT[((size_t)chain * DK + crow + r) * DV + v0 + vcol] : 0.f;
     *reinterpret_cast<float4*>(sDST + vcol * LDK + crow) = make_float4(ds[u][0], ds[u][1], ds[u][2], ds[u][3]);
   }
-  const int64_t slot0 = start / C + n;
 
-  // The inputs of the next chunk (in reverse order) are loaded into registers while the
-  // current one is processed: q, k (16 bytes per item), log a and dO (float4), beta.
-  constexpr int VE = Vec<InT>::N, NV = C * DK / VE;
-  constexpr int IQK = (2 * NV + NT - 1) / NT, ILA = (C * DK / 4 + NT - 1) / NT, IDO = (C * BV / 4 + NT - 1) / NT;
-  uint4 rqk[IQK];
-  float4 rla[ILA], rdo[IDO];
-  float rb = 0.f;
+  float4 rbig[IBIG], rsm = make_float4(0.f, 0.f, 0.f, 0.f), rdo = make_float4(0.f, 0.f, 0.f, 0.f);
   auto fetch = [&](int64_t jj) {
+    const float* op = ops + ((size_t)(slot0 + jj) * H + h) * O::FLOATS;
     const int64_t t0 = start + C * jj;
     const int Lc = (int)(len - C * jj < C ? len - C * jj : C);
 #pragma unroll
-    for (int it = 0; it < IQK; ++it) {
-      const int e = threadIdx.x + NT * it, which = e / NV, ee = e - which * NV;
-      const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
-      rqk[it] = make_uint4(0u, 0u, 0u, 0u);
-      if (e < 2 * NV && i < Lc)
-        rqk[it] = *reinterpret_cast<const uint4*>((which ? k : q) + ((size_t)(t0 + i) * H + h) * DK + c);
+    for (int it = 0; it < IBIG; ++it) {
+      const int e = tid + NT * it;
+      rbig[it] = e < NBIG ? *reinterpret_cast<const float4*>(op + O::QG + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-#pragma unroll
-    for (int it = 0; it < ILA; ++it) {
-      const int e = threadIdx.x + NT * it, i = e / (DK / 4), c = (e - i * (DK / 4)) * 4;
-      rla[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < C * DK / 4 && i < Lc) rla[it] = *reinterpret_cast<const float4*>(la + ((size_t)(t0 + i) * H + h) * DK + c);
+    if (tid < NMT) rsm = *reinterpret_cast<const float4*>(op + O::M + 4 * tid);
+    else if (tid < NSM) rsm = *reinterpret_cast<const float4*>(op + O::B + 4 * (tid - NMT));
+    rdo = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < NDO) {
+      const int i = tid / (BV / 4), c = (tid - i * (BV / 4)) * 4;
+      if (i < Lc) rdo = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + v0 + c);
     }
-#pragma unroll
-    for (int it = 0; it < IDO; ++it) {
-      const int e = threadIdx.x + NT * it, i = e / (BV / 4), c = (e - i * (BV / 4)) * 4;
-      rdo[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < C * BV / 4 && i < Lc)
-        rdo[it] = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + v0 + c);
-    }
-    rb = (int)threadIdx.x < Lc ? beta[(size_t)(t0 + threadIdx.x) * H + h] : 0.f;
   };
   auto put = [&]() {
 #pragma unroll
-    for (int it = 0; it < IQK; ++it) {
-      const int e = threadIdx.x + NT * it, which = e / NV, ee = e - which * NV;
-      const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
-      if (e < 2 * NV) widen16((which ? in.k : in.q) + i * LDK + c, rqk[it], InT{});
+    for (int it = 0; it < IBIG; ++it) {
+      const int e = tid + NT * it;
+      if (e < NBIG) {
+        const int m = e / (C * R4), ee = e - m * (C * R4), i = ee / R4, c = (ee - i * R4) * 4;
+        *reinterpret_cast<float4*>(sQG + m * C * LDK + i * LDK + c) = rbig[it];
+      }
     }
-#pragma unroll
-    for (int it = 0; it < ILA; ++it) {
-      const int e = threadIdx.x + NT * it, i = e / (DK / 4), c = (e - i * (DK / 4)) * 4;
-      if (e < C * DK / 4) *reinterpret_cast<float4*>(in.g + i * LDK + c) = rla[it];
+    if (tid < NMT) *reinterpret_cast<float4*>(sM + (tid / (C * C / 4)) * C * LDC + ((tid / 4) % C) * LDC + (tid % 4) * 4) = rsm;
+    else if (tid < NSM) *reinterpret_cast<float4*>(sB + 4 * (tid - NMT)) = rsm;
+    if (tid < NDO) {
+      const int i = tid / (BV / 4), c = (tid - i * (BV / 4)) * 4;
+      *reinterpret_cast<float4*>(sDO + i * LDO + c) = rdo;
     }
-#pragma unroll
-    for (int it = 0; it < IDO; ++it) {
-      const int e = threadIdx.x + NT * it, i = e / (BV / 4), c = (e - i * (BV / 4)) * 4;
-      if (e < C * BV / 4) *reinterpret_cast<float4*>(sDO + i * LDO + c) = rdo[it];
-    }
-    if (threadIdx.x < C) in.b[threadIdx.x] = rb;
   };
   if (nch > 0) fetch(nch - 1);
 
   for (int64_t j = nch - 1; j >= 0; --j) {
     put();
     if (j > 0) fetch(j - 1);
-    {
+    {  // dS' of chunk j
       float* dst = dsw + ((size_t)(slot0 + j) * H + h) * DK * DV;
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int tt = w + 8 * u, ct = tt % NCT, vt = tt / NCT;
-        const int crow = 16 * ct + 4 * (l >> 4), vcol = 16 * vt + (l & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(size_t)(crow + r) * DV + v0 + vcol] = ds[u][r];
+        *reinterpret_cast<float4*>(dst + frag_off(ct, v0 / 16 + vt, NCT)) =
+            make_float4(ds[u][0], ds[u][1], ds[u][2], ds[u][3]);
       }
     }
     __syncthreads();
-    const bool exact = __syncthreads_or(in.prefix());
-    in.scale(exact);
-    __syncthreads();
-    if (exact) {
-      if (w < 4) in.gram_exact();
-    } else if (w < 2) {
-      in.gram(w);
-    }
-    {  // partial Kc dS' over one k-range: job w = (v-tile w % NVT, k-range w / NVT)
+    {  // partial Kc dS' over one k-range: job w = (value block w % NVT, k-range w / NVT)
       const int vt = w % NVT, kq = w / NVT;
       f32x4 acc = zero4();
-      mma<KR / 16, LDK, 1, LDK, 1>(acc, in.kc + kq * KR, sDST + 16 * vt * LDK + kq * KR);
+      mma<KR / 16, LDK, 1, LDK, 1>(acc, sKC + kq * KR, sDST + 16 * vt * LDK + kq * KR);
       store_tile(sPart + w * C * LDC, LDC, acc);
     }
     __syncthreads();
-    if (w == 0) in.inverse();
-    if (w >= 8 - NVT) {  // dU = M^T dO + Kc dS'
+    if (w >= 8 - NVT) {  // dU = M^T dO + Kc dS', then lambda = T^T dU and -dY = -b lambda
       const int vt = w - (8 - NVT);
       f32x4 acc = zero4();
-      mma<1, 1, LDC, 1, LDO>(acc, in.M, sDO + 16 * vt);
+      mma<1, 1, LDC, 1, LDO>(acc, sM, sDO + 16 * vt);
 #pragma unroll
       for (int kq = 0; kq < KSPLIT; ++kq) add_tile(acc, sPart + (vt + kq * NVT) * C * LDC, LDC);
       store_tile(sDU + 16 * vt, LDO, acc);
-    }
-    __syncthreads();
-    if (w >= 8 - NVT) {  // lambda = T^T dU; -dY = -b lambda
-      const int vt = w - (8 - NVT);
-      f32x4 acc = zero4();
-      mma<1, 1, LDC, 1, LDO>(acc, in.T, sDU + 16 * vt);
+      wave_lds_order();
+      f32x4 lam = zero4();
+      mma<1, 1, LDC, 1, LDO>(lam, sT, sDU + 16 * vt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r;
-        sNDY[i * LDO + 16 * vt + (l & 15)] = -in.b[i] * acc[r];
+        sNDY[i * LDO + 16 * vt + (l & 15)] = -sB[i] * lam[r];
       }
     }
     __syncthreads();
@@ -435,9 +714,9 @@ __global__ __launch_bounds__(NT) void bwd_ds_kernel(const InT* __restrict__ q, c
       const int crow = 16 * ct + 4 * (l >> 4), vcol = 16 * vt + (l & 15);
       f32x4 acc;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = in.el[crow + r] * ds[u][r];
-      mma<1, 1, LDK, 1, LDO>(acc, in.qg + 16 * ct, sDO + 16 * vt);
-      mma<1, 1, LDK, 1, LDO>(acc, in.kg + 16 * ct, sNDY + 16 * vt);
+      for (int r = 0; r < 4; ++r) acc[r] = sEL[crow + r] * ds[u][r];
+      mma<1, 1, LDK, 1, LDO>(acc, sQG + 16 * ct, sDO + 16 * vt);
+      mma<1, 1, LDK, 1, LDO>(acc, sKG + 16 * ct, sNDY + 16 * vt);
       ds[u] = acc;
       *reinterpret_cast<float4*>(sDST + vcol * LDK + crow) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
@@ -456,26 +735,28 @@ __global__ __launch_bounds__(NT) void bwd_ds_kernel(const InT* __restrict__ q, c
 
 template <int DK, int BV>
 constexpr size_t ds_lds_bytes() {
-  constexpr int LDK = Intra<DK>::LDK, LDO = BV + 4;
-  return sizeof(float) * ((size_t)Intra<DK>::FLOATS + 3 * C * LDO + (size_t)BV * LDK + 8 * C * LDC);
+  using Sh = SerialShape<DK, BV>;
+  return sizeof(float) * ((size_t)3 * C * Sh::LDK + 2 * C * LDC + C + DK + 3 * C * Sh::LDO + (size_t)BV * Sh::LDK +
+                          8 * C * LDC);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Gradient pass: one workgroup per (chunk slot, head).  Value columns in tiles of BV = 32:
-// per tile, S and dS' columns are staged in LDS and the dv-reductions (dQg, dKg, dKc, dM, dA,
-// db and sum_v S dS') accumulate in registers.
+// per tile, S, dS' and V columns are staged in LDS and the dv-reductions (dQg, dKg, dKc, dM,
+// dA, db and sum_v S dS') accumulate in registers.
 template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(
-    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v, const float* __restrict__ la,
-    const float* __restrict__ beta, const float* __restrict__ h0, const int32_t* __restrict__ cu,
-    const float* __restrict__ dout, const float* __restrict__ ckpt, const float* __restrict__ dsw,
-    float* __restrict__ dq, float* __restrict__ dk_out, float* __restrict__ dv_out, float* __restrict__ dla,
-    float* __restrict__ dbeta, int H, int64_t seq_len, int n_seqs) {
+    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v, const int32_t* __restrict__ cu,
+    const float* __restrict__ dout, const float* __restrict__ ops, const float* __restrict__ sw,
+    const float* __restrict__ dsw, float* __restrict__ dq, float* __restrict__ dk_out, float* __restrict__ dv_out,
+    float* __restrict__ dla, float* __restrict__ dbeta, int H, int64_t seq_len, int n_seqs) {
   using In = Intra<DK>;
-  constexpr int BV = 32, LDK = In::LDK, LDO = DV + 4, LDB = BV + 4, LDY = BV + 4;
+  using O = OpTile<DK>;
+  constexpr int BV = 32, LDK = In::LDK, LDO = DV + 4, LDB = BV + 4, LDY = BV + 4, R4 = DK / 4;
   constexpr int NCT = DK / 16, NTV = DV / BV, UPT = DK * BV / 4 / NT;
   constexpr int XW0 = NCT % 8, XW1 = (NCT + 1) % 8, XW2 = (NCT + 2) % 8;
-  static_assert(NCT <= 8 && UPT >= 1 && DK * BV / 4 % NT == 0, "tiling");
+  constexpr int VE = (int)(16 / sizeof(InT)), NVI = C * BV / VE;  // 16-byte items of a value tile
+  static_assert(NCT <= 8 && UPT >= 1 && DK * BV / 4 % NT == 0 && NVI <= NT, "tiling");
 
   extern __shared__ __attribute__((aligned(16))) float smem[];
   In in(smem);
@@ -490,75 +771,122 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   float* sDY = sL + C * LDY;
   float* sDM = sDY + C * LDY;      // [C][LDC]
   float* sDA = sDM + C * LDC;
-  float* sGS = sDA + C * LDC;      // [DK]: sum_v S dS'
+  float* sGS = sDA + C * LDC;      // [2][DK]: sum_v S dS' over the even / odd value blocks
+  float* sV = sGS + 2 * DK;        // [C][LDY]
 
   const int slot = blockIdx.x / H, h = blockIdx.x - slot * H;
-  // the sequence of this slot: the last n with start(n) / C + n <= slot
-  int lo = 0, hi = n_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    const int64_t st = cu ? (int64_t)cu[mid] : (int64_t)mid * seq_len;
-    if (st / C + mid <= slot) lo = mid;
-    else hi = mid - 1;
-  }
-  const int n = lo;
-  int64_t start, len;
-  seq_range(cu, n, seq_len, start, len);
-  const int64_t j = (int64_t)slot - (start / C + n);
-  if (j < 0 || C * j >= len) return;  // a slot no chunk maps to (whole workgroup)
+  int n;
+  int64_t start, len, j;
+  if (!slot_chunk(cu, n_seqs, seq_len, slot, n, start, len, j)) return;  // (whole workgroup)
   const int64_t t0 = start + C * j;
   const int Lc = (int)(len - C * j < C ? len - C * j : C);
-  const int chain = n * H + h;
-  const float* S0 = j == 0 ? (h0 ? h0 + (size_t)chain * DK * DV : nullptr)
-                           : ckpt + ((size_t)((start + C * j) / C - 1) * H + h) * DK * DV;
+  const float* S0 = sw + ((size_t)slot * H + h) * DK * DV;
   const float* dSC = dsw + ((size_t)slot * H + h) * DK * DV;
-  const int w = threadIdx.x / kWave, l = lane();
+  const float* op = ops + ((size_t)slot * H + h) * O::FLOATS;
+  const int tid = threadIdx.x, w = tid / kWave, l = lane();
 
-  // S and dS' columns of value tile tv, in registers: the next tile's are in flight while
-  // the current one is worked on (the first tile's beside the chunk's input loads)
+  // S and dS' (fragment order) and V columns of value tile tv, in registers: the next tile's
+  // are in flight while the current one is worked on (the first tile's beside the chunk's
+  // operand loads).  Item e = tid + NT u is lane l of tile e / 64 of the tile's run: channel
+  // block (e / 64) % NCT, value block (e / 64) / NCT.
   float4 pS[UPT], pD[UPT];
+  uint4 pv = make_uint4(0u, 0u, 0u, 0u);
   auto fetch = [&](int tv) {
+    const size_t base = (size_t)(2 * tv) * NCT * 256;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int e = threadIdx.x + NT * u, c = e / (BV / 4), c4 = (e - c * (BV / 4)) * 4;
-      pS[u] = S0 ? *reinterpret_cast<const float4*>(S0 + (size_t)c * DV + tv * BV + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      pD[u] = *reinterpret_cast<const float4*>(dSC + (size_t)c * DV + tv * BV + c4);
+      const size_t o4 = base + 4 * (size_t)(tid + NT * u);
+      pS[u] = *reinterpret_cast<const float4*>(S0 + o4);
+      pD[u] = *reinterpret_cast<const float4*>(dSC + o4);
+    }
+    if (tid < NVI) {
+      const int i = tid / (BV / VE), c = (tid - i * (BV / VE)) * VE;
+      pv = make_uint4(0u, 0u, 0u, 0u);
+      if (i < Lc) pv = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + i) * H + h) * DV + tv * BV + c);
     }
   };
   fetch(0);
-  in.load(q, k, la, beta, t0, Lc, H, h);
-  for (int e = threadIdx.x; e < C * DV / 4; e += NT) {
-    const int i = e / (DV / 4), c = (e - i * (DV / 4)) * 4;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < Lc) x = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + c);
-    *reinterpret_cast<float4*>(sDO + i * LDO + c) = x;
+  // the chunk's operands (prep tile: Kg, Kc, g; A, M, T, T Diag(b); b, e^{g_L}), q, k and dO:
+  // every load issued before the first is used, then put in LDS
+  constexpr int NOP = 3 * C * R4, IOP = (NOP + NT - 1) / NT;
+  constexpr int NSM = 4 * C * C / 4 + C / 4 + R4;
+  constexpr int NQK = 2 * C * DK / VE, IQK = (NQK + NT - 1) / NT;
+  constexpr int NDO = C * DV / 4, IDO = (NDO + NT - 1) / NT;
+  static_assert(NSM <= NT, "one small item per thread");
+  float4 rop[IOP], rdo[IDO], rsm = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint4 rqk[IQK];
+#pragma unroll
+  for (int it = 0; it < IOP; ++it) {
+    const int e = tid + NT * it;
+    rop[it] = e < NOP ? *reinterpret_cast<const float4*>(op + O::KG + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (tid < 4 * C * C / 4) rsm = *reinterpret_cast<const float4*>(op + O::A + 4 * tid);
+  else if (tid < NSM) rsm = *reinterpret_cast<const float4*>(op + O::B + 4 * (tid - 4 * C * C / 4));
+#pragma unroll
+  for (int it = 0; it < IQK; ++it) {
+    const int e = tid + NT * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
+    const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
+    rqk[it] = make_uint4(0u, 0u, 0u, 0u);
+    if (e < NQK && i < Lc) rqk[it] = *reinterpret_cast<const uint4*>((which ? k : q) + ((size_t)(t0 + i) * H + h) * DK + c);
+  }
+#pragma unroll
+  for (int it = 0; it < IDO; ++it) {
+    const int e = tid + NT * it, i = e / (DV / 4), c = (e - i * (DV / 4)) * 4;
+    rdo[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e < NDO && i < Lc) rdo[it] = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + c);
+  }
+  const bool exact = op[O::FLAG] != 0.f;
+#pragma unroll
+  for (int it = 0; it < IOP; ++it) {
+    const int e = tid + NT * it;
+    if (e < NOP) {
+      const int m = e / (C * R4), ee = e - m * (C * R4), i = ee / R4, c = (ee - i * R4) * 4;
+      *reinterpret_cast<float4*>((m == 0 ? in.kg : m == 1 ? in.kc : in.g) + i * LDK + c) = rop[it];
+    }
+  }
+  if (tid < 4 * C * C / 4) {
+    const int m = tid / (C * C / 4), i = (tid / 4) % C, c = (tid % 4) * 4;
+    *reinterpret_cast<float4*>(in.A + m * C * LDC + i * LDC + c) = rsm;
+  } else if (tid < NSM) {
+    *reinterpret_cast<float4*>(in.b + 4 * (tid - 4 * C * C / 4)) = rsm;
+  }
+#pragma unroll
+  for (int it = 0; it < IQK; ++it) {
+    const int e = tid + NT * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
+    const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
+    if (e < NQK) widen16((which ? in.k : in.q) + i * LDK + c, rqk[it], InT{});
+  }
+#pragma unroll
+  for (int it = 0; it < IDO; ++it) {
+    const int e = tid + NT * it, i = e / (DV / 4), c = (e - i * (DV / 4)) * 4;
+    if (e < NDO) *reinterpret_cast<float4*>(sDO + i * LDO + c) = rdo[it];
   }
   __syncthreads();
-  const bool exact = __syncthreads_or(in.prefix());
-  in.scale(exact);
-  __syncthreads();
-  if (exact) {
-    if (w < 4) in.gram_exact();
-  } else if (w < 2) {
-    in.gram(w);
-  }
-  __syncthreads();
-  if (w == 0) in.inverse();
+  if (!exact) in.scale_balanced();  // for the Gram terms' chain rule at the end
 
   f32x4 aQ = zero4(), aK = zero4(), aC = zero4(), aX = zero4(), db = zero4();
-  float gs[UPT];
+  float gs[UPT][4];
 #pragma unroll
-  for (int u = 0; u < UPT; ++u) gs[u] = 0.f;
+  for (int u = 0; u < UPT; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gs[u][r] = 0.f;
 
   for (int tv = 0; tv < NTV; ++tv) {
     const int vb = tv * BV;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {  // stage S and dS' columns [vb, vb + BV)
-      const int e = threadIdx.x + NT * u, c = e / (BV / 4), c4 = (e - c * (BV / 4)) * 4;
-      const float4 s4 = pS[u], d4 = pD[u];
-      *reinterpret_cast<float4*>(sS + c * LDB + c4) = s4;
-      *reinterpret_cast<float4*>(sD + c * LDB + c4) = d4;
-      gs[u] += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
+      const int tl = (tid + NT * u) / 64, c = 16 * (tl % NCT) + 4 * (l >> 4), col = 16 * (tl / NCT) + (l & 15);
+      const float sv[4] = {pS[u].x, pS[u].y, pS[u].z, pS[u].w}, dv[4] = {pD[u].x, pD[u].y, pD[u].z, pD[u].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sS[(c + r) * LDB + col] = sv[r];
+        sD[(c + r) * LDB + col] = dv[r];
+        gs[u][r] += sv[r] * dv[r];
+      }
+    }
+    if (tid < NVI) {
+      const int i = tid / (BV / VE), c = (tid - i * (BV / VE)) * VE;
+      widen16(sV + i * LDY + c, pv, InT{});
     }
     if (tv + 1 < NTV) fetch(tv + 1);
     __syncthreads();
@@ -578,9 +906,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r;
-        float vv = 0.f;
-        if (i < Lc) vv = to_f32(v[((size_t)(t0 + i) * H + h) * DV + vb + 16 * vt + (l & 15)]);
-        sY[i * LDY + 16 * vt + (l & 15)] = vv - acc[r];
+        sY[i * LDY + 16 * vt + (l & 15)] = sV[i * LDY + 16 * vt + (l & 15)] - acc[r];
       }
     } else if (w < 4) {  // dU = M^T dO + Kc dS'
       const int vt = w - 2;
@@ -659,12 +985,13 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
       }
     }
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {  // the BV/4 threads of one channel are consecutive lanes
-      float s = gs[u];
+    for (int u = 0; u < UPT; ++u) {  // over the 16 value columns of a lane row, then per block parity
+      const int tl = (tid + NT * u) / 64, c = 16 * (tl % NCT) + 4 * (l >> 4);
 #pragma unroll
-      for (int m = 1; m < BV / 4; m <<= 1) s += wave_xor(s, m);
-      const int e = threadIdx.x + NT * u, c = e / (BV / 4);
-      if ((e & (BV / 4 - 1)) == 0) sGS[c] = s;
+      for (int r = 0; r < 4; ++r) {
+        const float s = row_sum16(gs[u][r]);
+        if ((l & 15) == 0) sGS[(tl / NCT) * DK + c + r] = s;
+      }
     }
   }
   __syncthreads();
@@ -739,7 +1066,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   __syncthreads();
   if ((int)threadIdx.x < DK) {  // dlog a: suffix sums of dg, the last-row terms entering every row
     const int c = threadIdx.x;
-    float run = in.el[c] * sGS[c];
+    float run = in.el[c] * (sGS[c] + sGS[DK + c]);
 #pragma unroll
     for (int i = 0; i < C; ++i) run += sKCT[i * LDK + c];
 #pragma unroll
@@ -753,8 +1080,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
 template <int DK, int DV>
 constexpr size_t grad_lds_bytes() {
   constexpr int BV = 32, LDO = DV + 4, LDB = BV + 4, LDY = BV + 4;
-  return sizeof(float) * ((size_t)Intra<DK>::FLOATS + C * LDO + 2 * DK * LDB + 8 * C * LDC + 5 * C * LDY +
-                          2 * C * LDC + DK);
+  return sizeof(float) * ((size_t)Intra<DK>::FLOATS + C * LDO + 2 * DK * LDB + 8 * C * LDC + 6 * C * LDY +
+                          2 * C * LDC + 2 * DK);
 }
 
 static hipError_t set_lds(const void* kern, size_t lds, std::atomic<uint64_t>& done) {
@@ -770,61 +1097,85 @@ static hipError_t set_lds(const void* kern, size_t lds, std::atomic<uint64_t>& d
   return hipSuccess;
 }
 
-// value-tile width of the dS pass: 64 when that still gives a workgroup per CU
-static int ds_bv(int n_chains, int dv) { return ((int64_t)n_chains * (dv / 64) >= 256) ? 64 : 32; }
+// chunk slots (see slot_chunk) and the workspace: the prep tiles, then the states entering
+// every chunk, then the state cotangents leaving every chunk
+static int64_t n_slots(int64_t total_tokens, int n_seqs) { return total_tokens / C + n_seqs + 1; }
 
-template <int DK, int BV, typename InT>
-static hipError_t launch_ds(const BwdArgs& a, float* dsw) {
-  constexpr size_t lds = ds_lds_bytes<DK, BV>();
-  static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = bwd_ds_kernel<DK, BV, InT>;
+
+
+template <int DK, typename InT>
+static hipError_t launch_prep(const BwdArgs& a, float* ops) {
+  constexpr size_t lds = sizeof(float) * (size_t)PrepLay<DK>::FLOATS;
+  auto kern = bwd_prep_kernel<DK, InT>;
   static std::atomic<uint64_t> done{0};
   hipError_t e = set_lds((const void*)kern, lds, done);
   if (e != hipSuccess) return e;
-  const int64_t grid = (int64_t)a.n_seqs * a.n_heads * (a.dv_dim / BV);
+  const int64_t grid = n_slots(a.total_tokens, a.n_seqs) * a.n_heads;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q,
-                     (const InT*)a.k, a.log_alpha, a.beta, a.cu_seqlens, a.dout, a.dhT, dsw, a.dh0, a.n_heads,
-                     a.dv_dim, a.seq_len);
+                     (const InT*)a.k, a.log_alpha, a.beta, a.cu_seqlens, ops, a.n_heads, a.seq_len, a.n_seqs);
+  return hipGetLastError();
+}
+
+template <int DK, int BV, typename InT>
+static hipError_t launch_serial(const BwdArgs& a, const float* ops, float* sw, float* dsw) {
+  const int64_t grid = (int64_t)a.n_seqs * a.n_heads * (a.dv_dim / BV);
+  {
+    constexpr size_t lds = states_lds_bytes<DK, BV>();
+    static_assert(lds <= 160 * 1024, "LDS budget");
+    auto kern = bwd_states_kernel<DK, BV, InT>;
+    static std::atomic<uint64_t> done{0};
+    hipError_t e = set_lds((const void*)kern, lds, done);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.v, a.h0,
+                       a.cu_seqlens, ops, sw, a.n_heads, a.dv_dim, a.seq_len);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  constexpr size_t lds = ds_lds_bytes<DK, BV>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = bwd_ds_kernel<DK, BV>;
+  static std::atomic<uint64_t> done{0};
+  hipError_t e = set_lds((const void*)kern, lds, done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, a.cu_seqlens, a.dout, a.dhT,
+                     ops, dsw, a.dh0, a.n_heads, a.dv_dim, a.seq_len);
   return hipGetLastError();
 }
 
 template <int DK, int DV, typename InT>
-static hipError_t launch_grad(const BwdArgs& a, const float* ckpt, const float* dsw) {
+static hipError_t launch_grad(const BwdArgs& a, const float* ops, const float* sw, const float* dsw) {
   constexpr size_t lds = grad_lds_bytes<DK, DV>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = bwd_grad_kernel<DK, DV, InT>;
   static std::atomic<uint64_t> done{0};
   hipError_t e = set_lds((const void*)kern, lds, done);
   if (e != hipSuccess) return e;
-  const int64_t slots = a.total_tokens / C + a.n_seqs + 1;
-  const int64_t grid = slots * a.n_heads;
+  const int64_t grid = n_slots(a.total_tokens, a.n_seqs) * a.n_heads;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q,
-                     (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, a.h0, a.cu_seqlens, a.dout, ckpt, dsw,
-                     a.dq, a.dk, a.dv, a.dlog_alpha, a.dbeta, a.n_heads, a.seq_len, a.n_seqs);
+                     (const InT*)a.k, (const InT*)a.v, a.cu_seqlens, a.dout, ops, sw, dsw, a.dq, a.dk, a.dv,
+                     a.dlog_alpha, a.dbeta, a.n_heads, a.seq_len, a.n_seqs);
   return hipGetLastError();
 }
 
 template <int DK, int DV, typename InT>
 static hipError_t run(const BwdArgs& a) {
-  const size_t sd = (size_t)DK * DV;
-  const int64_t nck = a.total_tokens / C;
-  float* ckpt = (float*)a.ws;
-  float* dsw = ckpt + (size_t)nck * a.n_heads * sd;
-  // (1) forward states entering every chunk; o goes to dv, which the gradient pass overwrites
-  ChunkArgs f{};
-  f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.beta = a.beta; f.h0 = a.h0;
-  f.cu_seqlens = a.cu_seqlens; f.o = a.dv; f.hT = nullptr; f.ckpt = nck > 0 ? ckpt : nullptr;
-  f.ckpt_every = C; f.n_seqs = a.n_seqs; f.n_heads = a.n_heads; f.dk = DK; f.dv = DV; f.chunk_size = C;
-  f.total_tokens = a.total_tokens; f.seq_len = a.seq_len; f.bf16 = a.bf16; f.stream = a.stream;
-  hipError_t e = launch_chunk_fwd_f32(f);
+  const size_t per = (size_t)n_slots(a.total_tokens, a.n_seqs) * a.n_heads;
+  float* ops = (float*)a.ws;
+  float* sw = ops + per * OpTile<DK>::FLOATS;
+  float* dsw = sw + per * DK * DV;
+  // (1) every chunk's operands
+  hipError_t e = launch_prep<DK, InT>(a, ops);
   if (e != hipSuccess) return e;
-  // (2) dS' of every chunk, dh0
-  if (ds_bv(a.n_seqs * a.n_heads, DV) == 64) e = launch_ds<DK, 64, InT>(a, dsw);
-  else e = launch_ds<DK, 32, InT>(a, dsw);
+  // (2) the states entering every chunk, (3) the cotangents of the states leaving them and dh0,
+  // in 32-column value tiles: two or three workgroups share a CU, one's barrier waits filling
+  // the others' matrix-core work (on the Kimi-Linear layer 0.69 + 0.96 ms against 0.86 + 1.00
+  // with 64-column tiles, one workgroup per CU)
+  e = launch_serial<DK, 32, InT>(a, ops, sw, dsw);
   if (e != hipSuccess) return e;
-  // (3) the gradients of every chunk
-  return launch_grad<DK, DV, InT>(a, ckpt, dsw);
+  // (4) the gradients of every chunk
+  return launch_grad<DK, DV, InT>(a, ops, sw, dsw);
 }
 
 template <typename InT>
@@ -839,9 +1190,8 @@ static hipError_t dispatch(const BwdArgs& a) {
 }  // namespace bwdc
 
 size_t bwd_chunk_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv) {
-  const size_t sd = (size_t)dk * dv * sizeof(float);
-  const size_t nck = (size_t)(total_tokens / bwdc::C);
-  return (2 * nck + (size_t)n_seqs + 1) * (size_t)n_heads * sd;
+  const size_t per_slot = ((size_t)65 * dk + 1044 + 2 * (size_t)dk * dv) * sizeof(float);
+  return (size_t)bwdc::n_slots(total_tokens, n_seqs) * (size_t)n_heads * per_slot;
 }
 
 hipError_t launch_bwd_chunk(const BwdArgs& a) {

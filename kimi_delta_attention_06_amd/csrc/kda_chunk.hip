@@ -2164,15 +2164,6 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws) {
 #endif  // KDA_CHUNK_SPLIT
 
 #if KDA_CHUNK_FUSED
-hipError_t launch_chunk_fwd_f32(const ChunkArgs& a) {
-  using namespace chunkk;
-  if (a.chunk_size != 16 || !chunk_fwd_supported(a.dk, a.dv, 16, false)) return hipErrorInvalidValue;
-  if (a.bf16) {
-    return a.dk == 128 ? dispatch_bv<16, 128, 64, Prec::F32, bf16_t>(a) : dispatch_bv<16, 64, 64, Prec::F32, bf16_t>(a);
-  }
-  return a.dk == 128 ? dispatch_bv<16, 128, 64, Prec::F32, float>(a) : dispatch_bv<16, 64, 64, Prec::F32, float>(a);
-}
-
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {
   using namespace chunkk;
   if (!chunk_fwd_supported(a.dk, a.dv, a.chunk_size, a.bf16)) return hipErrorInvalidValue;

@@ -67,13 +67,11 @@ hipError_t launch_recurrent_step(const RecurrentArgs& a);
 // Backward pass (token-recurrent, fp32 state and gradients).
 hipError_t launch_bwd(const BwdArgs& a);
 size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv);
-// Backward pass (chunkwise, fp32 matrix core): forward states every 16 tokens, reverse dS pass,
-// per-chunk gradients.
+// Backward pass (chunkwise, fp32 matrix core): per-chunk operands, forward states and reverse
+// dS passes, per-chunk gradients.
 hipError_t launch_bwd_chunk(const BwdArgs& a);
 size_t bwd_chunk_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
-// The forward in fp32 matrix-core precision for either input type, chunk_size 16 only.
-hipError_t launch_chunk_fwd_f32(const ChunkArgs& a);
 // Split path (bf16 only): intra-chunk pass into `ws`, then the state pass.
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws);
 // Workspace bytes the split path needs for these sizes.

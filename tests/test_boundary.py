@@ -233,9 +233,9 @@ def bwd_call(fn="kda_bwd", **kw):
 def test_bwd_workspace_size():
     b = ctypes.c_size_t(0)
     assert lib.kda_bwd_workspace_size(1, 64, 2, 128, 128, ctypes.byref(b)) == 0
-    # states entering the 64 / 16 chunks + state cotangents of (64 / 16 + 1 + 1) chunk slots,
-    # x 2 heads x 64 KiB
-    assert b.value == (4 + 6) * 2 * 128 * 128 * 4
+    # (64 / 16 + 1 + 1) chunk slots x 2 heads, each: the chunk's operands (65 dk + 1044 floats),
+    # the state entering it and the cotangent of the state leaving it (dk x dv floats each)
+    assert b.value == 6 * 2 * (65 * 128 + 1044 + 2 * 128 * 128) * 4
     assert lib.kda_bwd_workspace_size(1, 64, 2, 96, 128, ctypes.byref(b)) == 2
     assert lib.kda_bwd_workspace_size(1, 64, 2, 128, 128, None) == 1
 
