@@ -436,6 +436,16 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(const InT* __restrict__ q,
 // its cotangent) lives in MFMA accumulators: wave w owns tiles tt = w + 8 u, channel block
 // tt % (DK/16), value block tt / (DK/16).  A chunk's operands are read from its prep tile into
 // registers while the chunk before is processed, and put in LDS at the top of the chunk.
+// Block -> (chain, value tile) of a serial pass.  Workgroups go to the 8 XCDs round-robin by
+// index, so the tiles of one chain take indices of one residue mod 8: they run on one XCD and
+// read each chunk's operand tile through one L2 (the grid is padded to a multiple of 8 chains).
+__device__ __forceinline__ bool serial_block(int n_chains, int ntile, int& chain, int& tile) {
+  const int xcd = blockIdx.x & 7, qd = blockIdx.x >> 3;
+  tile = qd % ntile;
+  chain = (qd / ntile) * 8 + xcd;
+  return chain < n_chains;
+}
+
 template <int DK, int BV>
 struct SerialShape {
   static constexpr int LDK = DK + 4, LDO = BV + 4;
@@ -450,7 +460,8 @@ struct SerialShape {
 template <int DK, int BV, typename InT>
 __global__ __launch_bounds__(NT) void bwd_states_kernel(const InT* __restrict__ v, const float* __restrict__ h0,
                                                         const int32_t* __restrict__ cu, const float* __restrict__ ops,
-                                                        float* __restrict__ sw, int H, int DV, int64_t seq_len) {
+                                                        float* __restrict__ sw, int n_chains, int H, int DV,
+                                                        int64_t seq_len) {
   using O = OpTile<DK>;
   using Sh = SerialShape<DK, BV>;
   constexpr int LDK = Sh::LDK, LDO = Sh::LDO, NVT = Sh::NVT, NCT = Sh::NCT, TPW = Sh::TPW;
@@ -471,8 +482,8 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const InT* __restrict__ 
   float* sY = sPart + 8 * C * LDC;     // [C][LDO]
   float* sU = sY + C * LDO;            // [C][LDO]
 
-  const int ntile = DV / BV;
-  const int chain = blockIdx.x / ntile, tile = blockIdx.x - chain * ntile;
+  int chain, tile;
+  if (!serial_block(n_chains, DV / BV, chain, tile)) return;
   const int n = chain / H, h = chain - n * H, v0 = tile * BV;
   int64_t start, len;
   seq_range(cu, n, seq_len, start, len);
@@ -590,8 +601,8 @@ constexpr size_t states_lds_bytes() {
 template <int DK, int BV>
 __global__ __launch_bounds__(NT) void bwd_ds_kernel(const int32_t* __restrict__ cu, const float* __restrict__ dout,
                                                     const float* __restrict__ dhT, const float* __restrict__ ops,
-                                                    float* __restrict__ dsw, float* __restrict__ dh0, int H, int DV,
-                                                    int64_t seq_len) {
+                                                    float* __restrict__ dsw, float* __restrict__ dh0, int n_chains,
+                                                    int H, int DV, int64_t seq_len) {
   using O = OpTile<DK>;
   using Sh = SerialShape<DK, BV>;
   constexpr int LDK = Sh::LDK, LDO = Sh::LDO, NVT = Sh::NVT, NCT = Sh::NCT, TPW = Sh::TPW;
@@ -615,8 +626,8 @@ __global__ __launch_bounds__(NT) void bwd_ds_kernel(const int32_t* __restrict__ 
   float* sDU = sPart + 8 * C * LDC;    // [C][LDO]
   float* sNDY = sDU + C * LDO;         // [C][LDO]: -dY
 
-  const int ntile = DV / BV;
-  const int chain = blockIdx.x / ntile, tile = blockIdx.x - chain * ntile;
+  int chain, tile;
+  if (!serial_block(n_chains, DV / BV, chain, tile)) return;
   const int n = chain / H, h = chain - n * H, v0 = tile * BV;
   int64_t start, len;
   seq_range(cu, n, seq_len, start, len);
@@ -743,7 +754,8 @@ constexpr size_t ds_lds_bytes() {
 // ---------------------------------------------------------------------------------------------
 // Gradient pass: one workgroup per (chunk slot, head).  Value columns in tiles of BV = 32:
 // per tile, S, dS' and V columns are staged in LDS and the dv-reductions (dQg, dKg, dKc, dM,
-// dA, db and sum_v S dS') accumulate in registers.
+// dA, db and sum_v S dS') accumulate in registers; then the chain rule through the decay
+// factors.
 template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v, const int32_t* __restrict__ cu,
@@ -763,8 +775,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   float* sDO = smem + In::FLOATS;  // [C][LDO]
   float* sS = sDO + C * LDO;       // [DK][LDB]
   float* sD = sS + DK * LDB;       // [DK][LDB]
-  float* sPart = sD + DK * LDB;    // [8][C][LDC]
-  float* sY = sPart + 8 * C * LDC; // [C][LDY]
+  float4* sQX = reinterpret_cast<float4*>(sD + DK * LDB);  // [NCT][64]: the dQg tiles ([8][C][LDC] floats reserved)
+  float* sY = sD + DK * LDB + 8 * C * LDC;                  // [C][LDY]
   float* sDU = sY + C * LDY;
   float* sU = sDU + C * LDY;
   float* sL = sU + C * LDY;        // lambda
@@ -864,7 +876,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   __syncthreads();
   if (!exact) in.scale_balanced();  // for the Gram terms' chain rule at the end
 
-  f32x4 aQ = zero4(), aK = zero4(), aC = zero4(), aX = zero4(), db = zero4();
+  f32x4 aQ[2] = {zero4(), zero4()}, aK = zero4(), aC = zero4(), aX = zero4(), db = zero4();
   float gs[UPT][4];
 #pragma unroll
   for (int u = 0; u < UPT; ++u)
@@ -890,55 +902,50 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     }
     if (tv + 1 < NTV) fetch(tv + 1);
     __syncthreads();
-    {  // partial Kg S (waves 0-3) and Kc dS' (waves 4-7) over one half of the channels
-      const int vt = w & 1, kh = (w >> 1) & 1;
-      f32x4 acc = zero4();
-      if (w < 4) mma<DK / 32, LDK, 1, 1, LDB>(acc, in.kg + kh * (DK / 2), sS + kh * (DK / 2) * LDB + 16 * vt);
-      else mma<DK / 32, LDK, 1, 1, LDB>(acc, in.kc + kh * (DK / 2), sD + kh * (DK / 2) * LDB + 16 * vt);
-      store_tile(sPart + w * C * LDC, LDC, acc);
-    }
-    __syncthreads();
-    if (w < 2) {  // Y = V - Kg S
+    // Each of waves 0-3 runs one chain of this tile without a barrier inside (the tiles it
+    // passes through LDS are its own): Y = V - Kg S then U = T Diag(b) Y (waves 0, 1, value
+    // block w), or dU = M^T dO + Kc dS' then lambda = T^T dU and dY = Diag(b) lambda (waves 2,
+    // 3).  Waves 4-7 meanwhile accumulate dQg = dO S^T, which needs neither.
+    if (w < 2) {
       const int vt = w;
       f32x4 acc = zero4();
-      add_tile(acc, sPart + vt * C * LDC, LDC);
-      add_tile(acc, sPart + (vt + 2) * C * LDC, LDC);
+      mma<DK / 16, LDK, 1, 1, LDB>(acc, in.kg, sS + 16 * vt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r;
         sY[i * LDY + 16 * vt + (l & 15)] = sV[i * LDY + 16 * vt + (l & 15)] - acc[r];
       }
-    } else if (w < 4) {  // dU = M^T dO + Kc dS'
+      wave_lds_order();
+      f32x4 u = zero4();
+      mma<1, LDC, 1, 1, LDY>(u, in.TB, sY + 16 * vt);
+      store_tile(sU + 16 * vt, LDY, u);
+    } else if (w < 4) {
       const int vt = w - 2;
       f32x4 acc = zero4();
       mma<1, 1, LDC, 1, LDO>(acc, in.M, sDO + vb + 16 * vt);
-      add_tile(acc, sPart + (4 + vt) * C * LDC, LDC);
-      add_tile(acc, sPart + (6 + vt) * C * LDC, LDC);
+      mma<DK / 16, LDK, 1, 1, LDB>(acc, in.kc, sD + 16 * vt);
       store_tile(sDU + 16 * vt, LDY, acc);
-    }
-    __syncthreads();
-    if (w < 2) {  // U = T Diag(b) Y
-      const int vt = w;
-      f32x4 acc = zero4();
-      mma<1, LDC, 1, 1, LDY>(acc, in.TB, sY + 16 * vt);
-      store_tile(sU + 16 * vt, LDY, acc);
-    } else if (w < 4) {  // lambda = T^T dU, dV = dY = b lambda
-      const int vt = w - 2;
-      f32x4 acc = zero4();
-      mma<1, 1, LDC, 1, LDY>(acc, in.T, sDU + 16 * vt);
+      wave_lds_order();
+      f32x4 lam = zero4();
+      mma<1, 1, LDC, 1, LDY>(lam, in.T, sDU + 16 * vt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r, col = 16 * vt + (l & 15);
-        const float dy = in.b[i] * acc[r];
-        sL[i * LDY + col] = acc[r];
+        const float dy = in.b[i] * lam[r];
+        sL[i * LDY + col] = lam[r];
         sDY[i * LDY + col] = dy;
         if (i < Lc) dv_out[((size_t)(t0 + i) * H + h) * DV + vb + col] = dy;
       }
+    } else {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int ct = 2 * (w - 4) + q2;
+        if (ct < NCT) mma<BV / 16, LDO, 1, LDB, 1>(aQ[q2], sDO + vb, sS + 16 * ct * LDB);
+      }
     }
     __syncthreads();
-    if (w < NCT) {  // dQg += dO S^T, sum dY S^T (= -dKg), dKc += U dS'^T
+    if (w < NCT) {  // sum dY S^T (= -dKg), dKc += U dS'^T
       const int ct = w;
-      mma<BV / 16, LDO, 1, LDB, 1>(aQ, sDO + vb, sS + 16 * ct * LDB);
       mma<BV / 16, LDY, 1, LDB, 1>(aK, sDY, sS + 16 * ct * LDB);
       mma<BV / 16, LDY, 1, LDB, 1>(aC, sU, sD + 16 * ct * LDB);
     }
@@ -957,6 +964,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
       }
     }
     __syncthreads();
+  }
+  // dQg tiles from waves 4-7 to the wave of their channel block
+  if (w >= 4) {
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int ct = 2 * (w - 4) + q2;
+      if (ct < NCT) sQX[ct * 64 + l] = make_float4(aQ[q2][0], aQ[q2][1], aQ[q2][2], aQ[q2][3]);
+    }
   }
 
   // dM, dA, db, sum_v S dS'
@@ -1000,6 +1015,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   float* sKCT = sD;  // [C][LDK]: k dKc e^{g_L - g}
   if (w < NCT) {
     const int ct = w;
+    const float4 dq4 = sQX[ct * 64 + l];
+    const float dqt[4] = {dq4.x, dq4.y, dq4.z, dq4.w};
     // Gram terms through the decay: P = (dM o E) K, R = (dM o E)^T Q, P' = (dA o E) K,
     // R' = (dA o E)^T K, on the matrix core from the balanced operands, or per element
     float pfa[4], rfa[4], ppfa[4], rpfa[4];
@@ -1050,7 +1067,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
       const float eg = expf(gi), ec = expf(gl - gi);
       const float qv = in.q[o], kv = in.k[o];
       const float pf = pfa[r], rf = rfa[r], ppf = ppfa[r], rpf = rpfa[r];
-      const float dqg = aQ[r], dkg = -aK[r], dkc = aC[r];
+      const float dqg = dqt[r], dkg = -aK[r], dkc = aC[r];
       const float dqv = dqg * eg + pf;
       const float dkv = dkg * eg + dkc * ec + rf + ppf + rpf;
       const float dgv = qv * dqv + kv * (dkg * eg - dkc * ec - rf + ppf - rpf);
@@ -1119,7 +1136,9 @@ static hipError_t launch_prep(const BwdArgs& a, float* ops) {
 
 template <int DK, int BV, typename InT>
 static hipError_t launch_serial(const BwdArgs& a, const float* ops, float* sw, float* dsw) {
-  const int64_t grid = (int64_t)a.n_seqs * a.n_heads * (a.dv_dim / BV);
+  const int n_chains = a.n_seqs * a.n_heads;
+  const int64_t grid = (int64_t)((n_chains + 7) / 8) * 8 * (a.dv_dim / BV);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   {
     constexpr size_t lds = states_lds_bytes<DK, BV>();
     static_assert(lds <= 160 * 1024, "LDS budget");
@@ -1128,7 +1147,7 @@ static hipError_t launch_serial(const BwdArgs& a, const float* ops, float* sw, f
     hipError_t e = set_lds((const void*)kern, lds, done);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.v, a.h0,
-                       a.cu_seqlens, ops, sw, a.n_heads, a.dv_dim, a.seq_len);
+                       a.cu_seqlens, ops, sw, n_chains, a.n_heads, a.dv_dim, a.seq_len);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1139,7 +1158,7 @@ static hipError_t launch_serial(const BwdArgs& a, const float* ops, float* sw, f
   hipError_t e = set_lds((const void*)kern, lds, done);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, a.cu_seqlens, a.dout, a.dhT,
-                     ops, dsw, a.dh0, a.n_heads, a.dv_dim, a.seq_len);
+                     ops, dsw, a.dh0, n_chains, a.n_heads, a.dv_dim, a.seq_len);
   return hipGetLastError();
 }
 
