@@ -752,39 +752,64 @@ constexpr size_t ds_lds_bytes() {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Gradient pass: one workgroup per (chunk slot, head).  Value columns in tiles of BV = 32:
-// per tile, S, dS' and V columns are staged in LDS and the dv-reductions (dQg, dKg, dKc, dM,
-// dA, db and sum_v S dS') accumulate in registers; then the chain rule through the decay
-// factors.
+// Gradient pass: one workgroup of 4 waves per (chunk slot, head), two per CU (about 76 KB of
+// LDS each), so one workgroup's memory phases overlap the other's matrix-core work.  Value
+// columns in tiles of BV = 16: per tile, the columns of S, dS', V and dO are staged in LDS and
+// the dv-reductions (dQg, dKg, dKc, dM, dA, db and sum_v S dS') accumulate in registers; then
+// the chain rule through the decay factors.  What only the tile loop reads (Kg, Kc, the staged
+// columns and products) and what only the chain-rule step reads (q, k, g, the balanced
+// operands, dg) share LDS.
+constexpr int NTG = 256;  // threads per gradient workgroup
+
+template <int DK, int DV>
+struct GradLay {
+  static constexpr int BV = 16, LDK = DK + 4, LDB = BV + 4, LDY = BV + 4;
+  // persistent: A, M, T, T Diag(b) [C][LDC]; b [C], e^{g_L} [DK]; dM, dA [C][LDC]; sum_v S dS' [DK]
+  static constexpr int A = 0, M = A + C * LDC, T = M + C * LDC, TB = T + C * LDC;
+  static constexpr int B = TB + C * LDC, EL = B + C, DM = EL + DK, DA = DM + C * LDC, GS = DA + C * LDC;
+  // R1: Kg, Kc [C][LDK] in the tile loop; then the dQg tiles (float4 [NCT][64]), then dg and
+  // k dKc e^{g_L - g} [C][LDK]
+  static constexpr int R1 = GS + DK, KG = R1, KC = KG + C * LDK, QX = R1, DG = R1, KCT = DG + C * LDK;
+  // R2, tile loop: S, dS' [DK][LDB]; partial Kg S and Kc dS' [2][4][C][LDC]; Y, dU, U, lambda,
+  // dY, V, dO [C][LDY]
+  static constexpr int R2 = KCT + C * LDK, SS = R2, SD = SS + DK * LDB, PART = SD + DK * LDB;
+  static constexpr int SY = PART + 8 * C * LDC, SDU = SY + C * LDY, SU = SDU + C * LDY, SL = SU + C * LDY;
+  static constexpr int SDY = SL + C * LDY, SV = SDY + C * LDY, SDO = SV + C * LDY, LOOP_END = SDO + C * LDY;
+  //     chain-rule step: q, k, g, ql, kl, kr [C][LDK]
+  static constexpr int Q = R2, K = Q + C * LDK, G = K + C * LDK, QL = G + C * LDK, KL = QL + C * LDK;
+  static constexpr int KR = KL + C * LDK, TAIL_END = KR + C * LDK;
+  static constexpr int FLOATS = LOOP_END > TAIL_END ? LOOP_END : TAIL_END;
+  static_assert(A % 4 == 0 && B % 4 == 0 && EL % 4 == 0 && DM % 4 == 0 && GS % 4 == 0 && R1 % 4 == 0 &&
+                    KC % 4 == 0 && R2 % 4 == 0 && SD % 4 == 0 && PART % 4 == 0 && SY % 4 == 0 && SDO % 4 == 0 &&
+                    K % 4 == 0 && G % 4 == 0 && QL % 4 == 0 && KR % 4 == 0,
+                "16-byte aligned regions");
+  static_assert(2 * C * LDK >= 4 * (DK / 16) * 64, "the dQg tiles fit in R1");
+};
+
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(NT) void bwd_grad_kernel(
+__global__ __launch_bounds__(NTG) void bwd_grad_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v, const int32_t* __restrict__ cu,
     const float* __restrict__ dout, const float* __restrict__ ops, const float* __restrict__ sw,
     const float* __restrict__ dsw, float* __restrict__ dq, float* __restrict__ dk_out, float* __restrict__ dv_out,
     float* __restrict__ dla, float* __restrict__ dbeta, int H, int64_t seq_len, int n_seqs) {
-  using In = Intra<DK>;
   using O = OpTile<DK>;
-  constexpr int BV = 32, LDK = In::LDK, LDO = DV + 4, LDB = BV + 4, LDY = BV + 4, R4 = DK / 4;
-  constexpr int NCT = DK / 16, NTV = DV / BV, UPT = DK * BV / 4 / NT;
-  constexpr int XW0 = NCT % 8, XW1 = (NCT + 1) % 8, XW2 = (NCT + 2) % 8;
-  constexpr int VE = (int)(16 / sizeof(InT)), NVI = C * BV / VE;  // 16-byte items of a value tile
-  static_assert(NCT <= 8 && UPT >= 1 && DK * BV / 4 % NT == 0 && NVI <= NT, "tiling");
+  using L = GradLay<DK, DV>;
+  constexpr int BV = L::BV, LDK = L::LDK, LDB = L::LDB, LDY = L::LDY, R4 = DK / 4;
+  constexpr int NCT = DK / 16, NTV = DV / BV, UPT = DK * BV / 4 / NTG, KQ = DK / 4;
+  constexpr int VE = (int)(16 / sizeof(InT)), NVI = C * BV / VE, NDI = C * BV / 4;
+  constexpr int NQH = (NCT + 1) / 2;  // dQg channel blocks per accumulating wave (waves 2, 3)
+  static_assert(NCT <= 8 && UPT >= 1 && DK * BV / 4 % NTG == 0 && NVI <= NTG && NDI <= NTG && KQ % 16 == 0,
+                "tiling");
 
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  In in(smem);
-  float* sDO = smem + In::FLOATS;  // [C][LDO]
-  float* sS = sDO + C * LDO;       // [DK][LDB]
-  float* sD = sS + DK * LDB;       // [DK][LDB]
-  float4* sQX = reinterpret_cast<float4*>(sD + DK * LDB);  // [NCT][64]: the dQg tiles ([8][C][LDC] floats reserved)
-  float* sY = sD + DK * LDB + 8 * C * LDC;                  // [C][LDY]
-  float* sDU = sY + C * LDY;
-  float* sU = sDU + C * LDY;
-  float* sL = sU + C * LDY;        // lambda
-  float* sDY = sL + C * LDY;
-  float* sDM = sDY + C * LDY;      // [C][LDC]
-  float* sDA = sDM + C * LDC;
-  float* sGS = sDA + C * LDC;      // [2][DK]: sum_v S dS' over the even / odd value blocks
-  float* sV = sGS + 2 * DK;        // [C][LDY]
+  float *sA = smem + L::A, *sM = smem + L::M, *sT = smem + L::T, *sTB = smem + L::TB, *sB = smem + L::B;
+  float *sEL = smem + L::EL, *sDM = smem + L::DM, *sDA = smem + L::DA, *sGS = smem + L::GS;
+  float *sKG = smem + L::KG, *sKC = smem + L::KC, *sDG = smem + L::DG, *sKCT = smem + L::KCT;
+  float4* sQX = reinterpret_cast<float4*>(smem + L::QX);
+  float *sS = smem + L::SS, *sD = smem + L::SD, *sPart = smem + L::PART, *sY = smem + L::SY, *sDU = smem + L::SDU;
+  float *sU = smem + L::SU, *sL = smem + L::SL, *sDY = smem + L::SDY, *sV = smem + L::SV, *sDO = smem + L::SDO;
+  float *sQ = smem + L::Q, *sK = smem + L::K, *sG = smem + L::G, *sQL = smem + L::QL, *sKL = smem + L::KL;
+  float* sKR = smem + L::KR;
 
   const int slot = blockIdx.x / H, h = blockIdx.x - slot * H;
   int n;
@@ -797,17 +822,16 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   const float* op = ops + ((size_t)slot * H + h) * O::FLOATS;
   const int tid = threadIdx.x, w = tid / kWave, l = lane();
 
-  // S and dS' (fragment order) and V columns of value tile tv, in registers: the next tile's
-  // are in flight while the current one is worked on (the first tile's beside the chunk's
-  // operand loads).  Item e = tid + NT u is lane l of tile e / 64 of the tile's run: channel
-  // block (e / 64) % NCT, value block (e / 64) / NCT.
-  float4 pS[UPT], pD[UPT];
+  // The columns of value tile tv, in registers: the next tile's are in flight while the
+  // current one is worked on.  S and dS' (fragment order): item e = tid + NTG u is lane l of
+  // channel block e / 64 of value block tv.  V and dO: row tid / (BV / VE) (resp. / (BV / 4)).
+  float4 pS[UPT], pD[UPT], pdo = make_float4(0.f, 0.f, 0.f, 0.f);
   uint4 pv = make_uint4(0u, 0u, 0u, 0u);
   auto fetch = [&](int tv) {
-    const size_t base = (size_t)(2 * tv) * NCT * 256;
+    const size_t base = (size_t)tv * NCT * 256;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const size_t o4 = base + 4 * (size_t)(tid + NT * u);
+      const size_t o4 = base + 4 * (size_t)(tid + NTG * u);
       pS[u] = *reinterpret_cast<const float4*>(S0 + o4);
       pD[u] = *reinterpret_cast<const float4*>(dSC + o4);
     }
@@ -816,78 +840,68 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
       pv = make_uint4(0u, 0u, 0u, 0u);
       if (i < Lc) pv = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + i) * H + h) * DV + tv * BV + c);
     }
+    if (tid < NDI) {
+      const int i = tid / (BV / 4), c = (tid - i * (BV / 4)) * 4;
+      pdo = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < Lc) pdo = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + tv * BV + c);
+    }
   };
   fetch(0);
-  // the chunk's operands (prep tile: Kg, Kc, g; A, M, T, T Diag(b); b, e^{g_L}), q, k and dO:
-  // every load issued before the first is used, then put in LDS
-  constexpr int NOP = 3 * C * R4, IOP = (NOP + NT - 1) / NT;
-  constexpr int NSM = 4 * C * C / 4 + C / 4 + R4;
-  constexpr int NQK = 2 * C * DK / VE, IQK = (NQK + NT - 1) / NT;
-  constexpr int NDO = C * DV / 4, IDO = (NDO + NT - 1) / NT;
-  static_assert(NSM <= NT, "one small item per thread");
-  float4 rop[IOP], rdo[IDO], rsm = make_float4(0.f, 0.f, 0.f, 0.f);
-  uint4 rqk[IQK];
+  // the tile loop's operands from the prep tile (Kg, Kc; A, M, T, T Diag(b); b, e^{g_L}):
+  // every load issued before the first is stored
+  constexpr int NOP = 2 * C * R4, IOP = (NOP + NTG - 1) / NTG;
+  constexpr int NSM = 4 * C * C / 4 + C / 4 + R4, ISM = (NSM + NTG - 1) / NTG;
+  float4 rop[IOP], rsm[ISM];
 #pragma unroll
   for (int it = 0; it < IOP; ++it) {
-    const int e = tid + NT * it;
+    const int e = tid + NTG * it;
     rop[it] = e < NOP ? *reinterpret_cast<const float4*>(op + O::KG + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (tid < 4 * C * C / 4) rsm = *reinterpret_cast<const float4*>(op + O::A + 4 * tid);
-  else if (tid < NSM) rsm = *reinterpret_cast<const float4*>(op + O::B + 4 * (tid - 4 * C * C / 4));
 #pragma unroll
-  for (int it = 0; it < IQK; ++it) {
-    const int e = tid + NT * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
-    const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
-    rqk[it] = make_uint4(0u, 0u, 0u, 0u);
-    if (e < NQK && i < Lc) rqk[it] = *reinterpret_cast<const uint4*>((which ? k : q) + ((size_t)(t0 + i) * H + h) * DK + c);
-  }
-#pragma unroll
-  for (int it = 0; it < IDO; ++it) {
-    const int e = tid + NT * it, i = e / (DV / 4), c = (e - i * (DV / 4)) * 4;
-    rdo[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (e < NDO && i < Lc) rdo[it] = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + c);
+  for (int it = 0; it < ISM; ++it) {
+    const int e = tid + NTG * it;
+    rsm[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e < 4 * C * C / 4) rsm[it] = *reinterpret_cast<const float4*>(op + O::A + 4 * e);
+    else if (e < NSM) rsm[it] = *reinterpret_cast<const float4*>(op + O::B + 4 * (e - 4 * C * C / 4));
   }
   const bool exact = op[O::FLAG] != 0.f;
 #pragma unroll
   for (int it = 0; it < IOP; ++it) {
-    const int e = tid + NT * it;
+    const int e = tid + NTG * it;
     if (e < NOP) {
       const int m = e / (C * R4), ee = e - m * (C * R4), i = ee / R4, c = (ee - i * R4) * 4;
-      *reinterpret_cast<float4*>((m == 0 ? in.kg : m == 1 ? in.kc : in.g) + i * LDK + c) = rop[it];
+      *reinterpret_cast<float4*>((m ? sKC : sKG) + i * LDK + c) = rop[it];
     }
   }
-  if (tid < 4 * C * C / 4) {
-    const int m = tid / (C * C / 4), i = (tid / 4) % C, c = (tid % 4) * 4;
-    *reinterpret_cast<float4*>(in.A + m * C * LDC + i * LDC + c) = rsm;
-  } else if (tid < NSM) {
-    *reinterpret_cast<float4*>(in.b + 4 * (tid - 4 * C * C / 4)) = rsm;
-  }
 #pragma unroll
-  for (int it = 0; it < IQK; ++it) {
-    const int e = tid + NT * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
-    const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
-    if (e < NQK) widen16((which ? in.k : in.q) + i * LDK + c, rqk[it], InT{});
+  for (int it = 0; it < ISM; ++it) {
+    const int e = tid + NTG * it;
+    if (e < 4 * C * C / 4) {  // A, M, T, T Diag(b): consecutive [C][LDC] regions
+      const int m = e / (C * C / 4), i = (e / 4) % C, c = (e % 4) * 4;
+      *reinterpret_cast<float4*>(sA + m * C * LDC + i * LDC + c) = rsm[it];
+    } else if (e < NSM) {  // b, e^{g_L}: consecutive
+      *reinterpret_cast<float4*>(sB + 4 * (e - 4 * C * C / 4)) = rsm[it];
+    }
   }
-#pragma unroll
-  for (int it = 0; it < IDO; ++it) {
-    const int e = tid + NT * it, i = e / (DV / 4), c = (e - i * (DV / 4)) * 4;
-    if (e < NDO) *reinterpret_cast<float4*>(sDO + i * LDO + c) = rdo[it];
-  }
-  __syncthreads();
-  if (!exact) in.scale_balanced();  // for the Gram terms' chain rule at the end
 
-  f32x4 aQ[2] = {zero4(), zero4()}, aK = zero4(), aC = zero4(), aX = zero4(), db = zero4();
+  f32x4 aQ[NQH], aK[2], aC[2], aX = zero4(), db = zero4();
+#pragma unroll
+  for (int u = 0; u < NQH; ++u) aQ[u] = zero4();
+  aK[0] = aK[1] = aC[0] = aC[1] = zero4();
   float gs[UPT][4];
 #pragma unroll
   for (int u = 0; u < UPT; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) gs[u][r] = 0.f;
+  // the chain-rule step's inputs (q, k, g), loaded during the last value tile
+  constexpr int NQK = 2 * C * DK / VE, IQK = (NQK + NTG - 1) / NTG, IG = (C * R4 + NTG - 1) / NTG;
+  uint4 rqk[IQK];
+  float4 rg[IG];
 
   for (int tv = 0; tv < NTV; ++tv) {
-    const int vb = tv * BV;
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {  // stage S and dS' columns [vb, vb + BV)
-      const int tl = (tid + NT * u) / 64, c = 16 * (tl % NCT) + 4 * (l >> 4), col = 16 * (tl / NCT) + (l & 15);
+    for (int u = 0; u < UPT; ++u) {  // stage S and dS' columns of value block tv
+      const int c = 16 * ((tid + NTG * u) / 64) + 4 * (l >> 4), col = l & 15;
       const float sv[4] = {pS[u].x, pS[u].y, pS[u].z, pS[u].w}, dv[4] = {pD[u].x, pD[u].y, pD[u].z, pD[u].w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -900,98 +914,132 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
       const int i = tid / (BV / VE), c = (tid - i * (BV / VE)) * VE;
       widen16(sV + i * LDY + c, pv, InT{});
     }
-    if (tv + 1 < NTV) fetch(tv + 1);
+    if (tid < NDI) {
+      const int i = tid / (BV / 4), c = (tid - i * (BV / 4)) * 4;
+      *reinterpret_cast<float4*>(sDO + i * LDY + c) = pdo;
+    }
+    if (tv + 1 < NTV) {
+      fetch(tv + 1);
+    } else {
+#pragma unroll
+      for (int it = 0; it < IQK; ++it) {
+        const int e = tid + NTG * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
+        const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
+        rqk[it] = make_uint4(0u, 0u, 0u, 0u);
+        if (e < NQK && i < Lc)
+          rqk[it] = *reinterpret_cast<const uint4*>((which ? k : q) + ((size_t)(t0 + i) * H + h) * DK + c);
+      }
+#pragma unroll
+      for (int it = 0; it < IG; ++it) {
+        const int e = tid + NTG * it;
+        rg[it] = e < C * R4 ? *reinterpret_cast<const float4*>(op + O::G + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
     __syncthreads();
-    // Each of waves 0-3 runs one chain of this tile without a barrier inside (the tiles it
-    // passes through LDS are its own): Y = V - Kg S then U = T Diag(b) Y (waves 0, 1, value
-    // block w), or dU = M^T dO + Kc dS' then lambda = T^T dU and dY = Diag(b) lambda (waves 2,
-    // 3).  Waves 4-7 meanwhile accumulate dQg = dO S^T, which needs neither.
-    if (w < 2) {
-      const int vt = w;
+    {  // partial Kg S and Kc dS' over channel quarter w
+      f32x4 pk = zero4(), pc = zero4();
+      mma<KQ / 16, LDK, 1, 1, LDB>(pk, sKG + w * KQ, sS + w * KQ * LDB);
+      mma<KQ / 16, LDK, 1, 1, LDB>(pc, sKC + w * KQ, sD + w * KQ * LDB);
+      store_tile(sPart + w * C * LDC, LDC, pk);
+      store_tile(sPart + (4 + w) * C * LDC, LDC, pc);
+    }
+    __syncthreads();
+    if (w == 0) {  // Y = V - Kg S, then U = T Diag(b) Y
       f32x4 acc = zero4();
-      mma<DK / 16, LDK, 1, 1, LDB>(acc, in.kg, sS + 16 * vt);
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) add_tile(acc, sPart + kq * C * LDC, LDC);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r;
-        sY[i * LDY + 16 * vt + (l & 15)] = sV[i * LDY + 16 * vt + (l & 15)] - acc[r];
+        sY[i * LDY + (l & 15)] = sV[i * LDY + (l & 15)] - acc[r];
       }
       wave_lds_order();
       f32x4 u = zero4();
-      mma<1, LDC, 1, 1, LDY>(u, in.TB, sY + 16 * vt);
-      store_tile(sU + 16 * vt, LDY, u);
-    } else if (w < 4) {
-      const int vt = w - 2;
+      mma<1, LDC, 1, 1, LDY>(u, sTB, sY);
+      store_tile(sU, LDY, u);
+    } else if (w == 1) {  // dU = M^T dO + Kc dS', then lambda = T^T dU and dY = Diag(b) lambda
       f32x4 acc = zero4();
-      mma<1, 1, LDC, 1, LDO>(acc, in.M, sDO + vb + 16 * vt);
-      mma<DK / 16, LDK, 1, 1, LDB>(acc, in.kc, sD + 16 * vt);
-      store_tile(sDU + 16 * vt, LDY, acc);
+      mma<1, 1, LDC, 1, LDY>(acc, sM, sDO);
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) add_tile(acc, sPart + (4 + kq) * C * LDC, LDC);
+      store_tile(sDU, LDY, acc);
       wave_lds_order();
       f32x4 lam = zero4();
-      mma<1, 1, LDC, 1, LDY>(lam, in.T, sDU + 16 * vt);
+      mma<1, 1, LDC, 1, LDY>(lam, sT, sDU);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 4 * (l >> 4) + r, col = 16 * vt + (l & 15);
-        const float dy = in.b[i] * lam[r];
+        const int i = 4 * (l >> 4) + r, col = l & 15;
+        const float dy = sB[i] * lam[r];
         sL[i * LDY + col] = lam[r];
         sDY[i * LDY + col] = dy;
-        if (i < Lc) dv_out[((size_t)(t0 + i) * H + h) * DV + vb + col] = dy;
+        if (i < Lc) dv_out[((size_t)(t0 + i) * H + h) * DV + tv * BV + col] = dy;
       }
-    } else {
+    } else {  // dQg += dO S^T over channel blocks (w - 2) NQH ..
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int ct = 2 * (w - 4) + q2;
-        if (ct < NCT) mma<BV / 16, LDO, 1, LDB, 1>(aQ[q2], sDO + vb, sS + 16 * ct * LDB);
-      }
-    }
-    __syncthreads();
-    if (w < NCT) {  // sum dY S^T (= -dKg), dKc += U dS'^T
-      const int ct = w;
-      mma<BV / 16, LDY, 1, LDB, 1>(aK, sDY, sS + 16 * ct * LDB);
-      mma<BV / 16, LDY, 1, LDB, 1>(aC, sU, sD + 16 * ct * LDB);
-    }
-    if (w == XW0) mma<BV / 16, LDO, 1, LDY, 1>(aX, sDO + vb, sU);  // dO U^T
-    if (w == XW1) mma<BV / 16, LDY, 1, LDY, 1>(aX, sDY, sU);       // dY U^T
-    if (w == XW2) {                                                // db += lambda . (Y - A U)
-#pragma unroll
-      for (int vt = 0; vt < 2; ++vt) {
-        f32x4 au = zero4();
-        mma<1, LDC, 1, 1, LDY>(au, in.A, sU + 16 * vt);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * (l >> 4) + r, col = 16 * vt + (l & 15);
-          db[r] += (sY[i * LDY + col] - au[r]) * sL[i * LDY + col];
-        }
+      for (int u = 0; u < NQH; ++u) {
+        const int ct = (w - 2) * NQH + u;
+        if (ct < NCT) mma<1, LDY, 1, LDB, 1>(aQ[u], sDO, sS + 16 * ct * LDB);
       }
     }
     __syncthreads();
-  }
-  // dQg tiles from waves 4-7 to the wave of their channel block
-  if (w >= 4) {
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const int ct = 2 * (w - 4) + q2;
-      if (ct < NCT) sQX[ct * 64 + l] = make_float4(aQ[q2][0], aQ[q2][1], aQ[q2][2], aQ[q2][3]);
+    for (int u = 0; u < 2; ++u) {  // sum dY S^T (= -dKg), dKc += U dS'^T over channel blocks w, w + 4
+      const int ct = w + 4 * u;
+      if (ct < NCT) {
+        mma<1, LDY, 1, LDB, 1>(aK[u], sDY, sS + 16 * ct * LDB);
+        mma<1, LDY, 1, LDB, 1>(aC[u], sU, sD + 16 * ct * LDB);
+      }
     }
+    if (w == 0) mma<1, LDY, 1, LDY, 1>(aX, sDO, sU);  // dO U^T
+    if (w == 1) mma<1, LDY, 1, LDY, 1>(aX, sDY, sU);  // dY U^T
+    if (w == 2) {                                     // db += lambda . (Y - A U)
+      f32x4 au = zero4();
+      mma<1, LDC, 1, 1, LDY>(au, sA, sU);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * (l >> 4) + r;
+        db[r] += (sY[i * LDY + (l & 15)] - au[r]) * sL[i * LDY + (l & 15)];
+      }
+    }
+    __syncthreads();
   }
 
-  // dM, dA, db, sum_v S dS'
+  // dQg tiles (waves 2, 3) to the shared tiles, q, k, g to LDS, dM, dA, db, sum_v S dS'
+  if (w >= 2) {
+#pragma unroll
+    for (int u = 0; u < NQH; ++u) {
+      const int ct = (w - 2) * NQH + u;
+      if (ct < NCT) sQX[ct * 64 + l] = make_float4(aQ[u][0], aQ[u][1], aQ[u][2], aQ[u][3]);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IQK; ++it) {
+    const int e = tid + NTG * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
+    const int i = ee / (DK / VE), c = (ee - i * (DK / VE)) * VE;
+    if (e < NQK) widen16((which ? sK : sQ) + i * LDK + c, rqk[it], InT{});
+  }
+#pragma unroll
+  for (int it = 0; it < IG; ++it) {
+    const int e = tid + NTG * it;
+    if (e < C * R4) *reinterpret_cast<float4*>(sG + (e / R4) * LDK + (e % R4) * 4) = rg[it];
+  }
   {
     const int jj = l & 15;
-    if (w == XW0) {
+    if (w == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r;
         sDM[i * LDC + jj] = jj <= i ? aX[r] : 0.f;
       }
     }
-    if (w == XW1) {
+    if (w == 1) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r;
         sDA[i * LDC + jj] = jj < i ? -aX[r] : 0.f;
       }
     }
-    if (w == XW2) {
+    if (w == 2) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r;
@@ -1000,36 +1048,52 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
       }
     }
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {  // over the 16 value columns of a lane row, then per block parity
-      const int tl = (tid + NT * u) / 64, c = 16 * (tl % NCT) + 4 * (l >> 4);
+    for (int u = 0; u < UPT; ++u) {  // over the 16 value columns of a lane row
+      const int c = 16 * ((tid + NTG * u) / 64) + 4 * (l >> 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float s = row_sum16(gs[u][r]);
-        if ((l & 15) == 0) sGS[(tl / NCT) * DK + c + r] = s;
+        if (jj == 0) sGS[c + r] = s;
       }
     }
   }
   __syncthreads();
+  // the balanced operands for the Gram terms' chain rule (not on the exact path), and each
+  // wave's dQg tiles into registers (their LDS is reused below)
+  if (!exact) {
+    for (int e = tid; e < C * DK; e += NTG) {
+      const int i = e / DK, c = e - i * DK, o = i * LDK + c;
+      const float gi = sG[o], m = 0.5f * sG[(C - 1) * LDK + c];
+      const float e1 = expf(gi - m), e2 = expf(m - gi);
+      const float qv = sQ[o], kv = sK[o];
+      sQL[o] = qv * e1;
+      sKL[o] = kv * e1;
+      sKR[o] = kv * e2;
+    }
+  }
+  float4 dq4[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) dq4[u] = w + 4 * u < NCT ? sQX[(w + 4 * u) * 64 + l] : make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();
 
-  float* sDG = sS;   // [C][LDK]: dg per row (sS and sD are free now)
-  float* sKCT = sD;  // [C][LDK]: k dKc e^{g_L - g}
-  if (w < NCT) {
-    const int ct = w;
-    const float4 dq4 = sQX[ct * 64 + l];
-    const float dqt[4] = {dq4.x, dq4.y, dq4.z, dq4.w};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ct = w + 4 * u;
+    if (ct >= NCT) continue;
+    const float dqt[4] = {dq4[u].x, dq4[u].y, dq4[u].z, dq4[u].w};
     // Gram terms through the decay: P = (dM o E) K, R = (dM o E)^T Q, P' = (dA o E) K,
     // R' = (dA o E)^T K, on the matrix core from the balanced operands, or per element
     float pfa[4], rfa[4], ppfa[4], rpfa[4];
     if (!exact) {
       f32x4 P = zero4(), R = zero4(), Pp = zero4(), Rp = zero4();
-      mma<1, LDC, 1, 1, LDK>(P, sDM, in.kr + 16 * ct);
-      mma<1, 1, LDC, 1, LDK>(R, sDM, in.ql + 16 * ct);
-      mma<1, LDC, 1, 1, LDK>(Pp, sDA, in.kr + 16 * ct);
-      mma<1, 1, LDC, 1, LDK>(Rp, sDA, in.kl + 16 * ct);
+      mma<1, LDC, 1, 1, LDK>(P, sDM, sKR + 16 * ct);
+      mma<1, 1, LDC, 1, LDK>(R, sDM, sQL + 16 * ct);
+      mma<1, LDC, 1, 1, LDK>(Pp, sDA, sKR + 16 * ct);
+      mma<1, 1, LDC, 1, LDK>(Rp, sDA, sKL + 16 * ct);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (l >> 4) + r, c = 16 * ct + (l & 15), o = i * LDK + c;
-        const float gi = in.g[o], m = 0.5f * in.g[(C - 1) * LDK + c];
+        const float gi = sG[o], m = 0.5f * sG[(C - 1) * LDK + c];
         const float e1 = expf(gi - m), e2 = expf(m - gi);
         pfa[r] = e1 * P[r];
         rfa[r] = e2 * R[r];
@@ -1043,11 +1107,11 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
       float gi[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        gi[r] = in.g[(4 * (l >> 4) + r) * LDK + c];
+        gi[r] = sG[(4 * (l >> 4) + r) * LDK + c];
         pfa[r] = rfa[r] = ppfa[r] = rpfa[r] = 0.f;
       }
       for (int y = 0; y < C; ++y) {
-        const float gy = in.g[y * LDK + c], ky = in.k[y * LDK + c], qy = in.q[y * LDK + c];
+        const float gy = sG[y * LDK + c], ky = sK[y * LDK + c], qy = sQ[y * LDK + c];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * (l >> 4) + r;
@@ -1063,11 +1127,11 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * (l >> 4) + r, c = 16 * ct + (l & 15), o = i * LDK + c;
-      const float gi = in.g[o], gl = in.g[(C - 1) * LDK + c];
+      const float gi = sG[o], gl = sG[(C - 1) * LDK + c];
       const float eg = expf(gi), ec = expf(gl - gi);
-      const float qv = in.q[o], kv = in.k[o];
+      const float qv = sQ[o], kv = sK[o];
       const float pf = pfa[r], rf = rfa[r], ppf = ppfa[r], rpf = rpfa[r];
-      const float dqg = dqt[r], dkg = -aK[r], dkc = aC[r];
+      const float dqg = dqt[r], dkg = -aK[u][r], dkc = aC[u][r];
       const float dqv = dqg * eg + pf;
       const float dkv = dkg * eg + dkc * ec + rf + ppf + rpf;
       const float dgv = qv * dqv + kv * (dkg * eg - dkc * ec - rf + ppf - rpf);
@@ -1083,7 +1147,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   __syncthreads();
   if ((int)threadIdx.x < DK) {  // dlog a: suffix sums of dg, the last-row terms entering every row
     const int c = threadIdx.x;
-    float run = in.el[c] * (sGS[c] + sGS[DK + c]);
+    float run = sEL[c] * sGS[c];
 #pragma unroll
     for (int i = 0; i < C; ++i) run += sKCT[i * LDK + c];
 #pragma unroll
@@ -1095,11 +1159,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
 }
 
 template <int DK, int DV>
-constexpr size_t grad_lds_bytes() {
-  constexpr int BV = 32, LDO = DV + 4, LDB = BV + 4, LDY = BV + 4;
-  return sizeof(float) * ((size_t)Intra<DK>::FLOATS + C * LDO + 2 * DK * LDB + 8 * C * LDC + 6 * C * LDY +
-                          2 * C * LDC + 2 * DK);
-}
+constexpr size_t grad_lds_bytes() { return sizeof(float) * (size_t)GradLay<DK, DV>::FLOATS; }
 
 static hipError_t set_lds(const void* kern, size_t lds, std::atomic<uint64_t>& done) {
   int dev = 0;
@@ -1172,7 +1232,7 @@ static hipError_t launch_grad(const BwdArgs& a, const float* ops, const float* s
   if (e != hipSuccess) return e;
   const int64_t grid = n_slots(a.total_tokens, a.n_seqs) * a.n_heads;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTG), lds, (hipStream_t)a.stream, (const InT*)a.q,
                      (const InT*)a.k, (const InT*)a.v, a.cu_seqlens, a.dout, ops, sw, dsw, a.dq, a.dk, a.dv,
                      a.dlog_alpha, a.dbeta, a.n_heads, a.seq_len, a.n_seqs);
   return hipGetLastError();
