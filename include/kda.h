@@ -151,8 +151,18 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
  * state pass fits on half of the CUs (chains x dv/32 <= 128) and the longest
  * sequence has at least 128 chunks, the chunks are cut into 2 to 32 ranges and
  * each launch runs pass 2 over one range beside pass 1 over the next, with the
- * state handed between ranges through the workspace.  Results equal
- * kda_chunk_fwd's up to rounding (the same operand precisions).
+ * state handed between ranges through the workspace.  With fewer chains still
+ * (chains x dv/32 <= 64: 16 at dv = 128) and at least 512 chunks in the longest
+ * sequence, pass 2 itself runs in parallel over S = 4 to 64 segments of each
+ * chain (in-device context parallelism, the same page: KDA states cannot simply
+ * be added, so they are composed by an associative scan): the affine map
+ * S_out = M S_in + B of every segment but the last is found in parallel (the
+ * recurrence run on a dk x (dk + dv) state [I | 0] with values [0 | v]), the maps
+ * are composed in fp32 from h0 in order, and every segment is then rerun from
+ * its entering state (1M tokens at dk = dv = 128: 1 head 2.6 ms, 8 heads 14.8 ms
+ * on MI355X, against 32-34 ms without segments).  Results equal kda_chunk_fwd's
+ * up to rounding (the same operand precisions; the segmented form also rounds
+ * each segment's map).
  *
  * Same arguments and results as kda_chunk_fwd, plus:
  *
@@ -227,7 +237,10 @@ kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void*
  * kda_chunk_fwd_split_workspace_size - bytes of workspace kda_chunk_fwd_split
  * needs: (total_tokens / chunk_size + n_seqs + 1) * n_heads tiles of the
  * per-chunk operands (66,304 B each for dk = 128, chunk 64), then
- * n_seqs * n_heads fp32 dk x dv states.  Writes *bytes.
+ * n_seqs * n_heads fp32 dk x dv states; then, when n_seqs * n_heads * dv / 32
+ * <= 64 and m = ceil(total_tokens / chunk_size) >= 512, for S = min(64, m / 64)
+ * segments, (S - 1) * n_seqs * n_heads fp32 dk x (dk + dv) segment maps and
+ * S * n_seqs * n_heads fp32 dk x dv segment states.  Writes *bytes.
  * Errors: KDA_ERR_INVALID_ARGUMENT (NULL bytes, negative or zero sizes, bad
  * dtype), KDA_ERR_UNSUPPORTED (a combination kda_chunk_fwd_split does not take).
  */

@@ -465,12 +465,32 @@ struct PipeArgs {
   float *o, *hT, *carry;
 };
 
+// What one workgroup of the state pass does beyond its chunk loop (see chunk_state_body).
+struct StateJob {
+  int chain, j0;             // chain, and the first state column of its tile
+  int64_t ch_begin, ch_end;  // chunk range (clipped to the chain's chunks)
+  const float* s_in;         // entering state ([n_chains][DK][DV], true units) or null for zeros
+  float* end_out;            // final state when the range reaches the chain's end ([n_chains][DK][DV]) or null
+  float* mid_out;            // final state otherwise ([n_chains][DK][mid_ld]) or null
+  int mid_ld;
+  bool map;                  // segment-map mode (see chunk_state_body)
+};
+
+// The (chain, value tile) of state-pass workgroup `bid` over n_chains chains of `ntile` tiles:
+// the tiles of one chain take indices of one residue mod 8, so they run on one XCD and read
+// each workspace fragment through one L2.  False for a padding workgroup (the grid covers a
+// multiple of 8 chains).
+__device__ __forceinline__ bool state_block(int bid, int n_chains, int ntile, int& chain, int& tile) {
+  const int xcd = bid & 7, qd = bid >> 3;
+  tile = qd % ntile;
+  chain = (qd / ntile) * 8 + xcd;
+  return chain < n_chains;
+}
+
 template <int C, int DK, int BV, typename InT>
 __device__ __forceinline__ void chunk_state_body(const uint4* __restrict__ ws, const InT* __restrict__ v,
-                                                 const float* h0, const int32_t* __restrict__ cu_seqlens,
-                                                 float* __restrict__ o, float* hT, int n_chains, int H, int DV,
-                                                 int64_t seq_len, int bid, int64_t ch_begin, int64_t ch_end,
-                                                 float* carry);
+                                                 const int32_t* __restrict__ cu_seqlens, float* __restrict__ o,
+                                                 int H, int DV, int64_t seq_len, const StateJob& job);
 
 template <int C, int DK, int BV, Prec P, typename InT, bool PREP, int PIPE_BV = 0>
 __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
@@ -481,9 +501,18 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   static_assert(PIPE_BV == 0 || PREP, "the pipelined mode pairs the state pass with the in-chunk pass");
   if constexpr (PIPE_BV > 0) {
     if ((int)blockIdx.x < pa.n_state_blocks) {
-      chunk_state_body<C, DK, PIPE_BV, InT>(reinterpret_cast<const uint4*>(ws), v, pa.h0, cu_seqlens, pa.o, pa.hT,
-                                            n_chains, H, DV, seq_len, (int)blockIdx.x, pa.ch_begin, pa.ch_end,
-                                            pa.carry);
+      StateJob job;
+      if (!state_block((int)blockIdx.x, n_chains, DV / PIPE_BV, job.chain, job.j0)) return;
+      job.j0 *= PIPE_BV;
+      job.ch_begin = pa.ch_begin;
+      job.ch_end = pa.ch_end;
+      job.s_in = pa.ch_begin > 0 ? pa.carry : pa.h0;
+      job.end_out = pa.hT;
+      job.mid_out = pa.carry;
+      job.mid_ld = DV;
+      job.map = false;
+      chunk_state_body<C, DK, PIPE_BV, InT>(reinterpret_cast<const uint4*>(ws), v, cu_seqlens, pa.o, H, DV, seq_len,
+                                            job);
       return;
     }
   }
@@ -1563,14 +1592,18 @@ struct SLay {
   static constexpr size_t TOTAL = MX + al16(size_t(NW) * 4);
 };
 
-// Chunks [ch_begin, ch_end) of every chain (clipped to the chain's length).  The state
-// enters from h0 (or zeros) when ch_begin is 0, else from `carry`; it leaves to hT when
-// the chain's last chunk is in the range, else to `carry` ([n_chains][DK][DV] fp32).
+// Chunks [job.ch_begin, job.ch_end) of one chain (clipped to its length), value columns
+// job.j0 .. + BV.  The state enters from job.s_in (or zeros) and leaves to job.end_out when the
+// chain's last chunk is in the range, else to job.mid_out (either may be null: not stored).
+// Segment-map mode (job.map) runs the same recurrence on a DK x (DK + DV) state whose first DK
+// columns start at the identity with zero values and whose last DV start at zero with the
+// chain's values (state column j0 >= DK is value column j0 - DK): its final state [M | B] is
+// the range's affine map S_out = M S_in + B.  It writes no o, and a range that reaches the
+// chain's end (whose map no later range needs) does nothing.
 template <int C, int DK, int BV, typename InT>
 __device__ __forceinline__ void chunk_state_body(
-    const uint4* __restrict__ ws, const InT* __restrict__ v, const float* h0,
-    const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT,
-    int n_chains, int H, int DV, int64_t seq_len, int bid, int64_t ch_begin, int64_t ch_end, float* carry) {
+    const uint4* __restrict__ ws, const InT* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
+    float* __restrict__ o, int H, int DV, int64_t seq_len, const StateJob& job) {
   using L = SLay<C, DK, BV>;
   using W = WsTile<C, DK>;
   using T = _Float16;
@@ -1585,13 +1618,11 @@ __device__ __forceinline__ void chunk_state_body(
   T* sUT = reinterpret_cast<T*>(smem + L::UT);
   uint32_t* sMX = reinterpret_cast<uint32_t*>(smem + L::MX);
 
-  const int ntile = DV / BV;
-  const int xcd = bid & 7, qd = bid >> 3;
-  const int tl = qd % ntile;
-  const int chain = (qd / ntile) * 8 + xcd;
-  if (chain >= n_chains) return;
+  const int chain = job.chain, j0 = job.j0;
+  const int64_t ch_begin = job.ch_begin, ch_end = job.ch_end;
   const int n = chain / H, h = chain - n * H;
-  const int j0 = tl * BV;
+  // value column of the tile (map mode: none for the identity columns)
+  const int vj0 = job.map ? (j0 >= DK ? j0 - DK : -1) : j0;
   int64_t t_begin, t_end;
   if (cu_seqlens) {
     t_begin = cu_seqlens[n];
@@ -1603,6 +1634,7 @@ __device__ __forceinline__ void chunk_state_body(
   const int64_t nchunks = (t_end - t_begin + C - 1) / C;
   if (ch_begin > 0 && ch_begin >= nchunks) return;  // the chain ended in an earlier range
   const int64_t ch_stop = ch_end < nchunks ? ch_end : nchunks;
+  if (job.map && ch_stop == nchunks) return;        // no later range of the chain needs this map
   auto chunk_len = [&](int64_t ch) -> int {
     const int64_t rem = t_end - (t_begin + ch * C);
     return (int)(rem < C ? rem : C);
@@ -1617,7 +1649,7 @@ __device__ __forceinline__ void chunk_state_body(
 
   constexpr int S_SLOTS = (NA * NJ + NW - 1) / NW;
   f32x4 Sacc[S_SLOTS];
-  const float* h0p = ch_begin > 0 ? carry + (size_t)chain * DK * DV : (h0 ? h0 + (size_t)chain * DK * DV : nullptr);
+  const float* h0p = (!job.map && job.s_in) ? job.s_in + (size_t)chain * DK * DV : nullptr;
   auto s_active = [&](int s) { return (NA * NJ) % NW == 0 || wave + NW * s < NA * NJ; };
   const int sa = wave % NA;  // row block of every state tile of this wave: tile (sa, (wave + NW s) / NA)
 #pragma unroll
@@ -1627,6 +1659,10 @@ __device__ __forceinline__ void chunk_state_body(
     if (s_active(s) && h0p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) Sacc[s][i] = h0p[(size_t)(16 * sa + 4 * lg + i) * DV + j0 + 16 * j + lr];
+    }
+    if (s_active(s) && job.map) {  // the identity in the map's first DK columns
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sacc[s][i] = (16 * sa + 4 * lg + i == j0 + 16 * j + lr) ? 1.f : 0.f;
     }
   }
   // The 16-bit state copy.  The fp32 state is held in the chunk's scaled units 2^-e (see
@@ -1639,13 +1675,13 @@ __device__ __forceinline__ void chunk_state_body(
         store4(sST + (16 * j + lr) * LDD + 16 * sa + 4 * lg, Sacc[s][0], Sacc[s][1], Sacc[s][2], Sacc[s][3]);
       }
   };
-  auto store_state = [&](float* sp, float f) {
+  auto store_state = [&](float* sp, int ld, float f) {
 #pragma unroll
     for (int s = 0; s < S_SLOTS; ++s)
       if (s_active(s)) {
         const int j = (wave + NW * s) / NA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * sa + 4 * lg + i) * DV + j0 + 16 * j + lr] = Sacc[s][i] * f;
+        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * sa + 4 * lg + i) * ld + j0 + 16 * j + lr] = Sacc[s][i] * f;
       }
   };
 
@@ -1708,8 +1744,8 @@ __device__ __forceinline__ void chunk_state_body(
   auto load_v = [&](int64_t chn) {
     const bool ok = chn < ch_stop;
     const int Lc = ok ? chunk_len(chn) : 0;
-    const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + j0,
-                              (k_wave && Lc > 0) ? (uint32_t)Lc * (uint32_t)(H * DV * 2) : 0u);
+    const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + (vj0 >= 0 ? vj0 : 0),
+                              (k_wave && Lc > 0 && vj0 >= 0) ? (uint32_t)Lc * (uint32_t)(H * DV * 2) : 0u);
     const int Rv = k_wave ? R : 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -1838,7 +1874,8 @@ __device__ __forceinline__ void chunk_state_body(
     {
       // o rows of the chunk (O waves; a store past the chunk's rows, or by another wave, is dropped)
       const uint32_t hdv = (uint32_t)(H * DV);
-      const auto ro = make_rsrc(o + ((size_t)c_begin * H + h) * DV + j0, o_wave ? (uint32_t)Lc * hdv * 4u : 0u);
+      const auto ro = job.map ? make_rsrc(o, 0u)
+                              : make_rsrc(o + ((size_t)c_begin * H + h) * DV + j0, o_wave ? (uint32_t)Lc * hdv * 4u : 0u);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
@@ -1872,9 +1909,9 @@ __device__ __forceinline__ void chunk_state_body(
     settle_range();
   }
   if (ch_stop == nchunks) {
-    if (hT) store_state(hT + (size_t)chain * DK * DV, sc_up);
-  } else {
-    store_state(carry + (size_t)chain * DK * DV, sc_up);
+    if (job.end_out) store_state(job.end_out + (size_t)chain * DK * DV, DV, sc_up);
+  } else if (job.mid_out) {
+    store_state(job.mid_out + (size_t)chain * DK * job.mid_ld, job.mid_ld, sc_up);
   }
 }
 
@@ -1883,8 +1920,110 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
     const uint4* __restrict__ ws, const InT* __restrict__ v, const float* h0,
     const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT,
     int n_chains, int H, int DV, int64_t seq_len) {
-  chunk_state_body<C, DK, BV, InT>(ws, v, h0, cu_seqlens, o, hT, n_chains, H, DV, seq_len, (int)blockIdx.x, 0,
-                                   INT64_MAX, nullptr);
+  StateJob job;
+  if (!state_block((int)blockIdx.x, n_chains, DV / BV, job.chain, job.j0)) return;
+  job.j0 *= BV;
+  job.ch_begin = 0;
+  job.ch_end = INT64_MAX;
+  job.s_in = h0;
+  job.end_out = hT;
+  job.mid_out = nullptr;
+  job.mid_ld = DV;
+  job.map = false;
+  chunk_state_body<C, DK, BV, InT>(ws, v, cu_seqlens, o, H, DV, seq_len, job);
+}
+
+// ---------------------------------------------------------------------------
+// Segmented state pass (in-device context parallelism for few long chains).  Each chain's
+// chunks are cut into n_seg segments of rl chunks.  Over a segment the chunk recurrence is
+// affine in the entering state, S_out = M S_in + B ("Kimi K3 model structure (7)", context
+// parallelism through an associative prefix scan, because KDA states cannot simply be
+// added): the map pass finds [M | B] of every segment but each chain's last, all in parallel;
+// the scan composes them in order, S_in(r + 1) = M_r S_in(r) + B_r, from h0; the rerun then
+// walks every segment in parallel from its entering state and writes o (and hT from the
+// chain's last segment).  Map and rerun workgroups take virtual chains u = r * n_chains +
+// chain (segment r), mapped like the state pass's chains.
+// ---------------------------------------------------------------------------
+template <int C, int DK, int BV, typename InT>
+__global__ __launch_bounds__(NT, 1) void chunk_seg_kernel(
+    const uint4* __restrict__ ws, const InT* __restrict__ v, const float* h0,
+    const int32_t* __restrict__ cu_seqlens, float* __restrict__ o, float* hT, const float* seg_in, float* maps,
+    int n_chains, int n_vchains, int64_t rl, int H, int DV, int64_t seq_len, int map) {
+  const int width = map ? DK + DV : DV;
+  int u = 0, tile = 0;
+  if (!state_block((int)blockIdx.x, n_vchains, width / BV, u, tile)) return;
+  const int r = u / n_chains;
+  StateJob job;
+  job.chain = u - r * n_chains;
+  job.j0 = tile * BV;
+  job.ch_begin = (int64_t)r * rl;
+  job.ch_end = (int64_t)(r + 1) * rl;
+  job.map = map != 0;
+  if (job.map) {
+    job.s_in = nullptr;
+    job.end_out = nullptr;
+    job.mid_out = maps + (size_t)r * n_chains * DK * (DK + DV);
+    job.mid_ld = DK + DV;
+  } else {
+    // (segment 0 too reads the copy of h0 the scan made: hT may alias h0, and the chain's last
+    // segment writes hT in the same launch)
+    job.s_in = seg_in + (size_t)r * n_chains * DK * DV;
+    job.end_out = hT;
+    job.mid_out = nullptr;
+    job.mid_ld = DV;
+  }
+  chunk_state_body<C, DK, BV, InT>(ws, v, cu_seqlens, o, H, DV, seq_len, job);
+}
+
+// The scan: one workgroup of 256 threads per (chain, 32 value columns), fp32; it copies
+// S_in(0) = h0 to the workspace, then thread t forms row t / 2, columns 16 (t & 1) .. + 15 of
+// S_in(r + 1) = M_r S_in(r) + B_r (the sum over k in order), the tile of S_in(r) in LDS.  It
+// stops at the chain's last segment.
+template <int C, int DK>
+__global__ __launch_bounds__(256) void chunk_seg_scan_kernel(const float* h0, const int32_t* __restrict__ cu_seqlens,
+                                                             const float* __restrict__ maps, float* __restrict__ seg_in,
+                                                             int n_chains, int n_seg, int64_t rl, int H, int DV,
+                                                             int64_t seq_len) {
+  __shared__ float sS[DK][32];
+  const int ntile = DV / 32;
+  const int chain = blockIdx.x / ntile, c0 = (blockIdx.x - chain * ntile) * 32;
+  const int n = chain / H;
+  int64_t len;
+  if (cu_seqlens) len = (int64_t)cu_seqlens[n + 1] - cu_seqlens[n];
+  else len = seq_len;
+  const int64_t nchunks = (len + C - 1) / C;
+  const int t = threadIdx.x, row = t >> 1, cb = 16 * (t & 1);
+  const bool act = row < DK;
+  for (int e = t; e < DK * 32; e += 256) {  // S_in(0): h0 (or zeros), also to the workspace
+    const int rr = e >> 5, cc = e & 31;
+    const float x = h0 ? h0[((size_t)chain * DK + rr) * DV + c0 + cc] : 0.f;
+    sS[rr][cc] = x;
+    seg_in[((size_t)chain * DK + rr) * DV + c0 + cc] = x;
+  }
+  const int W = DK + DV;
+  for (int r = 0; r + 1 < n_seg && nchunks > (int64_t)(r + 1) * rl; ++r) {
+    __syncthreads();  // S_in(r) in LDS
+    const float* mr = maps + ((size_t)r * n_chains + chain) * DK * W;
+    float acc[16];
+    if (act) {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) acc[jj] = mr[(size_t)row * W + DK + c0 + cb + jj];
+      for (int kk = 0; kk < DK; ++kk) {
+        const float m = mr[(size_t)row * W + kk];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[jj] = fmaf(m, sS[kk][cb + jj], acc[jj]);
+      }
+    }
+    __syncthreads();  // every read of S_in(r)
+    if (act) {
+      float* dst = seg_in + (((size_t)(r + 1) * n_chains + chain) * DK + row) * DV + c0 + cb;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        sS[row][cb + jj] = acc[jj];
+        dst[jj] = acc[jj];
+      }
+    }
+  }
 }
 
 
@@ -2039,9 +2178,100 @@ static hipError_t launch_split(const ChunkArgs& a, void* ws) {
   }
 }
 
+// Segments for the segmented state pass: taken for at most 64 state tiles of 32 columns
+// (n_chains x dv / 32; 16 chains at dv = 128 would leave 3/4 of the CUs idle in the state pass)
+// and at least 512 chunks in the longest sequence, with as many segments as keep the map pass
+// near 512 workgroups of 32 columns (two per CU; at most 64 segments, each at least 64 chunks)
+// and at least 4 (with fewer the pipelined form, which hides the in-chunk pass, is as fast).
+// 1M tokens at dk = dv = 128: 1 head 2.6 ms, 4 heads 7.5 ms, 8 heads 14.8 ms, against
+// 32-34 ms for the pipelined form (256 workgroups: 2.8, 9.8, 19.5 ms).
+static constexpr int kMaxSeg = 64;
+static bool split_segments(int n_chains, int dk, int dv, int64_t mc, int& n_seg, int64_t& rl) {
+  if (n_chains <= 0 || (int64_t)n_chains * (dv / 32) > 64 || mc < 512) return false;
+  int64_t sgs = 512 / ((int64_t)n_chains * ((dk + dv) / 32));
+  if (sgs > kMaxSeg) sgs = kMaxSeg;
+  if (sgs > mc / 64) sgs = mc / 64;
+  if (sgs < 4) return false;
+  rl = (mc + sgs - 1) / sgs;
+  n_seg = (int)((mc + rl - 1) / rl);
+  return n_seg >= 4;
+}
+// The most segments the segmented form can take for these sizes, known on the host from the
+// token total (the longest sequence has at most ceil(total / C) chunks), or 0 when it cannot
+// be taken; its workspace holds that many maps [n_chains][DK][DK + DV] (one fewer) and
+// entering states [n_chains][DK][DV] (fp32).
+static int split_seg_max(int n_chains, int dv, int64_t total_tokens, int chunk_size) {
+  const int64_t mc = (total_tokens + chunk_size - 1) / chunk_size;
+  if (n_chains <= 0 || (int64_t)n_chains * (dv / 32) > 64 || mc < 512) return 0;
+  return (int)(mc / 64 < kMaxSeg ? mc / 64 : kMaxSeg);
+}
+static size_t split_seg_bytes(int n_chains, int dk, int dv, int64_t total_tokens, int chunk_size) {
+  const int sm = split_seg_max(n_chains, dv, total_tokens, chunk_size);
+  if (sm == 0) return 0;
+  return ((size_t)(sm - 1) * dk * (dk + dv) + (size_t)sm * dk * dv) * (size_t)n_chains * sizeof(float);
+}
+
+template <int C, int DK, typename InT>
+static hipError_t launch_split_segmented(const ChunkArgs& a, void* ws, float* seg, int n_seg, int64_t rl) {
+  const int n_chains = a.n_seqs * a.n_heads;
+  const int sm = split_seg_max(n_chains, a.dv, a.total_tokens, a.chunk_size);
+  if (n_seg > sm) return hipErrorInvalidValue;  // (the workspace holds sm segments)
+  float* maps = seg;
+  float* seg_in = seg + (size_t)(sm - 1) * n_chains * DK * (DK + a.dv);
+  {  // the in-chunk pass over every chunk (as launch_split)
+    constexpr size_t lds = lds_bytes<C, DK, 16, Prec::Mixed>();
+    auto kern = chunk_fwd_kernel<C, DK, 16, Prec::Mixed, InT, true>;
+    static std::atomic<uint64_t> attr_done{0};
+    hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
+    if (e != hipSuccess) return e;
+    const int64_t mc = max_chunks_per_seq(a);
+    int64_t cpg = ((int64_t)n_chains * mc) / 2048;
+    cpg = cpg < 4 ? 4 : (cpg > 64 ? 64 : cpg);
+    const int64_t groups = (mc + cpg - 1) / cpg;
+    const int64_t grid = (int64_t)n_chains * (groups > 0 ? groups : 1);
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q,
+                       (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, nullptr, a.cu_seqlens, nullptr, nullptr,
+                       nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg, PipeArgs{});
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  constexpr size_t lds = SLay<C, DK, kPipeBV>::TOTAL;
+  auto kern = chunk_seg_kernel<C, DK, kPipeBV, InT>;
+  static std::atomic<uint64_t> attr_done{0};
+  hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
+  if (e != hipSuccess) return e;
+  {  // the maps of segments 0 .. n_seg - 2
+    const int nv = (n_seg - 1) * n_chains;
+    const int64_t grid = (int64_t)((nv + 7) / 8) * 8 * ((DK + a.dv) / kPipeBV);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const uint4*)ws,
+                       (const InT*)a.v, a.h0, a.cu_seqlens, a.o, a.hT, (const float*)seg_in, maps, n_chains, nv, rl,
+                       a.n_heads, a.dv, a.seq_len, 1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((chunk_seg_scan_kernel<C, DK>), dim3((unsigned)(n_chains * (a.dv / 32))), dim3(256), 0,
+                     (hipStream_t)a.stream, a.h0, a.cu_seqlens, (const float*)maps, seg_in, n_chains, n_seg, rl,
+                     a.n_heads, a.dv, a.seq_len);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {  // every segment from its entering state
+    const int nv = n_seg * n_chains;
+    const int64_t grid = (int64_t)((nv + 7) / 8) * 8 * (a.dv / kPipeBV);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const uint4*)ws,
+                       (const InT*)a.v, a.h0, a.cu_seqlens, a.o, a.hT, (const float*)seg_in, maps, n_chains, nv, rl,
+                       a.n_heads, a.dv, a.seq_len, 0);
+    return hipGetLastError();
+  }
+}
+
 template <int C, int DK, typename InT>
 static hipError_t dispatch_split_bv(const ChunkArgs& a, void* ws, float* carry) {
   const int64_t mc = max_chunks_per_seq(a);
+  int n_seg = 0;
+  int64_t rl = 0;
+  if (split_segments(a.n_seqs * a.n_heads, DK, a.dv, mc, n_seg, rl))
+    return launch_split_segmented<C, DK, InT>(a, ws, carry + (size_t)a.n_seqs * a.n_heads * DK * a.dv, n_seg, rl);
   int n_ranges = 0;
   if (split_pipelined(a, mc, n_ranges)) return launch_split_pipelined<C, DK, InT>(a, ws, carry, mc, n_ranges);
   // (a value tile as wide as dv when the chains alone fill the CUs: the state pass then runs
@@ -2127,7 +2357,8 @@ static size_t split_tiles_bytes(int64_t total_tokens, int n_seqs, int n_heads, i
 
 size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads, int dk, int dv, int chunk_size) {
   return split_tiles_bytes(total_tokens, n_seqs, n_heads, dk, chunk_size) +
-         (size_t)n_seqs * n_heads * dk * dv * sizeof(float);
+         (size_t)n_seqs * n_heads * dk * dv * sizeof(float) +
+         chunkk::split_seg_bytes(n_seqs * n_heads, dk, dv, total_tokens, chunk_size);
 }
 
 // Which forward path is faster for a bf16 input of this shape (measured on MI355X at

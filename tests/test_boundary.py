@@ -175,6 +175,11 @@ def test_split_workspace_size():
     # 128 x 128 state per (sequence, head) for the hand-over between chunk ranges
     assert rc == 0 and n == 3 * 2 * 66304 + 1 * 2 * 128 * 128 * 4
     assert ws_size(T=1 << 20, N=1, H=32)[1] == ((1 << 20) // 64 + 2) * 32 * 66304 + 32 * 128 * 128 * 4
+    # one chain of 512 chunks may take the segmented form: room for 8 segments (512 / 64), 7 maps
+    # [128][256] and 8 entering states [128][128]
+    assert ws_size(T=64 * 512, N=1, H=1)[1] == (514 * 66304 + 128 * 128 * 4 +
+                                               (7 * 128 * 256 + 8 * 128 * 128) * 4)
+    assert ws_size(T=64 * 511, N=1, H=1)[1] == 513 * 66304 + 128 * 128 * 4
     assert ws_size(dt=_lib.KDA_DTYPE_F32)[0] == 2
     assert ws_size(dk=96)[0] == 2
     assert ws_size(out=False)[0] == 1

@@ -88,6 +88,16 @@ def test_split_pipelined_adversarial(kind):
     check_bf16(o, hT, *ref(inp))
 
 
+@pytest.mark.parametrize("kind", KINDS)
+def test_split_segmented_adversarial(kind):
+    """One chain of 521 chunks: the state pass runs over 8 segments (maps, scan, rerun)."""
+    lens = [33300]
+    print("adversarial segmented split: %s, lens %s" % (kind, lens), flush=True)
+    inp = adv(kind, lens=lens, H=1, seed=131)
+    o, hT = fwd("split", inp, 64)
+    check_bf16(o, hT, *ref(inp))
+
+
 @pytest.mark.parametrize("C", [16, 32, 64])
 def test_forward_fp32_wide_decay(C):
     """fp32 inputs (every product on the fp32 matrix core), dk = dv = 128."""
