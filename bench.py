@@ -14,9 +14,10 @@ The other workloads are legs under "legs", each timed with HIP events on the lau
 stream, with its own roofline or bandwidth, its error against the oracle on a seeded
 slice, and the oracle's own time on the host: the Kimi-Linear-shaped layer (fused,
 with 512-token checkpoints, and split), the tiny fp32 case, the varlen packed batch (fused, split and the
-shape-chosen path of kda_chunk_fwd_auto),
-the decode / replay state update (1 and 8 tokens) and replay + verify, the backward
-pass, and the long-context sequence through the fused kernel.
+shape-chosen path of kda_chunk_fwd_auto), the long-context sequence with 4 heads (the
+split path's segment-parallel state pass), the decode / replay state update (1 and 8
+tokens) and replay + verify, the backward pass, and the long-context sequence through the
+fused kernel.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
                        [--legs all|headline] [--no-cpu-baseline] [--copy-calibration]
@@ -425,6 +426,40 @@ def leg_chunk_other(args, dev, stream, legs):
         del inp, o, hT
 
 
+def leg_long_context_few_heads(args, dev, stream, legs):
+    """The 1M-token sequence with 4 heads through kda_chunk_fwd_split: few chains, so its state pass
+    runs over segments in parallel (maps, scan, rerun); head 0 against the oracle."""
+    import torch
+    import kda_inputs
+    import kimi_delta_attention_06_amd as kda
+    w = kda_inputs.LONG_CONTEXT_4H
+    inp = kda_inputs.make_chunk_inputs(w, device=dev)
+    o = torch.empty(w.total_tokens, w.n_heads, w.dv, device=dev)
+    hT = torch.empty(w.n_seqs, w.n_heads, w.dk, w.dv, device=dev)
+    ws = torch.empty(kda.chunk_fwd_split_workspace_bytes(w.n_seqs, w.total_tokens, w.n_heads, w.dk, w.dv,
+                                                         w.chunk_size),
+                     dtype=torch.uint8, device=dev)
+    step = lambda: kda.chunk_fwd_split(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], h0=None,
+                                       chunk_size=w.chunk_size, o=o, hT=hT, workspace=ws)
+    ms = time_launches(step, 5, 2, stream)
+    leg = {"ms_per_step": round(ms, 3), "tokens_per_s": round(w.total_tokens / (ms * 1e-3), 1),
+           "heads": w.n_heads, "path": "kda_chunk_fwd_split (segmented state pass)"}
+    log("%s: %.3f ms/call" % (w.name, ms))
+    step()
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        import oracle
+        threads, _ = cpu_info()
+        sub = {k_: inp[k_][:, :1].cpu() for k_ in ("q", "k", "v", "log_alpha", "beta")}
+        (o_ref, h_ref), t_or = timed_oracle(oracle.kda_fwd, sub["q"], sub["k"], sub["v"], sub["log_alpha"],
+                                            sub["beta"], None, None, n_threads=threads)
+        leg["parity"] = {"o": errors(o[:, :1].cpu(), o_ref, BF16_TOL), "hT": errors(hT[:, :1].cpu(), h_ref, BF16_TOL),
+                         "sample": "head 0, all %d tokens" % w.total_tokens}
+    legs[w.name] = leg
+    del inp, o, hT, ws
+    torch.cuda.empty_cache()
+
+
 def leg_decode(args, dev, stream, copy_gbs, legs):
     import torch
     import kda_inputs
@@ -506,6 +541,7 @@ def main():
     if args.legs == "all":
         leg_kimi_linear(args, dev, stream, copy_gbs, legs)
         leg_chunk_other(args, dev, stream, legs)
+        leg_long_context_few_heads(args, dev, stream, legs)
         leg_decode(args, dev, stream, copy_gbs, legs)
 
     result = {

@@ -56,7 +56,12 @@ VARLEN_PACKED = ChunkWorkload("varlen-packed-bf16", 8, None, 32768, 32, 128, 128
 LONG_CONTEXT = ChunkWorkload("long-context-1m-bf16", 1, 1048576, 1048576, 32, 128, 128, 64,
                              torch.bfloat16, 1.0, 0.0, 1004)
 
-CHUNK_WORKLOADS = {w.name: w for w in (TINY_FP32, KIMI_LINEAR_LAYER, VARLEN_PACKED, LONG_CONTEXT)}
+# the 1M-token sequence with 4 heads (32 heads spread over 8 GPUs): few chains, so the split
+# path's state pass runs over segments in parallel
+LONG_CONTEXT_4H = ChunkWorkload("long-context-1m-4heads-bf16", 1, 1048576, 1048576, 4, 128, 128, 64,
+                                torch.bfloat16, 1.0, 0.0, 1006)
+
+CHUNK_WORKLOADS = {w.name: w for w in (TINY_FP32, KIMI_LINEAR_LAYER, VARLEN_PACKED, LONG_CONTEXT, LONG_CONTEXT_4H)}
 
 
 @dataclasses.dataclass(frozen=True)
