@@ -47,6 +47,7 @@
 // gradient of the chunk from its S, dS' and operands.  The two serial passes only run the
 // state-dependent products; every per-chunk operand they need is read, one chunk ahead.
 #include <atomic>
+#include <type_traits>
 
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
@@ -822,31 +823,35 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(
   const float* op = ops + ((size_t)slot * H + h) * O::FLOATS;
   const int tid = threadIdx.x, w = tid / kWave, l = lane();
 
-  // The columns of value tile tv, in registers: the next tile's are in flight while the
-  // current one is worked on.  S and dS' (fragment order): item e = tid + NTG u is lane l of
-  // channel block e / 64 of value block tv.  V and dO: row tid / (BV / VE) (resp. / (BV / 4)).
-  float4 pS[UPT], pD[UPT], pdo = make_float4(0.f, 0.f, 0.f, 0.f);
-  uint4 pv = make_uint4(0u, 0u, 0u, 0u);
-  auto fetch = [&](int tv) {
+  // The columns of value tile tv, in registers (two sets, by the tile's parity): the tile two
+  // ahead is in flight while the current one is worked on.  S and dS' (fragment order): item
+  // e = tid + NTG u is lane l of channel block e / 64 of value block tv.  V and dO: row
+  // tid / (BV / VE) (resp. / (BV / 4)).
+  static_assert(NTV % 2 == 0, "value tiles in pairs");
+  float4 pS[2][UPT], pD[2][UPT], pdo[2];
+  uint4 pv[2];
+  auto fetch = [&](int tv, auto pc) {
+    constexpr int P = decltype(pc)::value;
     const size_t base = (size_t)tv * NCT * 256;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const size_t o4 = base + 4 * (size_t)(tid + NTG * u);
-      pS[u] = *reinterpret_cast<const float4*>(S0 + o4);
-      pD[u] = *reinterpret_cast<const float4*>(dSC + o4);
+      pS[P][u] = *reinterpret_cast<const float4*>(S0 + o4);
+      pD[P][u] = *reinterpret_cast<const float4*>(dSC + o4);
     }
+    pv[P] = make_uint4(0u, 0u, 0u, 0u);
     if (tid < NVI) {
       const int i = tid / (BV / VE), c = (tid - i * (BV / VE)) * VE;
-      pv = make_uint4(0u, 0u, 0u, 0u);
-      if (i < Lc) pv = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + i) * H + h) * DV + tv * BV + c);
+      if (i < Lc) pv[P] = *reinterpret_cast<const uint4*>(v + ((size_t)(t0 + i) * H + h) * DV + tv * BV + c);
     }
+    pdo[P] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < NDI) {
       const int i = tid / (BV / 4), c = (tid - i * (BV / 4)) * 4;
-      pdo = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < Lc) pdo = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + tv * BV + c);
+      if (i < Lc) pdo[P] = *reinterpret_cast<const float4*>(dout + ((size_t)(t0 + i) * H + h) * DV + tv * BV + c);
     }
   };
-  fetch(0);
+  fetch(0, std::integral_constant<int, 0>{});
+  fetch(1, std::integral_constant<int, 1>{});
   // the tile loop's operands from the prep tile (Kg, Kc; A, M, T, T Diag(b); b, e^{g_L}):
   // every load issued before the first is stored
   constexpr int NOP = 2 * C * R4, IOP = (NOP + NTG - 1) / NTG;
@@ -893,16 +898,18 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(
   for (int u = 0; u < UPT; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) gs[u][r] = 0.f;
-  // the chain-rule step's inputs (q, k, g), loaded during the last value tile
+  // the chain-rule step's inputs (q, k, g), loaded two value tiles before the last
   constexpr int NQK = 2 * C * DK / VE, IQK = (NQK + NTG - 1) / NTG, IG = (C * R4 + NTG - 1) / NTG;
   uint4 rqk[IQK];
   float4 rg[IG];
 
-  for (int tv = 0; tv < NTV; ++tv) {
+  auto tile = [&](int tv, auto pc) {
+    constexpr int P = decltype(pc)::value;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {  // stage S and dS' columns of value block tv
       const int c = 16 * ((tid + NTG * u) / 64) + 4 * (l >> 4), col = l & 15;
-      const float sv[4] = {pS[u].x, pS[u].y, pS[u].z, pS[u].w}, dv[4] = {pD[u].x, pD[u].y, pD[u].z, pD[u].w};
+      const float sv[4] = {pS[P][u].x, pS[P][u].y, pS[P][u].z, pS[P][u].w};
+      const float dv[4] = {pD[P][u].x, pD[P][u].y, pD[P][u].z, pD[P][u].w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         sS[(c + r) * LDB + col] = sv[r];
@@ -912,15 +919,15 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(
     }
     if (tid < NVI) {
       const int i = tid / (BV / VE), c = (tid - i * (BV / VE)) * VE;
-      widen16(sV + i * LDY + c, pv, InT{});
+      widen16(sV + i * LDY + c, pv[P], InT{});
     }
     if (tid < NDI) {
       const int i = tid / (BV / 4), c = (tid - i * (BV / 4)) * 4;
-      *reinterpret_cast<float4*>(sDO + i * LDY + c) = pdo;
+      *reinterpret_cast<float4*>(sDO + i * LDY + c) = pdo[P];
     }
-    if (tv + 1 < NTV) {
-      fetch(tv + 1);
-    } else {
+    if (tv + 2 < NTV) {
+      fetch(tv + 2, pc);
+    } else if (tv + 2 == NTV) {
 #pragma unroll
       for (int it = 0; it < IQK; ++it) {
         const int e = tid + NTG * it, which = e / (NQK / 2), ee = e - which * (NQK / 2);
@@ -1002,6 +1009,10 @@ __global__ __launch_bounds__(NTG) void bwd_grad_kernel(
       }
     }
     __syncthreads();
+  };
+  for (int tv = 0; tv < NTV; tv += 2) {
+    tile(tv, std::integral_constant<int, 0>{});
+    tile(tv + 1, std::integral_constant<int, 1>{});
   }
 
   // dQg tiles (waves 2, 3) to the shared tiles, q, k, g to LDS, dM, dA, db, sum_v S dS'
