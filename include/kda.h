@@ -260,7 +260,10 @@ kda_status kda_chunk_fwd_split_workspace_size(int32_t n_seqs, int64_t total_toke
  * chunk's state-free operands into `workspace`, a forward pass over each
  * sequence's chunks stores the state entering every chunk, a reverse pass stores
  * the cotangent of the state leaving every chunk, and a parallel pass forms each
- * chunk's gradients from the three.
+ * chunk's gradients from the three.  When n_seqs * n_heads * dv / 64 <= 256 the
+ * reverse pass runs beside the forward pass on a second stream the library keeps
+ * per device, forked from and joined back to `stream` through events, so the call
+ * is still ordered on `stream` and can be captured into a HIP graph.
  *
  *   q, k, v, log_alpha, beta, h0, cu_seqlens, n_seqs, total_tokens, n_heads,
  *   dk, dv, qkv_dtype    as kda_chunk_fwd (the chunk size is fixed at 16)

@@ -47,6 +47,7 @@
 // gradient of the chunk from its S, dS' and operands.  The two serial passes only run the
 // state-dependent products; every per-chunk operand they need is read, one chunk ahead.
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "kda_common.hpp"
@@ -480,8 +481,8 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const InT* __restrict__ 
   float* sV = sEL + DK;                // [C][LDO]
   float* sST = sV + C * LDO;           // [BV][LDK]: S transposed
   float* sPart = sST + BV * LDK;       // [8][C][LDC]
-  float* sY = sPart + 8 * C * LDC;     // [C][LDO]
-  float* sU = sY + C * LDO;            // [C][LDO]
+  float* sY = sV;                      // Y = V - Kg S over V (each element read, then written, by one lane)
+  float* sU = sPart + 8 * C * LDC;     // [C][LDO]
 
   int chain, tile;
   if (!serial_block(n_chains, DV / BV, chain, tile)) return;
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const InT* __restrict__ 
 template <int DK, int BV>
 constexpr size_t states_lds_bytes() {
   using Sh = SerialShape<DK, BV>;
-  return sizeof(float) * ((size_t)2 * C * Sh::LDK + C * LDC + DK + 3 * C * Sh::LDO + (size_t)BV * Sh::LDK +
+  return sizeof(float) * ((size_t)2 * C * Sh::LDK + C * LDC + DK + 2 * C * Sh::LDO + (size_t)BV * Sh::LDK +
                           8 * C * LDC);
 }
 
@@ -1205,32 +1206,81 @@ static hipError_t launch_prep(const BwdArgs& a, float* ops) {
   return hipGetLastError();
 }
 
+// A second stream per device on which the reverse pass runs beside the forward-states pass
+// (created on first use, default priority, kept until the process ends).  Each call forks
+// to it and joins back through events of its own, so concurrent calls stay ordered on their
+// own streams and the pair can be captured into a HIP graph like any fork and join.
+static hipError_t side_stream(hipStream_t& out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+  }
+  out = streams[dev];
+  return hipSuccess;
+}
+
+// The two serial passes.  `concurrent`: the reverse pass on the side stream beside the
+// forward-states pass (64-column tiles: 71 + 86 KB of LDS, one workgroup of each per CU).
 template <int DK, int BV, typename InT>
-static hipError_t launch_serial(const BwdArgs& a, const float* ops, float* sw, float* dsw) {
+static hipError_t launch_serial(const BwdArgs& a, const float* ops, float* sw, float* dsw, bool concurrent) {
   const int n_chains = a.n_seqs * a.n_heads;
   const int64_t grid = (int64_t)((n_chains + 7) / 8) * 8 * (a.dv_dim / BV);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipStream_t main = (hipStream_t)a.stream, ds_stream = main;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (concurrent) {
+    hipError_t e = side_stream(ds_stream);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(fork, main);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ds_stream, fork, 0);
+    if (e != hipSuccess) {
+      if (fork) (void)hipEventDestroy(fork);
+      if (join) (void)hipEventDestroy(join);
+      return e;
+    }
+  }
+  auto finish = [&](hipError_t e) {  // join the side stream (also after a failed launch)
+    if (concurrent) {
+      hipError_t e2 = hipEventRecord(join, ds_stream);
+      if (e2 == hipSuccess) e2 = hipStreamWaitEvent(main, join, 0);
+      (void)hipEventDestroy(fork);
+      (void)hipEventDestroy(join);
+      if (e == hipSuccess) e = e2;
+    }
+    return e;
+  };
+  {
+    constexpr size_t lds = ds_lds_bytes<DK, BV>();
+    static_assert(lds <= 160 * 1024, "LDS budget");
+    auto kern = bwd_ds_kernel<DK, BV>;
+    static std::atomic<uint64_t> done{0};
+    hipError_t e = set_lds((const void*)kern, lds, done);
+    if (e != hipSuccess) return finish(e);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, ds_stream, a.cu_seqlens, a.dout, a.dhT, ops, dsw,
+                       a.dh0, n_chains, a.n_heads, a.dv_dim, a.seq_len);
+    e = hipGetLastError();
+    if (e != hipSuccess) return finish(e);
+  }
   {
     constexpr size_t lds = states_lds_bytes<DK, BV>();
     static_assert(lds <= 160 * 1024, "LDS budget");
+    static_assert(BV != 64 || lds + ds_lds_bytes<DK, BV>() <= 160 * 1024, "one workgroup of each pass per CU");
     auto kern = bwd_states_kernel<DK, BV, InT>;
     static std::atomic<uint64_t> done{0};
     hipError_t e = set_lds((const void*)kern, lds, done);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.v, a.h0,
-                       a.cu_seqlens, ops, sw, n_chains, a.n_heads, a.dv_dim, a.seq_len);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) return finish(e);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, main, (const InT*)a.v, a.h0, a.cu_seqlens, ops,
+                       sw, n_chains, a.n_heads, a.dv_dim, a.seq_len);
+    return finish(hipGetLastError());
   }
-  constexpr size_t lds = ds_lds_bytes<DK, BV>();
-  static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = bwd_ds_kernel<DK, BV>;
-  static std::atomic<uint64_t> done{0};
-  hipError_t e = set_lds((const void*)kern, lds, done);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, a.cu_seqlens, a.dout, a.dhT,
-                     ops, dsw, a.dh0, n_chains, a.n_heads, a.dv_dim, a.seq_len);
-  return hipGetLastError();
 }
 
 template <int DK, int DV, typename InT>
@@ -1258,11 +1308,12 @@ static hipError_t run(const BwdArgs& a) {
   // (1) every chunk's operands
   hipError_t e = launch_prep<DK, InT>(a, ops);
   if (e != hipSuccess) return e;
-  // (2) the states entering every chunk, (3) the cotangents of the states leaving them and dh0,
-  // in 32-column value tiles: two or three workgroups share a CU, one's barrier waits filling
-  // the others' matrix-core work (on the Kimi-Linear layer 0.69 + 0.96 ms against 0.86 + 1.00
-  // with 64-column tiles, one workgroup per CU)
-  e = launch_serial<DK, 32, InT>(a, ops, sw, dsw);
+  // (2) the states entering every chunk, (3) the cotangents of the states leaving them and dh0.
+  // The two passes are independent: when one workgroup of each fits on every CU at once
+  // (64-column tiles, chains x dv/64 <= 256) they run side by side; otherwise one after the
+  // other in 32-column tiles, two or three workgroups of one pass per CU
+  if ((int64_t)a.n_seqs * a.n_heads * (DV / 64) <= 256) e = launch_serial<DK, 64, InT>(a, ops, sw, dsw, true);
+  else e = launch_serial<DK, 32, InT>(a, ops, sw, dsw, false);
   if (e != hipSuccess) return e;
   // (4) the gradients of every chunk
   return launch_grad<DK, DV, InT>(a, ops, sw, dsw);

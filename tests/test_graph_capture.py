@@ -110,3 +110,46 @@ def test_decode_loop_graph_replays_match_eager():
         for i, (x, r) in enumerate(zip(outs + [o_ver, S], ref)):
             assert torch.equal(x, r), (rep, i)
         eager_noise(noise)
+
+
+def test_backward_graph_replays_match_eager():
+    """kda_bwd captured as one graph: its four launches, with the reverse pass forked to a second
+    stream beside the forward-states pass and joined back through events (one workgroup of each
+    per CU when chains x dv/64 <= 256, as here)."""
+    import kimi_delta_attention_06_amd as kda
+    print("graph backward", flush=True)
+    inp = kda_inputs.make_custom_chunk_inputs([300, 64, 1, 0, 129], 4, 128, 128, torch.bfloat16, h0_std=0.02,
+                                              seed=93, device="cuda")
+    T, H = inp["v"].shape[0], inp["v"].shape[1]
+    g0 = torch.Generator(device="cpu").manual_seed(94)
+    do = torch.randn(T, H, 128, generator=g0).cuda()
+    dhT = (0.1 * torch.randn(5, H, 128, 128, generator=g0)).cuda()
+    ws = torch.empty(kda.backward_workspace_bytes(5, T, H, 128, 128), dtype=torch.uint8, device="cuda")
+    keys = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0")
+
+    def body():
+        return kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do, h0=inp["h0"],
+                            cu_seqlens=inp["cu_seqlens"], dhT=dhT, workspace=ws)
+
+    ref = body()
+    torch.cuda.synchronize()
+    ref = {key: ref[key].clone() for key in keys}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = body()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for key in keys:
+            out[key].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in keys:
+            assert torch.equal(out[key], ref[key]), (rep, key)
+        eager_noise(inp)
