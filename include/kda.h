@@ -31,8 +31,11 @@
  * library allocates no memory at run time and is safe to call from several host
  * threads.  Its only mutable global state is set up once and never read back:
  * one word per kernel that records, thread-safely, on which devices the kernel's
- * LDS limit was raised, and the per-device address of the fixed device array of
- * kda_chunk_fwd_split_noalloc (looked up under a lock).  All pointers except
+ * LDS limit was raised, the per-device address of the fixed device array of
+ * kda_chunk_fwd_split_noalloc (looked up under a lock), and one non-blocking
+ * side stream per device that kda_bwd creates under a lock on first use and
+ * keeps until the process ends (each kda_bwd call that forks to it creates and
+ * destroys its own two events).  All pointers except
  * cu_seqlens-for-fixed-length, h0 and hT are required.  Device pointers must be
  * 16-byte aligned.
  *
