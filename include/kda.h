@@ -239,7 +239,7 @@ kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void*
 /*
  * kda_chunk_fwd_split_workspace_size - bytes of workspace kda_chunk_fwd_split
  * needs: (total_tokens / chunk_size + n_seqs + 1) * n_heads tiles of the
- * per-chunk operands (66,304 B each for dk = 128, chunk 64), then
+ * per-chunk operands (62,208 B each for dk = 128, chunk 64), then
  * n_seqs * n_heads fp32 dk x dv states; then, when n_seqs * n_heads * dv / 32
  * <= 64 and m = ceil(total_tokens / chunk_size) >= 512, for S = min(64, m / 64)
  * segments, (S - 1) * n_seqs * n_heads fp32 dk x (dk + dv) segment maps and

@@ -171,15 +171,15 @@ def ws_size(N=1, T=64, H=2, dk=128, dv=128, C=64, dt=_lib.KDA_DTYPE_BF16, out=Tr
 
 def test_split_workspace_size():
     rc, n = ws_size()
-    # (64 / 64 + 1 + 1) slots x 2 heads x 66,304-byte tiles (dk 128, chunk 64), then one fp32
+    # (64 / 64 + 1 + 1) slots x 2 heads x 62,208-byte tiles (dk 128, chunk 64), then one fp32
     # 128 x 128 state per (sequence, head) for the hand-over between chunk ranges
-    assert rc == 0 and n == 3 * 2 * 66304 + 1 * 2 * 128 * 128 * 4
-    assert ws_size(T=1 << 20, N=1, H=32)[1] == ((1 << 20) // 64 + 2) * 32 * 66304 + 32 * 128 * 128 * 4
+    assert rc == 0 and n == 3 * 2 * 62208 + 1 * 2 * 128 * 128 * 4
+    assert ws_size(T=1 << 20, N=1, H=32)[1] == ((1 << 20) // 64 + 2) * 32 * 62208 + 32 * 128 * 128 * 4
     # one chain of 512 chunks may take the segmented form: room for 8 segments (512 / 64), 7 maps
     # [128][256] and 8 entering states [128][128]
-    assert ws_size(T=64 * 512, N=1, H=1)[1] == (514 * 66304 + 128 * 128 * 4 +
+    assert ws_size(T=64 * 512, N=1, H=1)[1] == (514 * 62208 + 128 * 128 * 4 +
                                                (7 * 128 * 256 + 8 * 128 * 128) * 4)
-    assert ws_size(T=64 * 511, N=1, H=1)[1] == 513 * 66304 + 128 * 128 * 4
+    assert ws_size(T=64 * 511, N=1, H=1)[1] == 513 * 62208 + 128 * 128 * 4
     assert ws_size(dt=_lib.KDA_DTYPE_F32)[0] == 2
     assert ws_size(dk=96)[0] == 2
     assert ws_size(out=False)[0] == 1
@@ -282,11 +282,11 @@ def noalloc_call(**kw):
 
 
 def test_noalloc_rejects_sizes_past_its_array():
-    # the workspace of 32 heads x (4096 / 64 + 2) chunk slots (66,304 B each) + 32 states fits in 256 MiB;
-    # 8,192 tokens do not
-    need = lambda T: ((T // 64) + 2) * 32 * 66304 + 32 * 128 * 128 * 4
-    assert need(4096) <= _lib.NOALLOC_SCRATCH_BYTES < need(8192)
-    assert noalloc_call(T=8192, H=32, o=1 << 40, q=1 << 36, k=1 << 36, v=1 << 36, la=1 << 37, b=1 << 38) == 2
+    # the workspace of 32 heads x (8192 / 64 + 2) chunk slots (62,208 B each) + 32 states fits in 256 MiB;
+    # 16,384 tokens do not
+    need = lambda T: ((T // 64) + 2) * 32 * 62208 + 32 * 128 * 128 * 4
+    assert need(8192) <= _lib.NOALLOC_SCRATCH_BYTES < need(16384)
+    assert noalloc_call(T=16384, H=32, o=1 << 40, q=1 << 36, k=1 << 36, v=1 << 36, la=1 << 37, b=1 << 38) == 2
     assert noalloc_call(dt=_lib.KDA_DTYPE_F32) == 2
     assert noalloc_call(q=None) == 1 and noalloc_call(o=P) == 1  # o overlaps q
     assert noalloc_call(N=0, T=0, q=None, k=None, v=None, la=None, b=None, o=None) == 0
