@@ -347,7 +347,13 @@ def leg_kimi_linear(args, dev, stream, copy_gbs, legs):
     sstep = lambda: kda.chunk_fwd_split(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size, o=o, hT=hT,
                                         workspace=ws)
     s_ms = time_launches(sstep, 100, 20, stream)
-    legs[w.name + " split"] = {"ms_per_step": round(s_ms, 5), "tokens_per_s": round(w.total_tokens / (s_ms * 1e-3), 1)}
+    astep = lambda: kda.chunk_fwd_auto(qb, kb, vb, lab, beb, h0=None, chunk_size=w.chunk_size, o=o, hT=hT,
+                                       workspace=ws)
+    a_ms = time_launches(astep, 100, 20, stream)
+    legs[w.name + " split"] = {"ms_per_step": round(s_ms, 5), "tokens_per_s": round(w.total_tokens / (s_ms * 1e-3), 1),
+                               "auto_ms_per_step": round(a_ms, 5),
+                               "auto_tokens_per_s": round(w.total_tokens / (a_ms * 1e-3), 1)}
+    log("%s split: %.4f ms; kda_chunk_fwd_auto %.4f ms" % (w.name, s_ms, a_ms))
     del ws
     # backward on the same inputs
     b_do = torch.randn(w.total_tokens, w.n_heads, w.dv, generator=torch.Generator(device=dev).manual_seed(77),

@@ -188,18 +188,18 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
 /*
  * kda_chunk_fwd_auto - the chunked forward on whichever path is faster for the
  * input's shape: kda_chunk_fwd_split or kda_chunk_fwd (same results up to
- * rounding).  The fused kernel fills the CUs with value tiles of 64 columns and
- * redoes each chunk's in-chunk work once per tile; the split path does that work
- * once per chunk and head but writes it to the workspace and reads it back.  With
- * bf16 inputs, sequences of at least 4 chunks on average, and t64 = n_seqs *
- * n_heads * dv / 64 fused value tiles, the split path is taken when t64 < 256
- * (fewer chains than fill the CUs: the fused kernel would narrow its tiles and
- * repeat the in-chunk work 4 to 8 times) or t64 >= 512 (two or more rounds of
- * fused tiles, where the split path's state pass runs one round of full-width
- * tiles); otherwise, and for fp32 inputs, the fused kernel.  Measured on MI355X at
- * dk = dv = 128, chunk 64: 1M tokens x 32 heads 38 ms split vs 101 ms fused;
- * 8 x 4,096 tokens x 32 heads 0.85 vs 0.94 ms; 4 x 4,096 x 32 heads 0.445 ms
- * fused vs 0.46-0.48 ms split.
+ * rounding).  The fused kernel cuts each chain's dv columns into the widest value
+ * tiles (at most 64 columns) that still give every CU a workgroup and redoes each
+ * chunk's in-chunk work once per tile; the split path does that work once per
+ * chunk and head but writes it to the workspace and reads it back.  With bf16
+ * inputs and sequences of at least 4 chunks on average, the split path is taken
+ * when the fused kernel would use two or more tiles per chain and either those
+ * tiles need more than one round of 256 workgroups or the sequences average at
+ * least 16 chunks; otherwise, and for fp32 inputs, the fused kernel.  Measured on
+ * MI355X at dk = 128, chunk 64: 1M tokens x 32 heads (dv 128) 35 ms split vs 101
+ * ms fused; 8 x 4,096 tokens x 32 heads 0.79 vs 0.93 ms; 4 x 4,096 x 32 heads
+ * 0.42 vs 0.47 ms; 16 x 4,096 x 32 heads at dv = 64 (one tile per chain) 0.94 ms
+ * fused vs 1.42 ms split.
  *
  * Same arguments as kda_chunk_fwd_split.  The workspace is used only when the
  * split path is taken (it may be NULL with workspace_bytes 0 otherwise); a caller

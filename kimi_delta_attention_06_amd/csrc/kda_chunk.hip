@@ -785,7 +785,15 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
     static_assert(!PREP || sizeof(T) == 2, "fp16 operands");
     const int64_t slot = t_begin / C + n + chn;
     uint4* dst = reinterpret_cast<uint4*>(ws) + ((size_t)slot * H + h) * W::NU;
-    for (int i = tid; i < W::NU; i += NT) {
+    // Unrolled over blocks of NT units with the thread index the compiler can see (its range
+    // is the launch bound): all but the last two blocks lie in one region each, so their
+    // region tests fold and the fragment, row and column of a unit reduce to a per-thread
+    // constant plus an immediate (a rolled loop recomputed them for every unit: 6% of the
+    // varlen batch's split time).
+#pragma unroll
+    for (int m = 0; m < (W::NU + NT - 1) / NT; ++m) {
+      const int i = (int)threadIdx.x + NT * m;
+      if (W::NU % NT != 0 && i >= W::NU) break;
       // byte offset in LDS of unit i's source
       uint32_t off;
       bool pad = false;  // a k-unit past the chunk's tokens: zero
@@ -2396,20 +2404,26 @@ size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads
          chunkk::split_seg_bytes(n_seqs * n_heads, dk, dv, total_tokens, chunk_size);
 }
 
-// Which forward path is faster for a bf16 input of this shape (measured on MI355X at
-// dk = dv = 128, chunk 64): the fused kernel fills the CUs with value tiles of 64 columns and
-// redoes the in-chunk work once per tile.  With fewer chains than that fills (a few long
-// sequences) its tiles narrow and the work is repeated 4-8 times (1M tokens x 32 heads: split
-// 37.7-38.8 ms, fused 101 ms); with enough chains for two or more rounds of those tiles the
-// split path's state pass runs one round of full-width tiles (8 x 4,096 tokens x 32 heads:
-// split 0.85 ms, fused 0.94 ms); in between (4 x 4,096 tokens x 32 heads: one round) the fused
-// kernel is faster (0.445 vs 0.46-0.48 ms).  Sequences shorter than 4 chunks on average stay
-// on the fused kernel (the workspace round trip is not repaid).
+// Which forward path is faster for a bf16 input of this shape (measured on MI355X at dk = 128,
+// dv in {64, 128}, chunks of 16-64 tokens).  The fused kernel cuts each chain's dv columns
+// into the widest value tiles that still give every CU a workgroup (pick_bv, at most 64) and
+// redoes the chunk's in-chunk work once per tile; the split path does it once per chunk and
+// head, at the price of the workspace round trip.  So the split path is taken when the fused
+// kernel would repeat the in-chunk work (two or more tiles per chain) and either its tiles
+// take two or more rounds of workgroups or the sequences are long enough (16 chunks on
+// average) to repay the split path's extra launch.  Measured: 1M tokens x 32 heads split
+// 35.3 ms, fused 101 ms; 8 x 4,096 tokens x 32 heads, dv 128, split 0.79 ms, fused 0.93 ms;
+// 4 x 4,096 x 32 heads, dv 128, split 0.42 ms, fused 0.47 ms; 16 x 4,096 x 32 heads, dv 64
+// (one 64-column tile per chain): fused 0.94 ms, split 1.42 ms.  Sequences shorter than 4
+// chunks on average stay on the fused kernel.
 bool chunk_fwd_prefers_split(int n_seqs, int n_heads, int dv, int chunk_size, int64_t total_tokens) {
   if (n_seqs <= 0 || total_tokens <= 0) return false;
-  if (total_tokens / n_seqs < 4 * (int64_t)chunk_size) return false;
-  const int64_t tiles64 = (int64_t)n_seqs * n_heads * dv / 64;
-  return tiles64 < 256 || tiles64 >= 512;
+  const int64_t chunks = total_tokens / n_seqs / chunk_size;  // per sequence, on average
+  if (chunks < 4) return false;
+  const int chains = n_seqs * n_heads;
+  const int64_t tiles = dv / chunkk::pick_bv(chains, dv, 64);  // fused value tiles per chain
+  if (tiles < 2) return false;
+  return (int64_t)chains * tiles > 256 || chunks >= 16;
 }
 
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, void* ws) {

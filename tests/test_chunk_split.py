@@ -162,16 +162,19 @@ def test_split_long_context_workload_two_heads():
     check_bf16(o_s, h_s, o_ref, h_ref)
 
 
-@pytest.mark.parametrize("lens,H,path", [
-    ([600, 17, 400, 260], 2, "split"),      # 8 chains: the fused kernel would narrow its tiles
-    ([256] * 64, 2, "fused"),               # 128 chains of 4 chunks: one round of 64-column fused tiles
-    ([256] * 40 + [300, 212] * 12, 4, "split"),  # 256 chains: two rounds of fused tiles
+@pytest.mark.parametrize("lens,H,dv,path", [
+    ([2600, 17, 1400, 1260], 2, 128, "split"),   # 8 chains: the fused kernel would use 16-column tiles
+    ([600, 17, 400, 260], 2, 128, "fused"),      # the same chains, 5 chunks per sequence on average
+    ([256] * 64, 2, 128, "fused"),               # 128 chains of 4 chunks: one round of 64-column fused tiles
+    ([1100] * 64, 2, 128, "split"),              # one round of fused tiles, 17 chunks per sequence
+    ([256] * 40 + [300, 212] * 12, 4, 128, "split"),  # 256 chains: two rounds of fused tiles
+    ([256] * 128, 2, 64, "fused"),               # 256 chains at dv = 64: one fused tile per chain
 ])
-def test_auto_takes_the_path_its_rule_names(lens, H, path):
+def test_auto_takes_the_path_its_rule_names(lens, H, dv, path):
     """kda_chunk_fwd_auto: the same bits as the path the shape rule picks, against the oracle; the fused
     choice runs without a workspace."""
     import kimi_delta_attention_06_amd as kda
-    inp = kda_inputs.make_custom_chunk_inputs(lens, H, 128, 128, torch.bfloat16, h0_std=0.02, seed=len(lens) + H,
+    inp = kda_inputs.make_custom_chunk_inputs(lens, H, 128, dv, torch.bfloat16, h0_std=0.02, seed=len(lens) + H,
                                               device="cuda")
     args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
     kw = dict(h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], chunk_size=64)
