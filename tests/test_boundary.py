@@ -196,10 +196,10 @@ def split_call(**kw):
 
 
 def test_chunk_fwd_auto_checks_the_workspace_on_the_split_path():
-    """Two sequences of 4 chunks x 2 heads: few chains, so the split path, whose workspace is checked on
+    """Two sequences of 16 chunks x 2 heads: few chains, so the split path, whose workspace is checked on
     the host (a missing, small or misaligned one is rejected before any launch)."""
     def auto(**kw):
-        a = dict(q=P, k=P, v=P, la=P, b=P, h0=None, cu=None, N=2, T=512, H=2, dk=128, dv=128, C=64,
+        a = dict(q=P, k=P, v=P, la=P, b=P, h0=None, cu=None, N=2, T=2048, H=2, dk=128, dv=128, C=64,
                  dt=_lib.KDA_DTYPE_BF16, o=P * 8, hT=None, ws=P * 64, wsb=1 << 22)
         a.update(kw)
         return lib.kda_chunk_fwd_auto(a["q"], a["k"], a["v"], a["la"], a["b"], a["h0"], a["cu"], a["N"], a["T"],
