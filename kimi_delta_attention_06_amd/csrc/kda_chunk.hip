@@ -153,10 +153,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// every lane of a 16-lane row receives lane N of that row (DPP row_newbcast)
+// every lane of a 16-lane row receives lane N of that row (DPP row_newbcast).  Every lane is
+// written, so the move takes no old value (update_dpp with an old value of 0 made the
+// compiler set each destination to 0 first: one extra move per broadcast).
 template <int N>
 __device__ __forceinline__ float row_bcast16(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
 }
 
 

@@ -37,9 +37,8 @@ __device__ __forceinline__ float row_sum16(float x) {
   x = row_shr_add<2>(x);
   x = row_shr_add<4>(x);
   x = row_shr_add<8>(x);
-  // lane 15 of the row now holds the total: DPP row_newbcast:15
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x15f, 0xf, 0xf,
-                                                                false));
+  // lane 15 of the row now holds the total: DPP row_newbcast:15 (writes every lane: no old value)
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x15f, 0xf, 0xf, false));
 }
 
 }  // namespace kda
