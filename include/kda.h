@@ -196,7 +196,7 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
  * when the fused kernel would use two or more tiles per chain and either those
  * tiles need more than one round of 256 workgroups or the sequences average at
  * least 16 chunks; otherwise, and for fp32 inputs, the fused kernel.  Measured on
- * MI355X at dk = 128, chunk 64: 1M tokens x 32 heads (dv 128) 35 ms split vs 101
+ * MI355X at dk = 128, chunk 64: 1M tokens x 32 heads (dv 128) 35 ms split vs 96
  * ms fused; 8 x 4,096 tokens x 32 heads 0.79 vs 0.93 ms; 4 x 4,096 x 32 heads
  * 0.42 vs 0.47 ms; 16 x 4,096 x 32 heads at dv = 64 (one tile per chain) 0.94 ms
  * fused vs 1.42 ms split.

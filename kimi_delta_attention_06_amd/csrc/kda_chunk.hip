@@ -2414,7 +2414,7 @@ size_t chunk_split_workspace_bytes(int64_t total_tokens, int n_seqs, int n_heads
 // kernel would repeat the in-chunk work (two or more tiles per chain) and either its tiles
 // take two or more rounds of workgroups or the sequences are long enough (16 chunks on
 // average) to repay the split path's extra launch.  Measured: 1M tokens x 32 heads split
-// 35.3 ms, fused 101 ms; 8 x 4,096 tokens x 32 heads, dv 128, split 0.79 ms, fused 0.93 ms;
+// 35.3 ms, fused 96 ms; 8 x 4,096 tokens x 32 heads, dv 128, split 0.79 ms, fused 0.93 ms;
 // 4 x 4,096 x 32 heads, dv 128, split 0.42 ms, fused 0.47 ms; 16 x 4,096 x 32 heads, dv 64
 // (one 64-column tile per chain): fused 0.94 ms, split 1.42 ms.  Sequences shorter than 4
 // chunks on average stay on the fused kernel.
