@@ -152,9 +152,10 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
  * whole sequence, and writes each chunk's state-free operands to `workspace`;
  * pass 2 walks the chunks of each chain with the state, reading them.  When the
  * state pass fits on half of the CUs (chains x dv/32 <= 128) and the longest
- * sequence has at least 128 chunks, the chunks are cut into 2 to 32 ranges and
- * each launch runs pass 2 over one range beside pass 1 over the next, with the
- * state handed between ranges through the workspace.  With fewer chains still
+ * sequence has at least 144 chunks, the chunks are cut into 2 to 48 ranges, each
+ * 5/4 the size of the one before it, and each launch runs pass 2 over one range
+ * beside pass 1 over the next, with the state handed between ranges through the
+ * workspace.  With fewer chains still
  * (chains x dv/32 <= 64: 16 at dv = 128) and at least 512 chunks in the longest
  * sequence, pass 2 itself runs in parallel over S = 4 to 64 segments of each
  * chain (in-device context parallelism, the same page: KDA states cannot simply

@@ -467,14 +467,15 @@ struct WsTile {
 // The kernel.
 // ---------------------------------------------------------------------------
 // PREP = false: the fused forward.  PREP = true: the intra-chunk part only, for a group of
-// `cpg` consecutive chunks of one (sequence, head) per workgroup; each chunk's state-free
-// operands go to workspace slot (sequence start / C + sequence + chunk) (see write_ws).
-// Pipelined split (PIPE_BV > 0, in-chunk mode only): the first n_state_blocks workgroups
-// run the state pass over chunks [ch_begin, ch_end) with value tiles of PIPE_BV columns
-// (chunk_state_body, defined below), the others the in-chunk pass over the chunk groups
-// from grp0 on.
+// `cpg` consecutive chunks of one (sequence, head) per workgroup, over chunks [in_ch0,
+// in_ch_end) of every sequence (in_ch_end = 0: to the sequence's end); each chunk's
+// state-free operands go to workspace slot (sequence start / C + sequence + chunk) (see
+// write_ws).  Pipelined split (PIPE_BV > 0, in-chunk mode only): the first n_state_blocks
+// workgroups run the state pass over chunks [ch_begin, ch_end) with value tiles of PIPE_BV
+// columns (chunk_state_body, defined below), the others the in-chunk pass.
 struct PipeArgs {
-  int n_state_blocks, grp0;
+  int n_state_blocks;
+  int64_t in_ch0, in_ch_end;
   int64_t ch_begin, ch_end;
   const float* h0;
   float *o, *hT, *carry;
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   int chain, tile = 0, grp = 0;
   if constexpr (PREP) {
     chain = bid % n_chains;
-    grp = bid / n_chains + (PIPE_BV > 0 ? pa.grp0 : 0);
+    grp = bid / n_chains;
   } else {
     const int ntile = DV / BV;
     const int xcd = bid & 7, qd = bid >> 3;
@@ -695,8 +696,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
   const int64_t nchunks = (t_end - t_begin + C - 1) / C;
   int64_t ch_lo = 0, ch_hi = nchunks;
   if constexpr (PREP) {
-    ch_lo = (int64_t)grp * cpg;
-    ch_hi = ch_lo + cpg < nchunks ? ch_lo + cpg : nchunks;
+    const int64_t lim = pa.in_ch_end > 0 && pa.in_ch_end < nchunks ? pa.in_ch_end : nchunks;
+    ch_lo = pa.in_ch0 + (int64_t)grp * cpg;
+    ch_hi = ch_lo + cpg < lim ? ch_lo + cpg : lim;
     if (ch_lo >= ch_hi) return;
   }
 
@@ -2124,26 +2126,60 @@ static int64_t max_chunks_per_seq(const ChunkArgs& a) {
 }
 
 // Pipelined split (chunk_fwd_kernel with PIPE_BV): value tiles of 32 columns, so that a few
-// chains' state pass takes at most 128 CUs, and 2 to 32 ranges of at least 64 chunks.
+// chains' state pass takes at most 128 CUs.  Launch r runs the state pass over chunk range r
+// beside the in-chunk pass over range r + 1 on the other CUs; the in-chunk pass over the
+// first range runs alone before, the state pass over the last alone after.  On the other
+// half of the CUs the in-chunk pass takes about 0.8 of the state pass's time per chunk, so
+// with each range 5/4 the size of the one before it every launch stays bound by its state
+// pass, while the first range (its in-chunk pass not hidden) is short and the last (its
+// state pass alone, ~11% faster per chunk than beside the in-chunk pass) is long: ranges
+// in multiples of 16 chunks, the first at least 64, as many as that allows (at most 48).
 constexpr int kPipeBV = 32;
-static bool split_pipelined(const ChunkArgs& a, int64_t max_chunks, int& n_ranges) {
+struct PipeRanges {
+  static constexpr int kMax = 48;
+  int n = 0;
+  int64_t b[kMax + 1];  // range r: chunks [b[r], b[r + 1])
+};
+static bool pipe_ranges(int64_t mc, PipeRanges& pr) {
+  // the most ranges n whose geometric sizes f, 1.25 f, .. (summing to mc) start at f >= 64
+  int n = 1;
+  double f = (double)mc, qk = 1.25;
+  for (int k = 2; k <= PipeRanges::kMax; ++k) {
+    qk *= 1.25;  // 1.25^k
+    const double fk = (double)mc * 0.25 / (qk - 1.0);
+    if (fk < 64.0) break;
+    n = k;
+    f = fk;
+  }
+  if (n < 2) return false;
+  pr.n = n;
+  pr.b[0] = 0;
+  double s = f;
+  for (int r = 0; r < n - 1; ++r) {
+    int64_t sz = (int64_t)(s / 16.0 + 0.5) * 16;
+    pr.b[r + 1] = pr.b[r] + (sz < 64 ? 64 : sz);
+    s *= 1.25;
+  }
+  pr.b[n] = mc;  // the last range takes the rest (within a few chunks of f 1.25^(n-1))
+  return pr.b[n - 1] < mc;
+}
+static bool split_pipelined(const ChunkArgs& a, int64_t max_chunks, PipeRanges& pr) {
   const int64_t state_blocks = (int64_t)((a.n_seqs * a.n_heads + 7) / 8) * 8 * (a.dv / kPipeBV);
-  n_ranges = (int)(max_chunks / 64 < 32 ? max_chunks / 64 : 32);
-  return state_blocks <= 128 && n_ranges >= 2;
+  return state_blocks <= 128 && pipe_ranges(max_chunks, pr);
 }
 
 template <int C, int DK, typename InT>
-static hipError_t launch_split_pipelined(const ChunkArgs& a, void* ws, float* carry, int64_t mc, int n_ranges) {
+static hipError_t launch_split_pipelined(const ChunkArgs& a, void* ws, float* carry, const PipeRanges& pr) {
   const int n_chains = a.n_seqs * a.n_heads;
   const int state_blocks = ((n_chains + 7) / 8) * 8 * (a.dv / kPipeBV);
-  // range length in chunks: a multiple of the in-chunk pass's group size cpg (16 groups per range)
-  int64_t rl = (mc + n_ranges - 1) / n_ranges;
-  int64_t cpg = (rl + 15) / 16;
-  cpg = cpg < 4 ? 4 : (cpg > 64 ? 64 : cpg);
-  rl = ((rl + cpg - 1) / cpg) * cpg;
-  const int64_t groups = rl / cpg;
-  const int64_t nr = (mc + rl - 1) / rl;
-  if ((int64_t)n_chains * groups + state_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // the in-chunk pass over range r: groups of cpg chunks, about 16 per sequence and range
+  auto cpg_of = [&](int r) -> int64_t {
+    const int64_t c = (pr.b[r + 1] - pr.b[r] + 15) / 16;
+    return c < 4 ? 4 : (c > 64 ? 64 : c);
+  };
+  auto groups_of = [&](int r) -> int64_t { return (pr.b[r + 1] - pr.b[r] + cpg_of(r) - 1) / cpg_of(r); };
+  for (int r = 0; r < pr.n; ++r)
+    if ((int64_t)n_chains * groups_of(r) + state_blocks > 0x7fffffff) return hipErrorInvalidValue;
   // first range's in-chunk pass on its own
   {
     constexpr size_t lds = lds_bytes<C, DK, 16, Prec::Mixed>();
@@ -2151,9 +2187,12 @@ static hipError_t launch_split_pipelined(const ChunkArgs& a, void* ws, float* ca
     static std::atomic<uint64_t> attr_done{0};
     hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(n_chains * groups)), dim3(NT), lds, (hipStream_t)a.stream,
+    PipeArgs p0{};
+    p0.in_ch0 = 0;
+    p0.in_ch_end = pr.b[1];
+    hipLaunchKernelGGL(kern, dim3((unsigned)(n_chains * groups_of(0))), dim3(NT), lds, (hipStream_t)a.stream,
                        (const InT*)a.q, (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, nullptr, a.cu_seqlens,
-                       nullptr, nullptr, nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg, PipeArgs{});
+                       nullptr, nullptr, nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg_of(0), p0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2165,21 +2204,22 @@ static hipError_t launch_split_pipelined(const ChunkArgs& a, void* ws, float* ca
   static std::atomic<uint64_t> attr_done{0};
   hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
   if (e != hipSuccess) return e;
-  for (int64_t r = 0; r < nr; ++r) {
-    const bool next = r + 1 < nr;
-    const int64_t grid = state_blocks + (next ? (int64_t)n_chains * groups : 0);
+  for (int r = 0; r < pr.n; ++r) {
+    const bool next = r + 1 < pr.n;
+    const int64_t grid = state_blocks + (next ? (int64_t)n_chains * groups_of(r + 1) : 0);
     PipeArgs pa{};
     pa.n_state_blocks = state_blocks;
-    pa.grp0 = (int)((r + 1) * groups);
-    pa.ch_begin = r * rl;
-    pa.ch_end = next ? (r + 1) * rl : INT64_MAX;
+    pa.in_ch0 = next ? pr.b[r + 1] : 0;
+    pa.in_ch_end = next ? pr.b[r + 2] : 0;
+    pa.ch_begin = pr.b[r];
+    pa.ch_end = next ? pr.b[r + 1] : INT64_MAX;
     pa.h0 = a.h0;
     pa.o = a.o;
     pa.hT = a.hT;
     pa.carry = carry;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, (hipStream_t)a.stream, (const InT*)a.q,
                        (const InT*)a.k, (const InT*)a.v, a.log_alpha, a.beta, nullptr, a.cu_seqlens, nullptr, nullptr,
-                       nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)cpg, pa);
+                       nullptr, 0, n_chains, a.n_heads, a.dv, a.seq_len, ws, (int)(next ? cpg_of(r + 1) : 4), pa);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2317,8 +2357,8 @@ static hipError_t dispatch_split_bv(const ChunkArgs& a, void* ws, float* carry) 
   int64_t rl = 0;
   if (split_segments(a.n_seqs * a.n_heads, DK, a.dv, mc, n_seg, rl))
     return launch_split_segmented<C, DK, InT>(a, ws, carry + (size_t)a.n_seqs * a.n_heads * DK * a.dv, n_seg, rl);
-  int n_ranges = 0;
-  if (split_pipelined(a, mc, n_ranges)) return launch_split_pipelined<C, DK, InT>(a, ws, carry, mc, n_ranges);
+  PipeRanges pr;
+  if (split_pipelined(a, mc, pr)) return launch_split_pipelined<C, DK, InT>(a, ws, carry, pr);
   // (a value tile as wide as dv when the chains alone fill the CUs: the state pass then runs
   // in one round of workgroups instead of two)
   const int bv = pick_bv(a.n_seqs * a.n_heads, a.dv, 128);
