@@ -507,6 +507,10 @@ template <int C, int DK, int BV, typename InT>
 __device__ __forceinline__ void chunk_state_body(const uint4* __restrict__ ws, const InT* __restrict__ v,
                                                  const int32_t* __restrict__ cu_seqlens, float* __restrict__ o,
                                                  int H, int DV, int64_t seq_len, const StateJob& job);
+template <int C, int DK, int NCW, typename InT>
+__device__ __forceinline__ void chunk_state_wave_body(const uint4* __restrict__ ws, const InT* __restrict__ v,
+                                                      const int32_t* __restrict__ cu_seqlens, float* __restrict__ o,
+                                                      int H, int DV, int64_t seq_len, const StateJob& job);
 
 template <int C, int DK, int BV, Prec P, typename InT, bool PREP, int PIPE_BV = 0>
 __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
@@ -527,8 +531,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_fwd_kernel(
       job.mid_out = pa.carry;
       job.mid_ld = DV;
       job.map = false;
-      chunk_state_body<C, DK, PIPE_BV, InT>(reinterpret_cast<const uint4*>(ws), v, cu_seqlens, pa.o, H, DV, seq_len,
-                                            job);
+      chunk_state_wave_body<C, DK, PIPE_BV / 16, InT>(reinterpret_cast<const uint4*>(ws), v, cu_seqlens, pa.o, H, DV,
+                                                      seq_len, job);
       return;
     }
   }
@@ -1962,6 +1966,357 @@ __device__ __forceinline__ void chunk_state_body(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wave-parallel state pass.  The value columns of the state are independent chains given the
+// chunk's operands, so one wave can carry 16 of them through a whole chunk step on its own:
+// in the 16x16 matrix-core layout a product's accumulator (lane (j, g): rows 4g .. 4g+3 of
+// column j) is the B operand of the next product whose k runs over those rows, once each
+// 32-wide k-step takes its 32 rows in the order {4g .. 4g+3 of the first 16-row block, then of
+// the second} and the A operand (read from LDS) takes its columns in the same order.  So
+//   S (channels x 16) -> Kg S, Qg S;  Y = V - Kg S -> U = (T Diag beta) Y -> M U, Kd^T U;
+//   S' = Diag(gamma) S + Kd^T U;  O = Qg S + M U + diag(q.k) U
+// run in one wave's registers with no exchange and no barrier inside the step.  NCW such
+// waves take 16 NCW columns of one chain; the other NW - NCW waves of the workgroup stage each
+// chunk's workspace tile and values in LDS (two buffers, loaded two chunks ahead through two
+// register sets), and all waves meet at one barrier per chunk.  The operand precisions and
+// rounding points are the split path's (fp16 operands, fp32 accumulation; Y rounded to fp32,
+// then to fp16); the range exponent (see range_exponent) is taken per wave, over its columns.
+// ---------------------------------------------------------------------------
+template <int C, int DK, int NCW>
+struct WLay {
+  using W = WsTile<C, DK>;
+  static constexpr int WBV = 16 * NCW;                       // value columns per workgroup
+  static constexpr int LDT = C + 4;                          // V^T rows (tokens), bf16
+  static constexpr size_t TILE = al16(size_t(W::NU) * 16);
+  static constexpr size_t VT = al16(size_t(WBV) * LDT * 2);
+  static constexpr size_t T0 = 0, T1 = T0 + TILE, V0 = T1 + TILE, V1 = V0 + VT;
+  static constexpr size_t TOTAL = V1 + VT;
+};
+
+// The A operand of one 32-wide k-step from a stored fragment (lane (r, g') of the stored
+// fragment holds X[r][8g' .. 8g'+7]) in the accumulator k order: lane (r, g) takes
+// X[r][4g .. 4g+3] and X[r][16+4g .. 16+4g+3].  `off` = 16 (r + 16 (g >> 1)) + 8 (g & 1).
+__device__ __forceinline__ half8 ld_afrag(const unsigned char* frag, int off) {
+  const half4 a = *reinterpret_cast<const half4*>(frag + off);
+  const half4 b = *reinterpret_cast<const half4*>(frag + off + 512);
+  return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// The B operand of one 32-wide k-step from the accumulators of its two 16-row blocks.
+__device__ __forceinline__ half8 pack_b(const f32x4& lo, const f32x4& hi) {
+  return half8{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
+               (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
+}
+
+// The A operands of one chunk step in the order of their products: Kg (k-step outer, row block
+// inner: four independent accumulators in turn), T Diag(beta) (k-step outer), Kd^T (k-step
+// outer, channel block inner), Qg, strict M.
+template <int C, int DK>
+struct WOrder {
+  using W = WsTile<C, DK>;
+  static constexpr int NB = W::NB, NSD = W::NSD, NSC = W::NSC, NCB = DK / 16;
+  static constexpr int nA = NB * NSD, nB = W::NTRI, nC = NCB * NSC, nD = NB * NSD, nE = W::NTRI;
+  static constexpr int NFR = nA + nB + nC + nD + nE;
+  // (row block, k-step) of the j-th stored fragment of a lower-triangular token operand, k-step outer
+  __host__ __device__ static constexpr int tri_pair(int j, bool st_of) {
+    for (int st = 0; st < NSC; ++st)
+      for (int R = 0; R < NB; ++R)
+        if (st < W::tri(R)) {
+          if (j == 0) return st_of ? st : R;
+          --j;
+        }
+    return 0;
+  }
+  __host__ __device__ static constexpr int tri_R(int j) { return tri_pair(j, false); }
+  __host__ __device__ static constexpr int tri_st(int j) { return tri_pair(j, true); }
+  // first 16-byte unit of the k-th fragment
+  __host__ __device__ static constexpr int unit(int k) {
+    if (k < nA) return W::KG + 64 * ((k % NB) * NSD + k / NB);
+    k -= nA;
+    if (k < nB) return W::TB + 64 * (W::tri_base(tri_R(k)) + tri_st(k));
+    k -= nB;
+    if (k < nC) return W::KDT + 64 * ((k % NCB) * NSC + k / NCB);
+    k -= nC;
+    if (k < nD) return W::QG + 64 * ((k % NB) * NSD + k / NB);
+    k -= nD;
+    return W::AQ + 64 * (W::tri_base(tri_R(k)) + tri_st(k));
+  }
+};
+
+template <int C, int DK, int NCW, typename InT>
+__device__ __forceinline__ void chunk_state_wave_body(
+    const uint4* __restrict__ ws, const InT* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
+    float* __restrict__ o, int H, int DV, int64_t seq_len, const StateJob& job) {
+  using L = WLay<C, DK, NCW>;
+  using W = WsTile<C, DK>;
+  using Ord = WOrder<C, DK>;
+  constexpr int NB = W::NB, NSD = W::NSD, NSC = W::NSC, NCB = DK / 16;
+  constexpr int kAhead = 8;  // fragments in flight
+  constexpr int NL = NW - NCW, NLL = NL * kWave;
+  constexpr int TPL = (W::NU + NLL - 1) / NLL;  // tile units (16 B) per loader lane
+  constexpr int VG = L::WBV / 8;                // 8-column groups of a value row
+  constexpr int VU = C * VG;                    // value units per chunk
+  constexpr int VPL = (VU + NLL - 1) / NLL;
+  static_assert(sizeof(InT) == 2, "bf16 values");
+  static_assert(NCW >= 1 && NCW < NW, "compute and loader waves");
+  static_assert(2 * NSD == NCB && 2 * NSC >= NB, "k-steps pair 16-row blocks");
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int chain = job.chain, j0 = job.j0;
+  const int64_t ch_begin = job.ch_begin, ch_end = job.ch_end;
+  const int n = chain / H, h = chain - n * H;
+  const int vj0 = job.map ? (j0 >= DK ? j0 - DK : -1) : j0;  // first value column (-1: identity columns)
+  int64_t t_begin, t_end;
+  if (cu_seqlens) {
+    t_begin = cu_seqlens[n];
+    t_end = cu_seqlens[n + 1];
+  } else {
+    t_begin = (int64_t)n * seq_len;
+    t_end = t_begin + seq_len;
+  }
+  const int64_t nchunks = (t_end - t_begin + C - 1) / C;
+  if (ch_begin > 0 && ch_begin >= nchunks) return;  // the chain ended in an earlier range
+  const int64_t ch_stop = ch_end < nchunks ? ch_end : nchunks;
+  if (job.map && ch_stop == nchunks) return;        // no later range of the chain needs this map
+  auto chunk_len = [&](int64_t ch) -> int {
+    const int64_t rem = t_end - (t_begin + ch * C);
+    return (int)(rem < C ? rem : C);
+  };
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l = lane_id(), lr = l & 15, lg = l >> 4;
+
+  if (wave >= NCW) {
+    // ================= loader waves =================
+    const int li = tid - NCW * kWave;
+    uint4 ra[TPL], rb[TPL], va[VPL], vb[VPL];
+    auto fetch = [&](int64_t chn, uint4* r, uint4* vr) {
+      const bool ok = chn < ch_stop;
+      const int64_t slot = t_begin / C + n + chn;
+      const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * W::NU, ok ? (uint32_t)W::NU * 16u : 0u);
+#pragma unroll
+      for (int m = 0; m < TPL; ++m) r[m] = buf_load16(rs, (uint32_t)(li + NLL * m) * 16u);
+      const int Lc = ok ? chunk_len(chn) : 0;
+      const uint32_t row = (uint32_t)(H * DV * 2);
+      const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + (vj0 >= 0 ? vj0 : 0),
+                                (Lc > 0 && vj0 >= 0) ? (uint32_t)Lc * row : 0u);
+#pragma unroll
+      for (int m = 0; m < VPL; ++m) {
+        const int u = li + NLL * m;  // token u / VG (past the chunk: zero), columns 8 (u % VG) ..
+        vr[m] = buf_load16(rv, (uint32_t)(u / VG) * row + (uint32_t)(u % VG) * 16u);
+      }
+    };
+    auto stage = [&](const uint4* r, const uint4* vr, int buf) {
+      uint4* dt = reinterpret_cast<uint4*>(smem + (buf ? L::T1 : L::T0));
+#pragma unroll
+      for (int m = 0; m < TPL; ++m) {
+        const int u = li + NLL * m;
+        if (W::NU % NLL == 0 || u < W::NU) dt[u] = r[m];
+      }
+      uint16_t* dv_ = reinterpret_cast<uint16_t*>(smem + (buf ? L::V1 : L::V0));
+#pragma unroll
+      for (int m = 0; m < VPL; ++m) {
+        const int u = li + NLL * m;
+        if (VU % NLL == 0 || u < VU) {
+          const int t = u / VG, c = 8 * (u % VG);
+          const uint32_t w[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dv_[(c + 2 * e) * L::LDT + t] = (uint16_t)(w[e] & 0xffffu);
+            dv_[(c + 2 * e + 1) * L::LDT + t] = (uint16_t)(w[e] >> 16);
+          }
+        }
+      }
+    };
+    fetch(ch_begin, ra, va);
+    stage(ra, va, 0);
+    fetch(ch_begin + 1, rb, vb);
+    fetch(ch_begin + 2, ra, va);
+    __syncthreads();  // buffer 0 holds the first chunk
+    for (int64_t ch = ch_begin; ch < ch_stop; ch += 2) {
+      // step ch: buffer 1 <- chunk ch + 1 (set b), then set b <- chunk ch + 3
+      stage(rb, vb, 1);
+      fetch(ch + 3, rb, vb);
+      __syncthreads();
+      if (ch + 1 >= ch_stop) break;
+      // step ch + 1: buffer 0 <- chunk ch + 2 (set a), then set a <- chunk ch + 4
+      stage(ra, va, 0);
+      fetch(ch + 4, ra, va);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ================= compute waves: columns j0 + 16 wave + (0 .. 15) =================
+  const int col = j0 + 16 * wave + lr;        // state column of this lane
+  const int vcol = vj0 >= 0 ? vj0 + 16 * wave : 0;  // first value column of this wave
+  const int aoff = 16 * (lr + 16 * (lg >> 1)) + 8 * (lg & 1);
+  f32x4 Sacc[NCB];
+  const float* h0p = (!job.map && job.s_in) ? job.s_in + (size_t)chain * DK * DV : nullptr;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * cb + 4 * lg + i;
+      Sacc[cb][i] = h0p ? h0p[(size_t)row * DV + col] : (job.map ? (row == col ? 1.f : 0.f) : 0.f);
+    }
+  }
+  int sc_e = 0;
+  float sc_dn = 1.f, sc_up = 1.f;
+  __syncthreads();  // buffer 0 holds the first chunk
+  for (int64_t ch = ch_begin; ch < ch_stop; ++ch) {
+    const int p = (int)((ch - ch_begin) & 1);
+    const unsigned char* tile = smem + (p ? L::T1 : L::T0);
+    const uint16_t* vt = reinterpret_cast<const uint16_t*>(smem + (p ? L::V1 : L::V0));
+    const int64_t c_begin = t_begin + ch * C;
+    const int Lc = chunk_len(ch);
+
+    // this chunk's values: rows 16 R + 4 lg .. + 3 of column lr (bf16 pairs)
+    uint2 vv[NB];
+#pragma unroll
+    for (int R = 0; R < NB; ++R) vv[R] = *reinterpret_cast<const uint2*>(vt + (16 * wave + lr) * L::LDT + 16 * R + 4 * lg);
+    // the A operands of the step's products, kAhead products ahead of their use
+    half8 fb[kAhead];
+    auto fetch = [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k < Ord::NFR) fb[k % kAhead] = ld_afrag(tile + 16 * Ord::unit(k), aoff);
+    };
+    static_for<0, kAhead>(fetch);
+    // the chunk's range exponent from the largest |S| and |v| of this wave's columns
+    {
+      uint32_t w[2 * NB];
+#pragma unroll
+      for (int R = 0; R < NB; ++R) {
+        w[2 * R] = vv[R].x;
+        w[2 * R + 1] = vv[R].y;
+      }
+      const uint32_t mv = mag_max_bf16(w, 2 * NB);
+      float sv[4 * NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[4 * cb + i] = Sacc[cb][i];
+      const uint32_t m = wave_max_u32(max(mag_max<4 * NCB>(sv), sc_e == 0 ? mv : mag_scaled(mv, sc_e)));
+      const int e = range_exponent(__builtin_amdgcn_readfirstlane(m), sc_e);
+      if (e != sc_e) {
+        const int d = sc_e - e, d1 = d / 2;
+        const float f1 = pow2i(d1), f2 = pow2i(d - d1);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) Sacc[cb] = (Sacc[cb] * f1) * f2;
+        sc_e = e;
+        sc_dn = pow2i(-e);
+        sc_up = pow2i(e);
+      }
+    }
+    // S as the B operand of the products over channels
+    half8 Sb[NSD];
+#pragma unroll
+    for (int st = 0; st < NSD; ++st) Sb[st] = pack_b(Sacc[2 * st], Sacc[2 * st + 1]);
+    // product k of the step: its fragment is used, and the one kAhead later read into its
+    // registers; the fence keeps the reads where they are written
+    auto product = [&](auto kc, f32x4& d, const half8& b) {
+      constexpr int k = decltype(kc)::value;
+      mma_frag(d, fb[k % kAhead], b);
+      fetch(std::integral_constant<int, k + kAhead>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Kg S, then Y = V - Kg S
+    f32x4 acc[NB];
+#pragma unroll
+    for (int R = 0; R < NB; ++R) acc[R] = zero4();
+    static_for<0, Ord::nA>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      product(jc, acc[j % NB], Sb[j / NB]);
+    });
+    float4 gm[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) gm[cb] = *reinterpret_cast<const float4*>(tile + 16 * W::GM + 4 * (16 * cb + 4 * lg));
+    f32x4 Y[2 * NSC];
+#pragma unroll
+    for (int R = 0; R < 2 * NSC; ++R) Y[R] = zero4();
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int R = 0; R < NB; ++R) {
+        const float2 v01 = bf16x2_to_f32x2(vv[R].x), v23 = bf16x2_to_f32x2(vv[R].y);
+        const float x[4] = {v01.x, v01.y, v23.x, v23.y};
+        // rounded to fp32 here, to fp16 in the operand
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[R][i] = x[i] * sc_dn - acc[R][i];
+      }
+    }
+    half8 Yb[NSC];
+#pragma unroll
+    for (int st = 0; st < NSC; ++st) Yb[st] = pack_b(Y[2 * st], Y[2 * st + 1]);
+
+    // U = (T Diag beta) Y
+    f32x4 U[2 * NSC];
+#pragma unroll
+    for (int R = 0; R < 2 * NSC; ++R) U[R] = zero4();
+    static_for<0, Ord::nB>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      product(std::integral_constant<int, Ord::nA + j>{}, U[Ord::tri_R(j)], Yb[Ord::tri_st(j)]);
+    });
+    float4 dq[NB];
+#pragma unroll
+    for (int R = 0; R < NB; ++R) dq[R] = *reinterpret_cast<const float4*>(tile + 16 * W::DQ + 4 * (16 * R + 4 * lg));
+    half8 Ub[NSC];
+#pragma unroll
+    for (int st = 0; st < NSC; ++st) Ub[st] = pack_b(U[2 * st], U[2 * st + 1]);
+
+    // S <- Diag(gamma) S + Kd^T U (in the chunk's scaled units)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      Sacc[cb][0] *= gm[cb].x;
+      Sacc[cb][1] *= gm[cb].y;
+      Sacc[cb][2] *= gm[cb].z;
+      Sacc[cb][3] *= gm[cb].w;
+    }
+    static_for<0, Ord::nC>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      product(std::integral_constant<int, Ord::nA + Ord::nB + j>{}, Sacc[j % NCB], Ub[j / NCB]);
+    });
+
+    // O = Qg S + M U + diag(q.k) U, stored (map mode: no o)
+    f32x4 O[NB];
+#pragma unroll
+    for (int R = 0; R < NB; ++R) O[R] = zero4();
+    static_for<0, Ord::nD>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      product(std::integral_constant<int, Ord::nA + Ord::nB + Ord::nC + j>{}, O[j % NB], Sb[j / NB]);
+    });
+    static_for<0, Ord::nE>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      product(std::integral_constant<int, Ord::nA + Ord::nB + Ord::nC + Ord::nD + j>{}, O[Ord::tri_R(j)],
+              Ub[Ord::tri_st(j)]);
+    });
+    {
+      const uint32_t hdv = (uint32_t)(H * DV);
+      const auto ro = job.map ? make_rsrc(o, 0u) : make_rsrc(o + ((size_t)c_begin * H + h) * DV + vcol, (uint32_t)Lc * hdv * 4u);
+#pragma unroll
+      for (int R = 0; R < NB; ++R) {
+        const float d[4] = {dq[R].x, dq[R].y, dq[R].z, dq[R].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, (O[R][i] + d[i] * U[R][i]) * sc_up), ro,
+                                                (int)(((uint32_t)(16 * R + 4 * lg + i) * hdv + (uint32_t)lr) * 4u), 0, 0);
+      }
+    }
+    __syncthreads();  // every read of this chunk's buffers is done; the next chunk's are written
+  }
+  auto store_state = [&](float* sp, int ld) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sp[(size_t)(16 * cb + 4 * lg + i) * ld + col] = Sacc[cb][i] * sc_up;
+  };
+  if (ch_stop == nchunks) {
+    if (job.end_out) store_state(job.end_out + (size_t)chain * DK * DV, DV);
+  } else if (job.mid_out) {
+    store_state(job.mid_out + (size_t)chain * DK * job.mid_ld, job.mid_ld);
+  }
+}
+
 template <int C, int DK, int BV, typename InT>
 __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(
     const uint4* __restrict__ ws, const InT* __restrict__ v, const float* h0,
@@ -2197,7 +2552,7 @@ static hipError_t launch_split_pipelined(const ChunkArgs& a, void* ws, float* ca
     if (e != hipSuccess) return e;
   }
   // then per range r: the state pass over range r beside the in-chunk pass over range r + 1
-  constexpr size_t lds_p = lds_bytes<C, DK, 16, Prec::Mixed>(), lds_s = SLay<C, DK, kPipeBV>::TOTAL;
+  constexpr size_t lds_p = lds_bytes<C, DK, 16, Prec::Mixed>(), lds_s = WLay<C, DK, kPipeBV / 16>::TOTAL;
   constexpr size_t lds = lds_p > lds_s ? lds_p : lds_s;
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = chunk_fwd_kernel<C, DK, 16, Prec::Mixed, InT, true, kPipeBV>;

@@ -4,18 +4,45 @@ the fp64 oracle and against the fused kda_chunk_fwd.
 
 Shapes are chosen so that the state pass needs at most 128 workgroups (chains x dv/32)
 and the longest sequence has 128 to 511 chunks (two or more ranges; from 512 chunks, few
-enough chains take the segmented form of test_chunk_split_segmented).  Tolerances as in
-test_chunk_split: bf16 inputs, max |err| <= 2e-2 * RMS(ref) against the oracle, and
-max |diff| <= 1e-4 * RMS(ref) against the fused kernel.
+enough chains take the segmented form of test_chunk_split_segmented).  Against the oracle:
+bf16 inputs, max |err| <= 2e-2 * RMS(ref), as in test_chunk_split.
+
+Against the fused kernel: the state pass of this form runs one wave per 16 value columns,
+which feeds each product's accumulators to the next product as its B operand; the 32 terms
+of a k-step are then summed in another order than in the fused kernel, so an fp32 sum can
+differ in its last bit, and the fp16 rounding of Y or U that follows can then land one fp16
+ulp (2^-11 relative) away.  Such a flip moves the o rows of its chunk by about one fp16 ulp
+of U times |q.k| or an entry of M (both at most 1 for unit keys and queries), and the state by
+far less after the decay and the key product, while most elements are unaffected.  So the
+comparison bounds the largest difference by 1e-2 * RMS(ref) (half the oracle bound, several
+fp16 ulps of the largest U) and the RMS of the differences by 1e-4 * RMS(ref), which a
+systematic error (a wrong term, index or scale) would exceed by orders of magnitude.
 """
+import numpy as np
 import pytest
 import torch
 
 import kda_inputs
-from test_chunk_parity import check_bf16
+from test_chunk_parity import check_bf16, to64
 from test_chunk_split import check_same, ref, run_fused, run_split
 
 pytestmark = pytest.mark.gpu
+
+ORDER_MAX_TOL = 1e-2
+ORDER_RMS_TOL = 1e-4
+
+
+def check_close_order(a, b, ref_arr, name):
+    """a and b agree up to the fp16 rounding flips of a different fp32 summation order."""
+    if not ref_arr.size:
+        return
+    d = np.abs(to64(a) - to64(b))
+    rms = float(np.sqrt(np.mean(ref_arr ** 2)))
+    dmax, drms = float(d.max()), float(np.sqrt(np.mean(d ** 2)))
+    print("  %-3s pipelined vs fused max|diff|/rms %.3e  rms-diff/rms %.3e" % (name, dmax / rms, drms / rms),
+          flush=True)
+    assert dmax <= ORDER_MAX_TOL * rms, (dmax, rms)
+    assert drms <= ORDER_RMS_TOL * rms, (drms, rms)
 
 
 @pytest.mark.parametrize("lens,H,dk,dv,C", [
@@ -32,8 +59,8 @@ def test_split_pipelined_against_oracle_and_fused(lens, H, dk, dv, C):
     o_ref, h_ref = ref(inp)
     check_bf16(o, hT, o_ref, h_ref)
     of, hf = run_fused(inp, chunk_size=C)
-    check_same(o, of, o_ref, "o")
-    check_same(hT, hf, h_ref, "hT")
+    check_close_order(o, of, o_ref, "o")
+    check_close_order(hT, hf, h_ref, "hT")
 
 
 def test_split_pipelined_final_state_in_place_and_absent():
