@@ -152,8 +152,8 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
  * whole sequence, and writes each chunk's state-free operands to `workspace`;
  * pass 2 walks the chunks of each chain with the state, reading them.  When the
  * state pass fits on half of the CUs (chains x dv/32 <= 128) and the longest
- * sequence has at least 144 chunks, the chunks are cut into 2 to 48 ranges, each
- * 5/4 the size of the one before it, and each launch runs pass 2 over one range
+ * sequence has at least 135 chunks, the chunks are cut into 2 to 48 ranges, each
+ * about 1.1 times the size of the one before it, and each launch runs pass 2 over one range
  * beside pass 1 over the next, with the state handed between ranges through the
  * workspace.  With fewer chains still
  * (chains x dv/32 <= 64: 16 at dv = 128) and at least 512 chunks in the longest

@@ -2484,24 +2484,26 @@ static int64_t max_chunks_per_seq(const ChunkArgs& a) {
 // chains' state pass takes at most 128 CUs.  Launch r runs the state pass over chunk range r
 // beside the in-chunk pass over range r + 1 on the other CUs; the in-chunk pass over the
 // first range runs alone before, the state pass over the last alone after.  On the other
-// half of the CUs the in-chunk pass takes about 0.8 of the state pass's time per chunk, so
-// with each range 5/4 the size of the one before it every launch stays bound by its state
-// pass, while the first range (its in-chunk pass not hidden) is short and the last (its
-// state pass alone, ~11% faster per chunk than beside the in-chunk pass) is long: ranges
-// in multiples of 16 chunks, the first at least 64, as many as that allows (at most 48).
+// half of the CUs the in-chunk pass takes nearly as long per chunk as the wave-parallel
+// state pass, so each range is kRangeGrowth times the one before it: every launch stays
+// about balanced, while the first range (its in-chunk pass not hidden) is short and the
+// last (its state pass alone) is long.  Ranges in multiples of 16 chunks, the first at
+// least 64, as many as that allows (at most 48).
 constexpr int kPipeBV = 32;
+constexpr double kRangeGrowth = 1.10;
 struct PipeRanges {
   static constexpr int kMax = 48;
   int n = 0;
   int64_t b[kMax + 1];  // range r: chunks [b[r], b[r + 1])
 };
 static bool pipe_ranges(int64_t mc, PipeRanges& pr) {
-  // the most ranges n whose geometric sizes f, 1.25 f, .. (summing to mc) start at f >= 64
+  // the most ranges n whose geometric sizes f, g f, g^2 f, .. (g = kRangeGrowth, summing to
+  // mc) start at f >= 64
   int n = 1;
-  double f = (double)mc, qk = 1.25;
+  double f = (double)mc, qk = kRangeGrowth;
   for (int k = 2; k <= PipeRanges::kMax; ++k) {
-    qk *= 1.25;  // 1.25^k
-    const double fk = (double)mc * 0.25 / (qk - 1.0);
+    qk *= kRangeGrowth;  // g^k
+    const double fk = (double)mc * (kRangeGrowth - 1.0) / (qk - 1.0);
     if (fk < 64.0) break;
     n = k;
     f = fk;
@@ -2513,9 +2515,9 @@ static bool pipe_ranges(int64_t mc, PipeRanges& pr) {
   for (int r = 0; r < n - 1; ++r) {
     int64_t sz = (int64_t)(s / 16.0 + 0.5) * 16;
     pr.b[r + 1] = pr.b[r] + (sz < 64 ? 64 : sz);
-    s *= 1.25;
+    s *= kRangeGrowth;
   }
-  pr.b[n] = mc;  // the last range takes the rest (within a few chunks of f 1.25^(n-1))
+  pr.b[n] = mc;  // the last range takes the rest (within a few chunks of f g^(n-1))
   return pr.b[n - 1] < mc;
 }
 static bool split_pipelined(const ChunkArgs& a, int64_t max_chunks, PipeRanges& pr) {

@@ -46,10 +46,10 @@ def check_close_order(a, b, ref_arr, name):
 
 
 @pytest.mark.parametrize("lens,H,dk,dv,C", [
-    ([16384], 4, 128, 128, 64),          # 256 chunks: ranges of 64, 80 and 112
+    ([16384], 4, 128, 128, 64),          # 256 chunks: ranges of 80, 80 and 96
     ([9000, 3000, 70, 0], 2, 128, 128, 64),  # sequences ending in different ranges, one empty
     ([5000, 4097], 3, 64, 64, 32),       # dk = dv = 64, chunk 32
-    ([8100], 8, 128, 64, 16),            # dv = 64, chunk 16: 507 chunks, four ranges
+    ([8100], 8, 128, 64, 16),            # dv = 64, chunk 16: 507 chunks, six ranges
 ])
 def test_split_pipelined_against_oracle_and_fused(lens, H, dk, dv, C):
     print("split pipelined: lens=%s H=%d dk=%d dv=%d C=%d" % (lens, H, dk, dv, C), flush=True)
