@@ -1993,13 +1993,18 @@ struct WLay {
   static constexpr size_t TOTAL = V1 + VT;
 };
 
-// The A operand of one 32-wide k-step from a stored fragment (lane (r, g') of the stored
-// fragment holds X[r][8g' .. 8g'+7]) in the accumulator k order: lane (r, g) takes
-// X[r][4g .. 4g+3] and X[r][16+4g .. 16+4g+3].  `off` = 16 (r + 16 (g >> 1)) + 8 (g & 1).
-__device__ __forceinline__ half8 ld_afrag(const unsigned char* frag, int off) {
-  const half4 a = *reinterpret_cast<const half4*>(frag + off);
-  const half4 b = *reinterpret_cast<const half4*>(frag + off + 512);
-  return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// The A operand of one 32-wide k-step in the accumulator k order: lane (r, g) takes
+// X[r][4g .. 4g+3] and X[r][16+4g .. 16+4g+3].  The workspace holds each fragment in the
+// matrix core's own order (lane (r, g') of the stored fragment holds X[r][8g' .. 8g'+7]),
+// so lane (r, g) needs half of stored unit (r, g >> 1) and half of unit (r, (g >> 1) + 2).
+// The loader waves put them together when they stage a tile in LDS: from stored units
+// (r, g') and (r, g' + 2) they write staged units (r, 2g') = both low halves and (r, 2g' + 1)
+// = both high halves, so each compute lane reads its operand as 16 consecutive bytes (one
+// conflict-free 128-bit LDS read; two 64-bit reads at a 16-byte lane stride hit each bank
+// twice).
+__device__ __forceinline__ void stage_pair(uint4* dst_lo, uint4* dst_hi, const uint4& n1, const uint4& n2) {
+  *dst_lo = uint4{n1.x, n1.y, n2.x, n2.y};
+  *dst_hi = uint4{n1.z, n1.w, n2.z, n2.w};
 }
 // The B operand of one 32-wide k-step from the accumulators of its two 16-row blocks.
 __device__ __forceinline__ half8 pack_b(const f32x4& lo, const f32x4& hi) {
@@ -2052,7 +2057,13 @@ __device__ __forceinline__ void chunk_state_wave_body(
   constexpr int NB = W::NB, NSD = W::NSD, NSC = W::NSC, NCB = DK / 16;
   constexpr int kAhead = 8;  // fragments in flight
   constexpr int NL = NW - NCW, NLL = NL * kWave;
-  constexpr int TPL = (W::NU + NLL - 1) / NLL;  // tile units (16 B) per loader lane
+  // the tile's fragments [0, DQ) are staged in unit pairs (see stage_pair), the fp32 tail
+  // (q.k, gamma) [DQ, NU) unit by unit
+  constexpr int NPR = W::DQ / 2, NTL = W::NU - W::DQ;
+  static_assert(W::DQ % 64 == 0, "whole fragments before the fp32 tail");
+  constexpr int PPL = (NPR + NLL - 1) / NLL;    // unit pairs per loader lane
+  constexpr int TLL = (NTL + NLL - 1) / NLL;    // tail units per loader lane
+  constexpr int TPL = 2 * PPL + TLL;            // loaded 16-byte units per loader lane
   constexpr int VG = L::WBV / 8;                // 8-column groups of a value row
   constexpr int VU = C * VG;                    // value units per chunk
   constexpr int VPL = (VU + NLL - 1) / NLL;
@@ -2094,7 +2105,16 @@ __device__ __forceinline__ void chunk_state_wave_body(
       const int64_t slot = t_begin / C + n + chn;
       const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * W::NU, ok ? (uint32_t)W::NU * 16u : 0u);
 #pragma unroll
-      for (int m = 0; m < TPL; ++m) r[m] = buf_load16(rs, (uint32_t)(li + NLL * m) * 16u);
+      for (int m = 0; m < PPL; ++m) {
+        // pair p: stored units (r, g') and (r, g' + 2) of fragment p / 32, r = p % 16, g' = (p / 16) % 2
+        // (past the tile the loads return zero and the pair is not staged)
+        const int p = li + NLL * m;
+        const uint32_t u1 = (uint32_t)(64 * (p >> 5) + (p & 15) + 16 * ((p >> 4) & 1));
+        r[2 * m] = buf_load16(rs, u1 * 16u);
+        r[2 * m + 1] = buf_load16(rs, (u1 + 32u) * 16u);
+      }
+#pragma unroll
+      for (int m = 0; m < TLL; ++m) r[2 * PPL + m] = buf_load16(rs, (uint32_t)(W::DQ + li + NLL * m) * 16u);
       const int Lc = ok ? chunk_len(chn) : 0;
       const uint32_t row = (uint32_t)(H * DV * 2);
       const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + (vj0 >= 0 ? vj0 : 0),
@@ -2108,9 +2128,17 @@ __device__ __forceinline__ void chunk_state_wave_body(
     auto stage = [&](const uint4* r, const uint4* vr, int buf) {
       uint4* dt = reinterpret_cast<uint4*>(smem + (buf ? L::T1 : L::T0));
 #pragma unroll
-      for (int m = 0; m < TPL; ++m) {
+      for (int m = 0; m < PPL; ++m) {
+        const int p = li + NLL * m;
+        if (NPR % NLL == 0 || p < NPR) {
+          const int d = 64 * (p >> 5) + (p & 15) + 32 * ((p >> 4) & 1);  // staged unit (r, 2g')
+          stage_pair(dt + d, dt + d + 16, r[2 * m], r[2 * m + 1]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < TLL; ++m) {
         const int u = li + NLL * m;
-        if (W::NU % NLL == 0 || u < W::NU) dt[u] = r[m];
+        if (NTL % NLL == 0 || u < NTL) dt[W::DQ + u] = r[2 * PPL + m];
       }
       uint16_t* dv_ = reinterpret_cast<uint16_t*>(smem + (buf ? L::V1 : L::V0));
 #pragma unroll
@@ -2149,7 +2177,7 @@ __device__ __forceinline__ void chunk_state_wave_body(
   // ================= compute waves: columns j0 + 16 wave + (0 .. 15) =================
   const int col = j0 + 16 * wave + lr;        // state column of this lane
   const int vcol = vj0 >= 0 ? vj0 + 16 * wave : 0;  // first value column of this wave
-  const int aoff = 16 * (lr + 16 * (lg >> 1)) + 8 * (lg & 1);
+  const int aoff = 16 * l;  // this lane's staged unit of a fragment
   f32x4 Sacc[NCB];
   const float* h0p = (!job.map && job.s_in) ? job.s_in + (size_t)chain * DK * DV : nullptr;
 #pragma unroll
@@ -2178,7 +2206,7 @@ __device__ __forceinline__ void chunk_state_wave_body(
     half8 fb[kAhead];
     auto fetch = [&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      if constexpr (k < Ord::NFR) fb[k % kAhead] = ld_afrag(tile + 16 * Ord::unit(k), aoff);
+      if constexpr (k < Ord::NFR) fb[k % kAhead] = *reinterpret_cast<const half8*>(tile + 16 * Ord::unit(k) + aoff);
     };
     static_for<0, kAhead>(fetch);
     // the chunk's range exponent from the largest |S| and |v| of this wave's columns
