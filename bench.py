@@ -248,7 +248,7 @@ def headline(args, dev, stream, copy_gbs):
                                                                                      "hbm_bytes_per_call"),
                      "kernel": "split path: chunk_fwd_kernel's in-chunk pass over the first chunk range, then "
                                "one launch per range of its pipelined mode (the state pass over range r beside "
-                               "the in-chunk pass over range r + 1; 18 ranges growing by 5/4, 80 to 3,360 chunks): "
+                               "the in-chunk pass over range r + 1; 34 ranges growing by 1.10, 64 to 1,552 chunks): "
                                "one call = one step",
                      "algorithmic_bytes_per_launch": alg_bytes, "copy_GB/s": round(copy_gbs, 1),
                      "frac_of_copy": round(gbs / copy_gbs, 4)},
