@@ -2402,7 +2402,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_seg_kernel(
     job.mid_out = nullptr;
     job.mid_ld = DV;
   }
-  chunk_state_body<C, DK, BV, InT>(ws, v, cu_seqlens, o, H, DV, seq_len, job);
+  chunk_state_wave_body<C, DK, BV / 16, InT>(ws, v, cu_seqlens, o, H, DV, seq_len, job);
 }
 
 // The scan: one workgroup of 256 threads per (chain, 32 value columns), fp32; it copies
@@ -2706,7 +2706,7 @@ static hipError_t launch_split_segmented(const ChunkArgs& a, void* ws, float* se
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr size_t lds = SLay<C, DK, kPipeBV>::TOTAL;
+  constexpr size_t lds = WLay<C, DK, kPipeBV / 16>::TOTAL;
   auto kern = chunk_seg_kernel<C, DK, kPipeBV, InT>;
   static std::atomic<uint64_t> attr_done{0};
   hipError_t e = set_lds_limit((const void*)kern, lds, attr_done);
