@@ -2653,7 +2653,7 @@ static hipError_t launch_split(const ChunkArgs& a, void* ws) {
 // and at least 512 chunks in the longest sequence, with as many segments as keep the map pass
 // near 512 workgroups of 32 columns (two per CU; at most 64 segments, each at least 64 chunks)
 // and at least 4 (with fewer the pipelined form, which hides the in-chunk pass, is as fast).
-// 1M tokens at dk = dv = 128: 1 head 2.6 ms, 4 heads 7.5 ms, 8 heads 14.8 ms, against
+// 1M tokens at dk = dv = 128: 1 head 2.5 ms, 4 heads 6.6 ms, 8 heads 13.0 ms, against
 // 32-34 ms for the pipelined form (256 workgroups: 2.8, 9.8, 19.5 ms).
 static constexpr int kMaxSeg = 64;
 static bool split_segments(int n_chains, int dk, int dv, int64_t mc, int& n_seg, int64_t& rl) {
