@@ -472,7 +472,7 @@ struct WsTile {
 // state-free operands go to workspace slot (sequence start / C + sequence + chunk) (see
 // write_ws).  Pipelined split (PIPE_BV > 0, in-chunk mode only): the first n_state_blocks
 // workgroups run the state pass over chunks [ch_begin, ch_end) with value tiles of PIPE_BV
-// columns (chunk_state_body, defined below), the others the in-chunk pass.
+// columns (chunk_state_wave_body, defined below), the others the in-chunk pass.
 struct PipeArgs {
   int n_state_blocks;
   int64_t in_ch0, in_ch_end;
@@ -481,7 +481,8 @@ struct PipeArgs {
   float *o, *hT, *carry;
 };
 
-// What one workgroup of the state pass does beyond its chunk loop (see chunk_state_body).
+// What one workgroup of the state pass does beyond its chunk loop (chunk_state_body and
+// chunk_state_wave_body take the same job).
 struct StateJob {
   int chain, j0;             // chain, and the first state column of its tile
   int64_t ch_begin, ch_end;  // chunk range (clipped to the chain's chunks)
@@ -1629,6 +1630,8 @@ struct SLay {
   static constexpr size_t TOTAL = MX + al16(size_t(NW) * 4);
 };
 
+// The row-role state pass (the non-pipelined split path's; the pipelined and segmented forms
+// run chunk_state_wave_body below, which takes the same job).
 // Chunks [job.ch_begin, job.ch_end) of one chain (clipped to its length), value columns
 // job.j0 .. + BV.  The state enters from job.s_in (or zeros) and leaves to job.end_out when the
 // chain's last chunk is in the range, else to job.mid_out (either may be null: not stored).
