@@ -1979,9 +1979,10 @@ __device__ __forceinline__ void chunk_state_body(
 //   S (channels x 16) -> Kg S, Qg S;  Y = V - Kg S -> U = (T Diag beta) Y -> M U, Kd^T U;
 //   S' = Diag(gamma) S + Kd^T U;  O = Qg S + M U + diag(q.k) U
 // run in one wave's registers with no exchange and no barrier inside the step.  NCW such
-// waves take 16 NCW columns of one chain; the other NW - NCW waves of the workgroup stage each
-// chunk's workspace tile and values in LDS (two buffers, loaded two chunks ahead through two
-// register sets), and all waves meet at one barrier per chunk.  The operand precisions and
+// waves take 16 NCW columns of one chain and load their values straight from memory, one
+// chunk ahead; the other NW - NCW waves of the workgroup stage each chunk's workspace tile in
+// LDS (two buffers, loaded two chunks ahead through two register sets), and all waves meet at
+// one barrier per chunk.  The operand precisions and
 // rounding points are the split path's (fp16 operands, fp32 accumulation; Y rounded to fp32,
 // then to fp16); the range exponent (see range_exponent) is taken per wave, over its columns.
 // ---------------------------------------------------------------------------
@@ -1989,11 +1990,9 @@ template <int C, int DK, int NCW>
 struct WLay {
   using W = WsTile<C, DK>;
   static constexpr int WBV = 16 * NCW;                       // value columns per workgroup
-  static constexpr int LDT = C + 4;                          // V^T rows (tokens), bf16
   static constexpr size_t TILE = al16(size_t(W::NU) * 16);
-  static constexpr size_t VT = al16(size_t(WBV) * LDT * 2);
-  static constexpr size_t T0 = 0, T1 = T0 + TILE, V0 = T1 + TILE, V1 = V0 + VT;
-  static constexpr size_t TOTAL = V1 + VT;
+  static constexpr size_t T0 = 0, T1 = T0 + TILE;
+  static constexpr size_t TOTAL = T1 + TILE;
 };
 
 // The A operand of one 32-wide k-step in the accumulator k order: lane (r, g) takes
@@ -2067,9 +2066,6 @@ __device__ __forceinline__ void chunk_state_wave_body(
   constexpr int PPL = (NPR + NLL - 1) / NLL;    // unit pairs per loader lane
   constexpr int TLL = (NTL + NLL - 1) / NLL;    // tail units per loader lane
   constexpr int TPL = 2 * PPL + TLL;            // loaded 16-byte units per loader lane
-  constexpr int VG = L::WBV / 8;                // 8-column groups of a value row
-  constexpr int VU = C * VG;                    // value units per chunk
-  constexpr int VPL = (VU + NLL - 1) / NLL;
   static_assert(sizeof(InT) == 2, "bf16 values");
   static_assert(NCW >= 1 && NCW < NW, "compute and loader waves");
   static_assert(2 * NSD == NCB && 2 * NSC >= NB, "k-steps pair 16-row blocks");
@@ -2102,8 +2098,8 @@ __device__ __forceinline__ void chunk_state_wave_body(
   if (wave >= NCW) {
     // ================= loader waves =================
     const int li = tid - NCW * kWave;
-    uint4 ra[TPL], rb[TPL], va[VPL], vb[VPL];
-    auto fetch = [&](int64_t chn, uint4* r, uint4* vr) {
+    uint4 ra[TPL], rb[TPL];
+    auto fetch = [&](int64_t chn, uint4* r) {
       const bool ok = chn < ch_stop;
       const int64_t slot = t_begin / C + n + chn;
       const auto rs = make_rsrc(ws + ((size_t)(ok ? slot : 0) * H + h) * W::NU, ok ? (uint32_t)W::NU * 16u : 0u);
@@ -2118,17 +2114,8 @@ __device__ __forceinline__ void chunk_state_wave_body(
       }
 #pragma unroll
       for (int m = 0; m < TLL; ++m) r[2 * PPL + m] = buf_load16(rs, (uint32_t)(W::DQ + li + NLL * m) * 16u);
-      const int Lc = ok ? chunk_len(chn) : 0;
-      const uint32_t row = (uint32_t)(H * DV * 2);
-      const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + (vj0 >= 0 ? vj0 : 0),
-                                (Lc > 0 && vj0 >= 0) ? (uint32_t)Lc * row : 0u);
-#pragma unroll
-      for (int m = 0; m < VPL; ++m) {
-        const int u = li + NLL * m;  // token u / VG (past the chunk: zero), columns 8 (u % VG) ..
-        vr[m] = buf_load16(rv, (uint32_t)(u / VG) * row + (uint32_t)(u % VG) * 16u);
-      }
     };
-    auto stage = [&](const uint4* r, const uint4* vr, int buf) {
+    auto stage = [&](const uint4* r, int buf) {
       uint4* dt = reinterpret_cast<uint4*>(smem + (buf ? L::T1 : L::T0));
 #pragma unroll
       for (int m = 0; m < PPL; ++m) {
@@ -2143,35 +2130,21 @@ __device__ __forceinline__ void chunk_state_wave_body(
         const int u = li + NLL * m;
         if (NTL % NLL == 0 || u < NTL) dt[W::DQ + u] = r[2 * PPL + m];
       }
-      uint16_t* dv_ = reinterpret_cast<uint16_t*>(smem + (buf ? L::V1 : L::V0));
-#pragma unroll
-      for (int m = 0; m < VPL; ++m) {
-        const int u = li + NLL * m;
-        if (VU % NLL == 0 || u < VU) {
-          const int t = u / VG, c = 8 * (u % VG);
-          const uint32_t w[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dv_[(c + 2 * e) * L::LDT + t] = (uint16_t)(w[e] & 0xffffu);
-            dv_[(c + 2 * e + 1) * L::LDT + t] = (uint16_t)(w[e] >> 16);
-          }
-        }
-      }
     };
-    fetch(ch_begin, ra, va);
-    stage(ra, va, 0);
-    fetch(ch_begin + 1, rb, vb);
-    fetch(ch_begin + 2, ra, va);
+    fetch(ch_begin, ra);
+    stage(ra, 0);
+    fetch(ch_begin + 1, rb);
+    fetch(ch_begin + 2, ra);
     __syncthreads();  // buffer 0 holds the first chunk
     for (int64_t ch = ch_begin; ch < ch_stop; ch += 2) {
       // step ch: buffer 1 <- chunk ch + 1 (set b), then set b <- chunk ch + 3
-      stage(rb, vb, 1);
-      fetch(ch + 3, rb, vb);
+      stage(rb, 1);
+      fetch(ch + 3, rb);
       __syncthreads();
       if (ch + 1 >= ch_stop) break;
       // step ch + 1: buffer 0 <- chunk ch + 2 (set a), then set a <- chunk ch + 4
-      stage(ra, va, 0);
-      fetch(ch + 4, ra, va);
+      stage(ra, 0);
+      fetch(ch + 4, ra);
       __syncthreads();
     }
     return;
@@ -2193,18 +2166,37 @@ __device__ __forceinline__ void chunk_state_wave_body(
   }
   int sc_e = 0;
   float sc_dn = 1.f, sc_up = 1.f;
+  // this wave's values of a chunk straight from memory, one chunk ahead: lane (lr, lg) takes
+  // rows 16 R + 4 lg .. + 3 of column lr (rows past the chunk read as zero)
+  uint2 vnx[NB];
+  auto load_vw = [&](int64_t chn) {
+    const bool ok = chn < ch_stop;
+    const int Lc = ok ? chunk_len(chn) : 0;
+    const uint32_t hdv = (uint32_t)(H * DV);
+    const auto rv = make_rsrc(v + ((size_t)(t_begin + (ok ? chn : 0) * C) * H + h) * DV + (vj0 >= 0 ? vj0 + 16 * wave : 0),
+                              (Lc > 0 && vj0 >= 0) ? (uint32_t)Lc * hdv * 2u : 0u);
+#pragma unroll
+    for (int R = 0; R < NB; ++R) {
+      uint32_t e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        e[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, (int)(((uint32_t)(16 * R + 4 * lg + i) * hdv + (uint32_t)lr) * 2u), 0, 0);
+      vnx[R] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+    }
+  };
+  load_vw(ch_begin);
   __syncthreads();  // buffer 0 holds the first chunk
   for (int64_t ch = ch_begin; ch < ch_stop; ++ch) {
     const int p = (int)((ch - ch_begin) & 1);
     const unsigned char* tile = smem + (p ? L::T1 : L::T0);
-    const uint16_t* vt = reinterpret_cast<const uint16_t*>(smem + (p ? L::V1 : L::V0));
     const int64_t c_begin = t_begin + ch * C;
     const int Lc = chunk_len(ch);
 
     // this chunk's values: rows 16 R + 4 lg .. + 3 of column lr (bf16 pairs)
     uint2 vv[NB];
 #pragma unroll
-    for (int R = 0; R < NB; ++R) vv[R] = *reinterpret_cast<const uint2*>(vt + (16 * wave + lr) * L::LDT + 16 * R + 4 * lg);
+    for (int R = 0; R < NB; ++R) vv[R] = vnx[R];
+    load_vw(ch + 1);
     // the A operands of the step's products, kAhead products ahead of their use
     half8 fb[kAhead];
     auto fetch = [&](auto kc) {
