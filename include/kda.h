@@ -163,7 +163,7 @@ kda_status kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* 
  * S_out = M S_in + B of every segment but the last is found in parallel (the
  * recurrence run on a dk x (dk + dv) state [I | 0] with values [0 | v]), the maps
  * are composed in fp32 from h0 in order, and every segment is then rerun from
- * its entering state (1M tokens at dk = dv = 128: 1 head 2.5 ms, 8 heads 13.0 ms
+ * its entering state (1M tokens at dk = dv = 128: 1 head 2.5 ms, 8 heads 13.3 ms
  * on MI355X, against 32-34 ms without segments).  Results equal kda_chunk_fwd's
  * up to rounding (the same operand precisions; the segmented form also rounds
  * each segment's map).
